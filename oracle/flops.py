@@ -1,0 +1,27 @@
+"""Executed-work accounting for a block mask (oracle; test infrastructure only).
+
+Each selected (query block i, key block j) pair costs two matrix products,
+Q_i K_j^T and P_ij V_j, of 2 * n_i * n_j * d flops each (n = valid tokens);
+softmax and exponentials are not counted, by the usual convention for
+attention kernels.  Dense attention over N tokens is 4 * N^2 * d per head, and
+causal attention counts the N(N+1)/2 allowed (query, key) pairs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .routing import block_sizes
+
+
+def executed_flops(mask, n_tokens: int, block: int, head_dim: int) -> int:
+    """4 * d * sum over selected pairs of n_i * n_j (exact integer)."""
+    mask = np.asarray(mask)
+    n = block_sizes(n_tokens, block).astype(np.int64)
+    pair = np.outer(n, n)                     # [nb, nb]
+    per_row = (mask.astype(np.int64) * pair).sum()
+    return int(4 * head_dim * per_row)
+
+
+def dense_flops(batch: int, heads: int, n_tokens: int, head_dim: int, causal: bool = False) -> int:
+    pairs = n_tokens * (n_tokens + 1) // 2 if causal else n_tokens * n_tokens
+    return int(4 * batch * heads * head_dim * pairs)

@@ -1,0 +1,163 @@
+"""Top-p block routing in float64 (oracle; test infrastructure only).
+
+Source: FVAttn review page, section 1 (Key Terms, "Top-p routing"): for each
+query block, key blocks are chosen by importance score until the cumulative
+probability reaches a threshold p; section 3 (Method) applies this routing
+before load balancing.  The page leaves the importance score undefined; the
+reading used here is the plainest one consistent with a "pool" router:
+
+  1. nb = ceil(N / block); block i holds tokens [i*block, min((i+1)*block, N)),
+     n_i of them (the last block may be short).
+  2. Qbar_i = mean of Q over the n_i valid tokens of block i; Kbar_j likewise.
+  3. Z_ij = scale * <Qbar_i, Kbar_j>, scale = 1/sqrt(d) unless given.
+  4. P_i. = softmax over j of Z_i. .
+  5. Rank j by P_ij descending, equal probabilities by smaller j first;
+     C_r = sum of the first r ranked probabilities (r = 1..nb).
+  6. k_i = smallest r with C_r >= p ("reaches p" read as inclusive); k_i = nb
+     when p >= 1 (dense attention is the p = 1 case) or when no r qualifies.
+  7. The first k_i ranked blocks are selected: mask M_ij = 1, the selected
+     indices listed in ascending order, row count k_i, head count sum_i k_i.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+def num_blocks(n_tokens: int, block: int) -> int:
+    return -(-n_tokens // block)
+
+
+def block_sizes(n_tokens: int, block: int) -> np.ndarray:
+    """n_i: number of valid tokens in each block (int64, length nb)."""
+    nb = num_blocks(n_tokens, block)
+    starts = np.arange(nb, dtype=np.int64) * block
+    return np.minimum(block, n_tokens - starts)
+
+
+def pool_blocks(x: np.ndarray, block: int) -> np.ndarray:
+    """Mean of x over the valid tokens of each block.
+
+    x: [B, H, N, d] float64  ->  [B, H, nb, d] float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, H, N, d = x.shape
+    nb = num_blocks(N, block)
+    out = np.empty((B, H, nb, d), dtype=np.float64)
+    for i in range(nb):
+        lo, hi = i * block, min(N, (i + 1) * block)
+        out[:, :, i, :] = x[:, :, lo:hi, :].sum(axis=2) / (hi - lo)
+    return out
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray, scale: float) -> np.ndarray:
+    """Z = scale * Qbar Kbar^T per (b, h): [B, H, nb, nb]."""
+    return scale * np.matmul(qbar, np.swapaxes(kbar, -1, -2))
+
+
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    """Softmax along the last axis, shifted by the row maximum."""
+    m = np.max(z, axis=-1, keepdims=True)
+    e = np.exp(z - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def top_p_select(prob: np.ndarray, top_p: float):
+    """Top-p selection on rows of block probabilities.
+
+    Returns (order, cum, row_cnt) where order[..., r] is the r-th ranked key
+    block (P descending, ties by smaller index), cum[..., r] the inclusive
+    cumulative probability of the first r+1 ranked blocks, and row_cnt the
+    number of selected blocks k_i.
+    """
+    prob = np.asarray(prob, dtype=np.float64)
+    nb = prob.shape[-1]
+    order = np.argsort(-prob, axis=-1, kind="stable")
+    ranked = np.take_along_axis(prob, order, axis=-1)
+    cum = np.cumsum(ranked, axis=-1)
+    if top_p >= 1.0:
+        row_cnt = np.full(prob.shape[:-1], nb, dtype=np.int64)
+    else:
+        reached = cum >= top_p
+        first = np.argmax(reached, axis=-1) + 1
+        row_cnt = np.where(np.any(reached, axis=-1), first, nb).astype(np.int64)
+    return order, cum, row_cnt
+
+
+@dataclasses.dataclass
+class RouteResult:
+    qbar: np.ndarray        # [B,H,nb,d] float64
+    kbar: np.ndarray        # [B,H,nb,d] float64
+    scores: np.ndarray      # [B,H,nb,nb] float64
+    prob: np.ndarray        # [B,H,nb,nb] float64
+    order: np.ndarray       # [B,H,nb,nb] int64, ranked key blocks
+    cum: np.ndarray         # [B,H,nb,nb] float64, inclusive cumulative probability
+    row_cnt: np.ndarray     # [B,H,nb] int64
+    mask: np.ndarray        # [B,H,nb,nb] uint8
+    row_idx: np.ndarray     # [B,H,nb,nb] int32, ascending selected indices, -1 after row_cnt
+    head_cnt: np.ndarray    # [B,H] int64
+    top_p: float
+
+
+def route(q: np.ndarray, k: np.ndarray, block: int, top_p: float, scale: float | None = None,
+          ) -> RouteResult:
+    """Full top-p routing of one batch. q, k: [B, H, N, d] (any float dtype, upcast to fp64)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    qbar = pool_blocks(q, block)
+    kbar = pool_blocks(k, block)
+    scores = block_scores(qbar, kbar, scale)
+    prob = softmax_rows(scores)
+    order, cum, row_cnt = top_p_select(prob, top_p)
+    nb = prob.shape[-1]
+    rank_pos = np.arange(nb)
+    selected_ranked = rank_pos[None, None, None, :] < row_cnt[..., None]
+    mask = np.zeros(prob.shape, dtype=np.uint8)
+    np.put_along_axis(mask, order, selected_ranked.astype(np.uint8), axis=-1)
+    row_idx = np.full(prob.shape, -1, dtype=np.int32)
+    B, H = prob.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                sel = np.nonzero(mask[b, h, i])[0]
+                row_idx[b, h, i, : sel.size] = sel
+    head_cnt = row_cnt.sum(axis=-1)
+    return RouteResult(qbar, kbar, scores, prob, order, cum, row_cnt, mask, row_idx,
+                       head_cnt, float(top_p))
+
+
+def ambiguous_blocks(res: RouteResult, window: float = 1e-5) -> np.ndarray:
+    """Blocks whose selection could flip under a perturbation of size `window`.
+
+    A selected block is ambiguous when its probability exceeds the first
+    unselected block's by at most `window`, and an unselected block when the
+    last selected block's probability exceeds its own by at most `window`
+    (the two could swap across the cut).  Any block is ambiguous when the
+    cumulative probability just before or at its rank lies within `window`
+    of p (the count k_i could shift by one).  With p >= 1 every block is
+    selected by rule and none is ambiguous.
+    """
+    prob, order, cum = res.prob, res.order, res.cum
+    shape = prob.shape
+    nb = shape[-1]
+    if res.top_p >= 1.0:
+        return np.zeros(shape, dtype=bool)
+    k = np.asarray(res.row_cnt)
+    ranked = np.take_along_axis(prob, order, axis=-1)
+    last_in = np.take_along_axis(ranked, (k - 1)[..., None], axis=-1)
+    first_out = np.take_along_axis(ranked, np.minimum(k, nb - 1)[..., None], axis=-1)
+    first_out = np.where((k < nb)[..., None], first_out, -np.inf)
+    excl = cum - ranked
+    near_cut_ranked = (np.abs(excl - res.top_p) <= window) | (np.abs(cum - res.top_p) <= window)
+    near_cut = np.zeros(shape, dtype=bool)
+    np.put_along_axis(near_cut, order, near_cut_ranked, axis=-1)
+    rank_of = np.empty_like(order)
+    np.put_along_axis(rank_of, order, np.broadcast_to(np.arange(nb), shape), axis=-1)
+    selected = rank_of < k[..., None]
+    swap_in = selected & (prob - first_out <= window)
+    swap_out = ~selected & (last_in - prob <= window)
+    return near_cut | swap_in | swap_out

@@ -1,0 +1,64 @@
+"""Work ordering and load balance model (oracle; test infrastructure only).
+
+Source: FVAttn review page, section 1 (Key Terms, "Runtime Load Balancing"):
+after the sparse mask is fixed, the real per-head workload is profiled and
+work is redistributed to shorten the critical path; section 2 (Motivation):
+predicted or history-based layouts fail because workloads shift between
+few-step inference steps; section 3 (Method & Key Results) reports the load
+imbalance factor.  On one GPU the workers are compute units and the work
+items are (batch, head, query-block) units whose cost is the number of
+selected key blocks.
+
+* work list: units sorted by cost descending, equal costs by unit id
+  ascending (a stable sort), unit id = (b*H + h)*nb + i.
+* greedy longest-processing-time (LPT): in work-list order, each unit goes to
+  the worker with the least load so far, ties to the lowest worker id.
+* "before": a contiguous static partition of the natural unit order, worker w
+  taking units [floor(w*U/W), floor((w+1)*U/W)) -- the analogue of each rank
+  owning a fixed group of whole heads.
+* load imbalance factor (LIF) = max worker load / mean worker load (the page
+  names the factor but prints no formula; max/mean is the reading taken).
+"""
+from __future__ import annotations
+
+import heapq
+
+import numpy as np
+
+
+def work_list(costs) -> np.ndarray:
+    """Unit ids sorted by (cost desc, id asc)."""
+    costs = np.asarray(costs).reshape(-1)
+    return np.argsort(-costs, kind="stable").astype(np.int64)
+
+
+def lpt_assign(costs, order, num_workers: int):
+    """Greedy LPT over `order`; returns (worker_of [U], worker_load [W])."""
+    costs = np.asarray(costs, dtype=np.int64).reshape(-1)
+    heap = [(0, w) for w in range(num_workers)]
+    heapq.heapify(heap)
+    worker_of = np.empty(costs.size, dtype=np.int64)
+    load = np.zeros(num_workers, dtype=np.int64)
+    for u in order:
+        l, w = heapq.heappop(heap)
+        worker_of[u] = w
+        load[w] = l + costs[u]
+        heapq.heappush(heap, (int(load[w]), w))
+    return worker_of, load
+
+
+def static_partition_loads(costs, num_workers: int) -> np.ndarray:
+    """Loads when worker w owns the contiguous natural-order slice of units."""
+    costs = np.asarray(costs, dtype=np.int64).reshape(-1)
+    U = costs.size
+    load = np.zeros(num_workers, dtype=np.int64)
+    for w in range(num_workers):
+        lo, hi = (w * U) // num_workers, ((w + 1) * U) // num_workers
+        load[w] = costs[lo:hi].sum()
+    return load
+
+
+def load_imbalance(loads) -> float:
+    loads = np.asarray(loads, dtype=np.float64)
+    mean = loads.mean()
+    return float(loads.max() / mean) if mean > 0 else 1.0

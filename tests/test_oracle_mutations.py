@@ -1,0 +1,115 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each one: a transposed operand, a wrong divisor, an exclusive threshold,
+a reversed tie rule, a dropped scale, an off-by-one causal mask, a wrong log
+base and a wrong sort direction."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as att
+import oracle.routing as rt
+import test_oracle_attention as ta
+import test_oracle_routing as tr
+
+
+def _patch(monkeypatch, module, name, fn):
+    monkeypatch.setattr(module, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+def test_transposed_scores_caught(monkeypatch, golden_dir):
+    orig = rt.block_scores
+    _patch(monkeypatch, rt, "block_scores", lambda q, k, s: orig(k, q, s))
+    with pytest.raises(AssertionError):
+        tr.test_pool_and_scores_hand_example(golden_dir)
+
+
+def test_pool_divisor_caught(monkeypatch):
+    def bad_pool(x, block):
+        x = np.asarray(x, dtype=np.float64)
+        B, H, N, d = x.shape
+        nb = rt.num_blocks(N, block)
+        out = np.empty((B, H, nb, d))
+        for i in range(nb):
+            out[:, :, i] = x[:, :, i * block:(i + 1) * block].sum(axis=2) / block
+        return out
+    _patch(monkeypatch, rt, "pool_blocks", bad_pool)
+    with pytest.raises(AssertionError):
+        tr.test_pool_constant_blocks_with_ragged_tail()
+
+
+def test_exclusive_threshold_caught(monkeypatch, golden_dir):
+    orig = rt.top_p_select
+
+    def strict(prob, p):
+        order, cum, cnt = orig(prob, p)
+        if p < 1:
+            reached = cum > p
+            cnt = np.where(reached.any(-1), np.argmax(reached, -1) + 1, prob.shape[-1])
+        return order, cum, cnt
+    _patch(monkeypatch, rt, "top_p_select", strict)
+    with pytest.raises(AssertionError):
+        tr.test_topp_golden_rows(golden_dir)
+
+
+def test_reversed_tie_rule_caught(monkeypatch):
+    def rev_ties(prob, p):
+        nb = prob.shape[-1]
+        flipped = prob[..., ::-1]
+        order = nb - 1 - np.argsort(-flipped, axis=-1, kind="stable")
+        ranked = np.take_along_axis(prob, order, -1)
+        cum = np.cumsum(ranked, -1)
+        reached = cum >= p
+        cnt = np.where(reached.any(-1), np.argmax(reached, -1) + 1, nb) if p < 1 else np.full(prob.shape[:-1], nb)
+        return order, cum, cnt
+    _patch(monkeypatch, rt, "top_p_select", rev_ties)
+    with pytest.raises(AssertionError):
+        tr.test_topp_uniform_scores_take_lowest_indices()
+
+
+def test_ascending_sort_caught(monkeypatch):
+    def ascending(prob, p):
+        nb = prob.shape[-1]
+        order = np.argsort(prob, axis=-1, kind="stable")
+        cum = np.cumsum(np.take_along_axis(prob, order, -1), -1)
+        reached = cum >= p
+        cnt = np.where(reached.any(-1), np.argmax(reached, -1) + 1, nb) if p < 1 else np.full(prob.shape[:-1], nb)
+        return order, cum, cnt
+    _patch(monkeypatch, rt, "top_p_select", ascending)
+    with pytest.raises(AssertionError):
+        tr.test_topp_brute_force_subsets(7, 0.5)
+
+
+def test_dropped_scale_caught(monkeypatch):
+    orig = att._attend_rows
+    monkeypatch.setattr(att, "_attend_rows", lambda qr, qp, k, v, keys, s, c: orig(qr, qp, k, v, keys, 1.0, c))
+    with pytest.raises(AssertionError):
+        ta.test_dense_matches_torch_sdpa_fp64((1, 2, 256, 64), 64, False)
+
+
+def test_causal_off_by_one_caught(monkeypatch):
+    def strict_causal(q_rows, q_pos, k_h, v_h, keys, scale, causal):
+        kk, vv = k_h[keys], v_h[keys]
+        logits = scale * (q_rows @ kk.T)
+        if causal:
+            logits = np.where(keys[None, :] < q_pos[:, None], logits, -np.inf)
+        mu = np.max(logits, axis=1, keepdims=True)
+        mu = np.where(np.isfinite(mu), mu, 0.0)
+        w = np.exp(logits - mu)
+        den = np.sum(w, axis=1, keepdims=True)
+        return (w @ vv) / den, mu[:, 0] + np.log(den[:, 0])
+    monkeypatch.setattr(att, "_attend_rows", strict_causal)
+    with pytest.raises(AssertionError):
+        ta.test_dense_matches_torch_sdpa_fp64((2, 3, 77, 16), 16, True)
+
+
+def test_wrong_log_base_caught(monkeypatch):
+    orig = att._attend_rows
+
+    def log2_lse(*a):
+        o, lse = orig(*a)
+        return o, lse / np.log(2.0)
+    monkeypatch.setattr(att, "_attend_rows", log2_lse)
+    with pytest.raises(AssertionError):
+        ta.test_dense_matches_torch_sdpa_fp64((1, 2, 256, 64), 64, False)
