@@ -1,0 +1,203 @@
+/*
+ * attn_tbs.h -- top-p block-sparse attention forward for AMD MI355X (gfx950).
+ *
+ * The path, in call order on one stream:
+ *
+ *   attn_route       block mean-pooling of Q and K, block scores, a softmax
+ *                    over key blocks and the top-p cut, giving a block mask,
+ *                    per-row index lists and per-row / per-head work counts.
+ *   attn_schedule    turns the per-row counts into a longest-first work list
+ *                    that a persistent kernel dequeues, so heavily loaded
+ *                    heads do not straggle.
+ *   attn_sparse_fwd  exact softmax attention of every query block over the
+ *                    tokens of its selected key blocks (tiled, online
+ *                    softmax, one kernel launch).
+ *   attn_dense_fwd   the same kernel over every key block (optionally
+ *                    causal): dense attention is the p = 1 case.
+ *
+ * Sources.  Top-p routing: FVAttn review page, section 1 (Key Terms, "Top-p
+ * routing") and section 3 (Method): per query block, key blocks are taken by
+ * importance until their cumulative probability reaches p.  Runtime load
+ * balancing: same page, section 1 ("Runtime Load Balancing") and section 2:
+ * the work is profiled after the mask is fixed and redistributed so no
+ * worker straggles.  Exact fused tiled attention: FlashAttention review page,
+ * Introduction (exact attention), Model (one fused GPU call; tiling of the
+ * matrix products and of the softmax) and Background [3] (S = QK^T,
+ * P = softmax(S), O = PV, with S and P never written to memory).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All pointers except `problem` are device pointers (HBM) unless stated.
+ *   The caller owns every buffer; the library allocates no memory and keeps
+ *   no state between calls other than cached device properties.
+ * - Tensors are contiguous, row-major.  q, k, v, o: [B, H, N, d], element
+ *   type `dtype` (bf16 or fp32), 16-byte aligned.  Block i of a sequence
+ *   covers tokens [i*block, min((i+1)*block, N)); nb = ceil(N / block); the
+ *   last block may hold fewer than `block` tokens.  Unit u = (b*H + h)*nb + i
+ *   names query block i of head h of batch b; U = B*H*nb units.
+ * - All work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *   stream) and the calls return before it completes.  No call synchronises
+ *   with the host; route -> schedule -> sparse_fwd on one stream need no
+ *   synchronisation because every count stays on the device.
+ * - Errors: arguments are validated on the host before any HIP call; a
+ *   failed validation enqueues nothing and returns ATTN_E_INVALID,
+ *   ATTN_E_UNSUPPORTED or ATTN_E_WORKSPACE.  ATTN_E_DEVICE reports a HIP
+ *   error at launch.  attn_last_error() then describes the failure (per
+ *   thread).  No C++ exception crosses this interface.
+ * - Results are bitwise reproducible for identical inputs: each unit is
+ *   computed by one workgroup in a fixed key order, whichever workgroup
+ *   takes it.
+ * - Calls that share one workspace must not overlap in time (for example on
+ *   two streams without ordering between them).
+ */
+#ifndef ATTN_TBS_H
+#define ATTN_TBS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_TBS_ABI_VERSION 1
+
+/* Status codes. */
+#define ATTN_OK            0
+#define ATTN_E_INVALID     1  /* bad dimension, pointer, alignment or top_p */
+#define ATTN_E_UNSUPPORTED 2  /* valid but unsupported combination (d, block, dtype, nb) */
+#define ATTN_E_WORKSPACE   3  /* workspace missing or smaller than attn_workspace_bytes() */
+#define ATTN_E_DEVICE      4  /* HIP error reported at launch */
+
+/* Element types of q, k, v and o. */
+#define ATTN_DTYPE_BF16 0
+#define ATTN_DTYPE_F32  1
+
+/* Operations, for attn_workspace_bytes() and attn_num_workers(). */
+#define ATTN_OP_ROUTE      0
+#define ATTN_OP_SCHEDULE   1
+#define ATTN_OP_SPARSE_FWD 2
+#define ATTN_OP_DENSE_FWD  3
+
+/* Problem flags. */
+#define ATTN_FLAG_PROFILE_WORKERS 1  /* fwd calls record per-worker start/end
+                                        times in the workspace (see below) */
+
+typedef struct attn_problem {
+  int32_t batch;     /* B >= 1 */
+  int32_t heads;     /* H >= 1 */
+  int32_t seq_len;   /* N >= 1 */
+  int32_t head_dim;  /* d: 64 or 128 */
+  int32_t block;     /* block size for routing and for query/key tiles: 64 or 128 */
+  int32_t dtype;     /* ATTN_DTYPE_BF16 or ATTN_DTYPE_F32 */
+  int32_t causal;    /* 0 or 1; honoured by attn_dense_fwd, must be 0 for routing */
+  int32_t flags;     /* ATTN_FLAG_* bits, 0 for none */
+  double scale;      /* softmax scale; 0 selects 1/sqrt(head_dim) */
+} attn_problem;
+
+/* ABI version of the loaded library (ATTN_TBS_ABI_VERSION when it was built). */
+int32_t attn_abi_version(void);
+
+/* Message for the last failed call on this thread ("" if none).  The string
+ * stays valid until the next call on the same thread. */
+const char* attn_last_error(void);
+
+/* Bytes of workspace `op` needs for `problem` (0 if the problem is invalid).
+ * Workspaces must be 16-byte aligned.  Its first 256 bytes are a control
+ * block (the persistent kernel's queue counters): they must be zero when
+ * attn_sparse_fwd or attn_dense_fwd starts.  A zero-filled workspace
+ * satisfies this, and attn_schedule and every fwd call leave them zero when
+ * they complete, so one zero fill at allocation is enough.  One workspace of
+ * the largest size serves all four operations. */
+size_t attn_workspace_bytes(const attn_problem* problem, int32_t op);
+
+/* Number of persistent workgroups ("workers") the fwd kernel of `op`
+ * launches on the current device for `problem` (0 if invalid).  With
+ * ATTN_FLAG_PROFILE_WORKERS, worker w writes two uint64 values at workspace
+ * byte offset 256 + 16*w: its first and last s_memrealtime stamp (100 MHz). */
+int32_t attn_num_workers(const attn_problem* problem, int32_t op);
+
+/* Top-p block routing.
+ *
+ * Per (b, h): Qbar_i = mean of q over the valid tokens of block i, Kbar_j
+ * likewise; Z_ij = scale * <Qbar_i, Kbar_j>; P_i. = softmax_j(Z_i.).  Key
+ * blocks are ranked by P descending, equal P by smaller index; row i keeps
+ * the shortest ranked prefix whose cumulative probability is >= top_p
+ * (all nb blocks when top_p >= 1).  Pooling, scores, softmax and the cut are
+ * evaluated in fp64, so the decisions are those of exact arithmetic up to
+ * fp64 rounding.
+ *
+ *   q, k      [B,H,N,d] dtype, read only.
+ *   top_p     in (0, 1].
+ *   mask      [B,H,nb,nb] uint8 out: 1 where key block j is selected for row i.
+ *   row_cnt   [B,H,nb] int32 out: k_i, number of selected key blocks (>= 1).
+ *   row_idx   [B,H,nb,nb] int32 out: the first row_cnt entries of each row are
+ *             the selected key blocks in ascending order; later entries are
+ *             not written.
+ *   head_cnt  [B,H] int32 out: sum over i of row_cnt (overwritten, not added to).
+ *   block_prob [B,H,nb,nb] double out, nullable: the block probabilities P.
+ *   ws        workspace of attn_workspace_bytes(problem, ATTN_OP_ROUTE) bytes.
+ * Requires causal == 0 and nb <= 1024. */
+int32_t attn_route(const attn_problem* problem, const void* q, const void* k, double top_p,
+                   uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
+                   double* block_prob, void* ws, size_t ws_bytes, void* stream);
+
+/* Longest-first work list.
+ *
+ * Unit u costs row_cnt[u] key blocks.  work_list[0..U) receives every unit id
+ * once, sorted by cost descending and, for equal costs, by id ascending.  The
+ * persistent fwd kernel takes units from this list in order, each workgroup
+ * taking the next one when it becomes free (dynamic longest-first list
+ * scheduling).  Also zeroes the workspace control block.
+ *
+ *   row_cnt      [U] int32 in, each in [0, nb].
+ *   num_workers  workers for the optional static model; 0 selects the number
+ *                of compute units of the current device.
+ *   work_list    [U] int32 out.
+ *   worker_of    [U] int32 out, nullable: greedy longest-processing-time
+ *                assignment in work-list order (each unit to the least-loaded
+ *                worker, ties to the lowest id).  Only computed when
+ *                worker_of or worker_load is given; it runs one wavefront and
+ *                is meant for reporting load balance, not for the hot path.
+ *   worker_load  [num_workers] int64 out, nullable: summed cost per worker
+ *                under that assignment.
+ * Requires nb <= 1024 and num_workers <= 4096. */
+int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32_t num_workers,
+                      int32_t* work_list, int32_t* worker_of, int64_t* worker_load,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Block-sparse attention forward, one persistent kernel launch.
+ *
+ * For each unit (b, h, i) and each query token t of block i, over the key
+ * tokens s of the key blocks row_idx[u][0..row_cnt[u]):
+ *   O_t = sum_s exp(l_s - mu) V_s / sum_s exp(l_s - mu),  l_s = scale*<Q_t, K_s>,
+ *   LSE_t = mu + ln sum_s exp(l_s - mu)   (natural log), mu = max_s l_s.
+ * Products in MFMA with fp32 accumulation (bf16 operands for bf16 inputs;
+ * softmax weights are rounded to bf16 before the P*V product), online
+ * softmax in fp32; o is written in dtype (bf16 round-to-nearest-even).
+ *
+ *   q, k, v    [B,H,N,d] dtype.
+ *   row_cnt    [U] int32, row_idx [U, nb] int32 as written by attn_route
+ *              (indices ascending and < nb; the library reads them as given).
+ *   work_list  [U] int32, nullable: processing order (from attn_schedule);
+ *              NULL processes units in natural order.
+ *   o          [B,H,N,d] dtype out.  A unit whose row_cnt is 0 gets o = 0.
+ *   lse        [B,H,N] float out, nullable (-inf for a unit with no keys).
+ *   ws         attn_workspace_bytes(problem, ATTN_OP_SPARSE_FWD) bytes, control
+ *              block zero on entry (see attn_workspace_bytes). */
+int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
+                        const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
+                        void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Dense attention forward (every key block; causal keeps keys s <= t).
+ * Same arithmetic, layouts and workspace rules as attn_sparse_fwd; with
+ * causal the query blocks with the most keys are processed first.  Equals
+ * attn_sparse_fwd with every block selected, bit for bit, when causal == 0. */
+int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
+                       void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_TBS_H */

@@ -1,0 +1,110 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, reports sizes, and rejects bad arguments with the documented
+status codes before any HIP call is made (no compute runs here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import top_block_sparse_pool_amd as tbs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_tbs.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tbs.LIB_PATH), reason="HIP library not built")
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: validation fails first
+WS = ctypes.c_void_p(0x20000)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(attn_[a-z_]+)\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = tbs.lib()
+    names = _declared_functions()
+    assert set(names) == {"attn_abi_version", "attn_last_error", "attn_workspace_bytes", "attn_num_workers",
+                          "attn_route", "attn_schedule", "attn_sparse_fwd", "attn_dense_fwd"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.attn_abi_version() == 1
+
+
+def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0):
+    return tbs.Problem(B, H, N, d, block, dtype, causal, flags, scale)
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(tbs.Problem) == 40
+    assert tbs.Problem.scale.offset == 32
+
+
+def test_workspace_sizes():
+    L = tbs.lib()
+    p = _problem()
+    nb = 512
+    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_ROUTE) == 256 + 2 * 8 * 40 * nb * 128
+    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_SCHEDULE) == 256
+    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_SPARSE_FWD) == 256
+    p.flags = tbs.FLAG_PROFILE_WORKERS
+    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_DENSE_FWD) == 256 + 16 * 4096
+    assert L.attn_workspace_bytes(ctypes.byref(p), 9) == 0
+    assert L.attn_workspace_bytes(None, 0) == 0
+
+
+def _route(p, top_p=0.9, q=FAKE, k=FAKE, ws=WS, ws_bytes=1 << 40, mask=FAKE, rc=FAKE, ri=FAKE, hc=FAKE):
+    return tbs.lib().attn_route(ctypes.byref(p) if p is not None else None, q, k, top_p, mask, rc, ri, hc,
+                                None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(H=-1), 1), (dict(N=0), 1), (dict(d=96), 2), (dict(d=0), 1), (dict(block=32), 2),
+    (dict(dtype=7), 1), (dict(causal=2), 1), (dict(causal=1), 2), (dict(flags=8), 1), (dict(scale=-1.0), 1),
+    (dict(scale=math.inf), 1), (dict(N=64 * 1025), 2),
+])
+def test_route_rejects_bad_problem(kw, code):
+    assert _route(_problem(**kw)) == code
+    assert tbs.lib().attn_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("top_p", [0.0, -0.5, 1.5, math.nan])
+def test_route_rejects_bad_top_p(top_p):
+    assert _route(_problem(), top_p=top_p) == 1
+
+
+def test_route_rejects_pointers_and_workspace():
+    p = _problem()
+    assert _route(None) == 1
+    assert _route(p, q=None) == 1
+    assert _route(p, k=ctypes.c_void_p(0x10008)) == 1        # not 16-byte aligned
+    assert _route(p, mask=None) == 1
+    assert _route(p, rc=ctypes.c_void_p(0x10002)) == 1
+    assert _route(p, ws=None) == 3
+    assert _route(p, ws_bytes=1000) == 3
+    assert _route(p, ws=ctypes.c_void_p(0x20008)) == 3
+    assert "workspace" in tbs.lib().attn_last_error().decode()
+
+
+def test_schedule_and_fwd_validation():
+    L = tbs.lib()
+    p = _problem()
+    assert L.attn_schedule(ctypes.byref(p), FAKE, -1, FAKE, None, None, WS, 1 << 20, None) == 1
+    assert L.attn_schedule(ctypes.byref(p), FAKE, 5000, FAKE, None, None, WS, 1 << 20, None) == 1
+    assert L.attn_schedule(ctypes.byref(p), None, 0, FAKE, None, None, WS, 1 << 20, None) == 1
+    assert L.attn_schedule(ctypes.byref(p), FAKE, 0, FAKE, None, None, WS, 100, None) == 3
+    assert L.attn_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, WS, 1 << 20,
+                             None) == 1
+    assert L.attn_sparse_fwd(ctypes.byref(p), FAKE, FAKE, ctypes.c_void_p(0x10004), FAKE, FAKE, None, FAKE,
+                             None, WS, 1 << 20, None) == 1
+    assert L.attn_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, WS, 16, None) == 3
+    pc = _problem(causal=1)
+    assert L.attn_sparse_fwd(ctypes.byref(pc), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, WS, 1 << 20,
+                             None) == 2
+    assert L.attn_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, WS, 1 << 20, None) == 1
+    assert L.attn_dense_fwd(ctypes.byref(_problem(d=80)), FAKE, FAKE, FAKE, FAKE, None, WS, 1 << 20, None) == 2
+    assert L.attn_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10001), WS, 1 << 20,
+                            None) == 1

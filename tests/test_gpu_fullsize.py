@@ -1,0 +1,65 @@
+"""GPU parity at the full named workload sizes, in the launch configuration the
+benchmark times (route -> schedule -> persistent sparse kernel on one stream).
+The whole block mask, index lists and work list are compared with the oracle;
+attention outputs are compared on a sample of query blocks (the heaviest, the
+lightest and random ones in every head), which the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import top_block_sparse_pool_amd as tbs
+from parity import compare_route, compare_units, oracle_route_per_head
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sample_units(row_cnt, rows_agree, per_head_random=1, seed=0):
+    rng = np.random.default_rng(seed)
+    B, H, nb = row_cnt.shape
+    units = []
+    for b in range(B):
+        for h in range(H):
+            c = row_cnt[b, h]
+            cand = {int(np.argmax(c)), int(np.argmin(c)), nb - 1}
+            cand |= {int(x) for x in rng.integers(0, nb, size=per_head_random)}
+            units += [(b, h, i) for i in sorted(cand) if rows_agree[b, h, i]]
+    return units
+
+
+@pytest.mark.parametrize("name", ["video-32k", "skewed-32k", "video-119k"])
+def test_full_size_sparse_workload(name):
+    w = WORKLOADS[name]
+    print(f"[case] {w.describe()}", flush=True)
+    q, k, v = [t.to(DEV) for t in make_inputs(w, 0)]
+    pr = tbs.make_problem(q, w.block)
+    ws = tbs.workspace(pr, DEV)
+    r = tbs.route(q, k, w.top_p, w.block, ws=ws)
+    wl = tbs.schedule(pr, r.row_cnt, ws)
+    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws)
+    torch.cuda.synchronize()
+    print("  gpu done; oracle routing", flush=True)
+    ref = oracle_route_per_head(q, k, w.block, w.top_p)
+    cmp = compare_route(r, ref)
+    costs = r.row_cnt.cpu().numpy()
+    assert (wl.cpu().numpy() == oracle.work_list(costs.reshape(-1))).all()
+    density = costs.sum() / (pr.units * pr.num_blocks)
+    print(f"  mask ok (ambiguous mismatches {cmp['ambiguous_mismatches']}), density {density:.3f}", flush=True)
+    units = _sample_units(costs, cmp["rows_agree"])
+    e, le = compare_units(o, lse, q, k, v, w.block, units, ref["mask"], q.dtype)
+    print(f"  {len(units)} sampled blocks: max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)
+
+
+def test_full_size_long_video_dense():
+    w = WORKLOADS["video-119k"]
+    print(f"[case] dense {w.describe()}", flush=True)
+    q, k, v = [t.to(DEV) for t in make_inputs(w, 0)]
+    o, lse = tbs.dense_fwd(q, k, v, w.block)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    units = [(0, h, int(i)) for h in range(0, w.heads, 4) for i in rng.integers(0, w.num_blocks, size=1)]
+    units.append((0, w.heads - 1, w.num_blocks - 1))
+    e, le = compare_units(o, lse, q, k, v, w.block, units, None, q.dtype)
+    print(f"  {len(units)} sampled blocks: max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)

@@ -1,0 +1,267 @@
+"""Top-p block-sparse attention forward for AMD MI355X (gfx950).
+
+Python binding over the C ABI of ``libattn_tbs.so`` (declared in
+``include/attn_tbs.h``).  This layer only marshals arguments: it takes torch
+tensors as device memory, passes their pointers and sizes together with the
+current HIP stream, and raises on a non-zero status.  Every step of the path
+-- pooling, scores, softmax, top-p cut, scheduling and attention -- runs in
+the library's HIP kernels; there is no CPU fallback, and calls fail loudly if
+the library has not been built.
+
+The four calls of the path (same names as the C ABI):
+    route(q, k, top_p, block)            -> Route (mask, row_cnt, row_idx, head_cnt)
+    schedule(problem, row_cnt)           -> work list (longest first)
+    sparse_fwd(q, k, v, route, ...)      -> (o, lse)
+    dense_fwd(q, k, v, block, causal)    -> (o, lse)
+and a convenience ``sparse_attention`` that runs all three sparse steps.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_tbs.so")
+
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_DEVICE = 0, 1, 2, 3, 4
+ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1
+OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD = 0, 1, 2, 3
+FLAG_PROFILE_WORKERS = 1
+CTRL_BYTES = 256
+
+_STATUS_NAMES = {1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_WORKSPACE", 4: "ATTN_E_DEVICE"}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+    ]
+
+    @property
+    def num_blocks(self) -> int:
+        return -(-self.seq_len // self.block)
+
+    @property
+    def units(self) -> int:
+        return self.batch * self.heads * self.num_blocks
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn_tbs.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run `python -c 'import __graft_entry__ as g; g.build()'`)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp, i32, sz, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
+    L.attn_abi_version.restype = i32
+    L.attn_abi_version.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_workspace_bytes.restype = sz
+    L.attn_workspace_bytes.argtypes = [P, i32]
+    L.attn_num_workers.restype = i32
+    L.attn_num_workers.argtypes = [P, i32]
+    L.attn_route.restype = i32
+    L.attn_route.argtypes = [P, vp, vp, dbl, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_schedule.restype = i32
+    L.attn_schedule.argtypes = [P, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.attn_sparse_fwd.restype = i32
+    L.attn_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_dense_fwd.restype = i32
+    L.attn_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, lib().attn_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if dt == torch.float32:
+        return ATTN_DTYPE_F32
+    raise ValueError(f"unsupported dtype {dt} (bfloat16 or float32)")
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live in GPU memory")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def make_problem(q: torch.Tensor, block: int, causal: bool = False, scale: Optional[float] = None,
+                 flags: int = 0) -> Problem:
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N, d], got shape {tuple(q.shape)}")
+    B, H, N, d = q.shape
+    return Problem(B, H, N, d, block, _dtype_code(q.dtype), int(bool(causal)), flags,
+                   0.0 if scale is None else float(scale))
+
+
+def workspace_bytes(problem: Problem, op: Optional[int] = None) -> int:
+    ops = [op] if op is not None else [OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD]
+    n = max(lib().attn_workspace_bytes(ctypes.byref(problem), o) for o in ops)
+    if n == 0:
+        _check(ATTN_E_INVALID)
+    return n
+
+
+def workspace(problem: Problem, device=None, op: Optional[int] = None) -> torch.Tensor:
+    """A zero-filled workspace large enough for `op` (default: every op)."""
+    return torch.zeros(workspace_bytes(problem, op), dtype=torch.uint8, device=device or "cuda")
+
+
+def num_workers(problem: Problem, op: int = OP_SPARSE_FWD) -> int:
+    return int(lib().attn_num_workers(ctypes.byref(problem), op))
+
+
+@dataclasses.dataclass
+class Route:
+    problem: Problem
+    top_p: float
+    mask: torch.Tensor       # [B,H,nb,nb] uint8
+    row_cnt: torch.Tensor    # [B,H,nb] int32
+    row_idx: torch.Tensor    # [B,H,nb,nb] int32 (prefix of row_cnt entries valid)
+    head_cnt: torch.Tensor   # [B,H] int32
+    block_prob: Optional[torch.Tensor] = None   # [B,H,nb,nb] float64
+
+
+def route(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: Optional[float] = None,
+          ws: Optional[torch.Tensor] = None, return_prob: bool = False, out: Optional[Route] = None) -> Route:
+    """attn_route: block pooling, scores, softmax and top-p cut (all on the GPU)."""
+    _require_device(q, k)
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must share shape and dtype")
+    pr = make_problem(q, block, scale=scale)
+    B, H, nb = pr.batch, pr.heads, pr.num_blocks
+    dev = q.device
+    if out is None:
+        out = Route(pr, float(top_p),
+                    torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev),
+                    torch.empty((B, H, nb), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
+                    torch.empty((B, H), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, nb, nb), dtype=torch.float64, device=dev) if return_prob else None)
+    out.problem, out.top_p = pr, float(top_p)
+    if ws is None:
+        ws = workspace(pr, dev, OP_ROUTE)
+    _check(lib().attn_route(ctypes.byref(pr), _ptr(q), _ptr(k), float(top_p), _ptr(out.mask), _ptr(out.row_cnt),
+                            _ptr(out.row_idx), _ptr(out.head_cnt), _ptr(out.block_prob), _ptr(ws),
+                            ws.numel(), _stream()))
+    return out
+
+
+def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, num_workers: int = 0,
+             lpt: bool = False, work_list: Optional[torch.Tensor] = None):
+    """attn_schedule: longest-first work list; with lpt=True also the greedy
+    LPT assignment (worker_of, worker_load) used to report load balance."""
+    _require_device(row_cnt, ws)
+    dev = row_cnt.device
+    U = problem.units
+    if work_list is None:
+        work_list = torch.empty(U, dtype=torch.int32, device=dev)
+    worker_of = worker_load = None
+    if lpt:
+        W = num_workers or torch.cuda.get_device_properties(dev).multi_processor_count
+        worker_of = torch.empty(U, dtype=torch.int32, device=dev)
+        worker_load = torch.empty(W, dtype=torch.int64, device=dev)
+    _check(lib().attn_schedule(ctypes.byref(problem), _ptr(row_cnt), int(num_workers), _ptr(work_list),
+                               _ptr(worker_of), _ptr(worker_load), _ptr(ws), ws.numel(), _stream()))
+    if lpt:
+        return work_list, worker_of, worker_load
+    return work_list
+
+
+def _out_tensors(q, o, lse, want_lse):
+    B, H, N, d = q.shape
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    return o, lse
+
+
+def sparse_fwd(q, k, v, row_cnt, row_idx, block: int, work_list=None, scale: Optional[float] = None,
+               ws: Optional[torch.Tensor] = None, o=None, lse=None, want_lse: bool = True, flags: int = 0):
+    """attn_sparse_fwd: attention of each query block over its selected key blocks."""
+    _require_device(q, k, v, row_cnt, row_idx, work_list)
+    pr = make_problem(q, block, scale=scale, flags=flags)
+    o, lse = _out_tensors(q, o, lse, want_lse)
+    if ws is None:
+        ws = workspace(pr, q.device, OP_SPARSE_FWD)
+    _check(lib().attn_sparse_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(row_cnt), _ptr(row_idx),
+                                 _ptr(work_list), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return o, lse
+
+
+def dense_fwd(q, k, v, block: int, causal: bool = False, scale: Optional[float] = None,
+              ws: Optional[torch.Tensor] = None, o=None, lse=None, want_lse: bool = True, flags: int = 0):
+    """attn_dense_fwd: dense (optionally causal) attention, the p = 1 case."""
+    _require_device(q, k, v)
+    pr = make_problem(q, block, causal=causal, scale=scale, flags=flags)
+    o, lse = _out_tensors(q, o, lse, want_lse)
+    if ws is None:
+        ws = workspace(pr, q.device, OP_DENSE_FWD)
+    _check(lib().attn_dense_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws),
+                                ws.numel(), _stream()))
+    return o, lse
+
+
+def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] = None,
+                     ws: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list)."""
+    pr = make_problem(q, block, scale=scale)
+    if ws is None:
+        ws = workspace(pr, q.device)
+    r = route(q, k, top_p, block, scale=scale, ws=ws)
+    wl = schedule(pr, r.row_cnt, ws)
+    o, lse = sparse_fwd(q, k, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
+                        want_lse=want_lse)
+    return o, lse, r, wl
+
+
+__all__ = [
+    "lib", "AttnError", "Problem", "Route", "make_problem", "workspace", "workspace_bytes", "num_workers",
+    "route", "schedule", "sparse_fwd", "dense_fwd", "sparse_attention", "LIB_PATH",
+]

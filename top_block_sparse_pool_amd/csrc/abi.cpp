@@ -1,0 +1,265 @@
+// C ABI of the top-p block-sparse attention library: argument validation,
+// workspace layout and dispatch to the HIP launchers.  Every argument is
+// checked before the first HIP call; failures return a status code and set
+// a per-thread message.  No exception crosses the interface.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/attn_tbs.h"
+#include "launch.h"
+
+#define TBS_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kProfileBytes = 16 * 4096;   // per-worker stamps, at most 4096 workers
+constexpr int kMaxRouteBlocks = 1024;
+
+// Validates the problem descriptor and resolves it into a Shape.
+int32_t check_problem(const attn_problem* pr, tbs::Shape* s) {
+  if (!pr) return fail(ATTN_E_INVALID, "problem is NULL");
+  if (pr->batch < 1 || pr->heads < 1 || pr->seq_len < 1)
+    return fail(ATTN_E_INVALID, "batch, heads and seq_len must be >= 1 (got %d, %d, %d)", pr->batch,
+                pr->heads, pr->seq_len);
+  if (pr->head_dim < 1 || pr->block < 1)
+    return fail(ATTN_E_INVALID, "head_dim and block must be >= 1 (got %d, %d)", pr->head_dim, pr->block);
+  if (pr->dtype != ATTN_DTYPE_BF16 && pr->dtype != ATTN_DTYPE_F32)
+    return fail(ATTN_E_INVALID, "dtype must be ATTN_DTYPE_BF16 or ATTN_DTYPE_F32 (got %d)", pr->dtype);
+  if (pr->causal != 0 && pr->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
+  if (pr->flags & ~ATTN_FLAG_PROFILE_WORKERS) return fail(ATTN_E_INVALID, "unknown flag bits 0x%x", pr->flags);
+  if (!(pr->scale >= 0.0) || !std::isfinite(pr->scale))
+    return fail(ATTN_E_INVALID, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
+  if (pr->head_dim != 64 && pr->head_dim != 128)
+    return fail(ATTN_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", pr->head_dim);
+  if (pr->block != 64 && pr->block != 128)
+    return fail(ATTN_E_UNSUPPORTED, "block %d unsupported (64 or 128)", pr->block);
+  const long long nb = (static_cast<long long>(pr->seq_len) + pr->block - 1) / pr->block;
+  const long long units = static_cast<long long>(pr->batch) * pr->heads * nb;
+  if (units > 0x3fffffffLL) return fail(ATTN_E_UNSUPPORTED, "batch*heads*blocks = %lld too large", units);
+  const long long elems = static_cast<long long>(pr->batch) * pr->heads * pr->seq_len * pr->head_dim;
+  if (elems > (1LL << 40)) return fail(ATTN_E_UNSUPPORTED, "tensor of %lld elements too large", elems);
+  s->B = pr->batch;
+  s->H = pr->heads;
+  s->N = pr->seq_len;
+  s->d = pr->head_dim;
+  s->block = pr->block;
+  s->nb = static_cast<int>(nb);
+  s->dtype = pr->dtype;
+  s->causal = pr->causal;
+  s->flags = pr->flags;
+  s->scale = pr->scale > 0.0 ? pr->scale : 1.0 / std::sqrt(static_cast<double>(pr->head_dim));
+  return ATTN_OK;
+}
+
+size_t route_bytes(const tbs::Shape& s) {
+  return tbs::kCtrlBytes + 2 * sizeof(double) * static_cast<size_t>(s.B) * s.H * s.nb * s.d;
+}
+
+size_t fwd_bytes(const tbs::Shape& s) {
+  return tbs::kCtrlBytes + ((s.flags & ATTN_FLAG_PROFILE_WORKERS) ? kProfileBytes : 0);
+}
+
+int32_t check_tensor(const void* p, const char* name) {
+  if (!p) return fail(ATTN_E_INVALID, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s is not 16-byte aligned", name);
+  return ATTN_OK;
+}
+
+int32_t check_i32(const void* p, const char* name, bool nullable) {
+  if (!p) return nullable ? ATTN_OK : fail(ATTN_E_INVALID, "%s is NULL", name);
+  if (!aligned(p, 4)) return fail(ATTN_E_INVALID, "%s is not 4-byte aligned", name);
+  return ATTN_OK;
+}
+
+int32_t check_ws(const void* ws, size_t have, size_t need) {
+  if (need == 0) return ATTN_OK;
+  if (!ws) return fail(ATTN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, 16)) return fail(ATTN_E_WORKSPACE, "workspace is not 16-byte aligned");
+  if (have < need) return fail(ATTN_E_WORKSPACE, "workspace holds %zu bytes, %zu needed", have, need);
+  return ATTN_OK;
+}
+
+int32_t device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+std::mutex g_cu_mutex;
+int g_cu_count[64] = {0};
+
+}  // namespace
+
+namespace tbs {
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 1;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
+}
+}  // namespace tbs
+
+TBS_EXPORT int32_t attn_abi_version(void) { return ATTN_TBS_ABI_VERSION; }
+
+TBS_EXPORT const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+TBS_EXPORT size_t attn_workspace_bytes(const attn_problem* problem, int32_t op) {
+  tbs::Shape s;
+  if (check_problem(problem, &s) != ATTN_OK) return 0;
+  switch (op) {
+    case ATTN_OP_ROUTE: return route_bytes(s);
+    case ATTN_OP_SCHEDULE: return tbs::kCtrlBytes;
+    case ATTN_OP_SPARSE_FWD:
+    case ATTN_OP_DENSE_FWD: return fwd_bytes(s);
+    default: fail(ATTN_E_INVALID, "unknown op %d", op); return 0;
+  }
+}
+
+TBS_EXPORT int32_t attn_num_workers(const attn_problem* problem, int32_t op) {
+  tbs::Shape s;
+  if (check_problem(problem, &s) != ATTN_OK) return 0;
+  if (op != ATTN_OP_SPARSE_FWD && op != ATTN_OP_DENSE_FWD) {
+    fail(ATTN_E_INVALID, "attn_num_workers: op must be a fwd op");
+    return 0;
+  }
+  const int mode = op == ATTN_OP_SPARSE_FWD ? tbs::kSparse : (s.causal ? tbs::kCausal : tbs::kDense);
+  return tbs::fwd_workers(s, mode);
+}
+
+TBS_EXPORT int32_t attn_route(const attn_problem* problem, const void* q, const void* k, double top_p,
+                              uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
+                              double* block_prob, void* ws, size_t ws_bytes, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if (s.causal) return fail(ATTN_E_UNSUPPORTED, "attn_route: causal routing is not supported");
+  if (s.nb > kMaxRouteBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_route: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
+  if (!(top_p > 0.0 && top_p <= 1.0)) return fail(ATTN_E_INVALID, "top_p must be in (0, 1] (got %g)", top_p);
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k"))) return st;
+  if (!mask) return fail(ATTN_E_INVALID, "mask is NULL");
+  if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(row_idx, "row_idx", false)) ||
+      (st = check_i32(head_cnt, "head_cnt", false)))
+    return st;
+  if (block_prob && !aligned(block_prob, 8)) return fail(ATTN_E_INVALID, "block_prob is not 8-byte aligned");
+  if ((st = check_ws(ws, ws_bytes, route_bytes(s)))) return st;
+
+  auto* base = static_cast<unsigned char*>(ws) + tbs::kCtrlBytes;
+  auto* qbar = reinterpret_cast<double*>(base);
+  auto* kbar_t = qbar + static_cast<size_t>(s.B) * s.H * s.nb * s.d;
+  auto strm = static_cast<hipStream_t>(stream);
+  hipError_t e = tbs::launch_pool(s, q, k, qbar, kbar_t, head_cnt, strm);
+  if (e != hipSuccess) return device_status(e, "attn_route pool launch");
+  e = tbs::launch_select(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, strm);
+  return device_status(e, "attn_route select launch");
+}
+
+TBS_EXPORT int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32_t num_workers,
+                                 int32_t* work_list, int32_t* worker_of, int64_t* worker_load, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if (s.nb > kMaxRouteBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_schedule: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
+  if (num_workers < 0 || num_workers > 4096)
+    return fail(ATTN_E_INVALID, "num_workers must be in [0, 4096] (got %d)", num_workers);
+  if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(work_list, "work_list", false)) ||
+      (st = check_i32(worker_of, "worker_of", true)))
+    return st;
+  if (worker_load && !aligned(worker_load, 8)) return fail(ATTN_E_INVALID, "worker_load is not 8-byte aligned");
+  if ((st = check_ws(ws, ws_bytes, tbs::kCtrlBytes))) return st;
+  auto strm = static_cast<hipStream_t>(stream);
+  hipError_t e = tbs::launch_schedule(s, row_cnt, work_list, static_cast<uint32_t*>(ws), strm);
+  if (e != hipSuccess) return device_status(e, "attn_schedule launch");
+  if (worker_of || worker_load) {
+    const int W = num_workers > 0 ? num_workers : tbs::device_cu_count();
+    if (W > 4096) return fail(ATTN_E_UNSUPPORTED, "attn_schedule: %d workers exceed 4096", W);
+    e = tbs::launch_lpt(s, row_cnt, work_list, W, worker_of, worker_load, strm);
+    if (e != hipSuccess) return device_status(e, "attn_schedule lpt launch");
+  }
+  return ok();
+}
+
+namespace {
+int32_t run_fwd(const tbs::Shape& s, int mode, const void* q, const void* k, const void* v,
+                const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list, void* o, float* lse,
+                void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(o, "o")))
+    return st;
+  if (lse && !aligned(lse, 4)) return fail(ATTN_E_INVALID, "lse is not 4-byte aligned");
+  if ((st = check_ws(ws, ws_bytes, fwd_bytes(s)))) return st;
+  tbs::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.row_cnt = row_cnt;
+  a.row_idx = row_idx;
+  a.work_list = work_list;
+  a.ctrl = static_cast<uint32_t*>(ws);
+  a.prof = (s.flags & ATTN_FLAG_PROFILE_WORKERS)
+               ? reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(ws) + tbs::kCtrlBytes)
+               : nullptr;
+  if (a.prof && tbs::fwd_workers(s, mode) > 4096)
+    return fail(ATTN_E_UNSUPPORTED, "worker profiling supports at most 4096 workers");
+  hipError_t e = tbs::launch_fwd(s, mode, a, static_cast<hipStream_t>(stream));
+  return device_status(e, "attention kernel launch");
+}
+}  // namespace
+
+TBS_EXPORT int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
+                                   const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
+                                   void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if (s.causal) return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd: causal must be 0");
+  if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(row_idx, "row_idx", false)) ||
+      (st = check_i32(work_list, "work_list", true)))
+    return st;
+  return run_fwd(s, tbs::kSparse, q, k, v, row_cnt, row_idx, work_list, o, lse, ws, ws_bytes, stream);
+}
+
+TBS_EXPORT int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  return run_fwd(s, s.causal ? tbs::kCausal : tbs::kDense, q, k, v, nullptr, nullptr, nullptr, o, lse, ws,
+                 ws_bytes, stream);
+}

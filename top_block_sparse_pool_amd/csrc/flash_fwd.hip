@@ -1,0 +1,544 @@
+// Persistent tiled attention forward with online softmax for gfx950.
+//
+// Source: FlashAttention review page, Model ("fuse O = Attn(Q,K,V) into one
+// GPU call"; tile the matrix products; tile the softmax because it works
+// row by row) and Tiling Softmax (compute the softmax block by block from
+// on-chip tiles and combine the partial results), Introduction (the result
+// is exact attention); FVAttn review page, section 1 ("Top-p routing": each
+// query block attends only to its selected key blocks).
+//
+// Work unit: one query block (block rows) of one (b, h).  Workgroups are
+// persistent: each takes the next unit from a queue (the longest-first work
+// list, or natural order) with one atomic, so a heavy unit never waits
+// behind a fixed grid assignment.
+//
+// bf16 kernel layout (per workgroup: block/32 waves, each owning 32 query rows):
+//   * Key tiles of 64 keys.  K and V tiles are copied HBM -> LDS with
+//     global_load_lds (16 bytes per lane, no VGPR staging), double-buffered:
+//     tile t+1 streams in while tile t is computed.  Rows are stored with an
+//     XOR swizzle of their 16-byte chunks so the MFMA operand reads below hit
+//     distinct LDS banks.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K (A operand) from LDS, Q^T
+//     (B operand) held in registers for the whole unit.  Computing S
+//     transposed puts one query per lane (lanes l and l^32 share it), so the
+//     running max and sum of the online softmax are lane-local plus one
+//     permlane32 swap.
+//   * A-operand rows of K are permuted (bits 2 and 3 of the row swapped) so
+//     each lane's 16 accumulator values are 2 runs of 8 consecutive keys:
+//     exactly the B operand (P^T) the next product needs, with no shuffle.
+//   * O^T += V^T P^T on the same MFMA: V^T (A operand) comes straight from the
+//     row-major V tile through ds_read_b64_tr_b16 transposed reads.
+//   * Online softmax in fp32 with exp2 (scale*log2 e folded in); the running
+//     maximum is only moved when it grows by more than 2^8 somewhere in the
+//     wave (the result is exact for any reference maximum; the bound keeps
+//     every weight <= 256).  Weights are rounded to bf16 for the P V product.
+//   * Epilogue: O / l in fp32 -> bf16 (round to nearest even), LSE = m + ln l.
+//
+// fp32 kernel: same unit/tile/queue structure and the same transposed
+// formulation on v_mfma_f32_32x32x2_f32, operands read from padded LDS
+// tiles; weights stay fp32.
+#include <math.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace tbs {
+namespace {
+
+constexpr int kKeyTile = 64;
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* row_cnt;
+  const int32_t* row_idx;
+  const int32_t* work_list;
+  uint32_t* ctrl;
+  unsigned long long* prof;
+  int BH;
+  int N;
+  int nb;
+  int U;
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+};
+
+// Unit bookkeeping shared by both kernels.
+template <int BQ, int MODE>
+struct UnitInfo {
+  int bh, i, ntiles;
+  const int32_t* list;
+
+  __device__ __forceinline__ void decode(const FwdParams& p, int qpos) {
+    int u;
+    if (MODE == kCausal) {
+      // Longest first: the last query blocks of every head have the most keys.
+      i = p.nb - 1 - qpos / p.BH;
+      bh = qpos % p.BH;
+      u = bh * p.nb + i;
+    } else {
+      u = qpos;
+      if (MODE == kSparse && p.work_list) u = min(max(p.work_list[qpos], 0), p.U - 1);
+      bh = u / p.nb;
+      i = u - bh * p.nb;
+    }
+    constexpr int SPB = BQ / kKeyTile;   // key tiles per block
+    if (MODE == kSparse) {
+      const int cnt = min(max(p.row_cnt[u], 0), p.nb);
+      list = p.row_idx + static_cast<long long>(u) * p.nb;
+      ntiles = cnt * SPB;
+      if (SPB > 1 && cnt > 0 && list[cnt - 1] >= p.nb - 1) {
+        const int tail = p.N - (p.nb - 1) * BQ;
+        ntiles = (cnt - 1) * SPB + (tail + kKeyTile - 1) / kKeyTile;
+      }
+    } else if (MODE == kDense) {
+      list = nullptr;
+      ntiles = (p.N + kKeyTile - 1) / kKeyTile;
+    } else {
+      list = nullptr;
+      ntiles = (min(p.N, (i + 1) * BQ) + kKeyTile - 1) / kKeyTile;
+    }
+  }
+
+  __device__ __forceinline__ int key0(const FwdParams& p, int t) const {
+    if (MODE == kSparse) {
+      constexpr int SPB = BQ / kKeyTile;
+      const int jb = min(max(list[t / SPB], 0), p.nb - 1);
+      return jb * BQ + (t % SPB) * kKeyTile;
+    }
+    return t * kKeyTile;
+  }
+};
+
+__device__ __forceinline__ int swap_bits23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// 16-byte-chunk XOR swizzle of an LDS tile row (see the operand reads).
+template <int D>
+__device__ __forceinline__ int chunk_swz(int row) {
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return ((row & 3) << 1) | ((row >> 3) & 1);
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_bf16(const unsigned char* kg, const unsigned char* vg, int key0,
+                                                int N, unsigned char* lds_k, unsigned char* lds_v,
+                                                int wave, int lane) {
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = kKeyTile * ROWB;
+  constexpr int PER_WAVE = TILEB / 1024 / NW;
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int blk = j * NW + wave;
+    const int byte = blk * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int pch = (byte % ROWB) / 16;
+    const int lch = pch ^ chunk_swz<D>(row);
+    const long long key = min(key0 + row, N - 1);
+    const long long goff = key * ROWB + lch * 16;
+    __builtin_amdgcn_global_load_lds(kg + goff, (TBS_LDS void*)(lds_k + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vg + goff, (TBS_LDS void*)(lds_v + blk * 1024), 16, 0, 0);
+  }
+}
+
+template <int D, int BQ, int MODE>
+__global__ __launch_bounds__(BQ * 2) void flash_fwd_bf16(FwdParams p) {
+  constexpr int NW = BQ / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = kKeyTile * ROWB;
+  constexpr int NS = D / 16;   // k-steps of S^T
+  constexpr int NO = D / 32;   // 32-dim tiles of O^T
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TILEB];
+  __shared__ int s_unit;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+  const float sl2 = p.scale_log2;
+
+  if (p.prof && tid == 0) p.prof[2 * blockIdx.x] = wall_clock64();
+
+  const unsigned char* qg_all = static_cast<const unsigned char*>(p.q);
+  const unsigned char* kg_all = static_cast<const unsigned char*>(p.k);
+  const unsigned char* vg_all = static_cast<const unsigned char*>(p.v);
+
+  for (;;) {
+    if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
+    __syncthreads();
+    const int qpos = s_unit;
+    __syncthreads();
+    if (qpos >= p.U) break;
+
+    UnitInfo<BQ, MODE> ui;
+    ui.decode(p, qpos);
+    const long long head_off = static_cast<long long>(ui.bh) * p.N * ROWB;
+    const unsigned char* kg = kg_all + head_off;
+    const unsigned char* vg = vg_all + head_off;
+    const int q0w = ui.i * BQ + wave * 32;
+    const int qrow = q0w + col;
+
+    // Q^T as B operand: lane (h, col) holds Q[qrow][16s + 8h .. +7].
+    bf16x8 qf[NS];
+    {
+      const unsigned char* qr = qg_all + head_off + static_cast<long long>(min(qrow, p.N - 1)) * ROWB;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + (16 * s + 8 * h) * 2);
+    }
+
+    f32x16 acc_o[NO];
+#pragma unroll
+    for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc_o[mo][e] = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    const int nt = ui.ntiles;
+    if (nt > 0) issue_tile_bf16<D, NW>(kg, vg, ui.key0(p, 0), p.N, smem, smem + TILEB, wave, lane);
+
+    for (int t = 0; t < nt; ++t) {
+      const int st = t & 1;
+      unsigned char* lk = smem + st * 2 * TILEB;
+      unsigned char* lv = lk + TILEB;
+      wait_vmem();
+      __syncthreads();
+      if (t + 1 < nt) {
+        unsigned char* nk = smem + (st ^ 1) * 2 * TILEB;
+        issue_tile_bf16<D, NW>(kg, vg, ui.key0(p, t + 1), p.N, nk, nk + TILEB, wave, lane);
+      }
+      const int key0 = ui.key0(p, t);
+
+      // S^T = K Q^T for 64 keys x 32 queries.
+      f32x16 sacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int row = swap_bits23(col) + 32 * mt;
+          const int pch = (2 * s + h) ^ chunk_swz<D>(row);
+          const bf16x8 a = *(const TBS_LDS bf16x8*)((TBS_LDS unsigned char*)lk + row * ROWB + pch * 16);
+          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[mt], 0, 0, 0);
+        }
+      }
+
+      // Mask keys past the sequence end (ragged tail) and, if causal, keys
+      // after the query.  Lane value e of tile mt is key 32mt + 16(e>>3) + 8h + (e&7).
+      const bool need_mask = (key0 + kKeyTile > p.N) || (MODE == kCausal && key0 + kKeyTile - 1 > q0w);
+      if (need_mask) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = key0 + 32 * mt + 16 * (e >> 3) + 8 * h + (e & 7);
+            const bool bad = key >= p.N || (MODE == kCausal && key > qrow);
+            if (bad) sacc[mt][e] = -INFINITY;
+          }
+      }
+
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const bool grow = (m_run == -INFINITY) ? (m_new != -INFINITY) : ((m_new - m_run) * sl2 > 8.f);
+      if (__any(grow)) {
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * sl2);
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc_o[mo][e] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float mb = (m_run == -INFINITY) ? 0.f : m_run * sl2;
+
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2, -mb));
+            l_run += pv;
+            pb[mt][t2][e] = static_cast<__bf16>(pv);
+          }
+
+      // O^T += V^T P^T.  Key step kk covers keys 16kk .. 16kk+15; lane (h, col)
+      // supplies P for keys 16kk + 8h + 0..7.  V^T comes from two transposed
+      // reads: 16-lane group g reads rows 16kk + 8h + 4hf + 0..3 and dims
+      // 32mo + 16(g&1) + 0..15.
+      const int g = lane >> 4;
+      const int ii = lane & 15;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 b = pb[kk >> 1][kk & 1];
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo) {
+          bf16x4 part[2];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int row = 16 * kk + 8 * h + 4 * hf + (ii >> 2);
+            const int dim = 32 * mo + 16 * (g & 1) + 4 * (ii & 3);
+            const int pch = (dim >> 3) ^ chunk_swz<D>(row);
+            const int off = row * ROWB + pch * 16 + (dim & 7) * 2;
+            part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)((TBS_LDS unsigned char*)lv + off));
+          }
+          const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[mo], 0, 0, 0);
+        }
+      }
+    }
+
+    // Epilogue: lane (h, col) holds O[qrow][32mo + 8j + 4h + r] in acc_o[mo][4j + r].
+    const float l_tot = l_run + xor32(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < p.N) {
+      unsigned short* orow = static_cast<unsigned short*>(p.o) +
+                             (static_cast<long long>(ui.bh) * p.N + qrow) * D;
+#pragma unroll
+      for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = static_cast<__bf16>(acc_o[mo][4 * j + r] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * mo + 8 * j + 4 * h) = ov;
+        }
+      if (h == 0 && p.lse)
+        p.lse[static_cast<long long>(ui.bh) * p.N + qrow] =
+            l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+    }
+  }
+
+  if (tid == 0) {
+    if (p.prof) p.prof[2 * blockIdx.x + 1] = wall_clock64();
+    // The last workgroup to finish leaves the queue counters at zero.
+    if (atomicAdd(p.ctrl + 1, 1u) == gridDim.x - 1) {
+      atomicExch(p.ctrl, 0u);
+      atomicExch(p.ctrl + 1, 0u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 ---
+
+template <int D, int BQ, int MODE>
+__global__ __launch_bounds__(BQ * 2) void flash_fwd_f32(FwdParams p) {
+  constexpr int NW = BQ / 32;
+  constexpr int NT = NW * 64;
+  constexpr int LD = D + 1;           // padded row stride (floats)
+  constexpr int NQ = D / 2;           // k-steps of S^T (2 dims each)
+  constexpr int NO = D / 32;
+  __shared__ float ks[kKeyTile * LD];
+  __shared__ float vs[kKeyTile * LD];
+  __shared__ int s_unit;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+  const float sl2 = p.scale_log2;
+  const float* qa = static_cast<const float*>(p.q);
+  const float* ka = static_cast<const float*>(p.k);
+  const float* va = static_cast<const float*>(p.v);
+
+  if (p.prof && tid == 0) p.prof[2 * blockIdx.x] = wall_clock64();
+
+  for (;;) {
+    if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
+    __syncthreads();
+    const int qpos = s_unit;
+    __syncthreads();
+    if (qpos >= p.U) break;
+
+    UnitInfo<BQ, MODE> ui;
+    ui.decode(p, qpos);
+    const long long head_off = static_cast<long long>(ui.bh) * p.N * D;
+    const int q0w = ui.i * BQ + wave * 32;
+    const int qrow = q0w + col;
+
+    float qf[NQ];   // lane (h, col): Q[qrow][2s + h]
+    {
+      const float* qr = qa + head_off + static_cast<long long>(min(qrow, p.N - 1)) * D;
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) qf[s] = qr[2 * s + h];
+    }
+    f32x16 acc_o[NO];
+#pragma unroll
+    for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc_o[mo][e] = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    for (int t = 0; t < ui.ntiles; ++t) {
+      const int key0 = ui.key0(p, t);
+      __syncthreads();
+      for (int x = tid; x < kKeyTile * D; x += NT) {
+        const int r = x / D, c = x % D;
+        const long long key = min(key0 + r, p.N - 1);
+        ks[r * LD + c] = ka[head_off + key * D + c];
+        vs[r * LD + c] = va[head_off + key * D + c];
+      }
+      __syncthreads();
+
+      f32x16 sacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int s = 0; s < NQ; ++s)
+          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[(32 * mt + col) * LD + 2 * s + h], qf[s],
+                                                          sacc[mt], 0, 0, 0);
+      // Lane value e of tile mt is key 32mt + 8(e>>2) + 4h + (e&3).
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = key0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (key >= p.N || (MODE == kCausal && key > qrow)) sacc[mt][e] = -INFINITY;
+        }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      if (m_new != m_run) {
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * sl2);
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc_o[mo][e] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float mb = (m_run == -INFINITY) ? 0.f : m_run * sl2;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pv = fast_exp2(fmaf(sacc[mt][e], sl2, -mb));
+          l_run += pv;
+          sacc[mt][e] = pv;
+        }
+      // O^T += V^T P^T, two keys per step: step (mt, e) pairs slot h with key
+      // 32mt + 8(e>>2) + 4h + (e&3), the key this lane's P value belongs to.
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kl = 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo)
+            acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[kl * LD + 32 * mo + col], sacc[mt][e],
+                                                             acc_o[mo], 0, 0, 0);
+        }
+    }
+
+    const float l_tot = l_run + xor32(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < p.N) {
+      float* orow = static_cast<float*>(p.o) + head_off + static_cast<long long>(qrow) * D;
+#pragma unroll
+      for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = acc_o[mo][4 * j + r] * inv;
+          *reinterpret_cast<f32x4*>(orow + 32 * mo + 8 * j + 4 * h) = ov;
+        }
+      if (h == 0 && p.lse)
+        p.lse[static_cast<long long>(ui.bh) * p.N + qrow] =
+            l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+    }
+  }
+
+  if (tid == 0) {
+    if (p.prof) p.prof[2 * blockIdx.x + 1] = wall_clock64();
+    if (atomicAdd(p.ctrl + 1, 1u) == gridDim.x - 1) {
+      atomicExch(p.ctrl, 0u);
+      atomicExch(p.ctrl + 1, 0u);
+    }
+  }
+}
+
+// ------------------------------------------------------------- dispatch ---
+
+typedef void (*KernelFn)(FwdParams);
+
+template <int D, int BQ>
+KernelFn pick_mode(int dtype, int mode) {
+  if (dtype == 0) {
+    if (mode == kSparse) return flash_fwd_bf16<D, BQ, kSparse>;
+    if (mode == kDense) return flash_fwd_bf16<D, BQ, kDense>;
+    return flash_fwd_bf16<D, BQ, kCausal>;
+  }
+  if (mode == kSparse) return flash_fwd_f32<D, BQ, kSparse>;
+  if (mode == kDense) return flash_fwd_f32<D, BQ, kDense>;
+  return flash_fwd_f32<D, BQ, kCausal>;
+}
+
+KernelFn pick_kernel(const Shape& s, int mode) {
+  if (s.d == 128) return s.block == 128 ? pick_mode<128, 128>(s.dtype, mode) : pick_mode<128, 64>(s.dtype, mode);
+  return s.block == 128 ? pick_mode<64, 128>(s.dtype, mode) : pick_mode<64, 64>(s.dtype, mode);
+}
+
+}  // namespace
+
+int fwd_workers(const Shape& s, int mode) {
+  KernelFn fn = pick_kernel(s, mode);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), s.block * 2, 0) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const long long want = static_cast<long long>(device_cu_count()) * per_cu;
+  const long long units = s.units();
+  return static_cast<int>(want < units ? want : units);
+}
+
+hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t stream) {
+  FwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.row_cnt = a.row_cnt;
+  p.row_idx = a.row_idx;
+  p.work_list = a.work_list;
+  p.ctrl = a.ctrl;
+  p.prof = reinterpret_cast<unsigned long long*>(a.prof);
+  p.BH = s.B * s.H;
+  p.N = s.N;
+  p.nb = s.nb;
+  p.U = static_cast<int>(s.units());
+  p.scale = static_cast<float>(s.scale);
+  p.scale_log2 = static_cast<float>(s.scale * 1.4426950408889634);
+  const int grid = fwd_workers(s, mode);
+  KernelFn fn = pick_kernel(s, mode);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(s.block * 2), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace tbs

@@ -1,0 +1,57 @@
+// Internal launchers behind the C ABI.  Host-side declarations only; every
+// launcher enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tbs {
+
+struct Shape {
+  int B, H, N, d, block, nb;
+  int dtype;      // 0 bf16, 1 f32
+  int causal;
+  int flags;
+  double scale;   // resolved (never 0)
+  long long units() const { return static_cast<long long>(B) * H * nb; }
+};
+
+enum FwdMode { kSparse = 0, kDense = 1, kCausal = 2 };
+
+// Control block at workspace offset 0 (bytes [0, 256)): queue counters.
+constexpr size_t kCtrlBytes = 256;
+
+// Router: block means (Qbar row-major [B,H,nb,d], Kbar transposed [B,H,d,nb]),
+// zeroes head_cnt; then scores, softmax, top-p cut and outputs.
+hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qbar, double* kbar_t,
+                       int32_t* head_cnt, hipStream_t stream);
+hipError_t launch_select(const Shape& s, const double* qbar, const double* kbar_t, double top_p,
+                         uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
+                         double* block_prob, hipStream_t stream);
+
+// Scheduler: longest-first work list; zeroes the control block.
+hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int32_t* work_list,
+                           uint32_t* ctrl, hipStream_t stream);
+hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* work_list,
+                      int num_workers, int32_t* worker_of, int64_t* worker_load, hipStream_t stream);
+
+// Attention forward.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* row_cnt;
+  const int32_t* row_idx;
+  const int32_t* work_list;
+  uint32_t* ctrl;
+  uint64_t* prof;
+};
+int fwd_workers(const Shape& s, int mode);
+hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace tbs

@@ -1,0 +1,177 @@
+// Longest-first work list for the persistent attention kernel (gfx950).
+//
+// Source: FVAttn review page, section 1 (Key Terms, "Runtime Load
+// Balancing"): once the sparse mask is fixed, the real per-head workload is
+// profiled and work is redistributed to shorten the critical path; section 2
+// (Motivation): predicted or history-based layouts fail because the load
+// changes between steps, so the order is rebuilt on every call.  On one GPU
+// the workers are the compute units and the work items are (b, h, query
+// block) units costing row_cnt key blocks; a persistent kernel that takes
+// units in longest-first order performs greedy list scheduling.
+//
+// schedule_kernel: one workgroup, a stable counting sort by cost descending.
+//   Each wave owns a contiguous slice of unit ids and counts costs into its
+//   own LDS histogram; a prefix over (cost descending, wave ascending) gives
+//   every (wave, cost) pair its first output slot; each wave then walks its
+//   slice in order, ranking equal costs inside a 64-unit batch with ballots
+//   over the 11 cost bits, so equal costs keep ascending unit ids.
+// lpt_kernel: optional single-wave greedy longest-processing-time model of
+//   the same order over W workers, for reporting load balance.
+#include "device_common.h"
+#include "launch.h"
+
+namespace tbs {
+namespace {
+
+constexpr int kSchedThreads = 512;
+constexpr int kSchedWaves = kSchedThreads / kWave;
+constexpr int kMaxCost = 1024;
+constexpr int kCostBits = 11;   // costs are in [0, 1024]
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ row_cnt,
+                                                                 int U, int nb,
+                                                                 int32_t* __restrict__ work_list,
+                                                                 uint32_t* __restrict__ ctrl) {
+  __shared__ int cnt[kSchedWaves][kMaxCost + 1];
+  __shared__ int ctot[kSchedThreads];
+  __shared__ int cexc[kSchedThreads];
+  __shared__ int wtot[kSchedWaves];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int ncost = nb + 1;   // cost values 0..nb
+
+  for (int x = tid; x < kSchedWaves * (kMaxCost + 1); x += kSchedThreads) (&cnt[0][0])[x] = 0;
+  __syncthreads();
+
+  const int chunk = (U + kSchedWaves - 1) / kSchedWaves;
+  const int ubeg = min(U, wave * chunk);
+  const int uend = min(U, ubeg + chunk);
+  for (int u = ubeg + lane; u < uend; u += kWave) {
+    const int c = min(max(row_cnt[u], 0), nb);
+    atomicAdd(&cnt[wave][c], 1);
+  }
+  __syncthreads();
+
+  // Position x = 0..ncost-1 enumerates costs in descending order (c = nb - x).
+  // Each thread owns a contiguous run of positions; exclusive prefix over runs.
+  const int per = (ncost + kSchedThreads - 1) / kSchedThreads;
+  const int xbeg = tid * per;
+  int run = 0;
+  for (int e = 0; e < per; ++e) {
+    const int x = xbeg + e;
+    if (x < ncost) {
+      const int c = nb - x;
+      for (int w = 0; w < kSchedWaves; ++w) run += cnt[w][c];
+    }
+  }
+  ctot[tid] = run;
+  __syncthreads();
+  {
+    int v = ctot[tid];
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) wtot[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wtot[w];
+    cexc[tid] = base + incl - v;
+  }
+  __syncthreads();
+  {
+    int off = cexc[tid];
+    for (int e = 0; e < per; ++e) {
+      const int x = xbeg + e;
+      if (x < ncost) {
+        const int c = nb - x;
+        for (int w = 0; w < kSchedWaves; ++w) {
+          const int t = cnt[w][c];
+          cnt[w][c] = off;
+          off += t;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // Stable placement: rank among equal costs inside each 64-unit batch.
+  const uint64_t lt = lanemask_lt();
+  for (int base = ubeg; base < uend; base += kWave) {
+    const int u = base + lane;
+    const bool valid = u < uend;
+    const int c = valid ? min(max(row_cnt[u], 0), nb) : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kCostBits; ++b) {
+      const bool bit = (c >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    int slot = 0;
+    if (valid) slot = cnt[wave][c];
+    if (valid) work_list[slot + __popcll(same & lt)] = u;
+    const bool last_of_group = valid && ((same >> lane) >> 1) == 0;
+    if (last_of_group) cnt[wave][c] = slot + __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (tid < static_cast<int>(kCtrlBytes / sizeof(uint32_t))) ctrl[tid] = 0u;
+}
+
+__global__ __launch_bounds__(kWave) void lpt_kernel(const int32_t* __restrict__ row_cnt,
+                                                    const int32_t* __restrict__ work_list, int U, int nb,
+                                                    int W, int32_t* __restrict__ worker_of,
+                                                    int64_t* __restrict__ worker_load) {
+  __shared__ long long load[4096];
+  const int lane = threadIdx.x;
+  for (int w = lane; w < W; w += kWave) load[w] = 0;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  for (int t = 0; t < U; ++t) {
+    const int u = min(max(work_list[t], 0), U - 1);
+    const int c = min(max(row_cnt[u], 0), nb);
+    long long best = 0x7fffffffffffffffLL;
+    int bid = 0x7fffffff;
+    for (int w = lane; w < W; w += kWave) {
+      const long long l = load[w];
+      if (l < best) { best = l; bid = w; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const long long ob = __shfl_xor(best, off, kWave);
+      const int oi = __shfl_xor(bid, off, kWave);
+      if (ob < best || (ob == best && oi < bid)) { best = ob; bid = oi; }
+    }
+    if (lane == 0) {
+      load[bid] = best + c;
+      if (worker_of) worker_of[u] = bid;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  }
+  if (worker_load)
+    for (int w = lane; w < W; w += kWave) worker_load[w] = load[w];
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int32_t* work_list, uint32_t* ctrl,
+                           hipStream_t stream) {
+  const int U = static_cast<int>(s.units());
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, row_cnt, U, s.nb,
+                     work_list, ctrl);
+  return hipGetLastError();
+}
+
+hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* work_list, int num_workers,
+                      int32_t* worker_of, int64_t* worker_load, hipStream_t stream) {
+  const int U = static_cast<int>(s.units());
+  hipLaunchKernelGGL(lpt_kernel, dim3(1), dim3(kWave), 0, stream, row_cnt, work_list, U, s.nb,
+                     num_workers, worker_of, worker_load);
+  return hipGetLastError();
+}
+
+}  // namespace tbs
