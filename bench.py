@@ -1,0 +1,233 @@
+"""Benchmark: top-p block-sparse attention forward on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+attn_route -> attn_schedule -> attn_sparse_fwd, enqueued on one stream.
+Inputs are resident in HBM before timing starts.  W untimed warm-up steps,
+then K timed steps between device synchronisations; HIP events on the same
+stream time each call.  Prints one JSON line.
+
+Default workload: video-32k (B=1, H=40, N=32760, d=128, bf16, block 64,
+top_p 0.9).  `value` is executed TFLOP/s of the whole step (executed FLOPs =
+4*d*sum over selected block pairs of n_i*n_j; softmax not counted); the
+roofline block reports the attention kernel alone against the bf16 MFMA
+peak.  The CPU baseline is the fp64 oracle timed on a bounded sample of the
+same workload on this machine's host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+METRIC = "executed TFLOP/s + ms/call, top-p sparse attn fwd, N=32760 H=40 d=128 bf16"
+
+
+def executed_flops(mask: np.ndarray, n_tokens: int, block: int, head_dim: int) -> int:
+    nb = mask.shape[-1]
+    n = np.minimum(block, n_tokens - np.arange(nb) * block).astype(np.int64)
+    per_row = mask.astype(np.int64) @ n            # [..., nb]: sum over selected j of n_j
+    return int(4 * head_dim * int((per_row * n).sum()))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="video-32k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense same-shape comparison")
+    ap.add_argument("--dense-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed):
+    """Time the fp64 oracle on a bounded sample: routing of one head and the
+    attention of randomly chosen query blocks of that head."""
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    h = 0
+    sl = (slice(0, 1), slice(h, h + 1))
+    q64, k64, v64 = (t[sl].cpu().to(torch.float64).numpy() for t in (q, k, v))
+    t0 = time.perf_counter()
+    r = oracle.route(q64, k64, w.block, w.top_p)
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(w.num_blocks)
+    done, flops, t_attn = 0, 0, 0.0
+    while done < len(order) and t_attn + t_route * (done / w.num_blocks) < target_s:
+        i = int(order[done])
+        t0 = time.perf_counter()
+        oracle.attend_units(q64, k64, v64, w.block, [(0, 0, i)], mask=r.mask)
+        t_attn += time.perf_counter() - t0
+        n = np.minimum(w.block, w.seq_len - np.arange(w.num_blocks) * w.block).astype(np.int64)
+        flops += int(4 * w.head_dim * n[i] * (r.mask[0, 0, i].astype(np.int64) @ n))
+        done += 1
+    t_total = t_attn + t_route * (done / w.num_blocks)
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on head 0 of {w.name}: routing of all {w.num_blocks} query blocks "
+                   f"({t_route:.2f} s, charged pro rata) + masked attention of {done} random query blocks "
+                   f"({t_attn:.2f} s); value = their executed FLOPs / charged time"),
+        "ms_per_query_block": 1e3 * t_total / max(done, 1),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by head across GPUs, which this build does not run)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import top_block_sparse_pool_amd as tbs
+    from workloads import get_workload, make_inputs
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    q, k, v = (t.to(dev) for t in make_inputs(w, args.seed))
+    gen_s = time.perf_counter() - t0
+    pr = tbs.make_problem(q, w.block)
+    ws = tbs.workspace(pr, dev)
+    B, H, nb, N, d = w.batch, w.heads, w.num_blocks, w.seq_len, w.head_dim
+    route_out = tbs.Route(pr, w.top_p,
+                          torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev),
+                          torch.empty((B, H, nb), dtype=torch.int32, device=dev),
+                          torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
+                          torch.empty((B, H), dtype=torch.int32, device=dev))
+    work_list = torch.empty(pr.units, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        tbs.route(q, k, w.top_p, w.block, ws=ws, out=route_out)
+        if ev is not None:
+            ev[1].record()
+        tbs.schedule(pr, route_out.row_cnt, ws, work_list=work_list)
+        if ev is not None:
+            ev[2].record()
+        tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, w.block, work_list=work_list, ws=ws,
+                       o=o, lse=lse)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_route = np.array([e[0].elapsed_time(e[1]) for e in events])
+    t_sched = np.array([e[1].elapsed_time(e[2]) for e in events])
+    t_fwd = np.array([e[2].elapsed_time(e[3]) for e in events])
+
+    mask = route_out.mask.cpu().numpy()
+    flops = executed_flops(mask, N, w.block, d)
+    dense_flops = 4 * B * H * N * N * d
+    density = float(mask.mean())
+    ms_step = 1e3 * wall / args.steps
+    value = flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = flops / (t_fwd.mean() * 1e-3) / 1e12
+
+    # load balance: static contiguous partition vs the longest-first LPT model over the CUs
+    row_cnt = route_out.row_cnt.cpu().numpy().reshape(-1).astype(np.int64)
+    wl, worker_of, worker_load = tbs.schedule(pr, route_out.row_cnt, ws, lpt=True)
+    torch.cuda.synchronize()
+    W = worker_load.numel()
+    static = np.array([row_cnt[(i * row_cnt.size) // W:((i + 1) * row_cnt.size) // W].sum() for i in range(W)])
+    lpt = worker_load.cpu().numpy()
+    lif = {"workers": int(W), "static_partition": float(static.max() / static.mean()),
+           "longest_first_lpt": float(lpt.max() / lpt.mean())}
+    # measured per-workgroup busy time of the persistent kernel
+    prp = tbs.make_problem(q, w.block, flags=tbs.FLAG_PROFILE_WORKERS)
+    wsp = tbs.workspace(prp, dev)
+    tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, w.block, work_list=work_list, ws=wsp, o=o,
+                   lse=lse, flags=tbs.FLAG_PROFILE_WORKERS)
+    torch.cuda.synchronize()
+    nw = tbs.num_workers(prp, tbs.OP_SPARSE_FWD)
+    stamps = wsp[256:256 + 16 * nw].view(torch.int64).view(nw, 2).cpu().numpy()
+    busy = (stamps[:, 1] - stamps[:, 0]).astype(np.float64)
+    lif["measured_workgroups"] = int(nw)
+    lif["measured_busy_max_over_mean"] = float(busy.max() / busy.mean())
+
+    dense = None
+    if not args.no_dense:
+        od = torch.empty_like(q)
+        tbs.dense_fwd(q, k, v, w.block, ws=ws, o=od, want_lse=False)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.dense_reps):
+            tbs.dense_fwd(q, k, v, w.block, ws=ws, o=od, want_lse=False)
+        e1.record()
+        torch.cuda.synchronize()
+        t_dense = e0.elapsed_time(e1) / args.dense_reps
+        dense = {"ms_per_call": t_dense, "tflops": dense_flops / (t_dense * 1e-3) / 1e12,
+                 "speedup_sparse_total_vs_dense": t_dense / ms_step,
+                 "speedup_sparse_fwd_vs_dense": t_dense / float(t_fwd.mean())}
+        del od
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d, "block": w.block,
+                   "top_p": w.top_p, "density": density, "executed_tflop_per_step": flops / 1e12,
+                   "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
+        "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
+                         "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),
+                         "sparse_fwd_mean": float(t_fwd.mean()), "sparse_fwd_median": float(np.median(t_fwd))},
+        "sparse_fwd_tflops": fwd_tflops,
+        "roofline": {"bound": "mfma", "kernel": "flash_fwd_bf16 (sparse)", "achieved": fwd_tflops,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": fwd_tflops / BF16_PEAK_TFLOPS,
+                     "traffic": None},
+        "dense_same_shape": dense,
+        "load_imbalance": lif,
+        "cpu_baseline": cpu,
+        "input_generation_s": gen_s,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
