@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="video-32k")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--head-window", type=int, default=None, help="heads per scheduling window (default: library's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense same-shape comparison")
@@ -103,6 +104,7 @@ def main():
     from workloads import get_workload, make_inputs
 
     w = get_workload(args.workload)
+    hw = tbs.DEFAULT_HEAD_WINDOW if args.head_window is None else args.head_window
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
@@ -126,7 +128,7 @@ def main():
         tbs.route(q, k, w.top_p, w.block, ws=ws, out=route_out)
         if ev is not None:
             ev[1].record()
-        tbs.schedule(pr, route_out.row_cnt, ws, work_list=work_list)
+        tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         if ev is not None:
             ev[2].record()
         tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, w.block, work_list=work_list, ws=ws,
@@ -158,7 +160,7 @@ def main():
 
     # load balance: static contiguous partition vs the longest-first LPT model over the CUs
     row_cnt = route_out.row_cnt.cpu().numpy().reshape(-1).astype(np.int64)
-    wl, worker_of, worker_load = tbs.schedule(pr, route_out.row_cnt, ws, lpt=True)
+    wl, worker_of, worker_load = tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True)
     torch.cuda.synchronize()
     W = worker_load.numel()
     static = np.array([row_cnt[(i * row_cnt.size) // W:((i + 1) * row_cnt.size) // W].sum() for i in range(W)])
@@ -212,7 +214,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d, "block": w.block,
-                   "top_p": w.top_p, "density": density, "executed_tflop_per_step": flops / 1e12,
+                   "top_p": w.top_p, "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
                    "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
         "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
                          "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),

@@ -142,15 +142,21 @@ int32_t attn_route(const attn_problem* problem, const void* q, const void* k, do
                    uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                    double* block_prob, void* ws, size_t ws_bytes, void* stream);
 
-/* Longest-first work list.
+/* Longest-first work list, in head windows.
  *
- * Unit u costs row_cnt[u] key blocks.  work_list[0..U) receives every unit id
- * once, sorted by cost descending and, for equal costs, by id ascending.  The
- * persistent fwd kernel takes units from this list in order, each workgroup
- * taking the next one when it becomes free (dynamic longest-first list
- * scheduling).  Also zeroes the workspace control block.
+ * Unit u costs row_cnt[u] key blocks.  The (b, h) pairs are cut into windows
+ * of `head_window` consecutive pairs (window of unit u = (u / nb) / head_window);
+ * work_list[0..U) receives every unit id once, sorted by window ascending,
+ * then cost descending, then id ascending.  The persistent fwd kernel takes
+ * units from this list in order, each workgroup taking the next one when it
+ * becomes free (dynamic list scheduling): longest-first keeps heavy query
+ * blocks from straggling at the end, and the windows keep the query blocks
+ * that run at the same time on the K/V of a few heads, so that K/V is read
+ * from cache instead of HBM.  head_window = 0 (or >= B*H) gives one window:
+ * a pure longest-first list.  Also zeroes the workspace control block.
  *
  *   row_cnt      [U] int32 in, each in [0, nb].
+ *   head_window  >= 0, see above.
  *   num_workers  workers for the optional static model; 0 selects the number
  *                of compute units of the current device.
  *   work_list    [U] int32 out.
@@ -162,8 +168,8 @@ int32_t attn_route(const attn_problem* problem, const void* q, const void* k, do
  *   worker_load  [num_workers] int64 out, nullable: summed cost per worker
  *                under that assignment.
  * Requires nb <= 1024 and num_workers <= 4096. */
-int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32_t num_workers,
-                      int32_t* work_list, int32_t* worker_of, int64_t* worker_load,
+int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32_t head_window,
+                      int32_t num_workers, int32_t* work_list, int32_t* worker_of, int64_t* worker_load,
                       void* ws, size_t ws_bytes, void* stream);
 
 /* Block-sparse attention forward, one persistent kernel launch.

@@ -10,7 +10,11 @@ items are (batch, head, query-block) units whose cost is the number of
 selected key blocks.
 
 * work list: units sorted by cost descending, equal costs by unit id
-  ascending (a stable sort), unit id = (b*H + h)*nb + i.
+  ascending (a stable sort), unit id = (b*H + h)*nb + i.  The list may be
+  cut into windows of consecutive unit ids (whole heads): then it runs window
+  by window, longest first inside each window.  The windows are not from the
+  pages; they are this implementation's way of keeping the query blocks that
+  run together on the K/V of a few heads.
 * greedy longest-processing-time (LPT): in work-list order, each unit goes to
   the worker with the least load so far, ties to the lowest worker id.
 * "before": a contiguous static partition of the natural unit order, worker w
@@ -26,10 +30,18 @@ import heapq
 import numpy as np
 
 
-def work_list(costs) -> np.ndarray:
-    """Unit ids sorted by (cost desc, id asc)."""
+def work_list(costs, window_units: int | None = None) -> np.ndarray:
+    """Unit ids sorted by (window asc, cost desc, id asc); window = id // window_units
+    (None or 0: a single window)."""
     costs = np.asarray(costs).reshape(-1)
-    return np.argsort(-costs, kind="stable").astype(np.int64)
+    U = costs.size
+    if not window_units or window_units >= U:
+        return np.argsort(-costs, kind="stable").astype(np.int64)
+    parts = []
+    for lo in range(0, U, window_units):
+        hi = min(U, lo + window_units)
+        parts.append(lo + np.argsort(-costs[lo:hi], kind="stable"))
+    return np.concatenate(parts).astype(np.int64)
 
 
 def lpt_assign(costs, order, num_workers: int):

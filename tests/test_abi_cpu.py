@@ -92,10 +92,11 @@ def test_route_rejects_pointers_and_workspace():
 def test_schedule_and_fwd_validation():
     L = tbs.lib()
     p = _problem()
-    assert L.attn_schedule(ctypes.byref(p), FAKE, -1, FAKE, None, None, WS, 1 << 20, None) == 1
-    assert L.attn_schedule(ctypes.byref(p), FAKE, 5000, FAKE, None, None, WS, 1 << 20, None) == 1
-    assert L.attn_schedule(ctypes.byref(p), None, 0, FAKE, None, None, WS, 1 << 20, None) == 1
-    assert L.attn_schedule(ctypes.byref(p), FAKE, 0, FAKE, None, None, WS, 100, None) == 3
+    assert L.attn_schedule(ctypes.byref(p), FAKE, 4, -1, FAKE, None, None, WS, 1 << 20, None) == 1
+    assert L.attn_schedule(ctypes.byref(p), FAKE, 4, 5000, FAKE, None, None, WS, 1 << 20, None) == 1
+    assert L.attn_schedule(ctypes.byref(p), FAKE, -1, 0, FAKE, None, None, WS, 1 << 20, None) == 1
+    assert L.attn_schedule(ctypes.byref(p), None, 4, 0, FAKE, None, None, WS, 1 << 20, None) == 1
+    assert L.attn_schedule(ctypes.byref(p), FAKE, 4, 0, FAKE, None, None, WS, 100, None) == 3
     assert L.attn_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, WS, 1 << 20,
                              None) == 1
     assert L.attn_sparse_fwd(ctypes.byref(p), FAKE, FAKE, ctypes.c_void_p(0x10004), FAKE, FAKE, None, FAKE,

@@ -32,7 +32,7 @@ def _run_sparse(w, q, k, v):
     pr = tbs.make_problem(q, w.block)
     ws = tbs.workspace(pr, DEV)
     r = tbs.route(q, k, w.top_p, w.block, ws=ws)
-    wl, worker_of, worker_load = tbs.schedule(pr, r.row_cnt, ws, lpt=True)
+    wl, worker_of, worker_load = tbs.schedule(pr, r.row_cnt, ws, head_window=w.heads // 2 or 1, lpt=True)
     o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws)
     torch.cuda.synchronize()
     return pr, ws, r, (wl, worker_of, worker_load), o, lse
@@ -60,7 +60,7 @@ def test_sparse_path_matches_oracle(w):
     print(f"  ambiguous mismatches: {cmp['ambiguous_mismatches']}", flush=True)
     # scheduler: exact work list and LPT model
     costs = r.row_cnt.cpu().numpy().reshape(-1)
-    want_wl = oracle.work_list(costs)
+    want_wl = oracle.work_list(costs, (w.heads // 2 or 1) * pr.num_blocks)
     assert (wl.cpu().numpy() == want_wl).all()
     W = worker_load.numel()
     want_of, want_load = oracle.lpt_assign(costs, want_wl, W)
@@ -78,6 +78,23 @@ def test_sparse_path_matches_oracle(w):
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
     assert torch.equal(o, o3) and torch.equal(lse, lse3)
+
+
+@pytest.mark.parametrize("head_window", [0, 1, 3, 100])
+def test_schedule_windows_match_oracle(head_window):
+    w = custom_workload(2, 5, 2000, 128, 64, "bf16", 0.9, wid=215)
+    q, k, v = _inputs(w)
+    pr = tbs.make_problem(q, w.block)
+    ws = tbs.workspace(pr, DEV)
+    r = tbs.route(q, k, w.top_p, w.block, ws=ws)
+    wl, worker_of, worker_load = tbs.schedule(pr, r.row_cnt, ws, head_window=head_window, num_workers=7, lpt=True)
+    torch.cuda.synchronize()
+    costs = r.row_cnt.cpu().numpy().reshape(-1)
+    want = oracle.work_list(costs, head_window * pr.num_blocks)
+    assert (wl.cpu().numpy() == want).all()
+    want_of, want_load = oracle.lpt_assign(costs, want, 7)
+    assert (worker_of.cpu().numpy() == want_of).all() and (worker_load.cpu().numpy() == want_load).all()
+    assert (ws[:256] == 0).all()
 
 
 def test_tiny_fp32_workload_and_p1_equals_dense():

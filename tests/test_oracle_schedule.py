@@ -13,6 +13,14 @@ def test_work_list_hand_example():
     assert oracle.work_list(costs).tolist() == [1, 3, 0, 4, 5, 2]
 
 
+def test_work_list_windows_hand_example():
+    costs = np.array([3, 5, 1, 5, 3, 2, 9, 0])
+    # windows of 3 units: [3,5,1] -> 1,0,2 ; [5,3,2] -> 3,4,5 ; [9,0] -> 6,7
+    assert oracle.work_list(costs, 3).tolist() == [1, 0, 2, 3, 4, 5, 6, 7]
+    assert oracle.work_list(costs, 0).tolist() == oracle.work_list(costs).tolist()
+    assert oracle.work_list(costs, 100).tolist() == oracle.work_list(costs).tolist()
+
+
 def test_work_list_is_sorted_permutation():
     rng = np.random.default_rng(0)
     costs = rng.integers(0, 40, size=5000)

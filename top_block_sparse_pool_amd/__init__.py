@@ -33,6 +33,7 @@ ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1
 OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD = 0, 1, 2, 3
 FLAG_PROFILE_WORKERS = 1
 CTRL_BYTES = 256
+DEFAULT_HEAD_WINDOW = 4
 
 _STATUS_NAMES = {1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_WORKSPACE", 4: "ATTN_E_DEVICE"}
 
@@ -90,7 +91,7 @@ def lib() -> ctypes.CDLL:
     L.attn_route.restype = i32
     L.attn_route.argtypes = [P, vp, vp, dbl, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_schedule.restype = i32
-    L.attn_schedule.argtypes = [P, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.attn_schedule.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     L.attn_sparse_fwd.restype = i32
     L.attn_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_dense_fwd.restype = i32
@@ -192,10 +193,11 @@ def route(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: Opt
     return out
 
 
-def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, num_workers: int = 0,
-             lpt: bool = False, work_list: Optional[torch.Tensor] = None):
-    """attn_schedule: longest-first work list; with lpt=True also the greedy
-    LPT assignment (worker_of, worker_load) used to report load balance."""
+def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, head_window: int = DEFAULT_HEAD_WINDOW,
+             num_workers: int = 0, lpt: bool = False, work_list: Optional[torch.Tensor] = None):
+    """attn_schedule: longest-first work list inside windows of `head_window`
+    heads (0: one window); with lpt=True also the greedy LPT assignment
+    (worker_of, worker_load) used to report load balance."""
     _require_device(row_cnt, ws)
     dev = row_cnt.device
     U = problem.units
@@ -206,7 +208,8 @@ def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, num_work
         W = num_workers or torch.cuda.get_device_properties(dev).multi_processor_count
         worker_of = torch.empty(U, dtype=torch.int32, device=dev)
         worker_load = torch.empty(W, dtype=torch.int64, device=dev)
-    _check(lib().attn_schedule(ctypes.byref(problem), _ptr(row_cnt), int(num_workers), _ptr(work_list),
+    _check(lib().attn_schedule(ctypes.byref(problem), _ptr(row_cnt), int(head_window), int(num_workers),
+                               _ptr(work_list),
                                _ptr(worker_of), _ptr(worker_load), _ptr(ws), ws.numel(), _stream()))
     if lpt:
         return work_list, worker_of, worker_load
@@ -249,13 +252,14 @@ def dense_fwd(q, k, v, block: int, causal: bool = False, scale: Optional[float] 
 
 
 def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] = None,
-                     ws: Optional[torch.Tensor] = None, want_lse: bool = True):
+                     ws: Optional[torch.Tensor] = None, want_lse: bool = True,
+                     head_window: int = DEFAULT_HEAD_WINDOW):
     """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list)."""
     pr = make_problem(q, block, scale=scale)
     if ws is None:
         ws = workspace(pr, q.device)
     r = route(q, k, top_p, block, scale=scale, ws=ws)
-    wl = schedule(pr, r.row_cnt, ws)
+    wl = schedule(pr, r.row_cnt, ws, head_window=head_window)
     o, lse = sparse_fwd(q, k, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
                         want_lse=want_lse)
     return o, lse, r, wl

@@ -21,6 +21,9 @@ COMMON = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
     # Packed fp32 VALU ops are kept out of all generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the online softmax rescales them with VALU
+    # ops, and AGPR accumulators would be copied back and forth every tile.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

@@ -185,14 +185,15 @@ TBS_EXPORT int32_t attn_route(const attn_problem* problem, const void* q, const 
   return device_status(e, "attn_route select launch");
 }
 
-TBS_EXPORT int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32_t num_workers,
-                                 int32_t* work_list, int32_t* worker_of, int64_t* worker_load, void* ws,
-                                 size_t ws_bytes, void* stream) {
+TBS_EXPORT int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32_t head_window,
+                                 int32_t num_workers, int32_t* work_list, int32_t* worker_of,
+                                 int64_t* worker_load, void* ws, size_t ws_bytes, void* stream) {
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
   if (s.nb > kMaxRouteBlocks)
     return fail(ATTN_E_UNSUPPORTED, "attn_schedule: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
+  if (head_window < 0) return fail(ATTN_E_INVALID, "head_window must be >= 0 (got %d)", head_window);
   if (num_workers < 0 || num_workers > 4096)
     return fail(ATTN_E_INVALID, "num_workers must be in [0, 4096] (got %d)", num_workers);
   if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(work_list, "work_list", false)) ||
@@ -201,7 +202,7 @@ TBS_EXPORT int32_t attn_schedule(const attn_problem* problem, const int32_t* row
   if (worker_load && !aligned(worker_load, 8)) return fail(ATTN_E_INVALID, "worker_load is not 8-byte aligned");
   if ((st = check_ws(ws, ws_bytes, tbs::kCtrlBytes))) return st;
   auto strm = static_cast<hipStream_t>(stream);
-  hipError_t e = tbs::launch_schedule(s, row_cnt, work_list, static_cast<uint32_t*>(ws), strm);
+  hipError_t e = tbs::launch_schedule(s, row_cnt, head_window, work_list, static_cast<uint32_t*>(ws), strm);
   if (e != hipSuccess) return device_status(e, "attn_schedule launch");
   if (worker_of || worker_load) {
     const int W = num_workers > 0 ? num_workers : tbs::device_cu_count();

@@ -46,6 +46,10 @@ namespace tbs {
 namespace {
 
 constexpr int kKeyTile = 64;
+#ifndef TBS_STAGES64
+#define TBS_STAGES64 1
+#endif
+constexpr int kStages64 = TBS_STAGES64;
 
 struct FwdParams {
   const void* q;
@@ -124,49 +128,84 @@ __device__ __forceinline__ int chunk_swz(int row) {
   return ((row & 3) << 1) | ((row >> 3) & 1);
 }
 
-template <int D, int NW>
-__device__ __forceinline__ void issue_tile_bf16(const unsigned char* kg, const unsigned char* vg, int key0,
-                                                int N, unsigned char* lds_k, unsigned char* lds_v,
-                                                int wave, int lane) {
-  constexpr int ROWB = D * 2;
-  constexpr int TILEB = kKeyTile * ROWB;
-  constexpr int PER_WAVE = TILEB / 1024 / NW;
-#pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int blk = j * NW + wave;
-    const int byte = blk * 1024 + lane * 16;
-    const int row = byte / ROWB;
-    const int pch = (byte % ROWB) / 16;
-    const int lch = pch ^ chunk_swz<D>(row);
-    const long long key = min(key0 + row, N - 1);
-    const long long goff = key * ROWB + lch * 16;
-    __builtin_amdgcn_global_load_lds(kg + goff, (TBS_LDS void*)(lds_k + blk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vg + goff, (TBS_LDS void*)(lds_v + blk * 1024), 16, 0, 0);
-  }
-}
+// Copies one 64-key tile of K and V (rows key0 .. key0+63 of one head) from
+// HBM into LDS with buffer_load ... lds: each wave instruction writes 1 KB of
+// LDS (16 bytes per lane, lane-contiguous); the lane picks the global chunk
+// whose swizzled position is its LDS slot.  The buffer resource starts at row
+// key0 and holds the rows left in the sequence, so chunks past the end read
+// as zero (their logits are masked) without a separate tail path.
+constexpr int kRsrcWord3 = 0x00020000;   // raw dword buffer
 
-template <int D, int BQ, int MODE>
-__global__ __launch_bounds__(BQ * 2) void flash_fwd_bf16(FwdParams p) {
+template <int D, int NW>
+struct TileLoader {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILEB = kKeyTile * ROWB;
+  static constexpr int PER_WAVE = TILEB / 1024 / NW;
+  // Byte offset of this lane's chunk inside the tile for instruction j is
+  // j*NW*1024 + base[j & 1]: the swizzle of a row depends on its low four
+  // bits only, which repeat with period 2 in j for every supported shape.
+  unsigned base[2];
+
+  __device__ __forceinline__ static unsigned lane_off(int j, int wave, int lane) {
+    const int byte = (j * NW + wave) * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int lch = ((byte % ROWB) / 16) ^ chunk_swz<D>(row);
+    return static_cast<unsigned>(row * ROWB + lch * 16);
+  }
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    base[0] = lane_off(0, wave, lane);
+    base[1] = lane_off(1, wave, lane) - NW * 1024;
+  }
+
+  __device__ __forceinline__ void issue(const unsigned char* kg, const unsigned char* vg, int key0, int N,
+                                        TBS_LDS unsigned char* lds_k, TBS_LDS unsigned char* lds_v,
+                                        int wave) const {
+    const int bytes = (N - key0) * ROWB;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(kg) + static_cast<long long>(key0) * ROWB, 0, bytes, kRsrcWord3);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(vg) + static_cast<long long>(key0) * ROWB, 0, bytes, kRsrcWord3);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = j * NW + wave;
+      const int voff = static_cast<int>(j * NW * 1024 + base[j & 1]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (TBS_LDS void*)(lds_k + blk * 1024), 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (TBS_LDS void*)(lds_v + blk * 1024), 16, voff, 0, 0, 0);
+    }
+  }
+};
+
+// STAGES = 2: double-buffered tiles (the next tile streams in while this one
+// is computed); STAGES = 1: one tile buffer, half the LDS, so twice as many
+// workgroups share a CU and hide each other's load latency.
+template <int D, int BQ, int MODE, int STAGES>
+__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_bf16(FwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = kKeyTile * ROWB;
   constexpr int NS = D / 16;   // k-steps of S^T
   constexpr int NO = D / 32;   // 32-dim tiles of O^T
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * 2 * TILEB];
   __shared__ int s_unit;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int col = lane & 31;
   const float sl2 = p.scale_log2;
+  TBS_LDS unsigned char* lds = (TBS_LDS unsigned char*)smem;
 
   if (p.prof && tid == 0) p.prof[2 * blockIdx.x] = wall_clock64();
 
   const unsigned char* qg_all = static_cast<const unsigned char*>(p.q);
   const unsigned char* kg_all = static_cast<const unsigned char*>(p.k);
   const unsigned char* vg_all = static_cast<const unsigned char*>(p.v);
+  TileLoader<D, NW> loader;
+  loader.init(wave, lane);
+  // K operand rows (bits 2 and 3 of the row swapped) and their swizzled chunk.
+  const int krow0 = swap_bits23(col);
 
   for (;;) {
     if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
@@ -200,19 +239,19 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_bf16(FwdParams p) {
     float l_run = 0.f;
 
     const int nt = ui.ntiles;
-    if (nt > 0) issue_tile_bf16<D, NW>(kg, vg, ui.key0(p, 0), p.N, smem, smem + TILEB, wave, lane);
+    if (nt > 0) loader.issue(kg, vg, ui.key0(p, 0), p.N, lds, lds + TILEB, wave);
 
     for (int t = 0; t < nt; ++t) {
-      const int st = t & 1;
-      unsigned char* lk = smem + st * 2 * TILEB;
-      unsigned char* lv = lk + TILEB;
+      const int st = STAGES == 2 ? (t & 1) : 0;
+      TBS_LDS unsigned char* lk = lds + st * 2 * TILEB;
+      TBS_LDS unsigned char* lv = lk + TILEB;
+      const int key0 = ui.key0(p, t);
       wait_vmem();
       __syncthreads();
-      if (t + 1 < nt) {
-        unsigned char* nk = smem + (st ^ 1) * 2 * TILEB;
-        issue_tile_bf16<D, NW>(kg, vg, ui.key0(p, t + 1), p.N, nk, nk + TILEB, wave, lane);
+      if (STAGES == 2 && t + 1 < nt) {
+        TBS_LDS unsigned char* nk = lds + (st ^ 1) * 2 * TILEB;
+        loader.issue(kg, vg, ui.key0(p, t + 1), p.N, nk, nk + TILEB, wave);
       }
-      const int key0 = ui.key0(p, t);
 
       // S^T = K Q^T for 64 keys x 32 queries.
       f32x16 sacc[2];
@@ -224,9 +263,9 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_bf16(FwdParams p) {
       for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const int row = swap_bits23(col) + 32 * mt;
+          const int row = krow0 + 32 * mt;
           const int pch = (2 * s + h) ^ chunk_swz<D>(row);
-          const bf16x8 a = *(const TBS_LDS bf16x8*)((TBS_LDS unsigned char*)lk + row * ROWB + pch * 16);
+          const bf16x8 a = *(const TBS_LDS bf16x8*)(lk + row * ROWB + pch * 16);
           sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[mt], 0, 0, 0);
         }
       }
@@ -245,11 +284,14 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_bf16(FwdParams p) {
           }
       }
 
-      float mx = -INFINITY;
+      float mx0 = fmaxf(sacc[0][0], sacc[1][0]);
+      float mx1 = fmaxf(sacc[0][1], sacc[1][1]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+      for (int e = 2; e < 16; e += 2) {
+        mx0 = fmaxf(mx0, fmaxf(sacc[0][e], sacc[1][e]));
+        mx1 = fmaxf(mx1, fmaxf(sacc[0][e + 1], sacc[1][e + 1]));
+      }
+      float mx = fmaxf(mx0, mx1);
       mx = fmaxf(mx, xor32(mx));
       const float m_new = fmaxf(m_run, mx);
       const bool grow = (m_run == -INFINITY) ? (m_new != -INFINITY) : ((m_new - m_run) * sl2 > 8.f);
@@ -265,6 +307,7 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_bf16(FwdParams p) {
       const float mb = (m_run == -INFINITY) ? 0.f : m_run * sl2;
 
       bf16x8 pb[2][2];
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -272,9 +315,10 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_bf16(FwdParams p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2, -mb));
-            l_run += pv;
+            ls[e & 3] += pv;
             pb[mt][t2][e] = static_cast<__bf16>(pv);
           }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
       // O^T += V^T P^T.  Key step kk covers keys 16kk .. 16kk+15; lane (h, col)
       // supplies P for keys 16kk + 8h + 0..7.  V^T comes from two transposed
@@ -294,11 +338,16 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_bf16(FwdParams p) {
             const int dim = 32 * mo + 16 * (g & 1) + 4 * (ii & 3);
             const int pch = (dim >> 3) ^ chunk_swz<D>(row);
             const int off = row * ROWB + pch * 16 + (dim & 7) * 2;
-            part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)((TBS_LDS unsigned char*)lv + off));
+            part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + off));
           }
           const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
           acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[mo], 0, 0, 0);
         }
+      }
+
+      if (STAGES == 1) {
+        __syncthreads();
+        if (t + 1 < nt) loader.issue(kg, vg, ui.key0(p, t + 1), p.N, lds, lds + TILEB, wave);
       }
     }
 
@@ -486,16 +535,35 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_f32(FwdParams p) {
 
 typedef void (*KernelFn)(FwdParams);
 
+// Tile buffers per workgroup: one for 64-row query blocks (LDS then admits
+// four 2-wave workgroups per CU, two waves per SIMD), two for 128-row blocks
+// (two 4-wave workgroups per CU fit either way).
+template <int BQ>
+constexpr int stages_for() { return BQ == 64 ? kStages64 : 2; }
+
+// Every variant is instantiated explicitly: referencing a kernel template
+// only through a function-pointer table does not always emit its host stub.
+#define TBS_INSTANTIATE(D, BQ)                                                         \
+  template __global__ void flash_fwd_bf16<D, BQ, kSparse, stages_for<BQ>()>(FwdParams); \
+  template __global__ void flash_fwd_bf16<D, BQ, kDense, stages_for<BQ>()>(FwdParams);  \
+  template __global__ void flash_fwd_bf16<D, BQ, kCausal, stages_for<BQ>()>(FwdParams); \
+  template __global__ void flash_fwd_f32<D, BQ, kSparse>(FwdParams);                    \
+  template __global__ void flash_fwd_f32<D, BQ, kDense>(FwdParams);                     \
+  template __global__ void flash_fwd_f32<D, BQ, kCausal>(FwdParams);
+TBS_INSTANTIATE(128, 64)
+TBS_INSTANTIATE(128, 128)
+TBS_INSTANTIATE(64, 64)
+TBS_INSTANTIATE(64, 128)
+#undef TBS_INSTANTIATE
+
 template <int D, int BQ>
 KernelFn pick_mode(int dtype, int mode) {
-  if (dtype == 0) {
-    if (mode == kSparse) return flash_fwd_bf16<D, BQ, kSparse>;
-    if (mode == kDense) return flash_fwd_bf16<D, BQ, kDense>;
-    return flash_fwd_bf16<D, BQ, kCausal>;
-  }
-  if (mode == kSparse) return flash_fwd_f32<D, BQ, kSparse>;
-  if (mode == kDense) return flash_fwd_f32<D, BQ, kDense>;
-  return flash_fwd_f32<D, BQ, kCausal>;
+  constexpr int S = stages_for<BQ>();
+  static const KernelFn bf16_fns[3] = {flash_fwd_bf16<D, BQ, kSparse, S>, flash_fwd_bf16<D, BQ, kDense, S>,
+                                       flash_fwd_bf16<D, BQ, kCausal, S>};
+  static const KernelFn f32_fns[3] = {flash_fwd_f32<D, BQ, kSparse>, flash_fwd_f32<D, BQ, kDense>,
+                                      flash_fwd_f32<D, BQ, kCausal>};
+  return dtype == 0 ? bf16_fns[mode] : f32_fns[mode];
 }
 
 KernelFn pick_kernel(const Shape& s, int mode) {

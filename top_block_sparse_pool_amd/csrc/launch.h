@@ -31,7 +31,7 @@ hipError_t launch_select(const Shape& s, const double* qbar, const double* kbar_
                          double* block_prob, hipStream_t stream);
 
 // Scheduler: longest-first work list; zeroes the control block.
-hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int32_t* work_list,
+hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int head_window, int32_t* work_list,
                            uint32_t* ctrl, hipStream_t stream);
 hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* work_list,
                       int num_workers, int32_t* worker_of, int64_t* worker_load, hipStream_t stream);

@@ -9,12 +9,20 @@
 // block) units costing row_cnt key blocks; a persistent kernel that takes
 // units in longest-first order performs greedy list scheduling.
 //
-// schedule_kernel: one workgroup, a stable counting sort by cost descending.
-//   Each wave owns a contiguous slice of unit ids and counts costs into its
-//   own LDS histogram; a prefix over (cost descending, wave ascending) gives
-//   every (wave, cost) pair its first output slot; each wave then walks its
-//   slice in order, ranking equal costs inside a 64-unit batch with ballots
-//   over the 11 cost bits, so equal costs keep ascending unit ids.
+// Head windows: the (b, h) pairs are cut into windows of `head_window`
+// consecutive heads and the list runs window by window, longest first inside
+// each window.  Query blocks running at the same time then share the K/V of a
+// few heads, which stay cache-resident, instead of streaming every head's K/V
+// from HBM; the dynamic queue still balances the load, because a workgroup
+// that finishes early simply takes the next unit, from the next window.
+//
+// schedule_kernel: one workgroup per window, a stable counting sort by cost
+//   descending.  Each wave owns a contiguous slice of the window's unit ids
+//   and counts costs into its own LDS histogram; a prefix over (cost
+//   descending, wave ascending) gives every (wave, cost) pair its first output
+//   slot; each wave then walks its slice in order, ranking equal costs inside
+//   a 64-unit batch with ballots over the 11 cost bits, so equal costs keep
+//   ascending unit ids.
 // lpt_kernel: optional single-wave greedy longest-processing-time model of
 //   the same order over W workers, for reporting load balance.
 #include "device_common.h"
@@ -29,7 +37,7 @@ constexpr int kMaxCost = 1024;
 constexpr int kCostBits = 11;   // costs are in [0, 1024]
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ row_cnt,
-                                                                 int U, int nb,
+                                                                 int U, int nb, int window_units,
                                                                  int32_t* __restrict__ work_list,
                                                                  uint32_t* __restrict__ ctrl) {
   __shared__ int cnt[kSchedWaves][kMaxCost + 1];
@@ -44,9 +52,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   for (int x = tid; x < kSchedWaves * (kMaxCost + 1); x += kSchedThreads) (&cnt[0][0])[x] = 0;
   __syncthreads();
 
-  const int chunk = (U + kSchedWaves - 1) / kSchedWaves;
-  const int ubeg = min(U, wave * chunk);
-  const int uend = min(U, ubeg + chunk);
+  // This workgroup's window: unit ids [w0, w1); output slots start at w0.
+  const int w0 = blockIdx.x * window_units;
+  const int w1 = min(U, w0 + window_units);
+  const int chunk = (w1 - w0 + kSchedWaves - 1) / kSchedWaves;
+  const int ubeg = min(w1, w0 + wave * chunk);
+  const int uend = min(w1, ubeg + chunk);
   for (int u = ubeg + lane; u < uend; u += kWave) {
     const int c = min(max(row_cnt[u], 0), nb);
     atomicAdd(&cnt[wave][c], 1);
@@ -79,7 +90,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
     __syncthreads();
     int base = 0;
     for (int w = 0; w < wave; ++w) base += wtot[w];
-    cexc[tid] = base + incl - v;
+    cexc[tid] = w0 + base + incl - v;
   }
   __syncthreads();
   {
@@ -118,7 +129,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
     if (last_of_group) cnt[wave][c] = slot + __popcll(same);
     __builtin_amdgcn_wave_barrier();
   }
-  if (tid < static_cast<int>(kCtrlBytes / sizeof(uint32_t))) ctrl[tid] = 0u;
+  if (blockIdx.x == 0 && tid < static_cast<int>(kCtrlBytes / sizeof(uint32_t))) ctrl[tid] = 0u;
 }
 
 __global__ __launch_bounds__(kWave) void lpt_kernel(const int32_t* __restrict__ row_cnt,
@@ -158,11 +169,15 @@ __global__ __launch_bounds__(kWave) void lpt_kernel(const int32_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int32_t* work_list, uint32_t* ctrl,
-                           hipStream_t stream) {
+hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int head_window, int32_t* work_list,
+                           uint32_t* ctrl, hipStream_t stream) {
   const int U = static_cast<int>(s.units());
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, row_cnt, U, s.nb,
-                     work_list, ctrl);
+  const int BH = s.B * s.H;
+  const int hw = (head_window <= 0 || head_window > BH) ? BH : head_window;
+  const int window_units = hw * s.nb;
+  const int windows = (BH + hw - 1) / hw;
+  hipLaunchKernelGGL(schedule_kernel, dim3(windows), dim3(kSchedThreads), 0, stream, row_cnt, U, s.nb,
+                     window_units, work_list, ctrl);
   return hipGetLastError();
 }
 
