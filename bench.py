@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense same-shape comparison")
     ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -110,6 +112,12 @@ def main():
     t0 = time.perf_counter()
     q, k, v = (t.to(dev) for t in make_inputs(w, args.seed))
     gen_s = time.perf_counter() - t0
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     pr = tbs.make_problem(q, w.block)
     ws = tbs.workspace(pr, dev)
     B, H, nb, N, d = w.batch, w.heads, w.num_blocks, w.seq_len, w.head_dim
@@ -118,7 +126,7 @@ def main():
                           torch.empty((B, H, nb), dtype=torch.int32, device=dev),
                           torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
                           torch.empty((B, H), dtype=torch.int32, device=dev))
-    work_list = torch.empty(pr.units, dtype=torch.int32, device=dev)
+    work_list = torch.empty(pr.items, dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
 
@@ -159,13 +167,19 @@ def main():
     fwd_tflops = flops / (t_fwd.mean() * 1e-3) / 1e12
 
     # load balance: static contiguous partition vs the longest-first LPT model over the CUs
-    row_cnt = route_out.row_cnt.cpu().numpy().reshape(-1).astype(np.int64)
+    G = pr.group
+    rc = route_out.row_cnt.cpu().numpy().astype(np.int64).reshape(-1, nb)
+    ng = -(-nb // G)
+    padded = np.zeros((rc.shape[0], ng * G), dtype=np.int64)
+    padded[:, :nb] = rc
+    item_cost = padded.reshape(-1, ng, G).sum(-1).reshape(-1)        # cost of each work item
     wl, worker_of, worker_load = tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True)
     torch.cuda.synchronize()
     W = worker_load.numel()
-    static = np.array([row_cnt[(i * row_cnt.size) // W:((i + 1) * row_cnt.size) // W].sum() for i in range(W)])
+    static = np.array([item_cost[(i * item_cost.size) // W:((i + 1) * item_cost.size) // W].sum()
+                       for i in range(W)])
     lpt = worker_load.cpu().numpy()
-    lif = {"workers": int(W), "static_partition": float(static.max() / static.mean()),
+    lif = {"workers": int(W), "query_blocks_per_item": int(G), "static_partition": float(static.max() / static.mean()),
            "longest_first_lpt": float(lpt.max() / lpt.mean())}
     # measured per-workgroup busy time of the persistent kernel
     prp = tbs.make_problem(q, w.block, flags=tbs.FLAG_PROFILE_WORKERS)

@@ -111,6 +111,16 @@ const char* attn_last_error(void);
  * the largest size serves all four operations. */
 size_t attn_workspace_bytes(const attn_problem* problem, int32_t op);
 
+/* Query blocks per work item, G.  The persistent fwd kernel processes a work
+ * item -- G consecutive query blocks of one (b, h) -- in one workgroup: every
+ * K/V tile in the union of the G blocks' selected key blocks is loaded once and
+ * each block's waves compute only the tiles that block selected (adjacent
+ * query blocks select largely the same key blocks).  G = 2 for bf16 with
+ * block 64, otherwise 1.  Work item g = (b*H + h)*ceil(nb/G) + i/G covers query
+ * blocks G*(i/G) .. min(G*(i/G) + G, nb) - 1; there are B*H*ceil(nb/G) items.
+ * Returns 0 if the problem is invalid. */
+int32_t attn_group_size(const attn_problem* problem);
+
 /* Number of persistent workgroups ("workers") the fwd kernel of `op`
  * launches on the current device for `problem` (0 if invalid).  With
  * ATTN_FLAG_PROFILE_WORKERS, worker w writes two uint64 values at workspace
@@ -144,27 +154,29 @@ int32_t attn_route(const attn_problem* problem, const void* q, const void* k, do
 
 /* Longest-first work list, in head windows.
  *
- * Unit u costs row_cnt[u] key blocks.  The (b, h) pairs are cut into windows
- * of `head_window` consecutive pairs (window of unit u = (u / nb) / head_window);
- * work_list[0..U) receives every unit id once, sorted by window ascending,
- * then cost descending, then id ascending.  The persistent fwd kernel takes
- * units from this list in order, each workgroup taking the next one when it
- * becomes free (dynamic list scheduling): longest-first keeps heavy query
- * blocks from straggling at the end, and the windows keep the query blocks
- * that run at the same time on the K/V of a few heads, so that K/V is read
- * from cache instead of HBM.  head_window = 0 (or >= B*H) gives one window:
- * a pure longest-first list.  Also zeroes the workspace control block.
+ * Work item g (see attn_group_size) costs the summed row_cnt of its query
+ * blocks.  The (b, h) pairs are cut into windows of `head_window` consecutive
+ * pairs (window of item g = (g / ceil(nb/G)) / head_window); work_list
+ * receives every item id once, sorted by window ascending, then cost
+ * descending, then id ascending.  The persistent fwd kernel takes items from
+ * this list in order, each workgroup taking the next one when it becomes free
+ * (dynamic list scheduling): longest-first keeps heavy items from straggling
+ * at the end, and the windows keep the items that run at the same time on the
+ * K/V of a few heads, so that K/V is read from cache instead of HBM.
+ * head_window = 0 (or >= B*H) gives one window: a pure longest-first list.
+ * Also zeroes the workspace control block.
  *
- *   row_cnt      [U] int32 in, each in [0, nb].
+ *   row_cnt      [B*H*nb] int32 in, each in [0, nb].
  *   head_window  >= 0, see above.
  *   num_workers  workers for the optional static model; 0 selects the number
  *                of compute units of the current device.
- *   work_list    [U] int32 out.
- *   worker_of    [U] int32 out, nullable: greedy longest-processing-time
- *                assignment in work-list order (each unit to the least-loaded
- *                worker, ties to the lowest id).  Only computed when
- *                worker_of or worker_load is given; it runs one wavefront and
- *                is meant for reporting load balance, not for the hot path.
+ *   work_list    [B*H*ceil(nb/G)] int32 out.
+ *   worker_of    [B*H*ceil(nb/G)] int32 out, nullable: greedy
+ *                longest-processing-time assignment in work-list order (each
+ *                item to the least-loaded worker, ties to the lowest id).  Only
+ *                computed when worker_of or worker_load is given; it runs one
+ *                wavefront and is meant for reporting load balance, not for
+ *                the hot path.
  *   worker_load  [num_workers] int64 out, nullable: summed cost per worker
  *                under that assignment.
  * Requires nb <= 1024 and num_workers <= 4096. */
@@ -184,13 +196,14 @@ int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32
  *
  *   q, k, v    [B,H,N,d] dtype.
  *   row_cnt    [U] int32, row_idx [U, nb] int32 as written by attn_route
- *              (indices ascending and < nb; the library reads them as given).
- *   work_list  [U] int32, nullable: processing order (from attn_schedule);
- *              NULL processes units in natural order.
+ *              (indices in [0, nb); the library clamps out-of-range values).
+ *   work_list  [B*H*ceil(nb/G)] int32, nullable: work-item order (from
+ *              attn_schedule); NULL processes items in natural order.
  *   o          [B,H,N,d] dtype out.  A unit whose row_cnt is 0 gets o = 0.
  *   lse        [B,H,N] float out, nullable (-inf for a unit with no keys).
  *   ws         attn_workspace_bytes(problem, ATTN_OP_SPARSE_FWD) bytes, control
- *              block zero on entry (see attn_workspace_bytes). */
+ *              block zero on entry (see attn_workspace_bytes).
+ * Requires causal == 0 and nb <= 2048. */
 int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                         const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
                         void* o, float* lse, void* ws, size_t ws_bytes, void* stream);

@@ -32,13 +32,13 @@ library special cases or invariants.
 from .routing import (block_sizes, num_blocks, pool_blocks, block_scores, softmax_rows,
                       top_p_select, route, ambiguous_blocks, RouteResult)
 from .attention import attend, attend_units, attend_dense_masked_logits
-from .schedule import work_list, lpt_assign, static_partition_loads, load_imbalance
+from .schedule import group_costs, work_list, lpt_assign, static_partition_loads, load_imbalance
 from .flops import executed_flops, dense_flops
 
 __all__ = [
     "block_sizes", "num_blocks", "pool_blocks", "block_scores", "softmax_rows",
     "top_p_select", "route", "ambiguous_blocks", "RouteResult",
     "attend", "attend_units", "attend_dense_masked_logits",
-    "work_list", "lpt_assign", "static_partition_loads", "load_imbalance",
+    "group_costs", "work_list", "lpt_assign", "static_partition_loads", "load_imbalance",
     "executed_flops", "dense_flops",
 ]

@@ -15,6 +15,10 @@ selected key blocks.
   by window, longest first inside each window.  The windows are not from the
   pages; they are this implementation's way of keeping the query blocks that
   run together on the K/V of a few heads.
+* work items: the attention kernel of this implementation processes G
+  consecutive query blocks of one head together (G = 2 for bf16 with 64-row
+  blocks); an item costs the summed counts of its blocks, item id
+  g = (b*H + h)*ceil(nb/G) + i//G.
 * greedy longest-processing-time (LPT): in work-list order, each unit goes to
   the worker with the least load so far, ties to the lowest worker id.
 * "before": a contiguous static partition of the natural unit order, worker w
@@ -28,6 +32,17 @@ from __future__ import annotations
 import heapq
 
 import numpy as np
+
+
+def group_costs(row_cnt, group: int) -> np.ndarray:
+    """Cost of each work item: the sum of row_cnt over its G query blocks."""
+    rc = np.asarray(row_cnt, dtype=np.int64)
+    nb = rc.shape[-1]
+    flat = rc.reshape(-1, nb)
+    ng = -(-nb // group)
+    pad = np.zeros((flat.shape[0], ng * group), dtype=np.int64)
+    pad[:, :nb] = flat
+    return pad.reshape(flat.shape[0], ng, group).sum(-1).reshape(-1)
 
 
 def work_list(costs, window_units: int | None = None) -> np.ndarray:

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     L = tbs.lib()
     names = _declared_functions()
     assert set(names) == {"attn_abi_version", "attn_last_error", "attn_workspace_bytes", "attn_num_workers",
-                          "attn_route", "attn_schedule", "attn_sparse_fwd", "attn_dense_fwd"}
+                          "attn_group_size", "attn_route", "attn_schedule", "attn_sparse_fwd", "attn_dense_fwd"}
     for n in names:
         assert hasattr(L, n), n
     assert L.attn_abi_version() == 1
@@ -41,6 +41,15 @@ def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, sc
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(tbs.Problem) == 40
     assert tbs.Problem.scale.offset == 32
+
+
+def test_group_size():
+    L = tbs.lib()
+    assert L.attn_group_size(ctypes.byref(_problem())) == 2
+    assert L.attn_group_size(ctypes.byref(_problem(block=128))) == 1
+    assert L.attn_group_size(ctypes.byref(_problem(dtype=1))) == 1
+    assert L.attn_group_size(ctypes.byref(_problem(d=80))) == 0
+    assert _problem(N=1000).items == 40 * 8
 
 
 def test_workspace_sizes():
@@ -102,6 +111,9 @@ def test_schedule_and_fwd_validation():
     assert L.attn_sparse_fwd(ctypes.byref(p), FAKE, FAKE, ctypes.c_void_p(0x10004), FAKE, FAKE, None, FAKE,
                              None, WS, 1 << 20, None) == 1
     assert L.attn_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, WS, 16, None) == 3
+    big = _problem(N=64 * 2049)
+    assert L.attn_sparse_fwd(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, WS, 1 << 20,
+                             None) == 2
     pc = _problem(causal=1)
     assert L.attn_sparse_fwd(ctypes.byref(pc), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, WS, 1 << 20,
                              None) == 2

@@ -44,7 +44,8 @@ def test_full_size_sparse_workload(name):
     ref = oracle_route_per_head(q, k, w.block, w.top_p)
     cmp = compare_route(r, ref)
     costs = r.row_cnt.cpu().numpy()
-    want_wl = oracle.work_list(costs.reshape(-1), tbs.DEFAULT_HEAD_WINDOW * pr.num_blocks)
+    G = pr.group
+    want_wl = oracle.work_list(oracle.group_costs(costs, G), tbs.DEFAULT_HEAD_WINDOW * -(-pr.num_blocks // G))
     assert (wl.cpu().numpy() == want_wl).all()
     density = costs.sum() / (pr.units * pr.num_blocks)
     print(f"  mask ok (ambiguous mismatches {cmp['ambiguous_mismatches']}), density {density:.3f}", flush=True)

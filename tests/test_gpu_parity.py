@@ -59,8 +59,10 @@ def test_sparse_path_matches_oracle(w):
     cmp = compare_route(r, ref)
     print(f"  ambiguous mismatches: {cmp['ambiguous_mismatches']}", flush=True)
     # scheduler: exact work list and LPT model
-    costs = r.row_cnt.cpu().numpy().reshape(-1)
-    want_wl = oracle.work_list(costs, (w.heads // 2 or 1) * pr.num_blocks)
+    G = pr.group
+    ng = -(-pr.num_blocks // G)
+    costs = oracle.group_costs(r.row_cnt.cpu().numpy(), G)
+    want_wl = oracle.work_list(costs, (w.heads // 2 or 1) * ng)
     assert (wl.cpu().numpy() == want_wl).all()
     W = worker_load.numel()
     want_of, want_load = oracle.lpt_assign(costs, want_wl, W)
@@ -89,8 +91,9 @@ def test_schedule_windows_match_oracle(head_window):
     r = tbs.route(q, k, w.top_p, w.block, ws=ws)
     wl, worker_of, worker_load = tbs.schedule(pr, r.row_cnt, ws, head_window=head_window, num_workers=7, lpt=True)
     torch.cuda.synchronize()
-    costs = r.row_cnt.cpu().numpy().reshape(-1)
-    want = oracle.work_list(costs, head_window * pr.num_blocks)
+    G = pr.group
+    costs = oracle.group_costs(r.row_cnt.cpu().numpy(), G)
+    want = oracle.work_list(costs, head_window * -(-pr.num_blocks // G))
     assert (wl.cpu().numpy() == want).all()
     want_of, want_load = oracle.lpt_assign(costs, want, 7)
     assert (worker_of.cpu().numpy() == want_of).all() and (worker_load.cpu().numpy() == want_load).all()

@@ -21,6 +21,12 @@ def test_work_list_windows_hand_example():
     assert oracle.work_list(costs, 100).tolist() == oracle.work_list(costs).tolist()
 
 
+def test_group_costs_hand_example():
+    row_cnt = np.array([[[3, 5, 1, 4, 2], [1, 1, 1, 1, 9]]])       # B=1, H=2, nb=5
+    assert oracle.group_costs(row_cnt, 2).tolist() == [8, 5, 2, 2, 2, 9]
+    assert oracle.group_costs(row_cnt, 1).tolist() == row_cnt.reshape(-1).tolist()
+
+
 def test_work_list_is_sorted_permutation():
     rng = np.random.default_rng(0)
     costs = rng.integers(0, 40, size=5000)

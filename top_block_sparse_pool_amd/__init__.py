@@ -65,6 +65,19 @@ class Problem(ctypes.Structure):
     def units(self) -> int:
         return self.batch * self.heads * self.num_blocks
 
+    @property
+    def group(self) -> int:
+        """Query blocks per work item of the fwd kernel (attn_group_size)."""
+        g = int(lib().attn_group_size(ctypes.byref(self)))
+        if g == 0:
+            _check(ATTN_E_INVALID)
+        return g
+
+    @property
+    def items(self) -> int:
+        g = self.group
+        return self.batch * self.heads * (-(-self.num_blocks // g))
+
 
 _lib = None
 
@@ -86,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.attn_last_error.argtypes = []
     L.attn_workspace_bytes.restype = sz
     L.attn_workspace_bytes.argtypes = [P, i32]
+    L.attn_group_size.restype = i32
+    L.attn_group_size.argtypes = [P]
     L.attn_num_workers.restype = i32
     L.attn_num_workers.argtypes = [P, i32]
     L.attn_route.restype = i32
@@ -200,13 +215,13 @@ def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, head_win
     (worker_of, worker_load) used to report load balance."""
     _require_device(row_cnt, ws)
     dev = row_cnt.device
-    U = problem.units
+    n_items = problem.items
     if work_list is None:
-        work_list = torch.empty(U, dtype=torch.int32, device=dev)
+        work_list = torch.empty(n_items, dtype=torch.int32, device=dev)
     worker_of = worker_load = None
     if lpt:
         W = num_workers or torch.cuda.get_device_properties(dev).multi_processor_count
-        worker_of = torch.empty(U, dtype=torch.int32, device=dev)
+        worker_of = torch.empty(n_items, dtype=torch.int32, device=dev)
         worker_load = torch.empty(W, dtype=torch.int64, device=dev)
     _check(lib().attn_schedule(ctypes.byref(problem), _ptr(row_cnt), int(head_window), int(num_workers),
                                _ptr(work_list),

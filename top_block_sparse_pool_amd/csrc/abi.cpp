@@ -41,6 +41,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 constexpr size_t kProfileBytes = 16 * 4096;   // per-worker stamps, at most 4096 workers
 constexpr int kMaxRouteBlocks = 1024;
+constexpr int kMaxSparseBlocks = 2048;
 
 // Validates the problem descriptor and resolves it into a Shape.
 int32_t check_problem(const attn_problem* pr, tbs::Shape* s) {
@@ -144,6 +145,12 @@ TBS_EXPORT size_t attn_workspace_bytes(const attn_problem* problem, int32_t op) 
     case ATTN_OP_DENSE_FWD: return fwd_bytes(s);
     default: fail(ATTN_E_INVALID, "unknown op %d", op); return 0;
   }
+}
+
+TBS_EXPORT int32_t attn_group_size(const attn_problem* problem) {
+  tbs::Shape s;
+  if (check_problem(problem, &s) != ATTN_OK) return 0;
+  return tbs::group_size(s);
 }
 
 TBS_EXPORT int32_t attn_num_workers(const attn_problem* problem, int32_t op) {
@@ -250,6 +257,8 @@ TBS_EXPORT int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, c
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
   if (s.causal) return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd: causal must be 0");
+  if (s.nb > kMaxSparseBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd: %d blocks per sequence exceed %d", s.nb, kMaxSparseBlocks);
   if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(row_idx, "row_idx", false)) ||
       (st = check_i32(work_list, "work_list", true)))
     return st;

@@ -46,10 +46,6 @@ namespace tbs {
 namespace {
 
 constexpr int kKeyTile = 64;
-#ifndef TBS_STAGES64
-#define TBS_STAGES64 1
-#endif
-constexpr int kStages64 = TBS_STAGES64;
 
 struct FwdParams {
   const void* q;
@@ -65,7 +61,9 @@ struct FwdParams {
   int BH;
   int N;
   int nb;
-  int U;
+  int U;              // work items in the queue (query-block groups)
+  int G;              // query blocks per work item
+  int ng;             // work items per (b, h) = ceil(nb / G)
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
 };
@@ -176,24 +174,59 @@ struct TileLoader {
   }
 };
 
-// STAGES = 2: double-buffered tiles (the next tile streams in while this one
-// is computed); STAGES = 1: one tile buffer, half the LDS, so twice as many
-// workgroups share a CU and hide each other's load latency.
-template <int D, int BQ, int MODE, int STAGES>
-__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_bf16(FwdParams p) {
-  constexpr int NW = BQ / 32;
+// A work item is a group of G consecutive query blocks of one (b, h).  The
+// workgroup loads every 64-key K/V tile in the union of the group's key
+// blocks once; each wave (32 query rows of one member block) computes only
+// the tiles its own block selected.  Adjacent query blocks select largely the
+// same key blocks, so grouping cuts tile traffic without wasting much MFMA.
+constexpr int kMaxListBlocks = 2048;   // nb limit of the in-LDS union list
+constexpr int kMaxListWords = kMaxListBlocks / 32;
+
+template <int BQ, int G, int MODE>
+struct GroupInfo {
+  int bh, i0, gsz;   // head, first query block, member blocks present (1..G)
+
+  __device__ __forceinline__ void decode(const FwdParams& p, int qpos) {
+    int g;
+    if (MODE == kCausal) {
+      // Longest first: the last query blocks of every head have the most keys.
+      const int gi = p.ng - 1 - qpos / p.BH;
+      bh = qpos % p.BH;
+      g = bh * p.ng + gi;
+    } else {
+      g = qpos;
+      if (MODE == kSparse && p.work_list) g = min(max(p.work_list[qpos], 0), p.U - 1);
+      bh = g / p.ng;
+    }
+    i0 = (g - bh * p.ng) * G;
+    gsz = min(G, p.nb - i0);
+  }
+};
+
+template <int D, int BQ, int G, int MODE>
+__global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_bf16(FwdParams p) {
+  constexpr int NWB = BQ / 32;          // waves per member block
+  constexpr int NW = G * NWB;           // waves per workgroup
+  constexpr int NT = NW * 64;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = kKeyTile * ROWB;
-  constexpr int NS = D / 16;   // k-steps of S^T
-  constexpr int NO = D / 32;   // 32-dim tiles of O^T
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * 2 * TILEB];
+  constexpr int SPB = BQ / kKeyTile;    // key tiles per key block
+  constexpr int NS = D / 16;            // k-steps of S^T
+  constexpr int NO = D / 32;            // 32-dim tiles of O^T
+  static_assert(G == 1 || SPB == 1, "groups of 128-row blocks are not instantiated");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TILEB];
+  __shared__ unsigned s_bm[MODE == kSparse ? G * kMaxListWords : 1];
+  __shared__ unsigned short s_lj[MODE == kSparse ? kMaxListBlocks : 1];
+  __shared__ unsigned char s_lm[MODE == kSparse ? kMaxListBlocks : 1];
   __shared__ int s_unit;
+  __shared__ int s_nlist;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int col = lane & 31;
+  const int member = wave / NWB;
   const float sl2 = p.scale_log2;
   TBS_LDS unsigned char* lds = (TBS_LDS unsigned char*)smem;
 
@@ -204,8 +237,7 @@ __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const unsigned char* vg_all = static_cast<const unsigned char*>(p.v);
   TileLoader<D, NW> loader;
   loader.init(wave, lane);
-  // K operand rows (bits 2 and 3 of the row swapped) and their swizzled chunk.
-  const int krow0 = swap_bits23(col);
+  const int krow0 = swap_bits23(col);   // K operand row: bits 2 and 3 swapped
 
   for (;;) {
     if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
@@ -214,13 +246,75 @@ __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     __syncthreads();
     if (qpos >= p.U) break;
 
-    UnitInfo<BQ, MODE> ui;
-    ui.decode(p, qpos);
-    const long long head_off = static_cast<long long>(ui.bh) * p.N * ROWB;
+    GroupInfo<BQ, G, MODE> gi;
+    gi.decode(p, qpos);
+    const long long head_off = static_cast<long long>(gi.bh) * p.N * ROWB;
     const unsigned char* kg = kg_all + head_off;
     const unsigned char* vg = vg_all + head_off;
-    const int q0w = ui.i * BQ + wave * 32;
+    const bool active = member < gi.gsz;
+    const int qblk = gi.i0 + member;
+    const int q0w = qblk * BQ + (wave % NWB) * 32;
     const int qrow = q0w + col;
+
+    // Tile list of the group.
+    int nt;
+    if (MODE == kSparse) {
+      const int nwords = (p.nb + 31) / 32;
+      for (int x = tid; x < G * kMaxListWords; x += NT) s_bm[x] = 0u;
+      __syncthreads();
+      for (int m = 0; m < gi.gsz; ++m) {
+        const long long u = static_cast<long long>(gi.bh) * p.nb + gi.i0 + m;
+        const int cnt = min(max(p.row_cnt[u], 0), p.nb);
+        const int32_t* lst = p.row_idx + u * p.nb;
+        for (int x = tid; x < cnt; x += NT) {
+          const int j = min(max(lst[x], 0), p.nb - 1);
+          atomicOr(&s_bm[m * kMaxListWords + (j >> 5)], 1u << (j & 31));
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const unsigned a = lane < nwords ? s_bm[lane] : 0u;
+        const unsigned b = (G > 1 && lane < nwords) ? s_bm[kMaxListWords + lane] : 0u;
+        unsigned un = a | b;
+        const int c = __popc(un);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        int pos = incl - c;
+        while (un) {
+          const int bit = __ffs(un) - 1;
+          un &= un - 1;
+          s_lj[pos] = static_cast<unsigned short>(lane * 32 + bit);
+          s_lm[pos] = static_cast<unsigned char>(((a >> bit) & 1u) | (((b >> bit) & 1u) << 1));
+          ++pos;
+        }
+        if (lane == 63) s_nlist = incl;
+      }
+      __syncthreads();
+      const int nl = s_nlist;
+      nt = nl * SPB;
+      if (SPB > 1 && nl > 0 && s_lj[nl - 1] == p.nb - 1) {
+        const int tail = p.N - (p.nb - 1) * BQ;
+        nt = (nl - 1) * SPB + (tail + kKeyTile - 1) / kKeyTile;
+      }
+    } else if (MODE == kDense) {
+      nt = (p.N + kKeyTile - 1) / kKeyTile;
+    } else {
+      nt = (min(p.N, (gi.i0 + gi.gsz) * BQ) + kKeyTile - 1) / kKeyTile;
+    }
+    auto tile_key0 = [&](int t) -> int {
+      if (MODE == kSparse) return __builtin_amdgcn_readfirstlane(s_lj[t / SPB]) * BQ + (t % SPB) * kKeyTile;
+      return t * kKeyTile;
+    };
+    auto tile_mine = [&](int t, int key0) -> bool {
+      if (!active) return false;
+      if (MODE == kSparse) return (__builtin_amdgcn_readfirstlane(s_lm[t / SPB]) >> member) & 1;
+      if (MODE == kCausal) return key0 < (qblk + 1) * BQ;
+      return true;
+    };
 
     // Q^T as B operand: lane (h, col) holds Q[qrow][16s + 8h .. +7].
     bf16x8 qf[NS];
@@ -238,20 +332,20 @@ __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    const int nt = ui.ntiles;
-    if (nt > 0) loader.issue(kg, vg, ui.key0(p, 0), p.N, lds, lds + TILEB, wave);
+    if (nt > 0) loader.issue(kg, vg, tile_key0(0), p.N, lds, lds + TILEB, wave);
 
     for (int t = 0; t < nt; ++t) {
-      const int st = STAGES == 2 ? (t & 1) : 0;
+      const int st = t & 1;
       TBS_LDS unsigned char* lk = lds + st * 2 * TILEB;
       TBS_LDS unsigned char* lv = lk + TILEB;
-      const int key0 = ui.key0(p, t);
+      const int key0 = tile_key0(t);
       wait_vmem();
       __syncthreads();
-      if (STAGES == 2 && t + 1 < nt) {
+      if (t + 1 < nt) {
         TBS_LDS unsigned char* nk = lds + (st ^ 1) * 2 * TILEB;
-        loader.issue(kg, vg, ui.key0(p, t + 1), p.N, nk, nk + TILEB, wave);
+        loader.issue(kg, vg, tile_key0(t + 1), p.N, nk, nk + TILEB, wave);
       }
+      if (!tile_mine(t, key0)) continue;
 
       // S^T = K Q^T for 64 keys x 32 queries.
       f32x16 sacc[2];
@@ -344,19 +438,14 @@ __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[mo], 0, 0, 0);
         }
       }
-
-      if (STAGES == 1) {
-        __syncthreads();
-        if (t + 1 < nt) loader.issue(kg, vg, ui.key0(p, t + 1), p.N, lds, lds + TILEB, wave);
-      }
     }
 
     // Epilogue: lane (h, col) holds O[qrow][32mo + 8j + 4h + r] in acc_o[mo][4j + r].
     const float l_tot = l_run + xor32(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < p.N) {
+    if (active && qrow < p.N) {
       unsigned short* orow = static_cast<unsigned short*>(p.o) +
-                             (static_cast<long long>(ui.bh) * p.N + qrow) * D;
+                             (static_cast<long long>(gi.bh) * p.N + qrow) * D;
 #pragma unroll
       for (int mo = 0; mo < NO; ++mo)
 #pragma unroll
@@ -367,7 +456,7 @@ __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           *reinterpret_cast<bf16x4*>(orow + 32 * mo + 8 * j + 4 * h) = ov;
         }
       if (h == 0 && p.lse)
-        p.lse[static_cast<long long>(ui.bh) * p.N + qrow] =
+        p.lse[static_cast<long long>(gi.bh) * p.N + qrow] =
             l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
     }
   }
@@ -535,20 +624,18 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_f32(FwdParams p) {
 
 typedef void (*KernelFn)(FwdParams);
 
-// Tile buffers per workgroup: one for 64-row query blocks (LDS then admits
-// four 2-wave workgroups per CU, two waves per SIMD), two for 128-row blocks
-// (two 4-wave workgroups per CU fit either way).
-template <int BQ>
-constexpr int stages_for() { return BQ == 64 ? kStages64 : 2; }
+// Query blocks per work item: two 64-row blocks share a workgroup (4 waves);
+// 128-row blocks go alone (4 waves).  fp32 inputs use single blocks.
+constexpr int group_for(int dtype, int block) { return (dtype == 0 && block == 64) ? 2 : 1; }
 
 // Every variant is instantiated explicitly: referencing a kernel template
 // only through a function-pointer table does not always emit its host stub.
-#define TBS_INSTANTIATE(D, BQ)                                                         \
-  template __global__ void flash_fwd_bf16<D, BQ, kSparse, stages_for<BQ>()>(FwdParams); \
-  template __global__ void flash_fwd_bf16<D, BQ, kDense, stages_for<BQ>()>(FwdParams);  \
-  template __global__ void flash_fwd_bf16<D, BQ, kCausal, stages_for<BQ>()>(FwdParams); \
-  template __global__ void flash_fwd_f32<D, BQ, kSparse>(FwdParams);                    \
-  template __global__ void flash_fwd_f32<D, BQ, kDense>(FwdParams);                     \
+#define TBS_INSTANTIATE(D, BQ)                                                       \
+  template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kSparse>(FwdParams); \
+  template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kDense>(FwdParams);  \
+  template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kCausal>(FwdParams); \
+  template __global__ void flash_fwd_f32<D, BQ, kSparse>(FwdParams);                  \
+  template __global__ void flash_fwd_f32<D, BQ, kDense>(FwdParams);                   \
   template __global__ void flash_fwd_f32<D, BQ, kCausal>(FwdParams);
 TBS_INSTANTIATE(128, 64)
 TBS_INSTANTIATE(128, 128)
@@ -558,9 +645,9 @@ TBS_INSTANTIATE(64, 128)
 
 template <int D, int BQ>
 KernelFn pick_mode(int dtype, int mode) {
-  constexpr int S = stages_for<BQ>();
-  static const KernelFn bf16_fns[3] = {flash_fwd_bf16<D, BQ, kSparse, S>, flash_fwd_bf16<D, BQ, kDense, S>,
-                                       flash_fwd_bf16<D, BQ, kCausal, S>};
+  constexpr int G = group_for(0, BQ);
+  static const KernelFn bf16_fns[3] = {flash_fwd_bf16<D, BQ, G, kSparse>, flash_fwd_bf16<D, BQ, G, kDense>,
+                                       flash_fwd_bf16<D, BQ, G, kCausal>};
   static const KernelFn f32_fns[3] = {flash_fwd_f32<D, BQ, kSparse>, flash_fwd_f32<D, BQ, kDense>,
                                       flash_fwd_f32<D, BQ, kCausal>};
   return dtype == 0 ? bf16_fns[mode] : f32_fns[mode];
@@ -573,16 +660,24 @@ KernelFn pick_kernel(const Shape& s, int mode) {
 
 }  // namespace
 
+int group_size(const Shape& s) { return group_for(s.dtype, s.block); }
+
+long long work_items(const Shape& s) {
+  const int G = group_size(s);
+  return static_cast<long long>(s.B) * s.H * ((s.nb + G - 1) / G);
+}
+
 int fwd_workers(const Shape& s, int mode) {
   KernelFn fn = pick_kernel(s, mode);
+  const int threads = group_size(s) * s.block * 2;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), s.block * 2, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   const long long want = static_cast<long long>(device_cu_count()) * per_cu;
-  const long long units = s.units();
-  return static_cast<int>(want < units ? want : units);
+  const long long items = work_items(s);
+  return static_cast<int>(want < items ? want : items);
 }
 
 hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t stream) {
@@ -600,12 +695,14 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
   p.BH = s.B * s.H;
   p.N = s.N;
   p.nb = s.nb;
-  p.U = static_cast<int>(s.units());
+  p.G = group_size(s);
+  p.ng = (s.nb + p.G - 1) / p.G;
+  p.U = static_cast<int>(work_items(s));
   p.scale = static_cast<float>(s.scale);
   p.scale_log2 = static_cast<float>(s.scale * 1.4426950408889634);
   const int grid = fwd_workers(s, mode);
   KernelFn fn = pick_kernel(s, mode);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(s.block * 2), 0, stream, p);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(p.G * s.block * 2), 0, stream, p);
   return hipGetLastError();
 }
 

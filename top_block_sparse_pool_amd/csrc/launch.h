@@ -49,6 +49,9 @@ struct FwdArgs {
   uint32_t* ctrl;
   uint64_t* prof;
 };
+// Query blocks per work item (G) and number of work items B*H*ceil(nb/G).
+int group_size(const Shape& s);
+long long work_items(const Shape& s);
 int fwd_workers(const Shape& s, int mode);
 hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t stream);
 

@@ -16,6 +16,10 @@
 // from HBM; the dynamic queue still balances the load, because a workgroup
 // that finishes early simply takes the next unit, from the next window.
 //
+// Work items: the persistent kernel processes groups of G consecutive query
+// blocks of one head (G = 2 for 64-row blocks), so the list orders groups;
+// a group costs the summed selected-block counts of its blocks.
+//
 // schedule_kernel: one workgroup per window, a stable counting sort by cost
 //   descending.  Each wave owns a contiguous slice of the window's unit ids
 //   and counts costs into its own LDS histogram; a prefix over (cost
@@ -31,13 +35,24 @@
 namespace tbs {
 namespace {
 
-constexpr int kSchedThreads = 512;
+constexpr int kSchedThreads = 256;
 constexpr int kSchedWaves = kSchedThreads / kWave;
-constexpr int kMaxCost = 1024;
-constexpr int kCostBits = 11;   // costs are in [0, 1024]
+constexpr int kMaxCost = 2048;  // a work item holds at most 2 blocks of <= 1024 key blocks
+constexpr int kCostBits = 12;   // costs are in [0, 2048]
+
+// Cost of work item g: the summed selected-block counts of its query blocks.
+__device__ __forceinline__ int item_cost(const int32_t* __restrict__ row_cnt, int g, int nb, int G, int ng) {
+  const int bh = g / ng;
+  const int i0 = (g - bh * ng) * G;
+  const int gsz = min(G, nb - i0);
+  int c = 0;
+  for (int m = 0; m < gsz; ++m) c += min(max(row_cnt[static_cast<long long>(bh) * nb + i0 + m], 0), nb);
+  return c;
+}
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ row_cnt,
-                                                                 int U, int nb, int window_units,
+                                                                 int items, int nb, int G, int ng,
+                                                                 int window_items,
                                                                  int32_t* __restrict__ work_list,
                                                                  uint32_t* __restrict__ ctrl) {
   __shared__ int cnt[kSchedWaves][kMaxCost + 1];
@@ -47,24 +62,22 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
-  const int ncost = nb + 1;   // cost values 0..nb
+  const int maxc = G * nb;
+  const int ncost = maxc + 1;   // cost values 0..maxc
 
   for (int x = tid; x < kSchedWaves * (kMaxCost + 1); x += kSchedThreads) (&cnt[0][0])[x] = 0;
   __syncthreads();
 
-  // This workgroup's window: unit ids [w0, w1); output slots start at w0.
-  const int w0 = blockIdx.x * window_units;
-  const int w1 = min(U, w0 + window_units);
+  // This workgroup's window: item ids [w0, w1); output slots start at w0.
+  const int w0 = blockIdx.x * window_items;
+  const int w1 = min(items, w0 + window_items);
   const int chunk = (w1 - w0 + kSchedWaves - 1) / kSchedWaves;
   const int ubeg = min(w1, w0 + wave * chunk);
   const int uend = min(w1, ubeg + chunk);
-  for (int u = ubeg + lane; u < uend; u += kWave) {
-    const int c = min(max(row_cnt[u], 0), nb);
-    atomicAdd(&cnt[wave][c], 1);
-  }
+  for (int u = ubeg + lane; u < uend; u += kWave) atomicAdd(&cnt[wave][item_cost(row_cnt, u, nb, G, ng)], 1);
   __syncthreads();
 
-  // Position x = 0..ncost-1 enumerates costs in descending order (c = nb - x).
+  // Position x = 0..ncost-1 enumerates costs in descending order (c = maxc - x).
   // Each thread owns a contiguous run of positions; exclusive prefix over runs.
   const int per = (ncost + kSchedThreads - 1) / kSchedThreads;
   const int xbeg = tid * per;
@@ -72,14 +85,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   for (int e = 0; e < per; ++e) {
     const int x = xbeg + e;
     if (x < ncost) {
-      const int c = nb - x;
+      const int c = maxc - x;
       for (int w = 0; w < kSchedWaves; ++w) run += cnt[w][c];
     }
   }
   ctot[tid] = run;
   __syncthreads();
   {
-    int v = ctot[tid];
+    const int v = ctot[tid];
     int incl = v;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -98,7 +111,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
     for (int e = 0; e < per; ++e) {
       const int x = xbeg + e;
       if (x < ncost) {
-        const int c = nb - x;
+        const int c = maxc - x;
         for (int w = 0; w < kSchedWaves; ++w) {
           const int t = cnt[w][c];
           cnt[w][c] = off;
@@ -109,12 +122,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   }
   __syncthreads();
 
-  // Stable placement: rank among equal costs inside each 64-unit batch.
+  // Stable placement: rank among equal costs inside each 64-item batch.
   const uint64_t lt = lanemask_lt();
   for (int base = ubeg; base < uend; base += kWave) {
     const int u = base + lane;
     const bool valid = u < uend;
-    const int c = valid ? min(max(row_cnt[u], 0), nb) : 0;
+    const int c = valid ? item_cost(row_cnt, u, nb, G, ng) : 0;
     uint64_t same = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < kCostBits; ++b) {
@@ -133,17 +146,17 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
 }
 
 __global__ __launch_bounds__(kWave) void lpt_kernel(const int32_t* __restrict__ row_cnt,
-                                                    const int32_t* __restrict__ work_list, int U, int nb,
-                                                    int W, int32_t* __restrict__ worker_of,
+                                                    const int32_t* __restrict__ work_list, int items, int nb,
+                                                    int G, int ng, int W, int32_t* __restrict__ worker_of,
                                                     int64_t* __restrict__ worker_load) {
   __shared__ long long load[4096];
   const int lane = threadIdx.x;
   for (int w = lane; w < W; w += kWave) load[w] = 0;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  for (int t = 0; t < U; ++t) {
-    const int u = min(max(work_list[t], 0), U - 1);
-    const int c = min(max(row_cnt[u], 0), nb);
+  for (int t = 0; t < items; ++t) {
+    const int u = min(max(work_list[t], 0), items - 1);
+    const int c = item_cost(row_cnt, u, nb, G, ng);
     long long best = 0x7fffffffffffffffLL;
     int bid = 0x7fffffff;
     for (int w = lane; w < W; w += kWave) {
@@ -171,20 +184,23 @@ __global__ __launch_bounds__(kWave) void lpt_kernel(const int32_t* __restrict__ 
 
 hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int head_window, int32_t* work_list,
                            uint32_t* ctrl, hipStream_t stream) {
-  const int U = static_cast<int>(s.units());
+  const int G = group_size(s);
+  const int ng = (s.nb + G - 1) / G;
   const int BH = s.B * s.H;
+  const int items = BH * ng;
   const int hw = (head_window <= 0 || head_window > BH) ? BH : head_window;
-  const int window_units = hw * s.nb;
   const int windows = (BH + hw - 1) / hw;
-  hipLaunchKernelGGL(schedule_kernel, dim3(windows), dim3(kSchedThreads), 0, stream, row_cnt, U, s.nb,
-                     window_units, work_list, ctrl);
+  hipLaunchKernelGGL(schedule_kernel, dim3(windows), dim3(kSchedThreads), 0, stream, row_cnt, items, s.nb, G, ng,
+                     hw * ng, work_list, ctrl);
   return hipGetLastError();
 }
 
 hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* work_list, int num_workers,
                       int32_t* worker_of, int64_t* worker_load, hipStream_t stream) {
-  const int U = static_cast<int>(s.units());
-  hipLaunchKernelGGL(lpt_kernel, dim3(1), dim3(kWave), 0, stream, row_cnt, work_list, U, s.nb,
+  const int G = group_size(s);
+  const int ng = (s.nb + G - 1) / G;
+  const int items = s.B * s.H * ng;
+  hipLaunchKernelGGL(lpt_kernel, dim3(1), dim3(kWave), 0, stream, row_cnt, work_list, items, s.nb, G, ng,
                      num_workers, worker_of, worker_load);
   return hipGetLastError();
 }
