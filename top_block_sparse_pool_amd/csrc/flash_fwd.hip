@@ -115,6 +115,36 @@ struct UnitInfo {
   }
 };
 
+// max of three floats in one v_max3_f32 (operands are never NaN here: logits
+// are finite or -inf).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Wave priority while issuing MFMA chains: the SIMD arbiter then feeds the
+// matrix core first and fills the remaining issue slots with the other
+// wave's softmax VALU work.
+#ifndef TBS_MFMA_PRIO
+#define TBS_MFMA_PRIO 1
+#endif
+#if TBS_MFMA_PRIO
+#define TBS_PRIO_HI() __builtin_amdgcn_s_setprio(1)
+#define TBS_PRIO_LO() __builtin_amdgcn_s_setprio(0)
+#else
+#define TBS_PRIO_HI() ((void)0)
+#define TBS_PRIO_LO() ((void)0)
+#endif
+#ifndef TBS_FENCE_S
+#define TBS_FENCE_S 1
+#endif
+#if TBS_FENCE_S
+#define TBS_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define TBS_SCHED_FENCE() ((void)0)
+#endif
+
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
@@ -347,96 +377,98 @@ __global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2
       }
       if (!tile_mine(t, key0)) continue;
 
-      // S^T = K Q^T for 64 keys x 32 queries.
+      // S^T = K Q^T for 64 keys x 32 queries, as two independent 32-key
+      // halves (mt).  Both MFMA chains are issued first; the softmax of half 0
+      // then runs on the VALU while half 1's MFMAs execute, and half 0's P V
+      // MFMAs run while half 1's softmax does.
       f32x16 sacc[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+      TBS_PRIO_HI();
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+      for (int mt = 0; mt < 2; ++mt) {
+        const int row = krow0 + 32 * mt;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int row = krow0 + 32 * mt;
+        for (int s = 0; s < NS; ++s) {
           const int pch = (2 * s + h) ^ chunk_swz<D>(row);
           const bf16x8 a = *(const TBS_LDS bf16x8*)(lk + row * ROWB + pch * 16);
           sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[mt], 0, 0, 0);
         }
       }
+      TBS_PRIO_LO();
+      TBS_SCHED_FENCE();
 
-      // Mask keys past the sequence end (ragged tail) and, if causal, keys
-      // after the query.  Lane value e of tile mt is key 32mt + 16(e>>3) + 8h + (e&7).
       const bool need_mask = (key0 + kKeyTile > p.N) || (MODE == kCausal && key0 + kKeyTile - 1 > q0w);
-      if (need_mask) {
+      const int g = lane >> 4;
+      const int ii = lane & 15;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt) {
+        // Mask keys past the sequence end (ragged tail) and, if causal, keys
+        // after the query.  Lane value e of half mt is key 32mt + 16(e>>3) + 8h + (e&7).
+        if (need_mask) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = key0 + 32 * mt + 16 * (e >> 3) + 8 * h + (e & 7);
             const bool bad = key >= p.N || (MODE == kCausal && key > qrow);
             if (bad) sacc[mt][e] = -INFINITY;
           }
-      }
+        }
+        float mx = max3f(max3f(sacc[mt][0], sacc[mt][1], sacc[mt][2]), sacc[mt][3], sacc[mt][4]);
+        float my = max3f(max3f(sacc[mt][5], sacc[mt][6], sacc[mt][7]), sacc[mt][8], sacc[mt][9]);
+        float mz = max3f(max3f(sacc[mt][10], sacc[mt][11], sacc[mt][12]), sacc[mt][13], sacc[mt][14]);
+        mx = max3f(mx, my, fmaxf(mz, sacc[mt][15]));
+        mx = fmaxf(mx, xor32(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const bool grow = (m_run == -INFINITY) ? (m_new != -INFINITY) : ((m_new - m_run) * sl2 > 8.f);
+        if (__any(grow)) {
+          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * sl2);
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc_o[mo][e] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        const float mb = (m_run == -INFINITY) ? 0.f : m_run * sl2;
 
-      float mx0 = fmaxf(sacc[0][0], sacc[1][0]);
-      float mx1 = fmaxf(sacc[0][1], sacc[1][1]);
-#pragma unroll
-      for (int e = 2; e < 16; e += 2) {
-        mx0 = fmaxf(mx0, fmaxf(sacc[0][e], sacc[1][e]));
-        mx1 = fmaxf(mx1, fmaxf(sacc[0][e + 1], sacc[1][e + 1]));
-      }
-      float mx = fmaxf(mx0, mx1);
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const bool grow = (m_run == -INFINITY) ? (m_new != -INFINITY) : ((m_new - m_run) * sl2 > 8.f);
-      if (__any(grow)) {
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * sl2);
-#pragma unroll
-        for (int mo = 0; mo < NO; ++mo)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc_o[mo][e] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      const float mb = (m_run == -INFINITY) ? 0.f : m_run * sl2;
-
-      bf16x8 pb[2][2];
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        bf16x8 pb[2];
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2, -mb));
             ls[e & 3] += pv;
-            pb[mt][t2][e] = static_cast<__bf16>(pv);
+            pb[t2][e] = static_cast<__bf16>(pv);
           }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-      // O^T += V^T P^T.  Key step kk covers keys 16kk .. 16kk+15; lane (h, col)
-      // supplies P for keys 16kk + 8h + 0..7.  V^T comes from two transposed
-      // reads: 16-lane group g reads rows 16kk + 8h + 4hf + 0..3 and dims
-      // 32mo + 16(g&1) + 0..15.
-      const int g = lane >> 4;
-      const int ii = lane & 15;
+        // O^T += V^T P^T for key steps kk = 2mt, 2mt+1 (keys 16kk .. 16kk+15);
+        // lane (h, col) supplies P for keys 16kk + 8h + 0..7.  V^T comes from
+        // two transposed reads: 16-lane group g reads rows 16kk + 8h + 4hf + 0..3
+        // and dims 32mo + 16(g&1) + 0..15.
+        TBS_PRIO_HI();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 b = pb[kk >> 1][kk & 1];
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int kk = 2 * mt + t2;
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) {
-          bf16x4 part[2];
+          for (int mo = 0; mo < NO; ++mo) {
+            bf16x4 part[2];
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int row = 16 * kk + 8 * h + 4 * hf + (ii >> 2);
-            const int dim = 32 * mo + 16 * (g & 1) + 4 * (ii & 3);
-            const int pch = (dim >> 3) ^ chunk_swz<D>(row);
-            const int off = row * ROWB + pch * 16 + (dim & 7) * 2;
-            part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + off));
+            for (int hf = 0; hf < 2; ++hf) {
+              const int row = 16 * kk + 8 * h + 4 * hf + (ii >> 2);
+              const int dim = 32 * mo + 16 * (g & 1) + 4 * (ii & 3);
+              const int pch = (dim >> 3) ^ chunk_swz<D>(row);
+              const int off = row * ROWB + pch * 16 + (dim & 7) * 2;
+              part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + off));
+            }
+            const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t2], acc_o[mo], 0, 0, 0);
           }
-          const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-          acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[mo], 0, 0, 0);
         }
+        TBS_PRIO_LO();
       }
     }
 

@@ -12,9 +12,10 @@
 //                  (HBM-bound: reads Q and K once).
 //   select_kernel  one workgroup per (b, h, R query blocks): fp64 scores for R
 //                  rows against all key blocks (pooled K read transposed so
-//                  that lanes read consecutive key blocks), then per row a
-//                  max/sum softmax, an LDS bitonic sort by (P desc, index asc),
-//                  a fixed-order prefix sum to find the cut, and the outputs.
+//                  that lanes read consecutive key blocks); then one wave per
+//                  row: a max/sum softmax, a register bitonic sort by
+//                  (P desc, index asc), a fixed-order prefix sum to find the
+//                  cut, and the outputs -- no workgroup barriers per row.
 #include <math.h>
 
 #include "device_common.h"
@@ -95,83 +96,159 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
     for (int x2 = tid; x2 < BH; x2 += kPoolThreads) head_cnt[x2] = 0;
 }
 
-struct SelectSmem {
-  double* z;         // [R][NP] scores, then probabilities (bit patterns sort as uint64)
-  int* sidx;         // [NP] key-block index travelling with each key
-  unsigned char* flag;  // [NP] selected flags by key-block index
-  double* tot;       // [kSelThreads] chunk sums
-  double* tot2;      // [kSelThreads] exclusive chunk prefixes
-  int* itot;         // [kSelThreads]
-  int* itot2;        // [kSelThreads]
-  double* red;       // [kSelWaves]
-  int* kfirst;       // [1]
-};
-
-__device__ double block_max(double x, double* red) {
-  x = wave_max_f64(x);
-  const int wave = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = x;
-  __syncthreads();
-  double r = red[0];
-#pragma unroll
-  for (int w = 1; w < kSelWaves; ++w) r = fmax(r, red[w]);
-  __syncthreads();
-  return r;
+// "a before b" in the ranking: larger probability first, then smaller index.
+// Probabilities are non-negative doubles, which order like their bit
+// patterns; padding elements (P = 0, index >= nb) rank after every real block.
+__device__ __forceinline__ bool ranks_before(unsigned long long ka, int ia, unsigned long long kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
 }
 
-__device__ double block_sum(double x, double* red) {
-  x = wave_sum_f64(x);
-  const int wave = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = x;
-  __syncthreads();
-  double r = red[0];
-#pragma unroll
-  for (int w = 1; w < kSelWaves; ++w) r += red[w];
-  __syncthreads();
-  return r;
-}
-
-// Exclusive prefix of in[0..256) into out[0..256), fixed summation order.
-// Called by wave 0 only.
-template <typename V>
-__device__ void wave0_exclusive_scan256(const V* in, V* out) {
+// Row phase of the selection, run by one wave per query-block row: E
+// elements per lane in blocked order (position = lane*E + i).
+template <int E>
+__device__ void select_row(const double* __restrict__ zr, int nb, double top_p, long long row, int bh,
+                           unsigned char* __restrict__ flag, uint8_t* __restrict__ mask,
+                           int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx,
+                           int32_t* __restrict__ head_cnt, double* __restrict__ block_prob) {
+  constexpr int NP = 64 * E;
   const int lane = threadIdx.x & (kWave - 1);
-  const V a0 = in[4 * lane], a1 = in[4 * lane + 1], a2 = in[4 * lane + 2], a3 = in[4 * lane + 3];
-  const V s = ((a0 + a1) + a2) + a3;
-  V incl = s;
+  const int base = lane * E;
+
+  // Softmax over key blocks (fp64), reductions in a fixed order.
+  double v[E];
+  double m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    v[i] = zr[base + i];
+    m = fmax(m, v[i]);
+  }
+  m = wave_max_f64(m);
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    v[i] = (base + i < nb) ? exp(v[i] - m) : 0.0;
+    s += v[i];
+  }
+  s = wave_sum_f64(s);
+  unsigned long long key[E];
+  int idx[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const double pj = v[i] / s;
+    if (block_prob && base + i < nb) block_prob[row * nb + base + i] = pj;
+    key[i] = __double_as_longlong(pj);
+    idx[i] = base + i;
+  }
+
+  // Bitonic sort into ranking order.
+#pragma unroll
+  for (int k = 2; k <= NP; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          if (i & j) continue;
+          const int b = i | j;
+          const bool up = ((base + i) & k) == 0;
+          const bool b_first = ranks_before(key[b], idx[b], key[i], idx[i]);
+          if (b_first == up) {
+            const unsigned long long tk = key[i]; key[i] = key[b]; key[b] = tk;
+            const int ti = idx[i]; idx[i] = idx[b]; idx[b] = ti;
+          }
+        }
+      } else {
+        const int lx = j / E;   // partner lane distance
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const unsigned long long ok = __shfl_xor(key[i], lx, kWave);
+          const int oi = __shfl_xor(idx[i], lx, kWave);
+          const int pos = base + i;
+          const bool lower = (pos & j) == 0;
+          const bool up = (pos & k) == 0;
+          const bool mine_first = ranks_before(key[i], idx[i], ok, oi);
+          const bool keep = (lower == up) ? mine_first : !mine_first;
+          if (!keep) { key[i] = ok; idx[i] = oi; }
+        }
+      }
+    }
+  }
+
+  // Inclusive prefix of the ranked probabilities; first rank reaching top_p.
+  double c[E];
+  double run = 0.0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    run += __longlong_as_double(key[i]);
+    c[i] = run;
+  }
+  double incl = run;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    const V y = __shfl_up(incl, off, kWave);
+    const double y = __shfl_up(incl, off, kWave);
     if (lane >= off) incl += y;
   }
-  V excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = V(0);
-  out[4 * lane] = excl;
-  out[4 * lane + 1] = excl + a0;
-  out[4 * lane + 2] = (excl + a0) + a1;
-  out[4 * lane + 3] = ((excl + a0) + a1) + a2;
+  double excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  int first = NP;
+#pragma unroll
+  for (int i = E - 1; i >= 0; --i)
+    if (base + i < nb && excl + c[i] >= top_p) first = base + i;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) first = min(first, __shfl_xor(first, off, kWave));
+  const int kcnt = (top_p >= 1.0 || first >= nb) ? nb : first + 1;
+
+  // Flags by key-block index (this wave's LDS strip), then the outputs.
+#pragma unroll
+  for (int i = 0; i < E; ++i) flag[base + i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (base + i < kcnt) flag[idx[i]] = 1;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int cnt = 0;
+  unsigned char f[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    f[i] = flag[base + i];
+    cnt += f[i];
+  }
+  uint8_t* mrow = mask + row * nb;
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (base + i < nb) mrow[base + i] = f[i];
+  int ic = cnt;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(ic, off, kWave);
+    if (lane >= off) ic += y;
+  }
+  int pos = ic - cnt;
+  int32_t* ridx = row_idx + row * nb;
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (f[i]) ridx[pos++] = base + i;
+  if (lane == 0) {
+    row_cnt[row] = kcnt;
+    atomicAdd(head_cnt + bh, kcnt);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
-template <int D, int R>
+template <int D, int R, int E>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ qbar, const double* __restrict__ kbar_t, double scale, double top_p,
-    int nb, int NP, int tiles_per_head, uint8_t* __restrict__ mask, int32_t* __restrict__ row_cnt,
+    int nb, int tiles_per_head, uint8_t* __restrict__ mask, int32_t* __restrict__ row_cnt,
     int32_t* __restrict__ row_idx, int32_t* __restrict__ head_cnt, double* __restrict__ block_prob) {
+  constexpr int NP = 64 * E;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  SelectSmem sm;
-  {
-    unsigned char* p = smem_raw;
-    sm.z = reinterpret_cast<double*>(p);            p += sizeof(double) * R * NP;
-    sm.tot = reinterpret_cast<double*>(p);          p += sizeof(double) * kSelThreads;
-    sm.tot2 = reinterpret_cast<double*>(p);         p += sizeof(double) * kSelThreads;
-    sm.red = reinterpret_cast<double*>(p);          p += sizeof(double) * kSelWaves;
-    sm.sidx = reinterpret_cast<int*>(p);            p += sizeof(int) * NP;
-    sm.itot = reinterpret_cast<int*>(p);            p += sizeof(int) * kSelThreads;
-    sm.itot2 = reinterpret_cast<int*>(p);           p += sizeof(int) * kSelThreads;
-    sm.kfirst = reinterpret_cast<int*>(p);          p += sizeof(int) * 4;
-    sm.flag = p;
-  }
+  double* z = reinterpret_cast<double*>(smem_raw);                           // [R][NP]
+  unsigned char* flags = smem_raw + sizeof(double) * R * NP;                 // [waves][NP]
   const int tid = threadIdx.x;
+  const int wave = tid / kWave;
   const int bh = blockIdx.x / tiles_per_head;
   const int i0 = (blockIdx.x % tiles_per_head) * R;
   const int rows = min(R, nb - i0);
@@ -193,118 +270,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) sm.z[r * NP + j] = scale * acc[r];
+      for (int r = 0; r < R; ++r) z[r * NP + j] = scale * acc[r];
     } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r) sm.z[r * NP + j] = -INFINITY;
+      for (int r = 0; r < R; ++r) z[r * NP + j] = -INFINITY;
     }
   }
   __syncthreads();
 
-  for (int r = 0; r < rows; ++r) {
-    const int i = i0 + r;
-    const long long row = static_cast<long long>(bh) * nb + i;
-    double* zr = sm.z + r * NP;
-
-    // Softmax over key blocks.
-    double m = -INFINITY;
-    for (int j = tid; j < nb; j += kSelThreads) m = fmax(m, zr[j]);
-    m = block_max(m, sm.red);
-    double s = 0.0;
-    for (int j = tid; j < nb; j += kSelThreads) {
-      const double e = exp(zr[j] - m);
-      zr[j] = e;
-      s += e;
-    }
-    s = block_sum(s, sm.red);
-    for (int j = tid; j < NP; j += kSelThreads) {
-      double pj = 0.0;
-      if (j < nb) {
-        pj = zr[j] / s;
-        if (block_prob) block_prob[row * nb + j] = pj;
-      }
-      zr[j] = pj;
-      sm.sidx[j] = j;
-    }
-    if (tid == 0) sm.kfirst[0] = NP;
-    __syncthreads();
-
-    // Bitonic sort: "a before b" iff P_a > P_b, or P_a == P_b and a < b.
-    // Non-negative doubles order like their bit patterns; padding (P = 0,
-    // index >= nb) sorts after every real block.
-    unsigned long long* key = reinterpret_cast<unsigned long long*>(zr);
-    for (int kk = 2; kk <= NP; kk <<= 1) {
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int e = tid; e < (NP >> 1); e += kSelThreads) {
-          const int a = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
-          const int b = a | jj;
-          const bool up = (a & kk) == 0;
-          const unsigned long long ka = key[a], kb = key[b];
-          const int ia = sm.sidx[a], ib = sm.sidx[b];
-          const bool b_first = (kb > ka) || (kb == ka && ib < ia);
-          if (b_first == up) {
-            key[a] = kb; key[b] = ka;
-            sm.sidx[a] = ib; sm.sidx[b] = ia;
-          }
-        }
-        __syncthreads();
-      }
-    }
-
-    // Inclusive prefix sums of the ranked probabilities; first rank reaching p.
-    const int per = NP >= kSelThreads ? NP / kSelThreads : 1;
-    const int beg = tid * per;
-    double loc = 0.0;
-    for (int e = 0; e < per; ++e)
-      if (beg + e < NP) loc += zr[beg + e];
-    sm.tot[tid] = loc;
-    __syncthreads();
-    if (tid < kWave) wave0_exclusive_scan256<double>(sm.tot, sm.tot2);
-    __syncthreads();
-    {
-      double run = sm.tot2[tid];
-      for (int e = 0; e < per; ++e) {
-        const int pos = beg + e;
-        if (pos >= nb) break;
-        run += zr[pos];
-        if (run >= top_p) {
-          atomicMin(sm.kfirst, pos);
-          break;
-        }
-      }
-    }
-    for (int j = tid; j < NP; j += kSelThreads) sm.flag[j] = 0;
-    __syncthreads();
-    const int kf = sm.kfirst[0];
-    const int kcnt = (top_p >= 1.0 || kf >= nb) ? nb : kf + 1;
-    for (int e = tid; e < kcnt; e += kSelThreads) sm.flag[sm.sidx[e]] = 1;
-    __syncthreads();
-
-    // Mask row, ascending index list, counts.
-    uint8_t* mrow = mask + row * nb;
-    for (int j = tid; j < nb; j += kSelThreads) mrow[j] = sm.flag[j];
-    const int per2 = (nb + kSelThreads - 1) / kSelThreads;
-    const int beg2 = tid * per2;
-    int cnt = 0;
-    for (int e = 0; e < per2; ++e)
-      if (beg2 + e < nb) cnt += sm.flag[beg2 + e];
-    sm.itot[tid] = cnt;
-    __syncthreads();
-    if (tid < kWave) wave0_exclusive_scan256<int>(sm.itot, sm.itot2);
-    __syncthreads();
-    {
-      int pos = sm.itot2[tid];
-      int32_t* ridx = row_idx + row * nb;
-      for (int e = 0; e < per2; ++e) {
-        const int j = beg2 + e;
-        if (j < nb && sm.flag[j]) ridx[pos++] = j;
-      }
-    }
-    if (tid == 0) {
-      row_cnt[row] = kcnt;
-      atomicAdd(head_cnt + bh, kcnt);
-    }
-    __syncthreads();
+  // Phase 2: one wave per row.
+  for (int r = wave; r < rows; r += kSelWaves) {
+    const long long row = static_cast<long long>(bh) * nb + i0 + r;
+    select_row<E>(z + r * NP, nb, top_p, row, bh, flags + wave * NP, mask, row_cnt, row_idx, head_cnt,
+                  block_prob);
   }
 }
 
@@ -314,23 +292,35 @@ int next_pow2(int x) {
   return p;
 }
 
-template <int D, int R>
+template <int D, int R, int E>
 hipError_t launch_select_t(const Shape& s, const double* qbar, const double* kbar_t, double top_p,
                            uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                            double* block_prob, hipStream_t stream) {
-  const int NP = next_pow2(s.nb);
-  const size_t smem = sizeof(double) * (static_cast<size_t>(R) * NP + 2 * kSelThreads + kSelWaves) +
-                      sizeof(int) * (NP + 2 * kSelThreads + 4) + NP;
-  auto kern = select_kernel<D, R>;
+  constexpr int NP = 64 * E;
+  const size_t smem = sizeof(double) * static_cast<size_t>(R) * NP + static_cast<size_t>(kSelWaves) * NP;
+  auto kern = select_kernel<D, R, E>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
   const int tiles = (s.nb + R - 1) / R;
   const long long grid = static_cast<long long>(s.B) * s.H * tiles;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSelThreads), smem, stream, qbar,
-                     kbar_t, s.scale, top_p, s.nb, NP, tiles, mask, row_cnt, row_idx, head_cnt,
-                     block_prob);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSelThreads), smem, stream, qbar, kbar_t,
+                     s.scale, top_p, s.nb, tiles, mask, row_cnt, row_idx, head_cnt, block_prob);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_select_d(const Shape& s, const double* qbar, const double* kbar_t, double top_p,
+                           uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
+                           double* block_prob, hipStream_t stream) {
+  const int np = next_pow2(s.nb < 64 ? 64 : s.nb);
+  switch (np) {
+    case 64: return launch_select_t<D, 16, 1>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+    case 128: return launch_select_t<D, 16, 2>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+    case 256: return launch_select_t<D, 16, 4>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+    case 512: return launch_select_t<D, 16, 8>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+    default: return launch_select_t<D, 8, 16>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+  }
 }
 
 }  // namespace
@@ -365,16 +355,9 @@ hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qba
 hipError_t launch_select(const Shape& s, const double* qbar, const double* kbar_t, double top_p,
                          uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                          double* block_prob, hipStream_t stream) {
-  const bool big = next_pow2(s.nb) > 512;
   if (s.d == 128)
-    return big ? launch_select_t<128, 8>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt,
-                                         block_prob, stream)
-               : launch_select_t<128, 16>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt,
-                                          block_prob, stream);
-  return big ? launch_select_t<64, 8>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt,
-                                      block_prob, stream)
-             : launch_select_t<64, 16>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt,
-                                       block_prob, stream);
+    return launch_select_d<128>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+  return launch_select_d<64>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
 }
 
 }  // namespace tbs
