@@ -14,7 +14,7 @@
 //
 // bf16 kernel layout (per workgroup: block/32 waves, each owning 32 query rows):
 //   * Key tiles of 64 keys.  K and V tiles are copied HBM -> LDS with
-//     global_load_lds (16 bytes per lane, no VGPR staging), double-buffered:
+//     buffer_load ... lds (16 bytes per lane, no VGPR staging), double-buffered:
 //     tile t+1 streams in while tile t is computed.  Rows are stored with an
 //     XOR swizzle of their 16-byte chunks so the MFMA operand reads below hit
 //     distinct LDS banks.
@@ -139,6 +139,12 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 #ifndef TBS_FENCE_S
 #define TBS_FENCE_S 1
 #endif
+#ifndef TBS_KPF
+#define TBS_KPF 4
+#endif
+#ifndef TBS_KPF_PIN
+#define TBS_KPF_PIN 1
+#endif
 #if TBS_FENCE_S
 #define TBS_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 #else
@@ -186,20 +192,49 @@ struct TileLoader {
     base[1] = lane_off(1, wave, lane) - NW * 1024;
   }
 
+  __device__ __forceinline__ static u32x4 rsrc(const unsigned char* base, int bytes) {
+    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32) & 0xffffu);   // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(bytes));
+    r[3] = kRsrcWord3;
+    return r;
+  }
+
+  // One buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + voff into
+  // LDS at lds_addr + 16 * lane.  Written as inline asm so that the compiler
+  // does not count it as a pending write to the tile being read: the loop
+  // below orders every tile's reads after its own copy with an explicit
+  // vmcnt wait and a barrier, and the copy into the other stage stays in
+  // flight meanwhile.  M0 (the LDS base operand) is restored afterwards.
+  __device__ __forceinline__ static void dma16(u32x4 r, int voff, unsigned lds_addr) {
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(r)
+        : "memory");
+  }
+
   __device__ __forceinline__ void issue(const unsigned char* kg, const unsigned char* vg, int key0, int N,
                                         TBS_LDS unsigned char* lds_k, TBS_LDS unsigned char* lds_v,
                                         int wave) const {
     const int bytes = (N - key0) * ROWB;
-    const auto rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(kg) + static_cast<long long>(key0) * ROWB, 0, bytes, kRsrcWord3);
-    const auto rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(vg) + static_cast<long long>(key0) * ROWB, 0, bytes, kRsrcWord3);
+    const u32x4 rk = rsrc(kg + static_cast<long long>(key0) * ROWB, bytes);
+    const u32x4 rv = rsrc(vg + static_cast<long long>(key0) * ROWB, bytes);
+    const unsigned lk = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)lds_k);
+    const unsigned lv = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)lds_v);
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int blk = j * NW + wave;
+      const unsigned blk = static_cast<unsigned>((j * NW + wave) * 1024);
       const int voff = static_cast<int>(j * NW * 1024 + base[j & 1]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (TBS_LDS void*)(lds_k + blk * 1024), 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (TBS_LDS void*)(lds_v + blk * 1024), 16, voff, 0, 0, 0);
+      dma16(rk, voff, lk + blk);
+      dma16(rv, voff, lv + blk);
     }
   }
 };
@@ -386,16 +421,37 @@ __global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-      TBS_PRIO_HI();
+      // K fragments stream through a ring of TBS_KPF registers, read that many
+      // MFMAs ahead, so LDS latency overlaps the matrix core instead of
+      // stalling every product.  Fragment f is half f / NS, k-step f % NS.
+      {
+        constexpr int NF = 2 * NS;
+        constexpr int KP = TBS_KPF < NF ? TBS_KPF : NF;
+        const int kswz = chunk_swz<D>(krow0);   // the same for both halves
+        const TBS_LDS unsigned char* kbase = lk + krow0 * ROWB;
+        auto kread = [&](int f) -> bf16x8 {
+          const int pch = (2 * (f % NS) + h) ^ kswz;
+          return *(const TBS_LDS bf16x8*)(kbase + (f / NS) * 32 * ROWB + pch * 16);
+        };
+        bf16x8 kr[KP];
+        TBS_PRIO_HI();
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int row = krow0 + 32 * mt;
+        for (int f = 0; f < KP; ++f) kr[f] = kread(f);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int pch = (2 * s + h) ^ chunk_swz<D>(row);
-          const bf16x8 a = *(const TBS_LDS bf16x8*)(lk + row * ROWB + pch * 16);
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[mt], 0, 0, 0);
+        for (int f = 0; f < NF; ++f) {
+          const bf16x8 a = kr[f % KP];
+          if (f + KP < NF) kr[f % KP] = kread(f + KP);
+          sacc[f / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[f % NS], sacc[f / NS], 0, 0, 0);
         }
+#if TBS_KPF_PIN
+        __builtin_amdgcn_sched_group_barrier(0x100, KP, 0);
+#pragma unroll
+        for (int f = 0; f < NF - KP; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, KP, 0);
+#endif
       }
       TBS_PRIO_LO();
       TBS_SCHED_FENCE();
