@@ -45,11 +45,12 @@ def test_struct_layout_matches_header():
 
 def test_group_size():
     L = tbs.lib()
-    assert L.attn_group_size(ctypes.byref(_problem())) == 2
-    assert L.attn_group_size(ctypes.byref(_problem(block=128))) == 1
+    # bf16: 256 query rows per work item; fp32: one block
+    assert L.attn_group_size(ctypes.byref(_problem())) == 4
+    assert L.attn_group_size(ctypes.byref(_problem(block=128))) == 2
     assert L.attn_group_size(ctypes.byref(_problem(dtype=1))) == 1
     assert L.attn_group_size(ctypes.byref(_problem(d=80))) == 0
-    assert _problem(N=1000).items == 40 * 8
+    assert _problem(N=1000).items == 40 * 4
 
 
 def test_workspace_sizes():

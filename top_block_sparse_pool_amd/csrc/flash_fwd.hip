@@ -151,6 +151,11 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 #define TBS_SCHED_FENCE() ((void)0)
 #endif
 
+template <int S>
+struct Stage {
+  static constexpr int value = S;
+};
+
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
@@ -219,6 +224,16 @@ struct TileLoader {
         : "=&s"(saved)
         : "s"(lds_addr), "v"(voff), "s"(r)
         : "memory");
+  }
+
+  // One tile (K or V) of rows key0 .. key0+63 into dst.
+  __device__ __forceinline__ void issue_one(const unsigned char* g, int key0, int N, TBS_LDS unsigned char* dst,
+                                            int wave) const {
+    const u32x4 r = rsrc(g + static_cast<long long>(key0) * ROWB, (N - key0) * ROWB);
+    const unsigned l = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)dst);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j)
+      dma16(r, static_cast<int>(j * NW * 1024 + base[j & 1]), l + static_cast<unsigned>((j * NW + wave) * 1024));
   }
 
   __device__ __forceinline__ void issue(const unsigned char* kg, const unsigned char* vg, int key0, int N,
@@ -303,6 +318,28 @@ __global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2
   TileLoader<D, NW> loader;
   loader.init(wave, lane);
   const int krow0 = swap_bits23(col);   // K operand row: bits 2 and 3 swapped
+
+  // Lane byte offsets of the MFMA operands inside a K or V tile.  K (A
+  // operand of S^T): row krow0 (+32 for the second half), 16-byte chunk
+  // 2s + h of k-step s.  V^T (A operand of O^T, read transposed): for
+  // 32-dim tile mo and half-read hf, row 8h + 4hf + (lane&15)/4 and dims
+  // 32mo + 16((lane>>4)&1) + 4(lane&3) .. +3; key step kk adds 16 rows.  The
+  // chunk swizzle depends on the low four row bits only, which neither the
+  // half (+32 rows) nor the key step (+16 rows) changes, so both are
+  // immediate offsets.
+  unsigned koff[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) koff[s] = krow0 * ROWB + (((2 * s + h) ^ chunk_swz<D>(krow0)) * 16);
+  unsigned voff[NO][2];
+#pragma unroll
+  for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int ii = lane & 15;
+      const int row = 8 * h + 4 * hf + (ii >> 2);
+      const int dim = 32 * mo + 16 * ((lane >> 4) & 1) + 4 * (ii & 3);
+      voff[mo][hf] = row * ROWB + ((dim >> 3) ^ chunk_swz<D>(row)) * 16 + (dim & 7) * 2;
+    }
 
   for (;;) {
     if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
@@ -394,44 +431,46 @@ __global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int mo = 0; mo < NO; ++mo)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc_o[mo][e] = 0.f;
+    // Running maximum (raw logits), its scaled value (0 while no finite
+    // logit has been seen) and the threshold past which it is moved.
     float m_run = -INFINITY;
+    float m_b = 0.f;
+    float m_thr = -INFINITY;
     float l_run = 0.f;
+    const float grow_span = 8.f / sl2;   // weights stay <= 2^8 below it
 
-    if (nt > 0) loader.issue(kg, vg, tile_key0(0), p.N, lds, lds + TILEB, wave);
-
-    for (int t = 0; t < nt; ++t) {
-      const int st = t & 1;
-      TBS_LDS unsigned char* lk = lds + st * 2 * TILEB;
+    // One key tile.  ST is the LDS stage (tile t lives in stage t & 1); it is
+    // a compile-time constant so that every LDS operand address below is a
+    // loop-invariant register plus an immediate offset.
+    auto tile = [&](auto stage, int t) {
+      constexpr int ST = decltype(stage)::value;
+      TBS_LDS unsigned char* lk = lds + ST * 2 * TILEB;
       TBS_LDS unsigned char* lv = lk + TILEB;
       const int key0 = tile_key0(t);
       wait_vmem();
       __syncthreads();
       if (t + 1 < nt) {
-        TBS_LDS unsigned char* nk = lds + (st ^ 1) * 2 * TILEB;
+        TBS_LDS unsigned char* nk = lds + (ST ^ 1) * 2 * TILEB;
         loader.issue(kg, vg, tile_key0(t + 1), p.N, nk, nk + TILEB, wave);
       }
-      if (!tile_mine(t, key0)) continue;
+      if (!tile_mine(t, key0)) return;
 
       // S^T = K Q^T for 64 keys x 32 queries, as two independent 32-key
       // halves (mt).  Both MFMA chains are issued first; the softmax of half 0
       // then runs on the VALU while half 1's MFMAs execute, and half 0's P V
-      // MFMAs run while half 1's softmax does.
+      // MFMAs run while half 1's softmax does.  K fragments stream through a
+      // ring of TBS_KPF registers, read that many MFMAs ahead, so LDS latency
+      // overlaps the matrix core.  Fragment f is half f / NS, k-step f % NS.
       f32x16 sacc[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-      // K fragments stream through a ring of TBS_KPF registers, read that many
-      // MFMAs ahead, so LDS latency overlaps the matrix core instead of
-      // stalling every product.  Fragment f is half f / NS, k-step f % NS.
       {
         constexpr int NF = 2 * NS;
         constexpr int KP = TBS_KPF < NF ? TBS_KPF : NF;
-        const int kswz = chunk_swz<D>(krow0);   // the same for both halves
-        const TBS_LDS unsigned char* kbase = lk + krow0 * ROWB;
         auto kread = [&](int f) -> bf16x8 {
-          const int pch = (2 * (f % NS) + h) ^ kswz;
-          return *(const TBS_LDS bf16x8*)(kbase + (f / NS) * 32 * ROWB + pch * 16);
+          return *(const TBS_LDS bf16x8*)(lk + (f / NS) * 32 * ROWB + koff[f % NS]);
         };
         bf16x8 kr[KP];
         TBS_PRIO_HI();
@@ -457,8 +496,6 @@ __global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2
       TBS_SCHED_FENCE();
 
       const bool need_mask = (key0 + kKeyTile > p.N) || (MODE == kCausal && key0 + kKeyTile - 1 > q0w);
-      const int g = lane >> 4;
-      const int ii = lane & 15;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         // Mask keys past the sequence end (ragged tail) and, if causal, keys
@@ -476,26 +513,33 @@ __global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2
         float mz = max3f(max3f(sacc[mt][10], sacc[mt][11], sacc[mt][12]), sacc[mt][13], sacc[mt][14]);
         mx = max3f(mx, my, fmaxf(mz, sacc[mt][15]));
         mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const bool grow = (m_run == -INFINITY) ? (m_new != -INFINITY) : ((m_new - m_run) * sl2 > 8.f);
+        // The reference maximum of a row moves only when the tile maximum
+        // exceeds it by more than 2^8 in weight (any reference gives the exact
+        // result; the bound keeps every weight <= 2^8).  Lanes l and l^32 hold
+        // the same row and take the same decision.
+        const bool grow = mx > m_thr;
         if (__any(grow)) {
-          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * sl2);
+          const float alpha = grow ? fast_exp2((m_run - mx) * sl2) : 1.f;   // 0 on the first move
 #pragma unroll
           for (int mo = 0; mo < NO; ++mo)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc_o[mo][e] *= alpha;
           l_run *= alpha;
-          m_run = m_new;
+          if (grow) {
+            m_run = mx;
+            m_b = mx * sl2;
+            m_thr = mx + grow_span;
+          }
         }
-        const float mb = (m_run == -INFINITY) ? 0.f : m_run * sl2;
 
+        // Weights in fp32 (their row sum) and rounded to bf16 (the P V operand).
         bf16x8 pb[2];
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2, -mb));
+            const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2, -m_b));
             ls[e & 3] += pv;
             pb[t2][e] = static_cast<__bf16>(pv);
           }
@@ -503,29 +547,437 @@ __global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2
 
         // O^T += V^T P^T for key steps kk = 2mt, 2mt+1 (keys 16kk .. 16kk+15);
         // lane (h, col) supplies P for keys 16kk + 8h + 0..7.  V^T comes from
-        // two transposed reads: 16-lane group g reads rows 16kk + 8h + 4hf + 0..3
-        // and dims 32mo + 16(g&1) + 0..15.
+        // two transposed reads per 32-dim tile (voff).
         TBS_PRIO_HI();
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
           const int kk = 2 * mt + t2;
 #pragma unroll
           for (int mo = 0; mo < NO; ++mo) {
-            bf16x4 part[2];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              const int row = 16 * kk + 8 * h + 4 * hf + (ii >> 2);
-              const int dim = 32 * mo + 16 * (g & 1) + 4 * (ii & 3);
-              const int pch = (dim >> 3) ^ chunk_swz<D>(row);
-              const int off = row * ROWB + pch * 16 + (dim & 7) * 2;
-              part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + off));
-            }
-            const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + 16 * kk * ROWB + voff[mo][0]));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + 16 * kk * ROWB + voff[mo][1]));
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t2], acc_o[mo], 0, 0, 0);
           }
         }
         TBS_PRIO_LO();
       }
+    };
+
+    if (nt > 0) loader.issue(kg, vg, tile_key0(0), p.N, lds, lds + TILEB, wave);
+    for (int t = 0; t < nt; t += 2) {
+      tile(Stage<0>{}, t);
+      if (t + 1 < nt) tile(Stage<1>{}, t + 1);
+    }
+
+    // Epilogue: lane (h, col) holds O[qrow][32mo + 8j + 4h + r] in acc_o[mo][4j + r].
+    const float l_tot = l_run + xor32(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (active && qrow < p.N) {
+      unsigned short* orow = static_cast<unsigned short*>(p.o) +
+                             (static_cast<long long>(gi.bh) * p.N + qrow) * D;
+#pragma unroll
+      for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = static_cast<__bf16>(acc_o[mo][4 * j + r] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * mo + 8 * j + 4 * h) = ov;
+        }
+      if (h == 0 && p.lse)
+        p.lse[static_cast<long long>(gi.bh) * p.N + qrow] =
+            l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+    }
+  }
+
+  if (tid == 0) {
+    if (p.prof) p.prof[2 * blockIdx.x + 1] = wall_clock64();
+    // The last workgroup to finish leaves the queue counters at zero.
+    if (atomicAdd(p.ctrl + 1, 1u) == gridDim.x - 1) {
+      atomicExch(p.ctrl, 0u);
+      atomicExch(p.ctrl + 1, 0u);
+    }
+  }
+}
+
+// ------------------------------------------------------- bf16, two groups ---
+//
+// Workgroup of 8 waves covering 256 query rows: G = 256 / block consecutive
+// query blocks of one (b, h), each 32-row slice owned by one wave.  Waves
+// w and w + 4 share a SIMD, so the workgroup splits into two groups (waves
+// 0-3 and 4-7) with one wave of each group on every SIMD.  A wave's work on
+// tile t is an MFMA part M(t) = S(t) = K(t) Q^T, then O^T += V^T P^T for
+// tile t - 1, and a VALU part V(t) = the online-softmax update of tile t.
+// The workgroup advances in steps separated by barriers; group 1 runs one
+// step behind group 0, so on every SIMD one wave issues MFMAs while the other
+// computes exponentials and the matrix core and the VALU work side by side:
+//
+//   step       2t            2t+1          2t+2
+//   group 0    M(t)          V(t)          M(t+1)
+//   group 1    V(t-1)        M(t)          V(t)
+//
+// K(t) is read in steps 2t and 2t+1 and V(t) in steps 2t+2 and 2t+3; both
+// have two LDS stages, and the copies of K(t+1) and V(t) start at step 2t and
+// must land by the end of step 2t+1, two steps ahead of their first use.
+constexpr int kWaves = 8;
+
+template <int D, int BQ, int MODE>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_bf16_pp(
+    FwdParams p) {
+  constexpr int G = 256 / BQ;           // query blocks per work item
+  constexpr int NWB = BQ / 32;          // waves per member block
+  constexpr int NT = kWaves * 64;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = kKeyTile * ROWB;
+  constexpr int SPB = BQ / kKeyTile;    // key tiles per key block
+  constexpr int NS = D / 16;            // k-steps of S^T
+  constexpr int NO = D / 32;            // 32-dim tiles of O^T
+  // LDS: K stage 0, K stage 1, V stage 0, V stage 1.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILEB];
+  __shared__ unsigned s_bm[MODE == kSparse ? G * kMaxListWords : 1];
+  __shared__ unsigned short s_lj[MODE == kSparse ? kMaxListBlocks : 1];
+  __shared__ unsigned char s_lm[MODE == kSparse ? kMaxListBlocks : 1];
+  __shared__ int s_unit;
+  __shared__ int s_nlist;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+  const int grp = wave >> 2;
+  const int member = wave / NWB;
+  const float sl2 = p.scale_log2;
+  TBS_LDS unsigned char* lds = (TBS_LDS unsigned char*)smem;
+
+  if (p.prof && tid == 0) p.prof[2 * blockIdx.x] = wall_clock64();
+
+  const unsigned char* qg_all = static_cast<const unsigned char*>(p.q);
+  const unsigned char* kg_all = static_cast<const unsigned char*>(p.k);
+  const unsigned char* vg_all = static_cast<const unsigned char*>(p.v);
+  TileLoader<D, kWaves> loader;
+  loader.init(wave, lane);
+  const int krow0 = swap_bits23(col);   // K operand row: bits 2 and 3 swapped
+
+  // Lane byte offsets of the MFMA operands inside a K or V tile.  K (A
+  // operand of S^T): row krow0 (+32 for the second half), 16-byte chunk
+  // 2s + h of k-step s.  V^T (A operand of O^T, read transposed): for
+  // 32-dim tile mo and half-read hf, row 8h + 4hf + (lane&15)/4 and dims
+  // 32mo + 16((lane>>4)&1) + 4(lane&3) .. +3; key step kk adds 16 rows.  The
+  // chunk swizzle depends on the low four row bits only, which neither the
+  // half (+32 rows) nor the key step (+16 rows) changes, so both are
+  // immediate offsets.
+  unsigned koff[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) koff[s] = krow0 * ROWB + (((2 * s + h) ^ chunk_swz<D>(krow0)) * 16);
+  unsigned voff[NO][2];
+#pragma unroll
+  for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int ii = lane & 15;
+      const int row = 8 * h + 4 * hf + (ii >> 2);
+      const int dim = 32 * mo + 16 * ((lane >> 4) & 1) + 4 * (ii & 3);
+      voff[mo][hf] = row * ROWB + ((dim >> 3) ^ chunk_swz<D>(row)) * 16 + (dim & 7) * 2;
+    }
+
+  for (;;) {
+    if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
+    __syncthreads();
+    const int qpos = s_unit;
+    __syncthreads();
+    if (qpos >= p.U) break;
+
+    GroupInfo<BQ, G, MODE> gi;
+    gi.decode(p, qpos);
+    const long long head_off = static_cast<long long>(gi.bh) * p.N * ROWB;
+    const unsigned char* kg = kg_all + head_off;
+    const unsigned char* vg = vg_all + head_off;
+    const bool active = member < gi.gsz;
+    const int qblk = gi.i0 + member;
+    const int q0w = qblk * BQ + (wave % NWB) * 32;
+    const int qrow = q0w + col;
+
+    // Tile list of the work item: the union of its blocks' key blocks, with
+    // a bit per member block saying whether that block selected it.
+    int nt;
+    if (MODE == kSparse) {
+      const int nwords = (p.nb + 31) / 32;
+      for (int x = tid; x < G * kMaxListWords; x += NT) s_bm[x] = 0u;
+      __syncthreads();
+      for (int m = 0; m < gi.gsz; ++m) {
+        const long long u = static_cast<long long>(gi.bh) * p.nb + gi.i0 + m;
+        const int cnt = min(max(p.row_cnt[u], 0), p.nb);
+        const int32_t* lst = p.row_idx + u * p.nb;
+        for (int x = tid; x < cnt; x += NT) {
+          const int j = min(max(lst[x], 0), p.nb - 1);
+          atomicOr(&s_bm[m * kMaxListWords + (j >> 5)], 1u << (j & 31));
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        unsigned wm[G];
+        unsigned un = 0u;
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+          wm[m] = lane < nwords ? s_bm[m * kMaxListWords + lane] : 0u;
+          un |= wm[m];
+        }
+        const int c = __popc(un);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        int pos = incl - c;
+        while (un) {
+          const int bit = __ffs(un) - 1;
+          un &= un - 1;
+          unsigned msk = 0u;
+#pragma unroll
+          for (int m = 0; m < G; ++m) msk |= ((wm[m] >> bit) & 1u) << m;
+          s_lj[pos] = static_cast<unsigned short>(lane * 32 + bit);
+          s_lm[pos] = static_cast<unsigned char>(msk);
+          ++pos;
+        }
+        if (lane == 63) s_nlist = incl;
+      }
+      __syncthreads();
+      const int nl = s_nlist;
+      nt = nl * SPB;
+      if (SPB > 1 && nl > 0 && s_lj[nl - 1] == p.nb - 1) {
+        const int tail = p.N - (p.nb - 1) * BQ;
+        nt = (nl - 1) * SPB + (tail + kKeyTile - 1) / kKeyTile;
+      }
+    } else if (MODE == kDense) {
+      nt = (p.N + kKeyTile - 1) / kKeyTile;
+    } else {
+      nt = (min(p.N, (gi.i0 + gi.gsz) * BQ) + kKeyTile - 1) / kKeyTile;
+    }
+    auto tile_key0 = [&](int t) __attribute__((always_inline)) -> int {
+      if (MODE == kSparse) return __builtin_amdgcn_readfirstlane(s_lj[t / SPB]) * BQ + (t % SPB) * kKeyTile;
+      return t * kKeyTile;
+    };
+    auto tile_mine = [&](int t) __attribute__((always_inline)) -> bool {
+      if (!active) return false;
+      if (MODE == kSparse) return (__builtin_amdgcn_readfirstlane(s_lm[t / SPB]) >> member) & 1;
+      if (MODE == kCausal) return t * kKeyTile < (qblk + 1) * BQ;
+      return true;
+    };
+
+    // Q^T as B operand: lane (h, col) holds Q[qrow][16s + 8h .. +7].
+    bf16x8 qf[NS];
+    {
+      const unsigned char* qr = qg_all + head_off + static_cast<long long>(min(qrow, p.N - 1)) * ROWB;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + (16 * s + 8 * h) * 2);
+    }
+
+    f32x16 acc_o[NO];
+#pragma unroll
+    for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc_o[mo][e] = 0.f;
+    // Running maximum (raw logits), its scaled value (0 while no finite
+    // logit has been seen) and the threshold past which it is moved.
+    float m_run = -INFINITY;
+    float m_b = 0.f;
+    float m_thr = -INFINITY;
+    float l_run = 0.f;
+    const float grow_span = 8.f / sl2;   // weights stay <= 2^8 below it
+    f32x16 sacc[2];                      // S^T of the current tile (two 32-key halves)
+    bf16x8 pb[2][2];                     // P^T of the previous tile, per half and key step
+
+    // M(t): S(t) from K stage KS, then O^T += V^T P^T of tile t - 1 from V
+    // stage VS.  All 32 A-operand fragments (16 of K, 16 of V^T) stream
+    // through one ring of TBS_KPF registers, read that many MFMAs ahead.
+    auto mpart = [&](auto ks, auto vs, int t) __attribute__((always_inline)) {
+      constexpr int KS = decltype(ks)::value;
+      constexpr int VS = decltype(vs)::value;
+      const bool s_on = t < nt && tile_mine(t);
+      const bool pv_on = t >= 1 && t - 1 < nt && tile_mine(t - 1);
+      const TBS_LDS unsigned char* lk = lds + KS * TILEB;
+      const TBS_LDS unsigned char* lv = lds + (2 + VS) * TILEB;
+      constexpr int NF = 2 * NS;          // fragments of each product
+      constexpr int KP = TBS_KPF < NF ? TBS_KPF : NF;
+      if (s_on) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+        auto kread = [&](int f) __attribute__((always_inline)) -> bf16x8 {
+          return *(const TBS_LDS bf16x8*)(lk + (f / NS) * 32 * ROWB + koff[f % NS]);
+        };
+        bf16x8 kr[KP];
+#pragma unroll
+        for (int f = 0; f < KP; ++f) kr[f] = kread(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const bf16x8 a = kr[f % KP];
+          if (f + KP < NF) kr[f % KP] = kread(f + KP);
+          sacc[f / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[f % NS], sacc[f / NS], 0, 0, 0);
+        }
+#if TBS_KPF_PIN
+        __builtin_amdgcn_sched_group_barrier(0x100, KP, 0);
+#pragma unroll
+        for (int f = 0; f < NF - KP; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, KP, 0);
+#endif
+      }
+      if (pv_on) {
+        // Fragment f = kk * NO + mo: key step kk (keys 16kk .. 16kk+15), dims
+        // 32mo .. 32mo+31; lane (h, col) supplies P for keys 16kk + 8h + 0..7.
+        constexpr int NV = 4 * NO;
+        constexpr int VP = TBS_KPF < NV ? TBS_KPF : NV;
+        auto vread = [&](int f) __attribute__((always_inline)) -> bf16x8 {
+          const int kk = f / NO, mo = f % NO;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + 16 * kk * ROWB + voff[mo][0]));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + 16 * kk * ROWB + voff[mo][1]));
+          return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 vr[VP];
+#pragma unroll
+        for (int f = 0; f < VP; ++f) vr[f] = vread(f);
+#pragma unroll
+        for (int f = 0; f < NV; ++f) {
+          const bf16x8 a = vr[f % VP];
+          if (f + VP < NV) vr[f % VP] = vread(f + VP);
+          const int kk = f / NO, mo = f % NO;
+          acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk >> 1][kk & 1], acc_o[mo], 0, 0, 0);
+        }
+#if TBS_KPF_PIN
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VP, 1);
+#pragma unroll
+        for (int f = 0; f < NV - VP; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, VP, 1);
+#endif
+      }
+    };
+
+    // V(t): online-softmax update with the logits of tile t; leaves P^T(t) in
+    // pb.  The whole tile (both halves) shares one reference maximum: its
+    // P V product is accumulated only in M(t+1), after the rescale below has
+    // been applied to everything accumulated so far.
+    auto vpart = [&](int t) __attribute__((always_inline)) {
+      if (!(t < nt && tile_mine(t))) return;
+      const int key0 = tile_key0(t);
+      const bool need_mask = (key0 + kKeyTile > p.N) || (MODE == kCausal && key0 + kKeyTile - 1 > q0w);
+      if (need_mask) {
+        // Mask keys past the sequence end (ragged tail) and, if causal, keys
+        // after the query.  Lane value e of half mt is key 32mt + 16(e>>3) + 8h + (e&7).
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = key0 + 32 * mt + 16 * (e >> 3) + 8 * h + (e & 7);
+            const bool bad = key >= p.N || (MODE == kCausal && key > qrow);
+            if (bad) sacc[mt][e] = -INFINITY;
+          }
+      }
+      float m4[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        m4[2 * mt] = max3f(max3f(sacc[mt][0], sacc[mt][1], sacc[mt][2]), max3f(sacc[mt][3], sacc[mt][4], sacc[mt][5]),
+                           max3f(sacc[mt][6], sacc[mt][7], sacc[mt][8]));
+        m4[2 * mt + 1] = max3f(max3f(sacc[mt][9], sacc[mt][10], sacc[mt][11]),
+                               max3f(sacc[mt][12], sacc[mt][13], sacc[mt][14]), sacc[mt][15]);
+      }
+      float mx = max3f(m4[0], m4[1], max3f(m4[2], m4[3], m4[3]));
+      const float mo32 = xor32(mx);
+      mx = max3f(mx, mo32, mo32);
+      // The reference maximum of a row moves only when the tile maximum
+      // exceeds it by more than 2^8 in weight (any reference gives the exact
+      // result; the bound keeps every weight <= 2^8).  Lanes l and l^32 hold
+      // the same row and take the same decision.
+      const bool grow = mx > m_thr;
+      if (__any(grow)) {
+        const float alpha = grow ? fast_exp2((m_run - mx) * sl2) : 1.f;   // 0 on the first move
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc_o[mo][e] *= alpha;
+        l_run *= alpha;
+        if (grow) {
+          m_run = mx;
+          m_b = mx * sl2;
+          m_thr = mx + grow_span;
+        }
+      }
+      // Weights in fp32 (their row sum) and rounded to bf16 (the P V operand).
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2, -m_b));
+            ls[e & 3] += pv;
+            pb[mt][t2][e] = static_cast<__bf16>(pv);
+          }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+
+    auto step_barrier = []() __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    // Copies started at global step 2t: K(t+1) into K stage (t+1)&1 and
+    // V(t) into V stage t&1 (P = t&1); every wave issues its share.
+    auto issue = [&](auto pp, int t) __attribute__((always_inline)) {
+      constexpr int P = decltype(pp)::value;
+      if (t + 1 < nt) loader.issue_one(kg, tile_key0(t + 1), p.N, lds + (P ^ 1) * TILEB, wave);
+      if (t < nt) loader.issue_one(vg, tile_key0(t), p.N, lds + (2 + P) * TILEB, wave);
+    };
+
+    // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(nt), one
+    // barrier after each part; group 1 first passes one empty step, which
+    // puts it one step behind group 0.  Global step 2t starts the copies of
+    // K(t+1) and V(t) (group 0 at the start of M(t), group 1 at the start of
+    // V(t-1)); each wave waits for its copies at the end of global step 2t+1
+    // (group 0 after V(t), group 1 after M(t)), so they have landed before
+    // the barrier that opens step 2t+2.  The loop is unrolled twice so the
+    // LDS stages of K(t) and V(t-1) are compile-time constants.
+    if (nt > 0) {
+      loader.issue_one(kg, tile_key0(0), p.N, lds, wave);
+      wait_vmem();
+      step_barrier();
+      if (grp == 1) {
+        issue(Stage<0>{}, 0);
+        step_barrier();
+      }
+      for (int t = 0;; t += 2) {
+        if (grp == 0) issue(Stage<0>{}, t);
+        mpart(Stage<0>{}, Stage<1>{}, t);
+        if (grp == 1) wait_vmem();
+        step_barrier();
+        if (t == nt) break;
+        if (grp == 1) issue(Stage<1>{}, t + 1);
+        vpart(t);
+        if (grp == 0) wait_vmem();
+        step_barrier();
+
+        if (grp == 0) issue(Stage<1>{}, t + 1);
+        mpart(Stage<1>{}, Stage<0>{}, t + 1);
+        if (grp == 1) wait_vmem();
+        step_barrier();
+        if (t + 1 == nt) break;
+        if (grp == 1) issue(Stage<0>{}, t + 2);
+        vpart(t + 1);
+        if (grp == 0) wait_vmem();
+        step_barrier();
+      }
+      if (grp == 0) step_barrier();
     }
 
     // Epilogue: lane (h, col) holds O[qrow][32mo + 8j + 4h + r] in acc_o[mo][4j + r].
@@ -714,14 +1166,30 @@ typedef void (*KernelFn)(FwdParams);
 
 // Query blocks per work item: two 64-row blocks share a workgroup (4 waves);
 // 128-row blocks go alone (4 waves).  fp32 inputs use single blocks.
+#ifndef TBS_PINGPONG
+#define TBS_PINGPONG 1
+#endif
+#if TBS_PINGPONG
+constexpr int group_for(int dtype, int block) { return dtype == 0 ? 256 / block : 1; }
+#else
 constexpr int group_for(int dtype, int block) { return (dtype == 0 && block == 64) ? 2 : 1; }
+#endif
 
 // Every variant is instantiated explicitly: referencing a kernel template
 // only through a function-pointer table does not always emit its host stub.
-#define TBS_INSTANTIATE(D, BQ)                                                       \
+#if TBS_PINGPONG
+#define TBS_INSTANTIATE_BF16(D, BQ)                                      \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, kSparse>(FwdParams); \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, kDense>(FwdParams);  \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, kCausal>(FwdParams);
+#else
+#define TBS_INSTANTIATE_BF16(D, BQ)                                                         \
   template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kSparse>(FwdParams); \
   template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kDense>(FwdParams);  \
-  template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kCausal>(FwdParams); \
+  template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kCausal>(FwdParams);
+#endif
+#define TBS_INSTANTIATE(D, BQ)                                                       \
+  TBS_INSTANTIATE_BF16(D, BQ)                                                        \
   template __global__ void flash_fwd_f32<D, BQ, kSparse>(FwdParams);                  \
   template __global__ void flash_fwd_f32<D, BQ, kDense>(FwdParams);                   \
   template __global__ void flash_fwd_f32<D, BQ, kCausal>(FwdParams);
@@ -733,9 +1201,14 @@ TBS_INSTANTIATE(64, 128)
 
 template <int D, int BQ>
 KernelFn pick_mode(int dtype, int mode) {
+#if TBS_PINGPONG
+  static const KernelFn bf16_fns[3] = {flash_fwd_bf16_pp<D, BQ, kSparse>, flash_fwd_bf16_pp<D, BQ, kDense>,
+                                       flash_fwd_bf16_pp<D, BQ, kCausal>};
+#else
   constexpr int G = group_for(0, BQ);
   static const KernelFn bf16_fns[3] = {flash_fwd_bf16<D, BQ, G, kSparse>, flash_fwd_bf16<D, BQ, G, kDense>,
                                        flash_fwd_bf16<D, BQ, G, kCausal>};
+#endif
   static const KernelFn f32_fns[3] = {flash_fwd_f32<D, BQ, kSparse>, flash_fwd_f32<D, BQ, kDense>,
                                       flash_fwd_f32<D, BQ, kCausal>};
   return dtype == 0 ? bf16_fns[mode] : f32_fns[mode];
@@ -750,6 +1223,15 @@ KernelFn pick_kernel(const Shape& s, int mode) {
 
 int group_size(const Shape& s) { return group_for(s.dtype, s.block); }
 
+// Threads per workgroup: 8 waves for bf16 (two groups of four), one wave per
+// 32 query rows for fp32.
+int fwd_threads(const Shape& s) {
+#if TBS_PINGPONG
+  if (s.dtype == 0) return kWaves * 64;
+#endif
+  return group_size(s) * s.block * 2;
+}
+
 long long work_items(const Shape& s) {
   const int G = group_size(s);
   return static_cast<long long>(s.B) * s.H * ((s.nb + G - 1) / G);
@@ -757,7 +1239,7 @@ long long work_items(const Shape& s) {
 
 int fwd_workers(const Shape& s, int mode) {
   KernelFn fn = pick_kernel(s, mode);
-  const int threads = group_size(s) * s.block * 2;
+  const int threads = fwd_threads(s);
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0) !=
           hipSuccess ||
@@ -790,7 +1272,7 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
   p.scale_log2 = static_cast<float>(s.scale * 1.4426950408889634);
   const int grid = fwd_workers(s, mode);
   KernelFn fn = pick_kernel(s, mode);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(p.G * s.block * 2), 0, stream, p);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(fwd_threads(s)), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -17,15 +17,16 @@
 // that finishes early simply takes the next unit, from the next window.
 //
 // Work items: the persistent kernel processes groups of G consecutive query
-// blocks of one head (G = 2 for 64-row blocks), so the list orders groups;
-// a group costs the summed selected-block counts of its blocks.
+// blocks of one head (256 query rows: G = 4 for 64-row blocks, 2 for 128-row
+// blocks), so the list orders groups; a group costs the summed
+// selected-block counts of its blocks.
 //
 // schedule_kernel: one workgroup per window, a stable counting sort by cost
 //   descending.  Each wave owns a contiguous slice of the window's unit ids
 //   and counts costs into its own LDS histogram; a prefix over (cost
 //   descending, wave ascending) gives every (wave, cost) pair its first output
 //   slot; each wave then walks its slice in order, ranking equal costs inside
-//   a 64-unit batch with ballots over the 11 cost bits, so equal costs keep
+//   a 64-unit batch with ballots over the cost bits, so equal costs keep
 //   ascending unit ids.
 // lpt_kernel: optional single-wave greedy longest-processing-time model of
 //   the same order over W workers, for reporting load balance.
@@ -37,8 +38,10 @@ namespace {
 
 constexpr int kSchedThreads = 256;
 constexpr int kSchedWaves = kSchedThreads / kWave;
-constexpr int kMaxCost = 2048;  // a work item holds at most 2 blocks of <= 1024 key blocks
-constexpr int kCostBits = 12;   // costs are in [0, 2048]
+constexpr int kMaxCost = 4096;  // a work item holds at most 4 blocks of <= 1024 key blocks
+constexpr int kCostBits = 13;   // costs are in [0, 4096]
+// LDS histogram: one row of G * nb + 1 counters per wave.
+constexpr size_t sched_lds_bytes(int maxc) { return sizeof(int) * kSchedWaves * (maxc + 1); }
 
 // Cost of work item g: the summed selected-block counts of its query blocks.
 __device__ __forceinline__ int item_cost(const int32_t* __restrict__ row_cnt, int g, int nb, int G, int ng) {
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
                                                                  int window_items,
                                                                  int32_t* __restrict__ work_list,
                                                                  uint32_t* __restrict__ ctrl) {
-  __shared__ int cnt[kSchedWaves][kMaxCost + 1];
+  extern __shared__ int sched_hist[];   // [kSchedWaves][ncost]
   __shared__ int ctot[kSchedThreads];
   __shared__ int cexc[kSchedThreads];
   __shared__ int wtot[kSchedWaves];
@@ -64,8 +67,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   const int lane = tid & (kWave - 1);
   const int maxc = G * nb;
   const int ncost = maxc + 1;   // cost values 0..maxc
+  auto cnt = [&](int w, int c) -> int& { return sched_hist[w * ncost + c]; };
 
-  for (int x = tid; x < kSchedWaves * (kMaxCost + 1); x += kSchedThreads) (&cnt[0][0])[x] = 0;
+  for (int x = tid; x < kSchedWaves * ncost; x += kSchedThreads) sched_hist[x] = 0;
   __syncthreads();
 
   // This workgroup's window: item ids [w0, w1); output slots start at w0.
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   const int chunk = (w1 - w0 + kSchedWaves - 1) / kSchedWaves;
   const int ubeg = min(w1, w0 + wave * chunk);
   const int uend = min(w1, ubeg + chunk);
-  for (int u = ubeg + lane; u < uend; u += kWave) atomicAdd(&cnt[wave][item_cost(row_cnt, u, nb, G, ng)], 1);
+  for (int u = ubeg + lane; u < uend; u += kWave) atomicAdd(&cnt(wave, item_cost(row_cnt, u, nb, G, ng)), 1);
   __syncthreads();
 
   // Position x = 0..ncost-1 enumerates costs in descending order (c = maxc - x).
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
     const int x = xbeg + e;
     if (x < ncost) {
       const int c = maxc - x;
-      for (int w = 0; w < kSchedWaves; ++w) run += cnt[w][c];
+      for (int w = 0; w < kSchedWaves; ++w) run += cnt(w, c);
     }
   }
   ctot[tid] = run;
@@ -113,8 +117,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
       if (x < ncost) {
         const int c = maxc - x;
         for (int w = 0; w < kSchedWaves; ++w) {
-          const int t = cnt[w][c];
-          cnt[w][c] = off;
+          const int t = cnt(w, c);
+          cnt(w, c) = off;
           off += t;
         }
       }
@@ -136,10 +140,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
       same &= bit ? ones : ~ones;
     }
     int slot = 0;
-    if (valid) slot = cnt[wave][c];
+    if (valid) slot = cnt(wave, c);
     if (valid) work_list[slot + __popcll(same & lt)] = u;
     const bool last_of_group = valid && ((same >> lane) >> 1) == 0;
-    if (last_of_group) cnt[wave][c] = slot + __popcll(same);
+    if (last_of_group) cnt(wave, c) = slot + __popcll(same);
     __builtin_amdgcn_wave_barrier();
   }
   if (blockIdx.x == 0 && tid < static_cast<int>(kCtrlBytes / sizeof(uint32_t))) ctrl[tid] = 0u;
@@ -190,7 +194,13 @@ hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int head_wind
   const int items = BH * ng;
   const int hw = (head_window <= 0 || head_window > BH) ? BH : head_window;
   const int windows = (BH + hw - 1) / hw;
-  hipLaunchKernelGGL(schedule_kernel, dim3(windows), dim3(kSchedThreads), 0, stream, row_cnt, items, s.nb, G, ng,
+  const int maxc = G * s.nb;
+  if (maxc > kMaxCost) return hipErrorInvalidValue;
+  const size_t lds = sched_lds_bytes(maxc);
+  const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(schedule_kernel),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(schedule_kernel, dim3(windows), dim3(kSchedThreads), lds, stream, row_cnt, items, s.nb, G, ng,
                      hw * ng, work_list, ctrl);
   return hipGetLastError();
 }
