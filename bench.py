@@ -29,6 +29,36 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 METRIC = "executed TFLOP/s + ms/call, top-p sparse attn fwd, N=32760 H=40 d=128 bf16"
+KERNEL_SOURCES = ("top_block_sparse_pool_amd/csrc/flash_fwd.hip", "top_block_sparse_pool_amd/csrc/device_common.h")
+TRAFFIC_SUMMARY = "profiles/flash_fwd_bf16_sparse_video-32k_traffic.md"
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the sparse attention kernel (FETCH_SIZE + WRITE_SIZE
+    counters, scaled by a plain copy of known size), read from the committed
+    rocprofv3 summary; None unless the summary covers this workload and was
+    taken on the kernel sources as they are now."""
+    import re
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        fields = dict(re.findall(r"^- (\w+): (\S+)\s*$", f.read(), flags=re.M))
+    if fields.get("workload") != workload or fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def executed_flops(mask: np.ndarray, n_tokens: int, block: int, head_dim: int) -> int:
@@ -234,9 +264,9 @@ def main():
                          "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),
                          "sparse_fwd_mean": float(t_fwd.mean()), "sparse_fwd_median": float(np.median(t_fwd))},
         "sparse_fwd_tflops": fwd_tflops,
-        "roofline": {"bound": "mfma", "kernel": "flash_fwd_bf16 (sparse)", "achieved": fwd_tflops,
+        "roofline": {"bound": "mfma", "kernel": "flash_fwd_bf16_pp (sparse)", "achieved": fwd_tflops,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": fwd_tflops / BF16_PEAK_TFLOPS,
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name)},
         "dense_same_shape": dense,
         "load_imbalance": lif,
         "cpu_baseline": cpu,
