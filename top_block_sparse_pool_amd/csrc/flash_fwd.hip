@@ -7,19 +7,19 @@
 // is exact attention); FVAttn review page, section 1 ("Top-p routing": each
 // query block attends only to its selected key blocks).
 //
-// Work unit: one query block (block rows) of one (b, h).  Workgroups are
-// persistent: each takes the next unit from a queue (the longest-first work
-// list, or natural order) with one atomic, so a heavy unit never waits
-// behind a fixed grid assignment.
+// Work item: 256 consecutive query rows of one (b, h) (for fp32: one query
+// block).  Workgroups are persistent: each takes the next item from a queue
+// (the longest-first work list, or natural order) with one atomic, so a heavy
+// item never waits behind a fixed grid assignment.
 //
-// bf16 kernel layout (per workgroup: block/32 waves, each owning 32 query rows):
+// bf16 kernel (8 waves, each owning 32 query rows; details at the kernel):
 //   * Key tiles of 64 keys.  K and V tiles are copied HBM -> LDS with
-//     buffer_load ... lds (16 bytes per lane, no VGPR staging), double-buffered:
-//     tile t+1 streams in while tile t is computed.  Rows are stored with an
-//     XOR swizzle of their 16-byte chunks so the MFMA operand reads below hit
-//     distinct LDS banks.
+//     buffer_load ... lds (16 bytes per lane, no VGPR staging), two stages
+//     each, two steps ahead of their use.  Rows are stored with an XOR
+//     swizzle of their 16-byte chunks so the MFMA operand reads hit distinct
+//     LDS banks.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K (A operand) from LDS, Q^T
-//     (B operand) held in registers for the whole unit.  Computing S
+//     (B operand) held in registers for the whole item.  Computing S
 //     transposed puts one query per lane (lanes l and l^32 share it), so the
 //     running max and sum of the online softmax are lane-local plus one
 //     permlane32 swap.
@@ -28,10 +28,13 @@
 //     exactly the B operand (P^T) the next product needs, with no shuffle.
 //   * O^T += V^T P^T on the same MFMA: V^T (A operand) comes straight from the
 //     row-major V tile through ds_read_b64_tr_b16 transposed reads.
-//   * Online softmax in fp32 with exp2 (scale*log2 e folded in); the running
-//     maximum is only moved when it grows by more than 2^8 somewhere in the
-//     wave (the result is exact for any reference maximum; the bound keeps
-//     every weight <= 256).  Weights are rounded to bf16 for the P V product.
+//   * Online softmax in fp32 with exp2 (scale*log2 e folded in); a row's
+//     reference maximum only moves when a tile's maximum exceeds it by more
+//     than 2^8 in weight (the result is exact for any reference maximum; the
+//     bound keeps every weight <= 256).  Weights are rounded to bf16 for the
+//     P V product.
+//   * The two waves of each SIMD alternate: one issues the MFMA part of a
+//     tile while the other runs the softmax of another.
 //   * Epilogue: O / l in fp32 -> bf16 (round to nearest even), LSE = m + ln l.
 //
 // fp32 kernel: same unit/tile/queue structure and the same transposed
@@ -123,32 +126,13 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
-// Wave priority while issuing MFMA chains: the SIMD arbiter then feeds the
-// matrix core first and fills the remaining issue slots with the other
-// wave's softmax VALU work.
-#ifndef TBS_MFMA_PRIO
-#define TBS_MFMA_PRIO 1
-#endif
-#if TBS_MFMA_PRIO
-#define TBS_PRIO_HI() __builtin_amdgcn_s_setprio(1)
-#define TBS_PRIO_LO() __builtin_amdgcn_s_setprio(0)
-#else
-#define TBS_PRIO_HI() ((void)0)
-#define TBS_PRIO_LO() ((void)0)
-#endif
-#ifndef TBS_FENCE_S
-#define TBS_FENCE_S 1
-#endif
+// MFMA A-operand fragments are read this many products ahead through a
+// register ring; TBS_KPF_PIN pins the read/MFMA interleave for the scheduler.
 #ifndef TBS_KPF
 #define TBS_KPF 4
 #endif
 #ifndef TBS_KPF_PIN
 #define TBS_KPF_PIN 1
-#endif
-#if TBS_FENCE_S
-#define TBS_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define TBS_SCHED_FENCE() ((void)0)
 #endif
 
 template <int S>
@@ -235,23 +219,6 @@ struct TileLoader {
     for (int j = 0; j < PER_WAVE; ++j)
       dma16(r, static_cast<int>(j * NW * 1024 + base[j & 1]), l + static_cast<unsigned>((j * NW + wave) * 1024));
   }
-
-  __device__ __forceinline__ void issue(const unsigned char* kg, const unsigned char* vg, int key0, int N,
-                                        TBS_LDS unsigned char* lds_k, TBS_LDS unsigned char* lds_v,
-                                        int wave) const {
-    const int bytes = (N - key0) * ROWB;
-    const u32x4 rk = rsrc(kg + static_cast<long long>(key0) * ROWB, bytes);
-    const u32x4 rv = rsrc(vg + static_cast<long long>(key0) * ROWB, bytes);
-    const unsigned lk = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)lds_k);
-    const unsigned lv = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)lds_v);
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const unsigned blk = static_cast<unsigned>((j * NW + wave) * 1024);
-      const int voff = static_cast<int>(j * NW * 1024 + base[j & 1]);
-      dma16(rk, voff, lk + blk);
-      dma16(rv, voff, lv + blk);
-    }
-  }
 };
 
 // A work item is a group of G consecutive query blocks of one (b, h).  The
@@ -282,324 +249,6 @@ struct GroupInfo {
     gsz = min(G, p.nb - i0);
   }
 };
-
-template <int D, int BQ, int G, int MODE>
-__global__ __launch_bounds__(G * BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_bf16(FwdParams p) {
-  constexpr int NWB = BQ / 32;          // waves per member block
-  constexpr int NW = G * NWB;           // waves per workgroup
-  constexpr int NT = NW * 64;
-  constexpr int ROWB = D * 2;
-  constexpr int TILEB = kKeyTile * ROWB;
-  constexpr int SPB = BQ / kKeyTile;    // key tiles per key block
-  constexpr int NS = D / 16;            // k-steps of S^T
-  constexpr int NO = D / 32;            // 32-dim tiles of O^T
-  static_assert(G == 1 || SPB == 1, "groups of 128-row blocks are not instantiated");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TILEB];
-  __shared__ unsigned s_bm[MODE == kSparse ? G * kMaxListWords : 1];
-  __shared__ unsigned short s_lj[MODE == kSparse ? kMaxListBlocks : 1];
-  __shared__ unsigned char s_lm[MODE == kSparse ? kMaxListBlocks : 1];
-  __shared__ int s_unit;
-  __shared__ int s_nlist;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int h = lane >> 5;
-  const int col = lane & 31;
-  const int member = wave / NWB;
-  const float sl2 = p.scale_log2;
-  TBS_LDS unsigned char* lds = (TBS_LDS unsigned char*)smem;
-
-  if (p.prof && tid == 0) p.prof[2 * blockIdx.x] = wall_clock64();
-
-  const unsigned char* qg_all = static_cast<const unsigned char*>(p.q);
-  const unsigned char* kg_all = static_cast<const unsigned char*>(p.k);
-  const unsigned char* vg_all = static_cast<const unsigned char*>(p.v);
-  TileLoader<D, NW> loader;
-  loader.init(wave, lane);
-  const int krow0 = swap_bits23(col);   // K operand row: bits 2 and 3 swapped
-
-  // Lane byte offsets of the MFMA operands inside a K or V tile.  K (A
-  // operand of S^T): row krow0 (+32 for the second half), 16-byte chunk
-  // 2s + h of k-step s.  V^T (A operand of O^T, read transposed): for
-  // 32-dim tile mo and half-read hf, row 8h + 4hf + (lane&15)/4 and dims
-  // 32mo + 16((lane>>4)&1) + 4(lane&3) .. +3; key step kk adds 16 rows.  The
-  // chunk swizzle depends on the low four row bits only, which neither the
-  // half (+32 rows) nor the key step (+16 rows) changes, so both are
-  // immediate offsets.
-  unsigned koff[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) koff[s] = krow0 * ROWB + (((2 * s + h) ^ chunk_swz<D>(krow0)) * 16);
-  unsigned voff[NO][2];
-#pragma unroll
-  for (int mo = 0; mo < NO; ++mo)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int ii = lane & 15;
-      const int row = 8 * h + 4 * hf + (ii >> 2);
-      const int dim = 32 * mo + 16 * ((lane >> 4) & 1) + 4 * (ii & 3);
-      voff[mo][hf] = row * ROWB + ((dim >> 3) ^ chunk_swz<D>(row)) * 16 + (dim & 7) * 2;
-    }
-
-  for (;;) {
-    if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
-    __syncthreads();
-    const int qpos = s_unit;
-    __syncthreads();
-    if (qpos >= p.U) break;
-
-    GroupInfo<BQ, G, MODE> gi;
-    gi.decode(p, qpos);
-    const long long head_off = static_cast<long long>(gi.bh) * p.N * ROWB;
-    const unsigned char* kg = kg_all + head_off;
-    const unsigned char* vg = vg_all + head_off;
-    const bool active = member < gi.gsz;
-    const int qblk = gi.i0 + member;
-    const int q0w = qblk * BQ + (wave % NWB) * 32;
-    const int qrow = q0w + col;
-
-    // Tile list of the group.
-    int nt;
-    if (MODE == kSparse) {
-      const int nwords = (p.nb + 31) / 32;
-      for (int x = tid; x < G * kMaxListWords; x += NT) s_bm[x] = 0u;
-      __syncthreads();
-      for (int m = 0; m < gi.gsz; ++m) {
-        const long long u = static_cast<long long>(gi.bh) * p.nb + gi.i0 + m;
-        const int cnt = min(max(p.row_cnt[u], 0), p.nb);
-        const int32_t* lst = p.row_idx + u * p.nb;
-        for (int x = tid; x < cnt; x += NT) {
-          const int j = min(max(lst[x], 0), p.nb - 1);
-          atomicOr(&s_bm[m * kMaxListWords + (j >> 5)], 1u << (j & 31));
-        }
-      }
-      __syncthreads();
-      if (wave == 0) {
-        const unsigned a = lane < nwords ? s_bm[lane] : 0u;
-        const unsigned b = (G > 1 && lane < nwords) ? s_bm[kMaxListWords + lane] : 0u;
-        unsigned un = a | b;
-        const int c = __popc(un);
-        int incl = c;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += y;
-        }
-        int pos = incl - c;
-        while (un) {
-          const int bit = __ffs(un) - 1;
-          un &= un - 1;
-          s_lj[pos] = static_cast<unsigned short>(lane * 32 + bit);
-          s_lm[pos] = static_cast<unsigned char>(((a >> bit) & 1u) | (((b >> bit) & 1u) << 1));
-          ++pos;
-        }
-        if (lane == 63) s_nlist = incl;
-      }
-      __syncthreads();
-      const int nl = s_nlist;
-      nt = nl * SPB;
-      if (SPB > 1 && nl > 0 && s_lj[nl - 1] == p.nb - 1) {
-        const int tail = p.N - (p.nb - 1) * BQ;
-        nt = (nl - 1) * SPB + (tail + kKeyTile - 1) / kKeyTile;
-      }
-    } else if (MODE == kDense) {
-      nt = (p.N + kKeyTile - 1) / kKeyTile;
-    } else {
-      nt = (min(p.N, (gi.i0 + gi.gsz) * BQ) + kKeyTile - 1) / kKeyTile;
-    }
-    auto tile_key0 = [&](int t) -> int {
-      if (MODE == kSparse) return __builtin_amdgcn_readfirstlane(s_lj[t / SPB]) * BQ + (t % SPB) * kKeyTile;
-      return t * kKeyTile;
-    };
-    auto tile_mine = [&](int t, int key0) -> bool {
-      if (!active) return false;
-      if (MODE == kSparse) return (__builtin_amdgcn_readfirstlane(s_lm[t / SPB]) >> member) & 1;
-      if (MODE == kCausal) return key0 < (qblk + 1) * BQ;
-      return true;
-    };
-
-    // Q^T as B operand: lane (h, col) holds Q[qrow][16s + 8h .. +7].
-    bf16x8 qf[NS];
-    {
-      const unsigned char* qr = qg_all + head_off + static_cast<long long>(min(qrow, p.N - 1)) * ROWB;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + (16 * s + 8 * h) * 2);
-    }
-
-    f32x16 acc_o[NO];
-#pragma unroll
-    for (int mo = 0; mo < NO; ++mo)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc_o[mo][e] = 0.f;
-    // Running maximum (raw logits), its scaled value (0 while no finite
-    // logit has been seen) and the threshold past which it is moved.
-    float m_run = -INFINITY;
-    float m_b = 0.f;
-    float m_thr = -INFINITY;
-    float l_run = 0.f;
-    const float grow_span = 8.f / sl2;   // weights stay <= 2^8 below it
-
-    // One key tile.  ST is the LDS stage (tile t lives in stage t & 1); it is
-    // a compile-time constant so that every LDS operand address below is a
-    // loop-invariant register plus an immediate offset.
-    auto tile = [&](auto stage, int t) {
-      constexpr int ST = decltype(stage)::value;
-      TBS_LDS unsigned char* lk = lds + ST * 2 * TILEB;
-      TBS_LDS unsigned char* lv = lk + TILEB;
-      const int key0 = tile_key0(t);
-      wait_vmem();
-      __syncthreads();
-      if (t + 1 < nt) {
-        TBS_LDS unsigned char* nk = lds + (ST ^ 1) * 2 * TILEB;
-        loader.issue(kg, vg, tile_key0(t + 1), p.N, nk, nk + TILEB, wave);
-      }
-      if (!tile_mine(t, key0)) return;
-
-      // S^T = K Q^T for 64 keys x 32 queries, as two independent 32-key
-      // halves (mt).  Both MFMA chains are issued first; the softmax of half 0
-      // then runs on the VALU while half 1's MFMAs execute, and half 0's P V
-      // MFMAs run while half 1's softmax does.  K fragments stream through a
-      // ring of TBS_KPF registers, read that many MFMAs ahead, so LDS latency
-      // overlaps the matrix core.  Fragment f is half f / NS, k-step f % NS.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-      {
-        constexpr int NF = 2 * NS;
-        constexpr int KP = TBS_KPF < NF ? TBS_KPF : NF;
-        auto kread = [&](int f) -> bf16x8 {
-          return *(const TBS_LDS bf16x8*)(lk + (f / NS) * 32 * ROWB + koff[f % NS]);
-        };
-        bf16x8 kr[KP];
-        TBS_PRIO_HI();
-#pragma unroll
-        for (int f = 0; f < KP; ++f) kr[f] = kread(f);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const bf16x8 a = kr[f % KP];
-          if (f + KP < NF) kr[f % KP] = kread(f + KP);
-          sacc[f / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[f % NS], sacc[f / NS], 0, 0, 0);
-        }
-#if TBS_KPF_PIN
-        __builtin_amdgcn_sched_group_barrier(0x100, KP, 0);
-#pragma unroll
-        for (int f = 0; f < NF - KP; ++f) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, KP, 0);
-#endif
-      }
-      TBS_PRIO_LO();
-      TBS_SCHED_FENCE();
-
-      const bool need_mask = (key0 + kKeyTile > p.N) || (MODE == kCausal && key0 + kKeyTile - 1 > q0w);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        // Mask keys past the sequence end (ragged tail) and, if causal, keys
-        // after the query.  Lane value e of half mt is key 32mt + 16(e>>3) + 8h + (e&7).
-        if (need_mask) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = key0 + 32 * mt + 16 * (e >> 3) + 8 * h + (e & 7);
-            const bool bad = key >= p.N || (MODE == kCausal && key > qrow);
-            if (bad) sacc[mt][e] = -INFINITY;
-          }
-        }
-        float mx = max3f(max3f(sacc[mt][0], sacc[mt][1], sacc[mt][2]), sacc[mt][3], sacc[mt][4]);
-        float my = max3f(max3f(sacc[mt][5], sacc[mt][6], sacc[mt][7]), sacc[mt][8], sacc[mt][9]);
-        float mz = max3f(max3f(sacc[mt][10], sacc[mt][11], sacc[mt][12]), sacc[mt][13], sacc[mt][14]);
-        mx = max3f(mx, my, fmaxf(mz, sacc[mt][15]));
-        mx = fmaxf(mx, xor32(mx));
-        // The reference maximum of a row moves only when the tile maximum
-        // exceeds it by more than 2^8 in weight (any reference gives the exact
-        // result; the bound keeps every weight <= 2^8).  Lanes l and l^32 hold
-        // the same row and take the same decision.
-        const bool grow = mx > m_thr;
-        if (__any(grow)) {
-          const float alpha = grow ? fast_exp2((m_run - mx) * sl2) : 1.f;   // 0 on the first move
-#pragma unroll
-          for (int mo = 0; mo < NO; ++mo)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc_o[mo][e] *= alpha;
-          l_run *= alpha;
-          if (grow) {
-            m_run = mx;
-            m_b = mx * sl2;
-            m_thr = mx + grow_span;
-          }
-        }
-
-        // Weights in fp32 (their row sum) and rounded to bf16 (the P V operand).
-        bf16x8 pb[2];
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2, -m_b));
-            ls[e & 3] += pv;
-            pb[t2][e] = static_cast<__bf16>(pv);
-          }
-        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-
-        // O^T += V^T P^T for key steps kk = 2mt, 2mt+1 (keys 16kk .. 16kk+15);
-        // lane (h, col) supplies P for keys 16kk + 8h + 0..7.  V^T comes from
-        // two transposed reads per 32-dim tile (voff).
-        TBS_PRIO_HI();
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int kk = 2 * mt + t2;
-#pragma unroll
-          for (int mo = 0; mo < NO; ++mo) {
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + 16 * kk * ROWB + voff[mo][0]));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TBS_LDS bf16x4*)(lv + 16 * kk * ROWB + voff[mo][1]));
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc_o[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t2], acc_o[mo], 0, 0, 0);
-          }
-        }
-        TBS_PRIO_LO();
-      }
-    };
-
-    if (nt > 0) loader.issue(kg, vg, tile_key0(0), p.N, lds, lds + TILEB, wave);
-    for (int t = 0; t < nt; t += 2) {
-      tile(Stage<0>{}, t);
-      if (t + 1 < nt) tile(Stage<1>{}, t + 1);
-    }
-
-    // Epilogue: lane (h, col) holds O[qrow][32mo + 8j + 4h + r] in acc_o[mo][4j + r].
-    const float l_tot = l_run + xor32(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (active && qrow < p.N) {
-      unsigned short* orow = static_cast<unsigned short*>(p.o) +
-                             (static_cast<long long>(gi.bh) * p.N + qrow) * D;
-#pragma unroll
-      for (int mo = 0; mo < NO; ++mo)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 ov;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ov[r] = static_cast<__bf16>(acc_o[mo][4 * j + r] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * mo + 8 * j + 4 * h) = ov;
-        }
-      if (h == 0 && p.lse)
-        p.lse[static_cast<long long>(gi.bh) * p.N + qrow] =
-            l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
-    }
-  }
-
-  if (tid == 0) {
-    if (p.prof) p.prof[2 * blockIdx.x + 1] = wall_clock64();
-    // The last workgroup to finish leaves the queue counters at zero.
-    if (atomicAdd(p.ctrl + 1, 1u) == gridDim.x - 1) {
-      atomicExch(p.ctrl, 0u);
-      atomicExch(p.ctrl + 1, 0u);
-    }
-  }
-}
 
 // ------------------------------------------------------- bf16, two groups ---
 //
@@ -1164,32 +813,17 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_f32(FwdParams p) {
 
 typedef void (*KernelFn)(FwdParams);
 
-// Query blocks per work item: two 64-row blocks share a workgroup (4 waves);
-// 128-row blocks go alone (4 waves).  fp32 inputs use single blocks.
-#ifndef TBS_PINGPONG
-#define TBS_PINGPONG 1
-#endif
-#if TBS_PINGPONG
+// Query blocks per work item: bf16 work items hold 256 query rows (four
+// 64-row or two 128-row blocks, one 8-wave workgroup); fp32 inputs use
+// single blocks.
 constexpr int group_for(int dtype, int block) { return dtype == 0 ? 256 / block : 1; }
-#else
-constexpr int group_for(int dtype, int block) { return (dtype == 0 && block == 64) ? 2 : 1; }
-#endif
 
 // Every variant is instantiated explicitly: referencing a kernel template
 // only through a function-pointer table does not always emit its host stub.
-#if TBS_PINGPONG
-#define TBS_INSTANTIATE_BF16(D, BQ)                                      \
+#define TBS_INSTANTIATE(D, BQ)                                          \
   template __global__ void flash_fwd_bf16_pp<D, BQ, kSparse>(FwdParams); \
   template __global__ void flash_fwd_bf16_pp<D, BQ, kDense>(FwdParams);  \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, kCausal>(FwdParams);
-#else
-#define TBS_INSTANTIATE_BF16(D, BQ)                                                         \
-  template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kSparse>(FwdParams); \
-  template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kDense>(FwdParams);  \
-  template __global__ void flash_fwd_bf16<D, BQ, group_for(0, BQ), kCausal>(FwdParams);
-#endif
-#define TBS_INSTANTIATE(D, BQ)                                                       \
-  TBS_INSTANTIATE_BF16(D, BQ)                                                        \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, kCausal>(FwdParams); \
   template __global__ void flash_fwd_f32<D, BQ, kSparse>(FwdParams);                  \
   template __global__ void flash_fwd_f32<D, BQ, kDense>(FwdParams);                   \
   template __global__ void flash_fwd_f32<D, BQ, kCausal>(FwdParams);
@@ -1201,14 +835,8 @@ TBS_INSTANTIATE(64, 128)
 
 template <int D, int BQ>
 KernelFn pick_mode(int dtype, int mode) {
-#if TBS_PINGPONG
   static const KernelFn bf16_fns[3] = {flash_fwd_bf16_pp<D, BQ, kSparse>, flash_fwd_bf16_pp<D, BQ, kDense>,
                                        flash_fwd_bf16_pp<D, BQ, kCausal>};
-#else
-  constexpr int G = group_for(0, BQ);
-  static const KernelFn bf16_fns[3] = {flash_fwd_bf16<D, BQ, G, kSparse>, flash_fwd_bf16<D, BQ, G, kDense>,
-                                       flash_fwd_bf16<D, BQ, G, kCausal>};
-#endif
   static const KernelFn f32_fns[3] = {flash_fwd_f32<D, BQ, kSparse>, flash_fwd_f32<D, BQ, kDense>,
                                       flash_fwd_f32<D, BQ, kCausal>};
   return dtype == 0 ? bf16_fns[mode] : f32_fns[mode];
@@ -1226,9 +854,7 @@ int group_size(const Shape& s) { return group_for(s.dtype, s.block); }
 // Threads per workgroup: 8 waves for bf16 (two groups of four), one wave per
 // 32 query rows for fp32.
 int fwd_threads(const Shape& s) {
-#if TBS_PINGPONG
   if (s.dtype == 0) return kWaves * 64;
-#endif
   return group_size(s) * s.block * 2;
 }
 
