@@ -151,12 +151,18 @@ __device__ __forceinline__ int chunk_swz(int row) {
   return ((row & 3) << 1) | ((row >> 3) & 1);
 }
 
-// Copies one 64-key tile of K and V (rows key0 .. key0+63 of one head) from
-// HBM into LDS with buffer_load ... lds: each wave instruction writes 1 KB of
-// LDS (16 bytes per lane, lane-contiguous); the lane picks the global chunk
-// whose swizzled position is its LDS slot.  The buffer resource starts at row
-// key0 and holds the rows left in the sequence, so chunks past the end read
-// as zero (their logits are masked) without a separate tail path.
+// Copies a 64-key tile of K or V (rows key0 .. key0+63 of one head) from HBM
+// into LDS with buffer_load ... lds: each instruction writes 1 KB of LDS (16
+// bytes per lane, lane-contiguous); the lane picks the global chunk whose
+// swizzled position is its LDS slot.  The buffer resource starts at row key0
+// and holds the rows left in the sequence, so chunks past the end read as
+// zero (their logits are masked) without a separate tail path.
+//
+// Wave w of NW copies the PER_WAVE consecutive 1 KB slices w*PER_WAVE ..
+// +PER_WAVE-1 of a tile.  The instruction offset (j * 1 KB) is added to both
+// the LDS and the global address, so one M0 value (the LDS base operand of
+// the copy) serves all of a wave's instructions for a tile: M0 is written
+// once per tile instead of once per instruction.
 constexpr int kRsrcWord3 = 0x00020000;   // raw dword buffer
 
 template <int D, int NW>
@@ -164,21 +170,21 @@ struct TileLoader {
   static constexpr int ROWB = D * 2;
   static constexpr int TILEB = kKeyTile * ROWB;
   static constexpr int PER_WAVE = TILEB / 1024 / NW;
-  // Byte offset of this lane's chunk inside the tile for instruction j is
-  // j*NW*1024 + base[j & 1]: the swizzle of a row depends on its low four
-  // bits only, which repeat with period 2 in j for every supported shape.
-  unsigned base[2];
-
-  __device__ __forceinline__ static unsigned lane_off(int j, int wave, int lane) {
-    const int byte = (j * NW + wave) * 1024 + lane * 16;
-    const int row = byte / ROWB;
-    const int lch = ((byte % ROWB) / 16) ^ chunk_swz<D>(row);
-    return static_cast<unsigned>(row * ROWB + lch * 16);
-  }
+  static_assert(PER_WAVE == 1 || PER_WAVE == 2 || PER_WAVE == 4, "copy slices per wave");
+  // Global byte offset, minus the instruction offset j * 1 KB, of this lane's
+  // chunk for the wave's slice j.
+  unsigned voff[PER_WAVE];
+  unsigned slice0;   // first LDS byte of the wave's slices
 
   __device__ __forceinline__ void init(int wave, int lane) {
-    base[0] = lane_off(0, wave, lane);
-    base[1] = lane_off(1, wave, lane) - NW * 1024;
+    slice0 = static_cast<unsigned>(wave * PER_WAVE * 1024);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int byte = (wave * PER_WAVE + j) * 1024 + lane * 16;
+      const int row = byte / ROWB;
+      const int lch = ((byte % ROWB) / 16) ^ chunk_swz<D>(row);
+      voff[j] = static_cast<unsigned>(row * ROWB + lch * 16 - j * 1024);
+    }
   }
 
   __device__ __forceinline__ static u32x4 rsrc(const unsigned char* base, int bytes) {
@@ -191,33 +197,51 @@ struct TileLoader {
     return r;
   }
 
-  // One buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + voff into
-  // LDS at lds_addr + 16 * lane.  Written as inline asm so that the compiler
-  // does not count it as a pending write to the tile being read: the loop
-  // below orders every tile's reads after its own copy with an explicit
-  // vmcnt wait and a barrier, and the copy into the other stage stays in
-  // flight meanwhile.  M0 (the LDS base operand) is restored afterwards.
-  __device__ __forceinline__ static void dma16(u32x4 r, int voff, unsigned lds_addr) {
-    unsigned saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_addr), "v"(voff), "s"(r)
-        : "memory");
-  }
-
-  // One tile (K or V) of rows key0 .. key0+63 into dst.
-  __device__ __forceinline__ void issue_one(const unsigned char* g, int key0, int N, TBS_LDS unsigned char* dst,
-                                            int wave) const {
+  // The wave's buffer_load_dwordx4 ... lds instructions for one tile, written
+  // as inline asm so that the compiler does not count them as pending writes
+  // to the tile being read: the loop orders every tile's reads after its own
+  // copy with an explicit vmcnt wait and a barrier, and the copy into the
+  // other stage stays in flight meanwhile.  M0 is restored afterwards.
+  __device__ __forceinline__ void issue_one(const unsigned char* g, int key0, int N, TBS_LDS unsigned char* dst) const {
     const u32x4 r = rsrc(g + static_cast<long long>(key0) * ROWB, (N - key0) * ROWB);
-    const unsigned l = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)dst);
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j)
-      dma16(r, static_cast<int>(j * NW * 1024 + base[j & 1]), l + static_cast<unsigned>((j * NW + wave) * 1024));
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)dst) + slice0;
+    unsigned saved;
+    if (PER_WAVE == 1) {
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(m0), "v"(voff[0]), "s"(r)
+          : "memory");
+    } else if (PER_WAVE == 2) {
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+          "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(m0), "v"(voff[0]), "v"(voff[PER_WAVE > 1 ? 1 : 0]), "s"(r)
+          : "memory");
+    } else {
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+          "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
+          "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
+          "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(m0), "v"(voff[0]), "v"(voff[PER_WAVE > 1 ? 1 : 0]), "v"(voff[PER_WAVE > 2 ? 2 : 0]),
+            "v"(voff[PER_WAVE > 3 ? 3 : 0]), "s"(r)
+          : "memory");
+    }
   }
 };
 
@@ -585,8 +609,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // V(t) into V stage t&1 (P = t&1); every wave issues its share.
     auto issue = [&](auto pp, int t) __attribute__((always_inline)) {
       constexpr int P = decltype(pp)::value;
-      if (t + 1 < nt) loader.issue_one(kg, tile_key0(t + 1), p.N, lds + (P ^ 1) * TILEB, wave);
-      if (t < nt) loader.issue_one(vg, tile_key0(t), p.N, lds + (2 + P) * TILEB, wave);
+      if (t + 1 < nt) loader.issue_one(kg, tile_key0(t + 1), p.N, lds + (P ^ 1) * TILEB);
+      if (t < nt) loader.issue_one(vg, tile_key0(t), p.N, lds + (2 + P) * TILEB);
     };
 
     // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(nt), one
@@ -598,7 +622,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // the barrier that opens step 2t+2.  The loop is unrolled twice so the
     // LDS stages of K(t) and V(t-1) are compile-time constants.
     if (nt > 0) {
-      loader.issue_one(kg, tile_key0(0), p.N, lds, wave);
+      loader.issue_one(kg, tile_key0(0), p.N, lds);
       wait_vmem();
       step_barrier();
       if (grp == 1) {
