@@ -13,7 +13,9 @@ What it computes, and where the definitions come from:
   cumulative probability reaches p.  Top-p routing is defined on the FVAttn
   review page, section 1 (Key Terms, "Top-p routing") and used in section 3
   (Method); the page does not define the block score, so the pooled score is
-  the reading taken here.
+  the reading taken here.  For causal models the routing cuts key blocks
+  after the query block before the softmax (``causal_cut``); the pages state
+  routing for full attention only, so this block-level cut is a reading too.
 * attention (``attention``): S = Q K^T scaled, P = softmax(S) restricted to the
   allowed keys, O = P V, and the log-sum-exp of each row -- the standard
   attention of the FlashAttention review page, Background [3] (Motivation),
@@ -30,14 +32,14 @@ function is pinned by the CPU tests against brute force, closed forms,
 library special cases or invariants.
 """
 from .routing import (block_sizes, num_blocks, pool_blocks, block_scores, softmax_rows,
-                      top_p_select, route, ambiguous_blocks, RouteResult)
+                      top_p_select, causal_cut, route, ambiguous_blocks, RouteResult)
 from .attention import attend, attend_units, attend_dense_masked_logits
 from .schedule import group_costs, work_list, lpt_assign, static_partition_loads, load_imbalance
 from .flops import executed_flops, dense_flops
 
 __all__ = [
     "block_sizes", "num_blocks", "pool_blocks", "block_scores", "softmax_rows",
-    "top_p_select", "route", "ambiguous_blocks", "RouteResult",
+    "top_p_select", "causal_cut", "route", "ambiguous_blocks", "RouteResult",
     "attend", "attend_units", "attend_dense_masked_logits",
     "group_costs", "work_list", "lpt_assign", "static_partition_loads", "load_imbalance",
     "executed_flops", "dense_flops",

@@ -13,11 +13,17 @@ import numpy as np
 from .routing import block_sizes
 
 
-def executed_flops(mask, n_tokens: int, block: int, head_dim: int) -> int:
-    """4 * d * sum over selected pairs of n_i * n_j (exact integer)."""
+def executed_flops(mask, n_tokens: int, block: int, head_dim: int, causal: bool = False) -> int:
+    """4 * d * sum over selected pairs of the allowed (query, key) pairs (exact integer).
+
+    A pair of blocks allows n_i * n_j token pairs; with `causal`, a diagonal
+    pair allows n_i (n_i + 1) / 2 and a pair above the diagonal none.
+    """
     mask = np.asarray(mask)
     n = block_sizes(n_tokens, block).astype(np.int64)
     pair = np.outer(n, n)                     # [nb, nb]
+    if causal:
+        pair = np.tril(pair, -1) + np.diag(n * (n + 1) // 2)
     per_row = (mask.astype(np.int64) * pair).sum()
     return int(4 * head_dim * per_row)
 

@@ -17,6 +17,14 @@ reading used here is the plainest one consistent with a "pool" router:
      when p >= 1 (dense attention is the p = 1 case) or when no r qualifies.
   7. The first k_i ranked blocks are selected: mask M_ij = 1, the selected
      indices listed in ascending order, row count k_i, head count sum_i k_i.
+
+Causal routing (the decoder setting; the page's routing is stated for
+encoder-style full attention, and the block-level causal cut is the reading
+taken for causal models): key blocks after the query block (j > i) are cut
+before the softmax (Z_ij = -inf, so P_ij = 0 and the softmax runs over the
+i+1 blocks j <= i), and "all blocks" in step 6 means those i+1 blocks.  The
+attention of a causal model additionally keeps only keys s <= t for query t
+(attention.attend with causal=True).
 """
 from __future__ import annotations
 
@@ -63,26 +71,37 @@ def softmax_rows(z: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def top_p_select(prob: np.ndarray, top_p: float):
+def top_p_select(prob: np.ndarray, top_p: float, valid=None):
     """Top-p selection on rows of block probabilities.
 
     Returns (order, cum, row_cnt) where order[..., r] is the r-th ranked key
     block (P descending, ties by smaller index), cum[..., r] the inclusive
     cumulative probability of the first r+1 ranked blocks, and row_cnt the
-    number of selected blocks k_i.
+    number of selected blocks k_i.  `valid` (broadcastable to the row shape,
+    default nb) is the number of eligible blocks of each row; the others have
+    P = 0 and higher indices, so they rank last and are never selected.
     """
     prob = np.asarray(prob, dtype=np.float64)
     nb = prob.shape[-1]
+    nvalid = np.broadcast_to(np.int64(nb) if valid is None else np.asarray(valid, dtype=np.int64),
+                             prob.shape[:-1])
     order = np.argsort(-prob, axis=-1, kind="stable")
     ranked = np.take_along_axis(prob, order, axis=-1)
     cum = np.cumsum(ranked, axis=-1)
     if top_p >= 1.0:
-        row_cnt = np.full(prob.shape[:-1], nb, dtype=np.int64)
+        row_cnt = nvalid.astype(np.int64).copy()
     else:
-        reached = cum >= top_p
+        reached = (cum >= top_p) & (np.arange(nb) < nvalid[..., None])
         first = np.argmax(reached, axis=-1) + 1
-        row_cnt = np.where(np.any(reached, axis=-1), first, nb).astype(np.int64)
+        row_cnt = np.where(np.any(reached, axis=-1), first, nvalid).astype(np.int64)
     return order, cum, row_cnt
+
+
+def causal_cut(scores: np.ndarray) -> np.ndarray:
+    """Block-level causal cut: Z_ij = -inf for key blocks after the query block (j > i)."""
+    nb = scores.shape[-1]
+    future = np.arange(nb)[None, :] > np.arange(scores.shape[-2])[:, None]
+    return np.where(future, -np.inf, scores)
 
 
 @dataclasses.dataclass
@@ -98,11 +117,13 @@ class RouteResult:
     row_idx: np.ndarray     # [B,H,nb,nb] int32, ascending selected indices, -1 after row_cnt
     head_cnt: np.ndarray    # [B,H] int64
     top_p: float
+    valid: np.ndarray | None = None   # [B,H,nb] int64, eligible key blocks per row (i+1 if causal, else nb; None = nb)
 
 
 def route(q: np.ndarray, k: np.ndarray, block: int, top_p: float, scale: float | None = None,
-          ) -> RouteResult:
-    """Full top-p routing of one batch. q, k: [B, H, N, d] (any float dtype, upcast to fp64)."""
+          causal: bool = False) -> RouteResult:
+    """Full top-p routing of one batch. q, k: [B, H, N, d] (any float dtype, upcast to fp64).
+    With `causal`, row i only considers key blocks j <= i (module docstring)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     d = q.shape[-1]
@@ -111,9 +132,14 @@ def route(q: np.ndarray, k: np.ndarray, block: int, top_p: float, scale: float |
     qbar = pool_blocks(q, block)
     kbar = pool_blocks(k, block)
     scores = block_scores(qbar, kbar, scale)
+    nb = scores.shape[-1]
+    if causal:
+        scores = causal_cut(scores)
+        valid = np.broadcast_to(np.arange(1, nb + 1, dtype=np.int64), scores.shape[:-1]).copy()
+    else:
+        valid = np.full(scores.shape[:-1], nb, dtype=np.int64)
     prob = softmax_rows(scores)
-    order, cum, row_cnt = top_p_select(prob, top_p)
-    nb = prob.shape[-1]
+    order, cum, row_cnt = top_p_select(prob, top_p, valid)
     rank_pos = np.arange(nb)
     selected_ranked = rank_pos[None, None, None, :] < row_cnt[..., None]
     mask = np.zeros(prob.shape, dtype=np.uint8)
@@ -127,7 +153,7 @@ def route(q: np.ndarray, k: np.ndarray, block: int, top_p: float, scale: float |
                 row_idx[b, h, i, : sel.size] = sel
     head_cnt = row_cnt.sum(axis=-1)
     return RouteResult(qbar, kbar, scores, prob, order, cum, row_cnt, mask, row_idx,
-                       head_cnt, float(top_p))
+                       head_cnt, float(top_p), valid)
 
 
 def ambiguous_blocks(res: RouteResult, window: float = 1e-5) -> np.ndarray:
@@ -147,10 +173,11 @@ def ambiguous_blocks(res: RouteResult, window: float = 1e-5) -> np.ndarray:
     if res.top_p >= 1.0:
         return np.zeros(shape, dtype=bool)
     k = np.asarray(res.row_cnt)
+    valid = np.full(k.shape, nb, dtype=np.int64) if res.valid is None else np.asarray(res.valid)
     ranked = np.take_along_axis(prob, order, axis=-1)
     last_in = np.take_along_axis(ranked, (k - 1)[..., None], axis=-1)
     first_out = np.take_along_axis(ranked, np.minimum(k, nb - 1)[..., None], axis=-1)
-    first_out = np.where((k < nb)[..., None], first_out, -np.inf)
+    first_out = np.where((k < valid)[..., None], first_out, -np.inf)
     excl = cum - ranked
     near_cut_ranked = (np.abs(excl - res.top_p) <= window) | (np.abs(cum - res.top_p) <= window)
     near_cut = np.zeros(shape, dtype=bool)
@@ -158,6 +185,7 @@ def ambiguous_blocks(res: RouteResult, window: float = 1e-5) -> np.ndarray:
     rank_of = np.empty_like(order)
     np.put_along_axis(rank_of, order, np.broadcast_to(np.arange(nb), shape), axis=-1)
     selected = rank_of < k[..., None]
+    eligible = np.arange(nb) < valid[..., None]
     swap_in = selected & (prob - first_out <= window)
-    swap_out = ~selected & (last_in - prob <= window)
-    return near_cut | swap_in | swap_out
+    swap_out = ~selected & eligible & (last_in - prob <= window)
+    return (near_cut & eligible) | swap_in | swap_out

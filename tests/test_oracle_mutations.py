@@ -1,7 +1,8 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the pins
 catch each one: a transposed operand, a wrong divisor, an exclusive threshold,
 a reversed tie rule, a dropped scale, an off-by-one causal mask, a wrong log
-base and a wrong sort direction."""
+base, a wrong sort direction, and a causal block cut that is missing, off by
+one, or applied after the softmax instead of before it."""
 import numpy as np
 import pytest
 
@@ -42,8 +43,8 @@ def test_pool_divisor_caught(monkeypatch):
 def test_exclusive_threshold_caught(monkeypatch, golden_dir):
     orig = rt.top_p_select
 
-    def strict(prob, p):
-        order, cum, cnt = orig(prob, p)
+    def strict(prob, p, valid=None):
+        order, cum, cnt = orig(prob, p, valid)
         if p < 1:
             reached = cum > p
             cnt = np.where(reached.any(-1), np.argmax(reached, -1) + 1, prob.shape[-1])
@@ -54,7 +55,7 @@ def test_exclusive_threshold_caught(monkeypatch, golden_dir):
 
 
 def test_reversed_tie_rule_caught(monkeypatch):
-    def rev_ties(prob, p):
+    def rev_ties(prob, p, valid=None):
         nb = prob.shape[-1]
         flipped = prob[..., ::-1]
         order = nb - 1 - np.argsort(-flipped, axis=-1, kind="stable")
@@ -69,7 +70,7 @@ def test_reversed_tie_rule_caught(monkeypatch):
 
 
 def test_ascending_sort_caught(monkeypatch):
-    def ascending(prob, p):
+    def ascending(prob, p, valid=None):
         nb = prob.shape[-1]
         order = np.argsort(prob, axis=-1, kind="stable")
         cum = np.cumsum(np.take_along_axis(prob, order, -1), -1)
@@ -113,3 +114,33 @@ def test_wrong_log_base_caught(monkeypatch):
     monkeypatch.setattr(att, "_attend_rows", log2_lse)
     with pytest.raises(AssertionError):
         ta.test_dense_matches_torch_sdpa_fp64((1, 2, 256, 64), 64, False)
+
+
+def test_missing_causal_cut_caught(monkeypatch):
+    _patch(monkeypatch, rt, "causal_cut", lambda z: z)
+    with pytest.raises(AssertionError):
+        tr.test_causal_route_never_looks_ahead(0.5)
+
+
+def test_causal_cut_off_by_one_caught(monkeypatch):
+    def late_cut(z):
+        nb = z.shape[-1]
+        ahead = np.arange(nb)[None, :] > np.arange(nb)[:, None] + 1
+        return np.where(ahead, -np.inf, z)
+    _patch(monkeypatch, rt, "causal_cut", late_cut)
+    with pytest.raises(AssertionError):
+        tr.test_causal_route_never_looks_ahead(0.9)
+
+
+def test_causal_cut_after_softmax_caught(monkeypatch):
+    # zero the future probabilities after a full softmax, without renormalising
+    orig = rt.softmax_rows
+
+    def cut_after(z):
+        prob = orig(z)
+        nb = z.shape[-1]
+        return np.where(np.arange(nb)[None, :] > np.arange(nb)[:, None], 0.0, prob)
+    _patch(monkeypatch, rt, "causal_cut", lambda z: z)
+    _patch(monkeypatch, rt, "softmax_rows", cut_after)
+    with pytest.raises(AssertionError):
+        tr.test_causal_route_against_brute_force()

@@ -192,3 +192,89 @@ def test_ambiguity_window_flags_near_cut_only():
     r2 = oracle.RouteResult(q, q, prob2, prob2, order, cum, cnt, None, None, None, 0.9)
     amb2 = oracle.ambiguous_blocks(r2, window=1e-5)
     assert amb2[0, 0, 0, 2] and amb2[0, 0, 0, 3] and not amb2[0, 0, 0, 0]
+
+
+# ----------------------------------------------------------- causal routing ---
+
+def test_causal_route_against_brute_force():
+    # Row i: softmax over the i+1 scores j <= i only, then top-p among them.
+    rng = np.random.default_rng(7)
+    B, H, N, d, block = 1, 2, 70, 6, 8            # nb = 9, ragged tail of 6
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d)) + q * 0.5
+    nb = oracle.num_blocks(N, block)
+    for p in (0.3, 0.6, 0.9):
+        r = oracle.route(q, k, block, p, causal=True)
+        for h in range(H):
+            qb = [np.mean(q[0, h, i * block:min(N, (i + 1) * block)], axis=0) for i in range(nb)]
+            kb = [np.mean(k[0, h, j * block:min(N, (j + 1) * block)], axis=0) for j in range(nb)]
+            for i in range(nb):
+                z = np.array([sum(qb[i][c] * kb[j][c] for c in range(d)) for j in range(i + 1)])
+                prob = scipy.special.softmax(z / math.sqrt(d))
+                want = _brute_force_topp(prob, p)
+                got = set(np.nonzero(r.mask[0, h, i])[0].tolist())
+                assert got == want, (p, h, i)
+                assert r.row_cnt[0, h, i] == len(want)
+                assert r.row_idx[0, h, i, : len(want)].tolist() == sorted(want)
+                np.testing.assert_allclose(r.prob[0, h, i, : i + 1], prob, rtol=1e-13, atol=0)
+                assert (r.prob[0, h, i, i + 1:] == 0).all()
+
+
+@pytest.mark.parametrize("p", [0.01, 0.5, 0.9, 1.0])
+def test_causal_route_never_looks_ahead(p):
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((2, 3, 300, 4))
+    k = rng.standard_normal((2, 3, 300, 4))
+    r = oracle.route(q, k, 32, p, causal=True)
+    nb = 10
+    assert (np.triu(np.ones((nb, nb), dtype=np.uint8), 1) * r.mask == 0).all()
+    assert (r.row_cnt >= 1).all() and (r.row_cnt <= np.arange(1, nb + 1)).all()
+    assert (r.mask[..., 0, :] == np.eye(1, nb, 0, dtype=np.uint8)).all()      # row 0 sees block 0 only
+    if p >= 1.0:                                                               # closed form: lower triangle
+        assert (r.mask == np.tril(np.ones((nb, nb), dtype=np.uint8))).all()
+        assert (r.head_cnt == nb * (nb + 1) // 2).all()
+
+
+def test_causal_uniform_scores_take_lowest_indices():
+    # Q = 0: the i+1 eligible blocks of row i tie at 1/(i+1) (exact for i+1 a
+    # power of two), so k_i = ceil(p (i+1)) and the lowest indices win.
+    q = np.zeros((1, 1, 512, 8))
+    k = np.random.default_rng(9).standard_normal((1, 1, 512, 8))
+    for p in (0.3, 0.5, 0.9):
+        r = oracle.route(q, k, 64, p, causal=True)
+        for i in (0, 1, 3, 7):
+            kk = math.ceil(p * (i + 1))
+            assert r.row_cnt[0, 0, i] == kk
+            assert r.mask[0, 0, i].tolist() == [1] * kk + [0] * (8 - kk)
+
+
+def test_causal_row_equals_full_routing_of_the_prefix():
+    # Cutting j > i before the softmax makes row i of causal routing the same
+    # as full routing of the key prefix that ends with block i.
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((1, 2, 200, 5))
+    k = rng.standard_normal((1, 2, 200, 5))
+    block, p = 16, 0.8
+    rc = oracle.route(q, k, block, p, causal=True)
+    for i in range(oracle.num_blocks(200, block)):
+        end = min(200, (i + 1) * block)
+        rf = oracle.route(q, k[:, :, :end], block, p)
+        np.testing.assert_array_equal(rc.mask[:, :, i, : i + 1], rf.mask[:, :, i])
+        np.testing.assert_array_equal(rc.row_cnt[:, :, i], rf.row_cnt[:, :, i])
+
+
+def test_causal_ambiguity_ignores_future_blocks():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 2, 256, 4))
+    r = oracle.route(q, q, 32, 0.7, causal=True)
+    amb = oracle.ambiguous_blocks(r, window=0.5)
+    assert not (amb & (np.triu(np.ones((8, 8), dtype=bool), 1))).any()
+    assert amb.any()
+
+
+def test_causal_executed_flops_closed_form():
+    N, block, d = 200, 64, 8                      # blocks of 64, 64, 64, 8
+    nb = oracle.num_blocks(N, block)
+    full = np.tril(np.ones((nb, nb), dtype=np.uint8))
+    assert oracle.executed_flops(full, N, block, d, causal=True) == oracle.dense_flops(1, 1, N, d, causal=True)
+    assert oracle.executed_flops(np.ones((nb, nb)), N, block, d) == oracle.dense_flops(1, 1, N, d)
