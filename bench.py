@@ -11,7 +11,9 @@ top_p 0.9).  `value` is executed TFLOP/s of the whole step (executed FLOPs =
 4*d*sum over selected block pairs of n_i*n_j; softmax not counted); the
 roofline block reports the attention kernel alone against the bf16 MFMA
 peak.  The CPU baseline is the fp64 oracle timed on a bounded sample of the
-same workload on this machine's host cores.
+same workload on this machine's host cores.  --causal runs the same workload
+with causal routing and causal attention (executed FLOPs then count the
+allowed token pairs of diagonal blocks only).
 """
 from __future__ import annotations
 
@@ -61,11 +63,14 @@ def measured_traffic(workload: str):
         return None
 
 
-def executed_flops(mask: np.ndarray, n_tokens: int, block: int, head_dim: int) -> int:
+def executed_flops(mask: np.ndarray, n_tokens: int, block: int, head_dim: int, causal: bool = False) -> int:
     nb = mask.shape[-1]
     n = np.minimum(block, n_tokens - np.arange(nb) * block).astype(np.int64)
-    per_row = mask.astype(np.int64) @ n            # [..., nb]: sum over selected j of n_j
-    return int(4 * head_dim * int((per_row * n).sum()))
+    if not causal:
+        per_row = mask.astype(np.int64) @ n            # [..., nb]: sum over selected j of n_j
+        return int(4 * head_dim * int((per_row * n).sum()))
+    pairs = np.tril(np.outer(n, n), -1) + np.diag(n * (n + 1) // 2)   # allowed token pairs per block pair
+    return int(4 * head_dim * int((mask.astype(np.int64) * pairs).sum()))
 
 
 def parse():
@@ -75,6 +80,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="video-32k")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--causal", action="store_true", help="causal routing and causal attention")
     ap.add_argument("--head-window", type=int, default=None, help="heads per scheduling window (default: library's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -85,7 +91,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed):
+def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False):
     """Time the fp64 oracle on a bounded sample: routing of one head and the
     attention of randomly chosen query blocks of that head."""
     import torch
@@ -99,7 +105,7 @@ def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed):
     sl = (slice(0, 1), slice(h, h + 1))
     q64, k64, v64 = (t[sl].cpu().to(torch.float64).numpy() for t in (q, k, v))
     t0 = time.perf_counter()
-    r = oracle.route(q64, k64, w.block, w.top_p)
+    r = oracle.route(q64, k64, w.block, w.top_p, causal=causal)
     t_route = time.perf_counter() - t0
     rng = np.random.default_rng(seed)
     order = rng.permutation(w.num_blocks)
@@ -107,10 +113,11 @@ def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed):
     while done < len(order) and t_attn + t_route * (done / w.num_blocks) < target_s:
         i = int(order[done])
         t0 = time.perf_counter()
-        oracle.attend_units(q64, k64, v64, w.block, [(0, 0, i)], mask=r.mask)
+        oracle.attend_units(q64, k64, v64, w.block, [(0, 0, i)], mask=r.mask, causal=causal)
         t_attn += time.perf_counter() - t0
-        n = np.minimum(w.block, w.seq_len - np.arange(w.num_blocks) * w.block).astype(np.int64)
-        flops += int(4 * w.head_dim * n[i] * (r.mask[0, 0, i].astype(np.int64) @ n))
+        row = np.zeros_like(r.mask[0, 0])
+        row[i] = r.mask[0, 0, i]
+        flops += executed_flops(row, w.seq_len, w.block, w.head_dim, causal)
         done += 1
     t_total = t_attn + t_route * (done / w.num_blocks)
     return {
@@ -118,7 +125,7 @@ def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed):
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"fp64 oracle on head 0 of {w.name}: routing of all {w.num_blocks} query blocks "
+        "sample": (f"fp64 oracle on head 0 of {w.name}{' (causal)' if causal else ''}: routing of all {w.num_blocks} query blocks "
                    f"({t_route:.2f} s, charged pro rata) + masked attention of {done} random query blocks "
                    f"({t_attn:.2f} s); value = their executed FLOPs / charged time"),
         "ms_per_query_block": 1e3 * t_total / max(done, 1),
@@ -148,7 +155,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    pr = tbs.make_problem(q, w.block)
+    causal = bool(args.causal)
+    pr = tbs.make_problem(q, w.block, causal=causal)
     ws = tbs.workspace(pr, dev)
     B, H, nb, N, d = w.batch, w.heads, w.num_blocks, w.seq_len, w.head_dim
     route_out = tbs.Route(pr, w.top_p,
@@ -163,14 +171,14 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        tbs.route(q, k, w.top_p, w.block, ws=ws, out=route_out)
+        tbs.route(q, k, w.top_p, w.block, ws=ws, out=route_out, causal=causal)
         if ev is not None:
             ev[1].record()
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         if ev is not None:
             ev[2].record()
         tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, w.block, work_list=work_list, ws=ws,
-                       o=o, lse=lse)
+                       o=o, lse=lse, causal=causal)
         if ev is not None:
             ev[3].record()
 
@@ -189,9 +197,10 @@ def main():
     t_fwd = np.array([e[2].elapsed_time(e[3]) for e in events])
 
     mask = route_out.mask.cpu().numpy()
-    flops = executed_flops(mask, N, w.block, d)
-    dense_flops = 4 * B * H * N * N * d
-    density = float(mask.mean())
+    flops = executed_flops(mask, N, w.block, d, causal)
+    dense_flops = 4 * B * H * d * (N * (N + 1) // 2 if causal else N * N)
+    # fraction of the eligible block pairs selected (the lower triangle under causal routing)
+    density = float(mask.sum() / (B * H * (nb * (nb + 1) // 2 if causal else nb * nb)))
     ms_step = 1e3 * wall / args.steps
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (t_fwd.mean() * 1e-3) / 1e12
@@ -212,10 +221,10 @@ def main():
     lif = {"workers": int(W), "query_blocks_per_item": int(G), "static_partition": float(static.max() / static.mean()),
            "longest_first_lpt": float(lpt.max() / lpt.mean())}
     # measured per-workgroup busy time of the persistent kernel
-    prp = tbs.make_problem(q, w.block, flags=tbs.FLAG_PROFILE_WORKERS)
+    prp = tbs.make_problem(q, w.block, causal=causal, flags=tbs.FLAG_PROFILE_WORKERS)
     wsp = tbs.workspace(prp, dev)
     tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, w.block, work_list=work_list, ws=wsp, o=o,
-                   lse=lse, flags=tbs.FLAG_PROFILE_WORKERS)
+                   lse=lse, flags=tbs.FLAG_PROFILE_WORKERS, causal=causal)
     torch.cuda.synchronize()
     nw = tbs.num_workers(prp, tbs.OP_SPARSE_FWD)
     stamps = wsp[256:256 + 16 * nw].view(torch.int64).view(nw, 2).cpu().numpy()
@@ -226,12 +235,12 @@ def main():
     dense = None
     if not args.no_dense:
         od = torch.empty_like(q)
-        tbs.dense_fwd(q, k, v, w.block, ws=ws, o=od, want_lse=False)
+        tbs.dense_fwd(q, k, v, w.block, causal=causal, ws=ws, o=od, want_lse=False)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.dense_reps):
-            tbs.dense_fwd(q, k, v, w.block, ws=ws, o=od, want_lse=False)
+            tbs.dense_fwd(q, k, v, w.block, causal=causal, ws=ws, o=od, want_lse=False)
         e1.record()
         torch.cuda.synchronize()
         t_dense = e0.elapsed_time(e1) / args.dense_reps
@@ -242,7 +251,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed)
+        cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed, causal)
 
     out = {
         "metric": METRIC,
@@ -258,15 +267,16 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d, "block": w.block,
-                   "top_p": w.top_p, "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
+                   "top_p": w.top_p, "causal": causal, "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
                    "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
         "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
                          "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),
                          "sparse_fwd_mean": float(t_fwd.mean()), "sparse_fwd_median": float(np.median(t_fwd))},
         "sparse_fwd_tflops": fwd_tflops,
-        "roofline": {"bound": "mfma", "kernel": "flash_fwd_bf16_pp (sparse)", "achieved": fwd_tflops,
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": fwd_tflops / BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(w.name)},
+        "roofline": {"bound": "mfma", "kernel": f"flash_fwd_bf16_pp ({'sparse causal' if causal else 'sparse'})",
+                     "achieved": fwd_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fwd_tflops / BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(w.name + ("-causal" if causal else ""))},
         "dense_same_shape": dense,
         "load_imbalance": lif,
         "cpu_baseline": cpu,

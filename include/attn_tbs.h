@@ -15,6 +15,10 @@
  *   attn_dense_fwd   the same kernel over every key block (optionally
  *                    causal): dense attention is the p = 1 case.
  *
+ * With causal == 1 (decoder models) every call keeps to the causal order:
+ * routing considers only key blocks j <= i for query block i, and the
+ * attention calls keep only keys s <= t for query token t.
+ *
  * Sources.  Top-p routing: FVAttn review page, section 1 (Key Terms, "Top-p
  * routing") and section 3 (Method): per query block, key blocks are taken by
  * importance until their cumulative probability reaches p.  Runtime load
@@ -90,7 +94,7 @@ typedef struct attn_problem {
   int32_t head_dim;  /* d: 64 or 128 */
   int32_t block;     /* block size for routing and for query/key tiles: 64 or 128 */
   int32_t dtype;     /* ATTN_DTYPE_BF16 or ATTN_DTYPE_F32 */
-  int32_t causal;    /* 0 or 1; honoured by attn_dense_fwd, must be 0 for routing */
+  int32_t causal;    /* 0 or 1: causal routing and causal attention (keys s <= t) */
   int32_t flags;     /* ATTN_FLAG_* bits, 0 for none */
   double scale;      /* softmax scale; 0 selects 1/sqrt(head_dim) */
 } attn_problem;
@@ -137,6 +141,13 @@ int32_t attn_num_workers(const attn_problem* problem, int32_t op);
  * evaluated in fp64, so the decisions are those of exact arithmetic up to
  * fp64 rounding.
  *
+ * Causal routing (causal == 1): row i only considers the key blocks j <= i.
+ * The others are cut before the softmax (Z_ij = -inf, P_ij = 0), so P_i. is a
+ * softmax over the i+1 eligible scores, the ranking and the cut run over
+ * those blocks only, and top_p >= 1 selects all i+1 of them.  The routing
+ * pages state top-p routing for full attention; cutting the future blocks
+ * before the softmax is the reading this library takes for decoders.
+ *
  *   q, k      [B,H,N,d] dtype, read only.
  *   top_p     in (0, 1].
  *   mask      [B,H,nb,nb] uint8 out: 1 where key block j is selected for row i.
@@ -145,9 +156,10 @@ int32_t attn_num_workers(const attn_problem* problem, int32_t op);
  *             the selected key blocks in ascending order; later entries are
  *             not written.
  *   head_cnt  [B,H] int32 out: sum over i of row_cnt (overwritten, not added to).
- *   block_prob [B,H,nb,nb] double out, nullable: the block probabilities P.
+ *   block_prob [B,H,nb,nb] double out, nullable: the block probabilities P
+ *             (0 for key blocks cut by causal routing).
  *   ws        workspace of attn_workspace_bytes(problem, ATTN_OP_ROUTE) bytes.
- * Requires causal == 0 and nb <= 1024. */
+ * Requires nb <= 1024. */
 int32_t attn_route(const attn_problem* problem, const void* q, const void* k, double top_p,
                    uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                    double* block_prob, void* ws, size_t ws_bytes, void* stream);
@@ -203,15 +215,20 @@ int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32
  *   lse        [B,H,N] float out, nullable (-inf for a unit with no keys).
  *   ws         attn_workspace_bytes(problem, ATTN_OP_SPARSE_FWD) bytes, control
  *              block zero on entry (see attn_workspace_bytes).
- * Requires causal == 0 and nb <= 2048. */
+ * With causal == 1, only keys s <= t enter the sums for query token t (the
+ * lists come from causal routing, so they hold blocks j <= i; a listed block
+ * j > i contributes no keys, and a unit left with no keys gets o = 0 and
+ * lse = -inf).
+ * Requires nb <= 2048. */
 int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                         const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
                         void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Dense attention forward (every key block; causal keeps keys s <= t).
  * Same arithmetic, layouts and workspace rules as attn_sparse_fwd; with
- * causal the query blocks with the most keys are processed first.  Equals
- * attn_sparse_fwd with every block selected, bit for bit, when causal == 0. */
+ * causal the query blocks with the most keys are processed first.  Equals,
+ * bit for bit, attn_sparse_fwd with every block selected (causal == 0) or
+ * with every block j <= i selected (causal == 1). */
 int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                        void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 

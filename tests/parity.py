@@ -25,7 +25,7 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def oracle_route_per_head(q: torch.Tensor, k: torch.Tensor, block: int, top_p: float, scale=None):
+def oracle_route_per_head(q: torch.Tensor, k: torch.Tensor, block: int, top_p: float, scale=None, causal=False):
     """Oracle routing head by head (bounded host memory at full sizes).
 
     Returns mask, row_cnt, row_idx, head_cnt and the ambiguity map, [B,H,...].
@@ -38,7 +38,8 @@ def oracle_route_per_head(q: torch.Tensor, k: torch.Tensor, block: int, top_p: f
     row_idx = np.full((B, H, nb, nb), -1, dtype=np.int32)
     for b in range(B):
         for h in range(H):
-            r = oracle.route(to64(q[b:b + 1, h:h + 1]), to64(k[b:b + 1, h:h + 1]), block, top_p, scale)
+            r = oracle.route(to64(q[b:b + 1, h:h + 1]), to64(k[b:b + 1, h:h + 1]), block, top_p, scale,
+                             causal=causal)
             mask[b, h] = r.mask[0, 0]
             row_cnt[b, h] = r.row_cnt[0, 0]
             row_idx[b, h] = r.row_idx[0, 0]

@@ -73,7 +73,7 @@ def _route(p, top_p=0.9, q=FAKE, k=FAKE, ws=WS, ws_bytes=1 << 40, mask=FAKE, rc=
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), 1), (dict(H=-1), 1), (dict(N=0), 1), (dict(d=96), 2), (dict(d=0), 1), (dict(block=32), 2),
-    (dict(dtype=7), 1), (dict(causal=2), 1), (dict(causal=1), 2), (dict(flags=8), 1), (dict(scale=-1.0), 1),
+    (dict(dtype=7), 1), (dict(causal=2), 1), (dict(flags=8), 1), (dict(scale=-1.0), 1),
     (dict(scale=math.inf), 1), (dict(N=64 * 1025), 2),
 ])
 def test_route_rejects_bad_problem(kw, code):
@@ -115,9 +115,11 @@ def test_schedule_and_fwd_validation():
     big = _problem(N=64 * 2049)
     assert L.attn_sparse_fwd(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, WS, 1 << 20,
                              None) == 2
-    pc = _problem(causal=1)
-    assert L.attn_sparse_fwd(ctypes.byref(pc), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, WS, 1 << 20,
-                             None) == 2
+    pc = _problem(causal=1)                       # causal is accepted; argument checks still apply
+    assert L.attn_sparse_fwd(ctypes.byref(pc), FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, WS, 1 << 20,
+                             None) == 1
+    assert _route(_problem(causal=1), top_p=0.0) == 1
+    assert _route(_problem(causal=1, N=64 * 1025)) == 2
     assert L.attn_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, WS, 1 << 20, None) == 1
     assert L.attn_dense_fwd(ctypes.byref(_problem(d=80)), FAKE, FAKE, FAKE, FAKE, None, WS, 1 << 20, None) == 2
     assert L.attn_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10001), WS, 1 << 20,

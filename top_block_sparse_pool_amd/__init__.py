@@ -9,11 +9,13 @@ the library's HIP kernels; there is no CPU fallback, and calls fail loudly if
 the library has not been built.
 
 The four calls of the path (same names as the C ABI):
-    route(q, k, top_p, block)            -> Route (mask, row_cnt, row_idx, head_cnt)
+    route(q, k, top_p, block, causal)    -> Route (mask, row_cnt, row_idx, head_cnt)
     schedule(problem, row_cnt)           -> work list (longest first)
-    sparse_fwd(q, k, v, route, ...)      -> (o, lse)
+    sparse_fwd(q, k, v, route, ..., causal) -> (o, lse)
     dense_fwd(q, k, v, block, causal)    -> (o, lse)
 and a convenience ``sparse_attention`` that runs all three sparse steps.
+``causal=True`` routes each query block over key blocks j <= i only and masks
+keys after each query token.
 """
 from __future__ import annotations
 
@@ -184,12 +186,13 @@ class Route:
 
 
 def route(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: Optional[float] = None,
-          ws: Optional[torch.Tensor] = None, return_prob: bool = False, out: Optional[Route] = None) -> Route:
+          ws: Optional[torch.Tensor] = None, return_prob: bool = False, out: Optional[Route] = None,
+          causal: bool = False) -> Route:
     """attn_route: block pooling, scores, softmax and top-p cut (all on the GPU)."""
     _require_device(q, k)
     if k.shape != q.shape or k.dtype != q.dtype:
         raise ValueError("q and k must share shape and dtype")
-    pr = make_problem(q, block, scale=scale)
+    pr = make_problem(q, block, causal=causal, scale=scale)
     B, H, nb = pr.batch, pr.heads, pr.num_blocks
     dev = q.device
     if out is None:
@@ -241,10 +244,11 @@ def _out_tensors(q, o, lse, want_lse):
 
 
 def sparse_fwd(q, k, v, row_cnt, row_idx, block: int, work_list=None, scale: Optional[float] = None,
-               ws: Optional[torch.Tensor] = None, o=None, lse=None, want_lse: bool = True, flags: int = 0):
+               ws: Optional[torch.Tensor] = None, o=None, lse=None, want_lse: bool = True, flags: int = 0,
+               causal: bool = False):
     """attn_sparse_fwd: attention of each query block over its selected key blocks."""
     _require_device(q, k, v, row_cnt, row_idx, work_list)
-    pr = make_problem(q, block, scale=scale, flags=flags)
+    pr = make_problem(q, block, causal=causal, scale=scale, flags=flags)
     o, lse = _out_tensors(q, o, lse, want_lse)
     if ws is None:
         ws = workspace(pr, q.device, OP_SPARSE_FWD)
@@ -268,15 +272,15 @@ def dense_fwd(q, k, v, block: int, causal: bool = False, scale: Optional[float] 
 
 def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] = None,
                      ws: Optional[torch.Tensor] = None, want_lse: bool = True,
-                     head_window: int = DEFAULT_HEAD_WINDOW):
+                     head_window: int = DEFAULT_HEAD_WINDOW, causal: bool = False):
     """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list)."""
-    pr = make_problem(q, block, scale=scale)
+    pr = make_problem(q, block, causal=causal, scale=scale)
     if ws is None:
         ws = workspace(pr, q.device)
-    r = route(q, k, top_p, block, scale=scale, ws=ws)
+    r = route(q, k, top_p, block, scale=scale, ws=ws, causal=causal)
     wl = schedule(pr, r.row_cnt, ws, head_window=head_window)
     o, lse = sparse_fwd(q, k, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
-                        want_lse=want_lse)
+                        want_lse=want_lse, causal=causal)
     return o, lse, r, wl
 
 

@@ -160,7 +160,8 @@ TBS_EXPORT int32_t attn_num_workers(const attn_problem* problem, int32_t op) {
     fail(ATTN_E_INVALID, "attn_num_workers: op must be a fwd op");
     return 0;
   }
-  const int mode = op == ATTN_OP_SPARSE_FWD ? tbs::kSparse : (s.causal ? tbs::kCausal : tbs::kDense);
+  const int mode = op == ATTN_OP_SPARSE_FWD ? (s.causal ? tbs::kSparseCausal : tbs::kSparse)
+                                            : (s.causal ? tbs::kCausal : tbs::kDense);
   return tbs::fwd_workers(s, mode);
 }
 
@@ -170,7 +171,6 @@ TBS_EXPORT int32_t attn_route(const attn_problem* problem, const void* q, const 
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
-  if (s.causal) return fail(ATTN_E_UNSUPPORTED, "attn_route: causal routing is not supported");
   if (s.nb > kMaxRouteBlocks)
     return fail(ATTN_E_UNSUPPORTED, "attn_route: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
   if (!(top_p > 0.0 && top_p <= 1.0)) return fail(ATTN_E_INVALID, "top_p must be in (0, 1] (got %g)", top_p);
@@ -256,13 +256,13 @@ TBS_EXPORT int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, c
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
-  if (s.causal) return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd: causal must be 0");
   if (s.nb > kMaxSparseBlocks)
     return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd: %d blocks per sequence exceed %d", s.nb, kMaxSparseBlocks);
   if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(row_idx, "row_idx", false)) ||
       (st = check_i32(work_list, "work_list", true)))
     return st;
-  return run_fwd(s, tbs::kSparse, q, k, v, row_cnt, row_idx, work_list, o, lse, ws, ws_bytes, stream);
+  return run_fwd(s, s.causal ? tbs::kSparseCausal : tbs::kSparse, q, k, v, row_cnt, row_idx, work_list, o, lse,
+                 ws, ws_bytes, stream);
 }
 
 TBS_EXPORT int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,

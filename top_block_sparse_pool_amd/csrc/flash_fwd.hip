@@ -86,12 +86,12 @@ struct UnitInfo {
       u = bh * p.nb + i;
     } else {
       u = qpos;
-      if (MODE == kSparse && p.work_list) u = min(max(p.work_list[qpos], 0), p.U - 1);
+      if (fwd_listed(MODE) && p.work_list) u = min(max(p.work_list[qpos], 0), p.U - 1);
       bh = u / p.nb;
       i = u - bh * p.nb;
     }
     constexpr int SPB = BQ / kKeyTile;   // key tiles per block
-    if (MODE == kSparse) {
+    if (fwd_listed(MODE)) {
       const int cnt = min(max(p.row_cnt[u], 0), p.nb);
       list = p.row_idx + static_cast<long long>(u) * p.nb;
       ntiles = cnt * SPB;
@@ -109,7 +109,7 @@ struct UnitInfo {
   }
 
   __device__ __forceinline__ int key0(const FwdParams& p, int t) const {
-    if (MODE == kSparse) {
+    if (fwd_listed(MODE)) {
       constexpr int SPB = BQ / kKeyTile;
       const int jb = min(max(list[t / SPB], 0), p.nb - 1);
       return jb * BQ + (t % SPB) * kKeyTile;
@@ -266,7 +266,7 @@ struct GroupInfo {
       g = bh * p.ng + gi;
     } else {
       g = qpos;
-      if (MODE == kSparse && p.work_list) g = min(max(p.work_list[qpos], 0), p.U - 1);
+      if (fwd_listed(MODE) && p.work_list) g = min(max(p.work_list[qpos], 0), p.U - 1);
       bh = g / p.ng;
     }
     i0 = (g - bh * p.ng) * G;
@@ -308,9 +308,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int NO = D / 32;            // 32-dim tiles of O^T
   // LDS: K stage 0, K stage 1, V stage 0, V stage 1.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILEB];
-  __shared__ unsigned s_bm[MODE == kSparse ? G * kMaxListWords : 1];
-  __shared__ unsigned short s_lj[MODE == kSparse ? kMaxListBlocks : 1];
-  __shared__ unsigned char s_lm[MODE == kSparse ? kMaxListBlocks : 1];
+  __shared__ unsigned s_bm[fwd_listed(MODE) ? G * kMaxListWords : 1];
+  __shared__ unsigned short s_lj[fwd_listed(MODE) ? kMaxListBlocks : 1];
+  __shared__ unsigned char s_lm[fwd_listed(MODE) ? kMaxListBlocks : 1];
   __shared__ int s_unit;
   __shared__ int s_nlist;
 
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // Tile list of the work item: the union of its blocks' key blocks, with
     // a bit per member block saying whether that block selected it.
     int nt;
-    if (MODE == kSparse) {
+    if (fwd_listed(MODE)) {
       const int nwords = (p.nb + 31) / 32;
       for (int x = tid; x < G * kMaxListWords; x += NT) s_bm[x] = 0u;
       __syncthreads();
@@ -430,13 +430,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       nt = (min(p.N, (gi.i0 + gi.gsz) * BQ) + kKeyTile - 1) / kKeyTile;
     }
     auto tile_key0 = [&](int t) __attribute__((always_inline)) -> int {
-      if (MODE == kSparse) return __builtin_amdgcn_readfirstlane(s_lj[t / SPB]) * BQ + (t % SPB) * kKeyTile;
+      if (fwd_listed(MODE)) return __builtin_amdgcn_readfirstlane(s_lj[t / SPB]) * BQ + (t % SPB) * kKeyTile;
       return t * kKeyTile;
     };
+    // Under a causal mask a wave skips tiles whose keys all follow its 32
+    // query rows (the second tile of a 128-row diagonal block, for the first
+    // half of its rows).
     auto tile_mine = [&](int t) __attribute__((always_inline)) -> bool {
       if (!active) return false;
+      if (MODE == kSparseCausal)
+        return ((__builtin_amdgcn_readfirstlane(s_lm[t / SPB]) >> member) & 1) && tile_key0(t) < q0w + 32;
       if (MODE == kSparse) return (__builtin_amdgcn_readfirstlane(s_lm[t / SPB]) >> member) & 1;
-      if (MODE == kCausal) return t * kKeyTile < (qblk + 1) * BQ;
+      if (MODE == kCausal) return t * kKeyTile < q0w + 32;
       return true;
     };
 
@@ -542,7 +547,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     auto vpart = [&](int t) __attribute__((always_inline)) {
       if (!(t < nt && tile_mine(t))) return;
       const int key0 = tile_key0(t);
-      const bool need_mask = (key0 + kKeyTile > p.N) || (MODE == kCausal && key0 + kKeyTile - 1 > q0w);
+      const bool need_mask = (key0 + kKeyTile > p.N) || (fwd_causal(MODE) && key0 + kKeyTile - 1 > q0w);
       if (need_mask) {
         // Mask keys past the sequence end (ragged tail) and, if causal, keys
         // after the query.  Lane value e of half mt is key 32mt + 16(e>>3) + 8h + (e&7).
@@ -551,7 +556,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = key0 + 32 * mt + 16 * (e >> 3) + 8 * h + (e & 7);
-            const bool bad = key >= p.N || (MODE == kCausal && key > qrow);
+            const bool bad = key >= p.N || (fwd_causal(MODE) && key > qrow);
             if (bad) sacc[mt][e] = -INFINITY;
           }
       }
@@ -764,7 +769,7 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_f32(FwdParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = key0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (key >= p.N || (MODE == kCausal && key > qrow)) sacc[mt][e] = -INFINITY;
+          if (key >= p.N || (fwd_causal(MODE) && key > qrow)) sacc[mt][e] = -INFINITY;
         }
       float mx = -INFINITY;
 #pragma unroll
@@ -848,9 +853,11 @@ constexpr int group_for(int dtype, int block) { return dtype == 0 ? 256 / block 
   template __global__ void flash_fwd_bf16_pp<D, BQ, kSparse>(FwdParams); \
   template __global__ void flash_fwd_bf16_pp<D, BQ, kDense>(FwdParams);  \
   template __global__ void flash_fwd_bf16_pp<D, BQ, kCausal>(FwdParams); \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, kSparseCausal>(FwdParams); \
   template __global__ void flash_fwd_f32<D, BQ, kSparse>(FwdParams);                  \
   template __global__ void flash_fwd_f32<D, BQ, kDense>(FwdParams);                   \
-  template __global__ void flash_fwd_f32<D, BQ, kCausal>(FwdParams);
+  template __global__ void flash_fwd_f32<D, BQ, kCausal>(FwdParams);                  \
+  template __global__ void flash_fwd_f32<D, BQ, kSparseCausal>(FwdParams);
 TBS_INSTANTIATE(128, 64)
 TBS_INSTANTIATE(128, 128)
 TBS_INSTANTIATE(64, 64)
@@ -859,10 +866,10 @@ TBS_INSTANTIATE(64, 128)
 
 template <int D, int BQ>
 KernelFn pick_mode(int dtype, int mode) {
-  static const KernelFn bf16_fns[3] = {flash_fwd_bf16_pp<D, BQ, kSparse>, flash_fwd_bf16_pp<D, BQ, kDense>,
-                                       flash_fwd_bf16_pp<D, BQ, kCausal>};
-  static const KernelFn f32_fns[3] = {flash_fwd_f32<D, BQ, kSparse>, flash_fwd_f32<D, BQ, kDense>,
-                                      flash_fwd_f32<D, BQ, kCausal>};
+  static const KernelFn bf16_fns[4] = {flash_fwd_bf16_pp<D, BQ, kSparse>, flash_fwd_bf16_pp<D, BQ, kDense>,
+                                       flash_fwd_bf16_pp<D, BQ, kCausal>, flash_fwd_bf16_pp<D, BQ, kSparseCausal>};
+  static const KernelFn f32_fns[4] = {flash_fwd_f32<D, BQ, kSparse>, flash_fwd_f32<D, BQ, kDense>,
+                                      flash_fwd_f32<D, BQ, kCausal>, flash_fwd_f32<D, BQ, kSparseCausal>};
   return dtype == 0 ? bf16_fns[mode] : f32_fns[mode];
 }
 

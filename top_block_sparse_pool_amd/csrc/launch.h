@@ -17,7 +17,12 @@ struct Shape {
   long long units() const { return static_cast<long long>(B) * H * nb; }
 };
 
-enum FwdMode { kSparse = 0, kDense = 1, kCausal = 2 };
+// Forward modes: a per-row block list (sparse), all keys (dense), all keys
+// up to the query (causal), or a per-row block list of blocks j <= i with
+// keys after the query masked (sparse causal).
+enum FwdMode { kSparse = 0, kDense = 1, kCausal = 2, kSparseCausal = 3 };
+constexpr bool fwd_listed(int m) { return m == kSparse || m == kSparseCausal; }
+constexpr bool fwd_causal(int m) { return m == kCausal || m == kSparseCausal; }
 
 // Control block at workspace offset 0 (bytes [0, 256)): queue counters.
 constexpr size_t kCtrlBytes = 256;

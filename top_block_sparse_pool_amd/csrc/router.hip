@@ -16,6 +16,12 @@
 //                  row: a max/sum softmax, a register bitonic sort by
 //                  (P desc, index asc), a fixed-order prefix sum to find the
 //                  cut, and the outputs -- no workgroup barriers per row.
+//
+// Causal routing (decoder models): row i only considers key blocks j <= i.
+// They are cut before the softmax, so the probabilities of row i are a
+// softmax over its i+1 eligible scores, and p >= 1 (or a cumulative sum that
+// never reaches p) selects those i+1 blocks.  The pages state top-p routing
+// for full attention only; this block-level cut is the reading taken here.
 #include <math.h>
 
 #include "device_common.h"
@@ -104,9 +110,11 @@ __device__ __forceinline__ bool ranks_before(unsigned long long ka, int ia, unsi
 }
 
 // Row phase of the selection, run by one wave per query-block row: E
-// elements per lane in blocked order (position = lane*E + i).
+// elements per lane in blocked order (position = lane*E + i).  Key blocks
+// nv..nb-1 are not eligible (nv = nb except under causal routing): they get
+// P = 0, rank after every eligible block and are never selected.
 template <int E>
-__device__ void select_row(const double* __restrict__ zr, int nb, double top_p, long long row, int bh,
+__device__ void select_row(const double* __restrict__ zr, int nb, int nv, double top_p, long long row, int bh,
                            unsigned char* __restrict__ flag, uint8_t* __restrict__ mask,
                            int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx,
                            int32_t* __restrict__ head_cnt, double* __restrict__ block_prob) {
@@ -119,14 +127,14 @@ __device__ void select_row(const double* __restrict__ zr, int nb, double top_p, 
   double m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    v[i] = zr[base + i];
+    v[i] = (base + i < nv) ? zr[base + i] : -INFINITY;
     m = fmax(m, v[i]);
   }
   m = wave_max_f64(m);
   double s = 0.0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    v[i] = (base + i < nb) ? exp(v[i] - m) : 0.0;
+    v[i] = (base + i < nv) ? exp(v[i] - m) : 0.0;
     s += v[i];
   }
   s = wave_sum_f64(s);
@@ -193,10 +201,10 @@ __device__ void select_row(const double* __restrict__ zr, int nb, double top_p, 
   int first = NP;
 #pragma unroll
   for (int i = E - 1; i >= 0; --i)
-    if (base + i < nb && excl + c[i] >= top_p) first = base + i;
+    if (base + i < nv && excl + c[i] >= top_p) first = base + i;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) first = min(first, __shfl_xor(first, off, kWave));
-  const int kcnt = (top_p >= 1.0 || first >= nb) ? nb : first + 1;
+  const int kcnt = (top_p >= 1.0 || first >= nv) ? nv : first + 1;
 
   // Flags by key-block index (this wave's LDS strip), then the outputs.
 #pragma unroll
@@ -241,7 +249,7 @@ __device__ void select_row(const double* __restrict__ zr, int nb, double top_p, 
 template <int D, int R, int E>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ qbar, const double* __restrict__ kbar_t, double scale, double top_p,
-    int nb, int tiles_per_head, uint8_t* __restrict__ mask, int32_t* __restrict__ row_cnt,
+    int nb, int causal, int tiles_per_head, uint8_t* __restrict__ mask, int32_t* __restrict__ row_cnt,
     int32_t* __restrict__ row_idx, int32_t* __restrict__ head_cnt, double* __restrict__ block_prob) {
   constexpr int NP = 64 * E;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -281,7 +289,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // Phase 2: one wave per row.
   for (int r = wave; r < rows; r += kSelWaves) {
     const long long row = static_cast<long long>(bh) * nb + i0 + r;
-    select_row<E>(z + r * NP, nb, top_p, row, bh, flags + wave * NP, mask, row_cnt, row_idx, head_cnt,
+    const int nv = causal ? i0 + r + 1 : nb;
+    select_row<E>(z + r * NP, nb, nv, top_p, row, bh, flags + wave * NP, mask, row_cnt, row_idx, head_cnt,
                   block_prob);
   }
 }
@@ -305,7 +314,7 @@ hipError_t launch_select_t(const Shape& s, const double* qbar, const double* kba
   const int tiles = (s.nb + R - 1) / R;
   const long long grid = static_cast<long long>(s.B) * s.H * tiles;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSelThreads), smem, stream, qbar, kbar_t,
-                     s.scale, top_p, s.nb, tiles, mask, row_cnt, row_idx, head_cnt, block_prob);
+                     s.scale, top_p, s.nb, s.causal ? 1 : 0, tiles, mask, row_cnt, row_idx, head_cnt, block_prob);
   return hipGetLastError();
 }
 
