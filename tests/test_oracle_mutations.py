@@ -2,15 +2,19 @@
 catch each one: a transposed operand, a wrong divisor, an exclusive threshold,
 a reversed tie rule, a dropped scale, an off-by-one causal mask, a wrong log
 base, a wrong sort direction, and a causal block cut that is missing, off by
-one, or applied after the softmax instead of before it."""
+one, or applied after the softmax instead of before it; and an augmentation
+that takes the lowest-probability candidates, measures slack from the mean
+load, or draws candidates from every worker's rows."""
 import numpy as np
 import pytest
 
 import oracle
 import oracle.attention as att
 import oracle.routing as rt
+import oracle.sasa as sa
 import test_oracle_attention as ta
 import test_oracle_routing as tr
+import test_oracle_sasa as ts
 
 
 def _patch(monkeypatch, module, name, fn):
@@ -144,3 +148,36 @@ def test_causal_cut_after_softmax_caught(monkeypatch):
     _patch(monkeypatch, rt, "softmax_rows", cut_after)
     with pytest.raises(AssertionError):
         tr.test_causal_route_against_brute_force()
+
+
+def test_sasa_lowest_probability_first_caught(monkeypatch):
+    orig = sa.augment
+
+    def low_first(prob, *a, **k):
+        return orig(-np.asarray(prob), *a, **k)
+    monkeypatch.setattr(oracle, "augment", low_first)
+    with pytest.raises(AssertionError):
+        ts.test_brute_force_added_blocks_carry_max_mass(0, 400, 1, 6)
+
+
+def test_sasa_slack_from_mean_caught(monkeypatch):
+    orig_lpt = sa.lpt_assign
+
+    def mean_makespan(costs, order, W):
+        worker_of, load = orig_lpt(costs, order, W)
+        # a wrong slack: measured from the mean load (raise every load to the max minus the mean)
+        return worker_of, load - (load.max() - int(load.mean()))
+    monkeypatch.setattr(sa, "lpt_assign", mean_makespan)
+    with pytest.raises(AssertionError):
+        ts.test_hand_example_two_workers()
+
+
+def test_sasa_candidates_from_all_rows_caught(monkeypatch):
+    orig_lpt = sa.lpt_assign
+
+    def one_worker_rows(costs, order, W):
+        worker_of, load = orig_lpt(costs, order, W)
+        return np.zeros_like(worker_of), load          # every row counted as worker 0's
+    monkeypatch.setattr(sa, "lpt_assign", one_worker_rows)
+    with pytest.raises(AssertionError):
+        ts.test_hand_example_three_workers_ties()
