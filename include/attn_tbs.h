@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define ATTN_TBS_ABI_VERSION 1
+#define ATTN_TBS_ABI_VERSION 2
 
 /* Status codes. */
 #define ATTN_OK            0
@@ -82,6 +82,7 @@ extern "C" {
 #define ATTN_OP_SCHEDULE   1
 #define ATTN_OP_SPARSE_FWD 2
 #define ATTN_OP_DENSE_FWD  3
+#define ATTN_OP_AUGMENT    4
 
 /* Problem flags. */
 #define ATTN_FLAG_PROFILE_WORKERS 1  /* fwd calls record per-worker start/end
@@ -111,16 +112,18 @@ const char* attn_last_error(void);
  * block (the persistent kernel's queue counters): they must be zero when
  * attn_sparse_fwd or attn_dense_fwd starts.  A zero-filled workspace
  * satisfies this, and attn_schedule and every fwd call leave them zero when
- * they complete, so one zero fill at allocation is enough.  One workspace of
- * the largest size serves all four operations. */
+ * they complete, so one zero fill at allocation is enough (attn_route and
+ * attn_augment use only the bytes after it).  One workspace of the largest
+ * size serves every operation. */
 size_t attn_workspace_bytes(const attn_problem* problem, int32_t op);
 
 /* Query blocks per work item, G.  The persistent fwd kernel processes a work
  * item -- G consecutive query blocks of one (b, h) -- in one workgroup: every
  * K/V tile in the union of the G blocks' selected key blocks is loaded once and
  * each block's waves compute only the tiles that block selected (adjacent
- * query blocks select largely the same key blocks).  G = 2 for bf16 with
- * block 64, otherwise 1.  Work item g = (b*H + h)*ceil(nb/G) + i/G covers query
+ * query blocks select largely the same key blocks).  For bf16 a work item
+ * holds 256 query rows: G = 4 with block 64, G = 2 with block 128; G = 1 for
+ * fp32.  Work item g = (b*H + h)*ceil(nb/G) + i/G covers query
  * blocks G*(i/G) .. min(G*(i/G) + G, nb) - 1; there are B*H*ceil(nb/G) items.
  * Returns 0 if the problem is invalid. */
 int32_t attn_group_size(const attn_problem* problem);
@@ -153,8 +156,11 @@ int32_t attn_num_workers(const attn_problem* problem, int32_t op);
  *   mask      [B,H,nb,nb] uint8 out: 1 where key block j is selected for row i.
  *   row_cnt   [B,H,nb] int32 out: k_i, number of selected key blocks (>= 1).
  *   row_idx   [B,H,nb,nb] int32 out: the first row_cnt entries of each row are
- *             the selected key blocks in ascending order; later entries are
- *             not written.
+ *             the selected key blocks in ascending order; the next entries,
+ *             up to the number of eligible blocks (nb, or i+1 under causal
+ *             routing), are the unselected eligible blocks in rank order
+ *             (P descending, equal P by smaller index), which attn_augment
+ *             reads; entries after those are not written.
  *   head_cnt  [B,H] int32 out: sum over i of row_cnt (overwritten, not added to).
  *   block_prob [B,H,nb,nb] double out, nullable: the block probabilities P
  *             (0 for key blocks cut by causal routing).
@@ -186,15 +192,48 @@ int32_t attn_route(const attn_problem* problem, const void* q, const void* k, do
  *   worker_of    [B*H*ceil(nb/G)] int32 out, nullable: greedy
  *                longest-processing-time assignment in work-list order (each
  *                item to the least-loaded worker, ties to the lowest id).  Only
- *                computed when worker_of or worker_load is given; it runs one
- *                wavefront and is meant for reporting load balance, not for
- *                the hot path.
+ *                computed when worker_of or worker_load is given: the greedy
+ *                is sequential (one wavefront, loads in registers), so it
+ *                costs time proportional to the number of work items; it
+ *                serves load-balance reports and attn_augment.
  *   worker_load  [num_workers] int64 out, nullable: summed cost per worker
  *                under that assignment.
  * Requires nb <= 1024 and num_workers <= 4096. */
 int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32_t head_window,
                       int32_t num_workers, int32_t* work_list, int32_t* worker_of, int64_t* worker_load,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* Slack-aware sparse augmentation (SASA) on one GPU.
+ *
+ * Source: FVAttn review page, section 1 (Key Terms, "Slack-Aware Sparse
+ * Augmentation") and section 3 (Method): after load balancing, ranks with
+ * slack compute extra high-value blocks.  Here the ranks are the workers of
+ * the LPT model of attn_schedule: with M the largest worker load, worker w
+ * has slack s_w = M - worker_load[w] and adds the first min(s_w, #candidates)
+ * of its candidates -- the eligible unselected key blocks of the query blocks
+ * of the work items assigned to it -- ordered by block probability
+ * descending, then unit id, then key-block index (inside a row that is the
+ * routing rank order, so every row's selection stays a prefix of its
+ * ranking).  An added block costs one unit, like a selected one, so no
+ * worker's modelled load exceeds M.  Updates the routing outputs in place;
+ * call attn_schedule again for a work list over the new counts.
+ *
+ *   block_prob   [B,H,nb,nb] double, from attn_route (block_prob output).
+ *   worker_of    [B*H*ceil(nb/G)] int32, worker_load [num_workers] int64:
+ *                from attn_schedule's LPT model with the same num_workers.
+ *   num_workers  1 .. 4096.
+ *   mask, row_cnt, row_idx, head_cnt   attn_route's outputs, updated in
+ *                place; row_idx must hold the ranked tail attn_route writes
+ *                after the selected blocks (its entries past the new count
+ *                keep the remaining unselected blocks in rank order).
+ *   added        [num_workers] int32 out, nullable: blocks added per worker.
+ *   ws           attn_workspace_bytes(problem, ATTN_OP_AUGMENT) bytes; the
+ *                control block is not touched.
+ * Honours causal (eligible blocks j <= i).  Requires nb <= 1024. */
+int32_t attn_augment(const attn_problem* problem, const double* block_prob, const int32_t* worker_of,
+                     const int64_t* worker_load, int32_t num_workers, uint8_t* mask, int32_t* row_cnt,
+                     int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* Block-sparse attention forward, one persistent kernel launch.
  *

@@ -28,10 +28,11 @@ def test_exports_every_declared_symbol():
     L = tbs.lib()
     names = _declared_functions()
     assert set(names) == {"attn_abi_version", "attn_last_error", "attn_workspace_bytes", "attn_num_workers",
-                          "attn_group_size", "attn_route", "attn_schedule", "attn_sparse_fwd", "attn_dense_fwd"}
+                          "attn_group_size", "attn_route", "attn_schedule", "attn_augment", "attn_sparse_fwd",
+                          "attn_dense_fwd"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 1
+    assert L.attn_abi_version() == 2
 
 
 def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0):
@@ -62,6 +63,9 @@ def test_workspace_sizes():
     assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_SPARSE_FWD) == 256
     p.flags = tbs.FLAG_PROFILE_WORKERS
     assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_DENSE_FWD) == 256 + 16 * 4096
+    U = 40 * nb
+    up = lambda x: (x + 255) // 256 * 256
+    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_AUGMENT) == 256 + up(4 * 4097) + 2 * up(4 * U) + up(64 * U)
     assert L.attn_workspace_bytes(ctypes.byref(p), 9) == 0
     assert L.attn_workspace_bytes(None, 0) == 0
 
@@ -124,3 +128,22 @@ def test_schedule_and_fwd_validation():
     assert L.attn_dense_fwd(ctypes.byref(_problem(d=80)), FAKE, FAKE, FAKE, FAKE, None, WS, 1 << 20, None) == 2
     assert L.attn_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10001), WS, 1 << 20,
                             None) == 1
+
+
+def test_augment_validation():
+    L = tbs.lib()
+    p = _problem()
+    D = ctypes.c_void_p(0x10000)
+
+    def aug(pr=p, bp=D, wo=D, wl=D, W=256, mask=D, rc=D, ri=D, hc=D, added=None, ws=WS, wsb=1 << 30):
+        return L.attn_augment(ctypes.byref(pr) if pr is not None else None, bp, wo, wl, W, mask, rc, ri, hc, added,
+                              ws, wsb, None)
+    assert aug(pr=None) == 1
+    assert aug(W=0) == 1 and aug(W=4097) == 1
+    assert aug(bp=None) == 1 and aug(bp=ctypes.c_void_p(0x10004)) == 1
+    assert aug(wl=ctypes.c_void_p(0x10004)) == 1
+    assert aug(wo=None) == 1 and aug(mask=None) == 1 and aug(ri=ctypes.c_void_p(0x10002)) == 1
+    assert aug(added=ctypes.c_void_p(0x10001)) == 1
+    assert aug(pr=_problem(N=64 * 1025)) == 2
+    assert aug(wsb=1000) == 3 and aug(ws=None) == 3
+    assert "workspace" in L.attn_last_error().decode()

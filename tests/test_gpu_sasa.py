@@ -1,0 +1,144 @@
+"""GPU parity of the ranked tail the router leaves after the selected blocks,
+of the LPT model for any worker count, and of slack-aware augmentation
+(attn_augment) against the fp64 oracle.  Every call goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import top_block_sparse_pool_amd as tbs
+from parity import compare_units, to64
+from workloads import custom_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(w, seed=0):
+    print(f"[case] {w.describe()} seed={seed}", flush=True)
+    return [t.to(DEV) for t in make_inputs(w, seed)]
+
+
+def _oracle_route(q, k, block, p, causal):
+    return oracle.route(to64(q), to64(k), block, p, causal=causal)
+
+
+TAIL = [
+    (custom_workload(1, 3, 1000, 128, 64, "bf16", 0.8, wid=501), False),
+    (custom_workload(1, 2, 1300, 128, 128, "bf16", 0.7, wid=502), True),
+    (custom_workload(1, 2, 600, 64, 64, "f32", 0.5, wid=503), False),
+]
+
+
+@pytest.mark.parametrize("w,causal", TAIL, ids=lambda x: getattr(x, "name", str(x)))
+def test_route_ranked_tail(w, causal):
+    q, k, v = _inputs(w)
+    r = tbs.route(q, k, w.top_p, w.block, causal=causal, return_prob=True)
+    torch.cuda.synchronize()
+    ref = _oracle_route(q, k, w.block, w.top_p, causal)
+    prob = r.block_prob.cpu().numpy()
+    assert np.abs(prob - ref.prob).max() <= 1e-12
+    mask, rc, ri = r.mask.cpu().numpy(), r.row_cnt.cpu().numpy(), r.row_idx.cpu().numpy()
+    B, H, nb = rc.shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                nv = i + 1 if causal else nb
+                kk = int(rc[b, h, i])
+                tail = ri[b, h, i, kk:nv]
+                assert sorted(tail.tolist()) == np.nonzero(mask[b, h, i, :nv] == 0)[0].tolist()
+                pt = prob[b, h, i, tail]
+                # ranked: P descending, equal P by smaller index
+                assert all(pt[x] > pt[x + 1] or (pt[x] == pt[x + 1] and tail[x] < tail[x + 1])
+                           for x in range(len(tail) - 1))
+
+
+@pytest.mark.parametrize("W", [7, 64, 65, 256, 300, 1024, 4096])
+def test_lpt_any_worker_count(W):
+    w = custom_workload(2, 5, 2000, 128, 64, "bf16", 0.9, wid=510)
+    q, k, v = _inputs(w)
+    pr = tbs.make_problem(q, w.block)
+    ws = tbs.workspace(pr, DEV)
+    r = tbs.route(q, k, w.top_p, w.block, ws=ws)
+    wl, worker_of, worker_load = tbs.schedule(pr, r.row_cnt, ws, head_window=2, num_workers=W, lpt=True)
+    torch.cuda.synchronize()
+    costs = oracle.group_costs(r.row_cnt.cpu().numpy(), pr.group)
+    want_of, want_load = oracle.lpt_assign(costs, wl.cpu().numpy(), W)
+    assert (worker_of.cpu().numpy() == want_of).all()
+    assert (worker_load.cpu().numpy() == want_load).all()
+
+
+AUG = [
+    (custom_workload(1, 4, 2000, 128, 64, "bf16", 0.8, wid=520), False, 16),     # G = 4
+    (custom_workload(1, 4, 2000, 128, 64, "bf16", 0.8, wid=520), False, 256),
+    (custom_workload(2, 3, 1500, 128, 128, "bf16", 0.7, wid=521), False, 7),     # G = 2
+    (custom_workload(1, 3, 900, 64, 64, "f32", 0.6, wid=522), False, 5),         # G = 1
+    (custom_workload(1, 4, 2000, 128, 64, "bf16", 0.8, wid=523), True, 16),      # causal
+    (custom_workload(1, 12, 16384, 64, 64, "bf16", 0.5, wid=524), False, 2),     # > 1024 rows per worker
+]
+
+
+@pytest.mark.parametrize("w,causal,W", AUG, ids=lambda x: getattr(x, "name", str(x)))
+def test_augment_matches_oracle(w, causal, W):
+    q, k, v = _inputs(w)
+    pr = tbs.make_problem(q, w.block, causal=causal)
+    ws = tbs.workspace(pr, DEV)
+    r = tbs.route(q, k, w.top_p, w.block, ws=ws, causal=causal, return_prob=True)
+    hw = 2
+    wl, worker_of, worker_load = tbs.schedule(pr, r.row_cnt, ws, head_window=hw, num_workers=W, lpt=True)
+    mask0 = r.mask.clone()
+    added = tbs.augment(pr, r, worker_of, worker_load, ws)
+    torch.cuda.synchronize()
+    G = pr.group
+    ng = -(-pr.num_blocks // G)
+    # The oracle routes and augments from q and k on its own.
+    rr = _oracle_route(q, k, w.block, w.top_p, causal)
+    ref = oracle.augment(rr.prob, rr.mask, rr.row_cnt, rr.valid, G, hw * ng, W)
+    same_route = bool((mask0.cpu().numpy() == rr.mask).all())
+    print(f"  routing identical: {same_route}; oracle adds {int(ref.added.sum())} blocks, "
+          f"slack {int(ref.slack.sum())}", flush=True)
+    rc = r.row_cnt.cpu().numpy()
+    mask = r.mask.cpu().numpy()
+    ri = r.row_idx.cpu().numpy()
+    if same_route:
+        assert (mask == ref.mask).all()
+        assert (rc == ref.row_cnt).all()
+        assert (r.head_cnt.cpu().numpy() == ref.head_cnt).all()
+        assert (added.cpu().numpy() == ref.added_per_worker).all()
+        valid = np.arange(pr.num_blocks) < rc[..., None]
+        assert (np.where(valid, ri, -1) == ref.row_idx).all()
+    # Properties that hold whatever the routing: the makespan is kept, every
+    # row is a prefix of its ranking, counts agree with the mask.
+    load = worker_load.cpu().numpy()
+    assert (load + added.cpu().numpy()).max() == load.max() or added.sum() == 0
+    assert (rc == mask.astype(np.int64).sum(-1)).all()
+    assert (r.head_cnt.cpu().numpy() == rc.sum(-1)).all()
+    assert (mask >= mask0.cpu().numpy()).all()
+    # attention over the augmented lists
+    wl2 = tbs.schedule(pr, r.row_cnt, ws, head_window=hw)
+    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl2, ws=ws, causal=causal)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    units = [(b, h, int(i)) for b in range(pr.batch) for h in range(pr.heads)
+             for i in rng.choice(pr.num_blocks, size=min(3, pr.num_blocks), replace=False)]
+    ref_mask = ref.mask if same_route else mask
+    e, le = compare_units(o, lse, q, k, v, w.block, units, ref_mask, q.dtype, causal=causal)
+    print(f"  attention on augmented lists: max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)
+
+
+def test_sparse_attention_with_sasa_end_to_end():
+    w = custom_workload(1, 4, 2000, 128, 64, "bf16", 0.8, wid=530)
+    q, k, v = _inputs(w)
+    o, lse, r, wl = tbs.sparse_attention(q, k, v, w.top_p, w.block, sasa=True, num_workers=16)
+    torch.cuda.synchronize()
+    pr = tbs.make_problem(q, w.block)
+    rr = _oracle_route(q, k, w.block, w.top_p, False)
+    G = pr.group
+    ng = -(-pr.num_blocks // G)
+    ref = oracle.augment(rr.prob, rr.mask, rr.row_cnt, rr.valid, G, tbs.DEFAULT_HEAD_WINDOW * ng, 16)
+    assert (r.mask.cpu().numpy() == ref.mask).all()
+    mass0 = oracle.retained_mass(rr.prob, rr.mask).mean()
+    mass1 = oracle.retained_mass(rr.prob, ref.mask).mean()
+    print(f"  mean retained mass {mass0:.4f} -> {mass1:.4f}, {int(ref.added.sum())} blocks added", flush=True)
+    units = [(0, h, i) for h in range(4) for i in (0, 7, pr.num_blocks - 1)]
+    compare_units(o, lse, q, k, v, w.block, units, ref.mask, q.dtype)

@@ -11,6 +11,7 @@ the library has not been built.
 The four calls of the path (same names as the C ABI):
     route(q, k, top_p, block, causal)    -> Route (mask, row_cnt, row_idx, head_cnt)
     schedule(problem, row_cnt)           -> work list (longest first)
+    augment(problem, route, worker_of, worker_load, ws) -> slack-aware augmentation, in place
     sparse_fwd(q, k, v, route, ..., causal) -> (o, lse)
     dense_fwd(q, k, v, block, causal)    -> (o, lse)
 and a convenience ``sparse_attention`` that runs all three sparse steps.
@@ -32,7 +33,7 @@ LIB_PATH = os.path.join(_PKG, "libattn_tbs.so")
 
 ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_DEVICE = 0, 1, 2, 3, 4
 ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1
-OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD = 0, 1, 2, 3
+OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD, OP_AUGMENT = 0, 1, 2, 3, 4
 FLAG_PROFILE_WORKERS = 1
 CTRL_BYTES = 256
 DEFAULT_HEAD_WINDOW = 4
@@ -113,6 +114,8 @@ def lib() -> ctypes.CDLL:
     L.attn_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_dense_fwd.restype = i32
     L.attn_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_augment.restype = i32
+    L.attn_augment.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -158,7 +161,7 @@ def make_problem(q: torch.Tensor, block: int, causal: bool = False, scale: Optio
 
 
 def workspace_bytes(problem: Problem, op: Optional[int] = None) -> int:
-    ops = [op] if op is not None else [OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD]
+    ops = [op] if op is not None else [OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD, OP_AUGMENT]
     n = max(lib().attn_workspace_bytes(ctypes.byref(problem), o) for o in ops)
     if n == 0:
         _check(ATTN_E_INVALID)
@@ -234,6 +237,25 @@ def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, head_win
     return work_list
 
 
+def augment(problem: Problem, r: Route, worker_of: torch.Tensor, worker_load: torch.Tensor, ws: torch.Tensor,
+            added: Optional[torch.Tensor] = None, want_added: bool = True) -> Optional[torch.Tensor]:
+    """attn_augment: slack-aware augmentation of the routing `r` in place.
+
+    worker_of / worker_load come from schedule(..., lpt=True) over the same
+    number of workers; r needs its block probabilities (route(...,
+    return_prob=True)).  Returns the blocks added per worker (int32)."""
+    if r.block_prob is None:
+        raise ValueError("augment needs the block probabilities: route(..., return_prob=True)")
+    _require_device(worker_of, worker_load, ws, r.mask, r.row_cnt, r.row_idx, r.head_cnt, r.block_prob)
+    W = worker_load.numel()
+    if added is None and want_added:
+        added = torch.empty(W, dtype=torch.int32, device=worker_load.device)
+    _check(lib().attn_augment(ctypes.byref(problem), _ptr(r.block_prob), _ptr(worker_of), _ptr(worker_load), int(W),
+                              _ptr(r.mask), _ptr(r.row_cnt), _ptr(r.row_idx), _ptr(r.head_cnt), _ptr(added),
+                              _ptr(ws), ws.numel(), _stream()))
+    return added
+
+
 def _out_tensors(q, o, lse, want_lse):
     B, H, N, d = q.shape
     if o is None:
@@ -272,12 +294,20 @@ def dense_fwd(q, k, v, block: int, causal: bool = False, scale: Optional[float] 
 
 def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] = None,
                      ws: Optional[torch.Tensor] = None, want_lse: bool = True,
-                     head_window: int = DEFAULT_HEAD_WINDOW, causal: bool = False):
-    """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list)."""
+                     head_window: int = DEFAULT_HEAD_WINDOW, causal: bool = False, sasa: bool = False,
+                     num_workers: int = 0):
+    """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list).
+
+    With sasa=True: route -> schedule with the LPT model -> augment -> schedule
+    again over the augmented counts -> sparse_fwd."""
     pr = make_problem(q, block, causal=causal, scale=scale)
     if ws is None:
         ws = workspace(pr, q.device)
-    r = route(q, k, top_p, block, scale=scale, ws=ws, causal=causal)
+    r = route(q, k, top_p, block, scale=scale, ws=ws, causal=causal, return_prob=sasa)
+    if sasa:
+        _, worker_of, worker_load = schedule(pr, r.row_cnt, ws, head_window=head_window,
+                                             num_workers=num_workers, lpt=True)
+        augment(pr, r, worker_of, worker_load, ws, want_added=False)
     wl = schedule(pr, r.row_cnt, ws, head_window=head_window)
     o, lse = sparse_fwd(q, k, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
                         want_lse=want_lse, causal=causal)
@@ -286,5 +316,5 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
 
 __all__ = [
     "lib", "AttnError", "Problem", "Route", "make_problem", "workspace", "workspace_bytes", "num_workers",
-    "route", "schedule", "sparse_fwd", "dense_fwd", "sparse_attention", "LIB_PATH",
+    "route", "schedule", "augment", "sparse_fwd", "dense_fwd", "sparse_attention", "LIB_PATH",
 ]

@@ -42,6 +42,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr size_t kProfileBytes = 16 * 4096;   // per-worker stamps, at most 4096 workers
 constexpr int kMaxRouteBlocks = 1024;
 constexpr int kMaxSparseBlocks = 2048;
+constexpr int kMaxWorkers = 4096;
 
 // Validates the problem descriptor and resolves it into a Shape.
 int32_t check_problem(const attn_problem* pr, tbs::Shape* s) {
@@ -143,6 +144,7 @@ TBS_EXPORT size_t attn_workspace_bytes(const attn_problem* problem, int32_t op) 
     case ATTN_OP_SCHEDULE: return tbs::kCtrlBytes;
     case ATTN_OP_SPARSE_FWD:
     case ATTN_OP_DENSE_FWD: return fwd_bytes(s);
+    case ATTN_OP_AUGMENT: return tbs::augment_ws_bytes(s, kMaxWorkers);
     default: fail(ATTN_E_INVALID, "unknown op %d", op); return 0;
   }
 }
@@ -201,8 +203,8 @@ TBS_EXPORT int32_t attn_schedule(const attn_problem* problem, const int32_t* row
   if (s.nb > kMaxRouteBlocks)
     return fail(ATTN_E_UNSUPPORTED, "attn_schedule: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
   if (head_window < 0) return fail(ATTN_E_INVALID, "head_window must be >= 0 (got %d)", head_window);
-  if (num_workers < 0 || num_workers > 4096)
-    return fail(ATTN_E_INVALID, "num_workers must be in [0, 4096] (got %d)", num_workers);
+  if (num_workers < 0 || num_workers > kMaxWorkers)
+    return fail(ATTN_E_INVALID, "num_workers must be in [0, %d] (got %d)", kMaxWorkers, num_workers);
   if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(work_list, "work_list", false)) ||
       (st = check_i32(worker_of, "worker_of", true)))
     return st;
@@ -218,6 +220,31 @@ TBS_EXPORT int32_t attn_schedule(const attn_problem* problem, const int32_t* row
     if (e != hipSuccess) return device_status(e, "attn_schedule lpt launch");
   }
   return ok();
+}
+
+TBS_EXPORT int32_t attn_augment(const attn_problem* problem, const double* block_prob, const int32_t* worker_of,
+                                const int64_t* worker_load, int32_t num_workers, uint8_t* mask, int32_t* row_cnt,
+                                int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, size_t ws_bytes,
+                                void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if (s.nb > kMaxRouteBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_augment: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
+  if (num_workers < 1 || num_workers > kMaxWorkers)
+    return fail(ATTN_E_INVALID, "num_workers must be in [1, %d] (got %d)", kMaxWorkers, num_workers);
+  if (!block_prob || !aligned(block_prob, 8)) return fail(ATTN_E_INVALID, "block_prob is NULL or not 8-byte aligned");
+  if (!worker_load || !aligned(worker_load, 8))
+    return fail(ATTN_E_INVALID, "worker_load is NULL or not 8-byte aligned");
+  if (!mask) return fail(ATTN_E_INVALID, "mask is NULL");
+  if ((st = check_i32(worker_of, "worker_of", false)) || (st = check_i32(row_cnt, "row_cnt", false)) ||
+      (st = check_i32(row_idx, "row_idx", false)) || (st = check_i32(head_cnt, "head_cnt", false)) ||
+      (st = check_i32(added, "added", true)))
+    return st;
+  if ((st = check_ws(ws, ws_bytes, tbs::augment_ws_bytes(s, num_workers)))) return st;
+  hipError_t e = tbs::launch_augment(s, block_prob, worker_of, worker_load, num_workers, mask, row_cnt, row_idx,
+                                     head_cnt, added, ws, static_cast<hipStream_t>(stream));
+  return device_status(e, "attn_augment launch");
 }
 
 namespace {

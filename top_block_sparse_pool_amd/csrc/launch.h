@@ -41,6 +41,14 @@ hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int head_wind
 hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* work_list,
                       int num_workers, int32_t* worker_of, int64_t* worker_load, hipStream_t stream);
 
+// Slack-aware augmentation: worker rows (CSR), a merge per worker, then the
+// rebuilt lists of the rows that gained blocks.  Workspace bytes after the
+// control block, for up to 4096 workers.
+size_t augment_ws_bytes(const Shape& s, int num_workers);
+hipError_t launch_augment(const Shape& s, const double* block_prob, const int32_t* worker_of,
+                          const int64_t* worker_load, int num_workers, uint8_t* mask, int32_t* row_cnt,
+                          int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, hipStream_t stream);
+
 // Attention forward.
 struct FwdArgs {
   const void* q;

@@ -238,6 +238,11 @@ __device__ void select_row(const double* __restrict__ zr, int nb, int nv, double
 #pragma unroll
   for (int i = 0; i < E; ++i)
     if (f[i]) ridx[pos++] = base + i;
+  // After the selected blocks: the unselected eligible blocks in rank order
+  // (rank positions kcnt .. nv-1), for slack-aware augmentation.
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (base + i >= kcnt && base + i < nv) ridx[base + i] = idx[i];
   if (lane == 0) {
     row_cnt[row] = kcnt;
     atomicAdd(head_cnt + bh, kcnt);

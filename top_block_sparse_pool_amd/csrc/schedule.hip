@@ -28,8 +28,9 @@
 //   slot; each wave then walks its slice in order, ranking equal costs inside
 //   a 64-unit batch with ballots over the cost bits, so equal costs keep
 //   ascending unit ids.
-// lpt_kernel: optional single-wave greedy longest-processing-time model of
-//   the same order over W workers, for reporting load balance.
+// lpt_kernel: greedy longest-processing-time model of the same order over W
+//   workers (the worker of every item and every worker's load), for
+//   reporting load balance and for slack-aware augmentation.
 #include "device_common.h"
 #include "launch.h"
 
@@ -149,39 +150,95 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   if (blockIdx.x == 0 && tid < static_cast<int>(kCtrlBytes / sizeof(uint32_t))) ctrl[tid] = 0u;
 }
 
-__global__ __launch_bounds__(kWave) void lpt_kernel(const int32_t* __restrict__ row_cnt,
-                                                    const int32_t* __restrict__ work_list, int items, int nb,
-                                                    int G, int ng, int W, int32_t* __restrict__ worker_of,
-                                                    int64_t* __restrict__ worker_load) {
-  __shared__ long long load[4096];
-  const int lane = threadIdx.x;
-  for (int w = lane; w < W; w += kWave) load[w] = 0;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  for (int t = 0; t < items; ++t) {
-    const int u = min(max(work_list[t], 0), items - 1);
-    const int c = item_cost(row_cnt, u, nb, G, ng);
-    long long best = 0x7fffffffffffffffLL;
-    int bid = 0x7fffffff;
-    for (int w = lane; w < W; w += kWave) {
-      const long long l = load[w];
-      if (l < best) { best = l; bid = w; }
-    }
+// Minimum of a uniform-free value over the wave, returned in every lane:
+// butterflies inside each row of 16 lanes (DPP), then the four row minima.
+__device__ __forceinline__ unsigned wave_min_u32(unsigned v) {
+  v = min(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0xB1, 0xF,
+                                                               0xF, false)));   // quad_perm 1,0,3,2
+  v = min(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x4E, 0xF,
+                                                               0xF, false)));   // quad_perm 2,3,0,1
+  v = min(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x141, 0xF,
+                                                               0xF, false)));   // row_half_mirror
+  v = min(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x140, 0xF,
+                                                               0xF, false)));   // row_mirror
+  const unsigned r0 = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+  const unsigned r1 = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+  const unsigned r2 = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+  const unsigned r3 = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+constexpr int kLptThreads = 1024;
+constexpr int kLptChunk = 8192;   // work-list entries staged in LDS per round
+
+// Greedy LPT in list order: every item goes to the worker with the least load
+// so far, equal loads to the lowest worker id.  All workgroup threads stage
+// the item costs of a chunk of the list in LDS; wave 0 then runs the
+// sequential greedy with the loads in registers (worker w = 64 s + lane in
+// slot s).  A worker is compared through the key (load - base) << 12 | w,
+// where base is the previous minimum: every load is at least base, and loads
+// never spread by more than the largest item cost (<= 4096), so the key fits
+// 32 bits and its minimum is the least load with the lowest id.
+template <int R>
+__global__ __launch_bounds__(kLptThreads) void lpt_kernel(const int32_t* __restrict__ row_cnt,
+                                                          const int32_t* __restrict__ work_list, int items, int nb,
+                                                          int G, int ng, int W, int32_t* __restrict__ worker_of,
+                                                          int64_t* __restrict__ worker_load) {
+  __shared__ unsigned short s_cost[kLptChunk];
+  __shared__ int s_id[kLptChunk];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  unsigned key[R];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const long long ob = __shfl_xor(best, off, kWave);
-      const int oi = __shfl_xor(bid, off, kWave);
-      if (ob < best || (ob == best && oi < bid)) { best = ob; bid = oi; }
-    }
-    if (lane == 0) {
-      load[bid] = best + c;
-      if (worker_of) worker_of[u] = bid;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  for (int r = 0; r < R; ++r) {
+    const int w = kWave * r + lane;
+    key[r] = w < W ? static_cast<unsigned>(w) : 0xffffffffu;
   }
-  if (worker_load)
-    for (int w = lane; w < W; w += kWave) worker_load[w] = load[w];
+  unsigned long long base = 0;
+  for (int c0 = 0; c0 < items; c0 += kLptChunk) {
+    const int n = min(kLptChunk, items - c0);
+    __syncthreads();
+    for (int x = tid; x < n; x += kLptThreads) {
+      const int u = min(max(work_list[c0 + x], 0), items - 1);
+      s_id[x] = u;
+      s_cost[x] = static_cast<unsigned short>(item_cost(row_cnt, u, nb, G, ng));
+    }
+    __syncthreads();
+    if (wave != 0) continue;
+    for (int b = 0; b < n; b += kWave) {
+      const int m = min(kWave, n - b);
+      const int my_cost = lane < m ? s_cost[b + lane] : 0;
+      const int my_id = lane < m ? s_id[b + lane] : 0;
+      int my_w = 0;
+      for (int e = 0; e < m; ++e) {
+        const unsigned c = static_cast<unsigned>(__builtin_amdgcn_readlane(my_cost, e));
+        unsigned k = key[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) k = min(k, key[r]);
+        const unsigned kmin = wave_min_u32(k);
+        const unsigned wmin = kmin & 0xfffu;
+        const unsigned shift = kmin & ~0xfffu;   // the new base, relative to the old one
+        base += kmin >> 12;
+        const int slot = static_cast<int>(wmin) / kWave;
+        const bool mine = lane == static_cast<int>(wmin) % kWave;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (key[r] != 0xffffffffu) key[r] -= shift;
+          if (r == slot && mine) key[r] += c << 12;
+        }
+        if (lane == e) my_w = static_cast<int>(wmin);
+      }
+      if (lane < m && worker_of) worker_of[my_id] = my_w;
+    }
+  }
+  if (wave == 0 && worker_load) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int w = kWave * r + lane;
+      if (w < W) worker_load[w] = static_cast<int64_t>(base + (key[r] >> 12));
+    }
+  }
 }
 
 }  // namespace
@@ -210,7 +267,10 @@ hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* wor
   const int G = group_size(s);
   const int ng = (s.nb + G - 1) / G;
   const int items = s.B * s.H * ng;
-  hipLaunchKernelGGL(lpt_kernel, dim3(1), dim3(kWave), 0, stream, row_cnt, work_list, items, s.nb, G, ng,
+  auto kern = num_workers <= 64 ? lpt_kernel<1>
+             : num_workers <= 256 ? lpt_kernel<4>
+             : num_workers <= 1024 ? lpt_kernel<16> : lpt_kernel<64>;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kLptThreads), 0, stream, row_cnt, work_list, items, s.nb, G, ng,
                      num_workers, worker_of, worker_load);
   return hipGetLastError();
 }
