@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--workload", default="video-32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--causal", action="store_true", help="causal routing and causal attention")
+    ap.add_argument("--sasa", action="store_true",
+                    help="slack-aware augmentation in the step: LPT model, attn_augment, a second schedule")
     ap.add_argument("--head-window", type=int, default=None, help="heads per scheduling window (default: library's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -163,8 +165,18 @@ def main():
                           torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev),
                           torch.empty((B, H, nb), dtype=torch.int32, device=dev),
                           torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
-                          torch.empty((B, H), dtype=torch.int32, device=dev))
+                          torch.empty((B, H), dtype=torch.int32, device=dev),
+                          torch.empty((B, H, nb, nb), dtype=torch.float64, device=dev) if args.sasa else None)
     work_list = torch.empty(pr.items, dtype=torch.int32, device=dev)
+    n_workers = torch.cuda.get_device_properties(dev).multi_processor_count
+    worker_of = torch.empty(pr.items, dtype=torch.int32, device=dev)
+    worker_load = torch.empty(n_workers, dtype=torch.int64, device=dev)
+    added = torch.empty(n_workers, dtype=torch.int32, device=dev)
+
+    def sasa_steps():
+        tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True, work_list=work_list,
+                     worker_of=worker_of, worker_load=worker_load)
+        tbs.augment(pr, route_out, worker_of, worker_load, ws, added=added)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
 
@@ -174,6 +186,8 @@ def main():
         tbs.route(q, k, w.top_p, w.block, ws=ws, out=route_out, causal=causal)
         if ev is not None:
             ev[1].record()
+        if args.sasa:
+            sasa_steps()
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         if ev is not None:
             ev[2].record()
@@ -212,12 +226,12 @@ def main():
     padded = np.zeros((rc.shape[0], ng * G), dtype=np.int64)
     padded[:, :nb] = rc
     item_cost = padded.reshape(-1, ng, G).sum(-1).reshape(-1)        # cost of each work item
-    wl, worker_of, worker_load = tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True)
+    _, _, lpt_load = tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True)
     torch.cuda.synchronize()
-    W = worker_load.numel()
+    W = lpt_load.numel()
     static = np.array([item_cost[(i * item_cost.size) // W:((i + 1) * item_cost.size) // W].sum()
                        for i in range(W)])
-    lpt = worker_load.cpu().numpy()
+    lpt = lpt_load.cpu().numpy()
     lif = {"workers": int(W), "query_blocks_per_item": int(G), "static_partition": float(static.max() / static.mean()),
            "longest_first_lpt": float(lpt.max() / lpt.mean())}
     # measured per-workgroup busy time of the persistent kernel
@@ -249,6 +263,44 @@ def main():
                  "speedup_sparse_fwd_vs_dense": t_dense / float(t_fwd.mean())}
         del od
 
+    sasa = None
+    if args.sasa:
+        # The same routing without augmentation, for the retained mass and the forward time before SASA.
+        plain = tbs.Route(pr, w.top_p, torch.empty_like(route_out.mask), torch.empty_like(route_out.row_cnt),
+                          torch.empty_like(route_out.row_idx), torch.empty_like(route_out.head_cnt))
+        tbs.route(q, k, w.top_p, w.block, ws=ws, out=plain, causal=causal)
+        wl0 = tbs.schedule(pr, plain.row_cnt, ws, head_window=hw)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        tbs.route(q, k, w.top_p, w.block, ws=ws, out=route_out, causal=causal)
+        ev[0].record()
+        tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True, work_list=work_list,
+                     worker_of=worker_of, worker_load=worker_load)
+        ev[1].record()
+        tbs.augment(pr, route_out, worker_of, worker_load, ws, added=added)
+        ev[2].record()
+        tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
+        ev[3].record()
+        for _ in range(3):
+            tbs.sparse_fwd(q, k, v, plain.row_cnt, plain.row_idx, w.block, work_list=wl0, ws=ws, o=o, lse=lse,
+                           causal=causal)
+        ev[4].record()
+        torch.cuda.synchronize()
+        prob = route_out.block_prob.cpu().numpy()
+        m0 = plain.mask.cpu().numpy()
+        m1 = route_out.mask.cpu().numpy()
+        mass0 = (prob * m0).sum(-1)
+        mass1 = (prob * m1).sum(-1)
+        load = worker_load.cpu().numpy()
+        sasa = {"workers": int(n_workers), "lpt_makespan": int(load.max()), "lpt_lif": float(load.max() / load.mean()),
+                "slack_total": int((load.max() - load).sum()), "blocks_added": int(m1.sum() - m0.sum()),
+                "blocks_before": int(m0.sum()), "mean_retained_mass_before": float(mass0.mean()),
+                "mean_retained_mass_after": float(mass1.mean()), "min_retained_mass_before": float(mass0.min()),
+                "min_retained_mass_after": float(mass1.min()),
+                "lpt_ms": ev[0].elapsed_time(ev[1]), "augment_ms": ev[1].elapsed_time(ev[2]),
+                "reschedule_ms": ev[2].elapsed_time(ev[3]), "sparse_fwd_ms_before": ev[3].elapsed_time(ev[4]) / 3,
+                "sparse_fwd_ms_after": float(t_fwd.mean())}
+        del plain
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed, causal)
@@ -267,7 +319,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d, "block": w.block,
-                   "top_p": w.top_p, "causal": causal, "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
+                   "top_p": w.top_p, "causal": causal, "sasa": bool(args.sasa), "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
                    "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
         "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
                          "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),
@@ -280,6 +332,7 @@ def main():
         "dense_same_shape": dense,
         "load_imbalance": lif,
         "cpu_baseline": cpu,
+        "sasa": sasa,
         "input_generation_s": gen_s,
     }
     print(json.dumps(out))

@@ -65,7 +65,7 @@ def test_workspace_sizes():
     assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_DENSE_FWD) == 256 + 16 * 4096
     U = 40 * nb
     up = lambda x: (x + 255) // 256 * 256
-    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_AUGMENT) == 256 + up(4 * 4097) + 2 * up(4 * U) + up(64 * U)
+    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_AUGMENT) == 256 + up(4 * 4097) + 2 * up(4 * U) + up(208 * U)
     assert L.attn_workspace_bytes(ctypes.byref(p), 9) == 0
     assert L.attn_workspace_bytes(None, 0) == 0
 

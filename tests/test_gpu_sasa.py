@@ -74,7 +74,7 @@ AUG = [
     (custom_workload(2, 3, 1500, 128, 128, "bf16", 0.7, wid=521), False, 7),     # G = 2
     (custom_workload(1, 3, 900, 64, 64, "f32", 0.6, wid=522), False, 5),         # G = 1
     (custom_workload(1, 4, 2000, 128, 64, "bf16", 0.8, wid=523), True, 16),      # causal
-    (custom_workload(1, 12, 16384, 64, 64, "bf16", 0.5, wid=524), False, 2),     # > 1024 rows per worker
+    (custom_workload(1, 12, 16384, 64, 64, "bf16", 0.5, wid=524), False, 5),     # > 512 rows per worker
 ]
 
 

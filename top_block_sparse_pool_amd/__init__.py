@@ -215,20 +215,25 @@ def route(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: Opt
 
 
 def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, head_window: int = DEFAULT_HEAD_WINDOW,
-             num_workers: int = 0, lpt: bool = False, work_list: Optional[torch.Tensor] = None):
+             num_workers: int = 0, lpt: bool = False, work_list: Optional[torch.Tensor] = None,
+             worker_of: Optional[torch.Tensor] = None, worker_load: Optional[torch.Tensor] = None):
     """attn_schedule: longest-first work list inside windows of `head_window`
     heads (0: one window); with lpt=True also the greedy LPT assignment
-    (worker_of, worker_load) used to report load balance."""
+    (worker_of, worker_load), for load-balance reports and augment()."""
     _require_device(row_cnt, ws)
     dev = row_cnt.device
     n_items = problem.items
     if work_list is None:
         work_list = torch.empty(n_items, dtype=torch.int32, device=dev)
-    worker_of = worker_load = None
     if lpt:
         W = num_workers or torch.cuda.get_device_properties(dev).multi_processor_count
-        worker_of = torch.empty(n_items, dtype=torch.int32, device=dev)
-        worker_load = torch.empty(W, dtype=torch.int64, device=dev)
+        if worker_of is None:
+            worker_of = torch.empty(n_items, dtype=torch.int32, device=dev)
+        if worker_load is None:
+            worker_load = torch.empty(W, dtype=torch.int64, device=dev)
+        num_workers = worker_load.numel()
+    else:
+        worker_of = worker_load = None
     _check(lib().attn_schedule(ctypes.byref(problem), _ptr(row_cnt), int(head_window), int(num_workers),
                                _ptr(work_list),
                                _ptr(worker_of), _ptr(worker_load), _ptr(ws), ws.numel(), _stream()))

@@ -17,10 +17,11 @@
 //   aug_csr_kernel     one workgroup: the query-block rows of every worker as
 //                      one array segmented by worker (counts, scan, fill).
 //   aug_merge_kernel   one wave per worker: a merge of its rows' ranked tails
-//                      by (P desc, unit asc); every row keeps its next few
+//                      by (P desc, unit asc); every row keeps its next 16
 //                      candidates cached (LDS, or workspace memory for a
-//                      worker with very many rows), so a pick costs an LDS
-//                      scan of the winning lane's rows and one wave argmax.
+//                      worker with more than 512 rows), so a pick costs a
+//                      scan of the winning lane's rows and one wave argmax,
+//                      and a row's cache is refilled every 16 picks.
 //   aug_rebuild_kernel one wave per row that gained blocks: the ascending
 //                      list of the new selection, mask bits, counts.
 #include "device_common.h"
@@ -30,15 +31,15 @@ namespace tbs {
 namespace {
 
 constexpr int kCsrThreads = 1024;
-constexpr int kAugCache = 4;         // cached candidates per row
-constexpr int kAugLdsRows = 1024;    // rows per worker whose state fits LDS
+constexpr int kAugCache = 16;        // cached candidates per row
+constexpr int kAugLdsRows = 512;     // rows per worker whose state fits LDS (104 KB)
 
 struct AugRow {
   int u;       // unit id (b*H + h)*nb + i
   int k;       // selected blocks before augmentation
   int rem;     // eligible unselected blocks (length of the ranked tail)
   int a;       // blocks added so far
-  double cp[kAugCache];   // P of ranked-tail entries a - a % kAugCache ... (a ring refilled kAugCache at a time)
+  double cp[kAugCache];   // P and index of ranked-tail entries a - a % kAugCache .. + kAugCache - 1
   int cj[kAugCache];
 };
 
@@ -98,14 +99,19 @@ __global__ __launch_bounds__(kCsrThreads) void aug_csr_kernel(const int32_t* __r
 __device__ __forceinline__ void aug_refill(AugRow* st, const int32_t* __restrict__ row_idx,
                                            const double* __restrict__ block_prob, int nb) {
   const long long rb = static_cast<long long>(st->u) * nb;
+  const int a = st->a, k = st->k, rem = st->rem;
+  // All index loads, then all probability loads, then the stores: the state
+  // may live in global memory, so stores between loads would serialise them.
+  int jv[kAugCache];
+#pragma unroll
+  for (int c = 0; c < kAugCache; ++c) jv[c] = a + c < rem ? min(max(row_idx[rb + k + a + c], 0), nb - 1) : 0;
+  double pv[kAugCache];
+#pragma unroll
+  for (int c = 0; c < kAugCache; ++c) pv[c] = a + c < rem ? block_prob[rb + jv[c]] : 0.0;
 #pragma unroll
   for (int c = 0; c < kAugCache; ++c) {
-    const int t = st->a + c;
-    if (t < st->rem) {
-      const int j = min(max(row_idx[rb + st->k + t], 0), nb - 1);
-      st->cj[c] = j;
-      st->cp[c] = block_prob[rb + j];
-    }
+    st->cj[c] = jv[c];
+    st->cp[c] = pv[c];
   }
 }
 
