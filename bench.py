@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense same-shape comparison")
     ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--cold-reps", type=int, default=5,
+                    help="steps timed with a 512 MB buffer written before each (0: skip the cold measurement)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -246,6 +248,25 @@ def main():
     lif["measured_workgroups"] = int(nw)
     lif["measured_busy_max_over_mean"] = float(busy.max() / busy.mean())
 
+    # Cold caches: a 512 MB buffer is written before every step (outside the
+    # timed events), evicting L2 and the MALL, so Q, K and V come from HBM.
+    cold = None
+    if args.cold_reps > 0:
+        evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold_reps)]
+        for rep_ in range(args.cold_reps):
+            evict.fill_(rep_ & 0xff)
+            step(ce[rep_])
+        torch.cuda.synchronize()
+        c_route = np.array([e[0].elapsed_time(e[1]) for e in ce])
+        c_fwd = np.array([e[2].elapsed_time(e[3]) for e in ce])
+        c_step = np.array([e[0].elapsed_time(e[3]) for e in ce])
+        cold = {"reps": args.cold_reps, "evict_bytes": 512 << 20, "step_ms_mean": float(c_step.mean()),
+                "route_ms_mean": float(c_route.mean()), "sparse_fwd_ms_mean": float(c_fwd.mean()),
+                "sparse_fwd_tflops": flops / (c_fwd.mean() * 1e-3) / 1e12,
+                "step_tflops": flops / (c_step.mean() * 1e-3) / 1e12}
+        del evict
+
     dense = None
     if not args.no_dense:
         od = torch.empty_like(q)
@@ -330,6 +351,7 @@ def main():
                      "frac": fwd_tflops / BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic(w.name + ("-causal" if causal else ""))},
         "dense_same_shape": dense,
+        "cold_cache": cold,
         "load_imbalance": lif,
         "cpu_baseline": cpu,
         "sasa": sasa,
