@@ -36,7 +36,7 @@ function is pinned by the CPU tests against brute force, closed forms,
 library special cases or invariants.
 """
 from .routing import (block_sizes, num_blocks, pool_blocks, block_scores, softmax_rows,
-                      top_p_select, causal_cut, route, ambiguous_blocks, RouteResult)
+                      top_p_select, causal_eligible, causal_cut, route, ambiguous_blocks, RouteResult)
 from .attention import attend, attend_units, attend_dense_masked_logits
 from .schedule import group_costs, work_list, lpt_assign, static_partition_loads, load_imbalance
 from .flops import executed_flops, dense_flops
@@ -44,7 +44,7 @@ from .sasa import Augmented, augment, retained_mass
 
 __all__ = [
     "block_sizes", "num_blocks", "pool_blocks", "block_scores", "softmax_rows",
-    "top_p_select", "causal_cut", "route", "ambiguous_blocks", "RouteResult",
+    "top_p_select", "causal_eligible", "causal_cut", "route", "ambiguous_blocks", "RouteResult",
     "attend", "attend_units", "attend_dense_masked_logits",
     "group_costs", "work_list", "lpt_assign", "static_partition_loads", "load_imbalance",
     "executed_flops", "dense_flops",

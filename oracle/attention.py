@@ -44,38 +44,42 @@ def _attend_rows(q_rows, q_pos, k_h, v_h, keys, scale, causal):
 
 
 def attend_units(q, k, v, block: int, units, mask=None, scale: float | None = None,
-                 causal: bool = False):
+                 causal: bool = False, key_block: int | None = None):
     """Attention output of selected query blocks.
 
-    q, k, v: [B, H, N, d]; units: iterable of (b, h, i); mask: [B, H, nb, nb]
-    block mask (None means every key block).  Returns {(b, h, i): (O, LSE)}
-    with O of shape [n_i, d] and LSE of shape [n_i], both float64.
+    q, k, v: [B, H, N, d]; units: iterable of (b, h, i) with i a query block of
+    `block` tokens; mask: [B, H, nbq, nbk] block mask over key blocks of
+    `key_block` tokens (default: block; None means every key block).  Returns
+    {(b, h, i): (O, LSE)} with O of shape [n_i, d] and LSE of shape [n_i],
+    both float64.
     """
+    kb = block if key_block is None else key_block
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, d = q.shape
-    nb = num_blocks(N, block)
+    nbk = num_blocks(N, kb)
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     out = {}
     for (b, h, i) in units:
         lo, hi = i * block, min(N, (i + 1) * block)
-        row = np.ones(nb, dtype=np.uint8) if mask is None else mask[b, h, i]
-        keys = _allowed_keys(row, N, block)
+        row = np.ones(nbk, dtype=np.uint8) if mask is None else mask[b, h, i]
+        keys = _allowed_keys(row, N, kb)
         q_pos = np.arange(lo, hi)
         out[(b, h, i)] = _attend_rows(q[b, h, lo:hi], q_pos, k[b, h], v[b, h], keys,
                                       scale, causal)
     return out
 
 
-def attend(q, k, v, block: int, mask=None, scale: float | None = None, causal: bool = False):
+def attend(q, k, v, block: int, mask=None, scale: float | None = None, causal: bool = False,
+           key_block: int | None = None):
     """Full output O [B, H, N, d] and LSE [B, H, N] (float64)."""
     q64 = np.asarray(q, dtype=np.float64)
     B, H, N, d = q64.shape
     nb = num_blocks(N, block)
     units = [(b, h, i) for b in range(B) for h in range(H) for i in range(nb)]
-    res = attend_units(q64, k, v, block, units, mask=mask, scale=scale, causal=causal)
+    res = attend_units(q64, k, v, block, units, mask=mask, scale=scale, causal=causal, key_block=key_block)
     o = np.empty((B, H, N, d), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     for (b, h, i), (ob, lb) in res.items():
@@ -86,7 +90,7 @@ def attend(q, k, v, block: int, mask=None, scale: float | None = None, causal: b
 
 
 def attend_dense_masked_logits(q, k, v, block: int, mask=None, scale: float | None = None,
-                               causal: bool = False):
+                               causal: bool = False, key_block: int | None = None):
     """Same result as `attend`, written as one full logit matrix per head with
     -inf at disallowed (query, key) pairs.  A second formulation used to pin
     the gather form above; O(N^2) memory, small inputs only."""
@@ -97,6 +101,7 @@ def attend_dense_masked_logits(q, k, v, block: int, mask=None, scale: float | No
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     tok_blk = np.arange(N) // block
+    key_blk = np.arange(N) // (block if key_block is None else key_block)
     o = np.empty_like(q)
     lse = np.empty((B, H, N))
     for b in range(B):
@@ -104,7 +109,7 @@ def attend_dense_masked_logits(q, k, v, block: int, mask=None, scale: float | No
             logits = scale * (q[b, h] @ k[b, h].T)
             allowed = np.ones((N, N), dtype=bool)
             if mask is not None:
-                allowed &= mask[b, h][tok_blk[:, None], tok_blk[None, :]].astype(bool)
+                allowed &= mask[b, h][tok_blk[:, None], key_blk[None, :]].astype(bool)
             if causal:
                 allowed &= np.arange(N)[None, :] <= np.arange(N)[:, None]
             logits = np.where(allowed, logits, -np.inf)

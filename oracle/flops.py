@@ -13,17 +13,26 @@ import numpy as np
 from .routing import block_sizes
 
 
-def executed_flops(mask, n_tokens: int, block: int, head_dim: int, causal: bool = False) -> int:
+def executed_flops(mask, n_tokens: int, block: int, head_dim: int, causal: bool = False,
+                   key_block: int | None = None) -> int:
     """4 * d * sum over selected pairs of the allowed (query, key) pairs (exact integer).
 
-    A pair of blocks allows n_i * n_j token pairs; with `causal`, a diagonal
-    pair allows n_i (n_i + 1) / 2 and a pair above the diagonal none.
+    A pair of query block i and key block j allows n_i * m_j token pairs; with
+    `causal`, only the pairs with key position s <= query position t count.
     """
     mask = np.asarray(mask)
+    kb = block if key_block is None else key_block
     n = block_sizes(n_tokens, block).astype(np.int64)
-    pair = np.outer(n, n)                     # [nb, nb]
-    if causal:
-        pair = np.tril(pair, -1) + np.diag(n * (n + 1) // 2)
+    m = block_sizes(n_tokens, kb).astype(np.int64)
+    if not causal:
+        pair = np.outer(n, m)                 # [nbq, nbk]
+    else:
+        # sum over t in query block i of #{s in key block j : s <= t}
+        pair = np.zeros((n.size, m.size), dtype=np.int64)
+        for i in range(n.size):
+            t = np.arange(i * block, i * block + n[i], dtype=np.int64)
+            for j in range(m.size):
+                pair[i, j] = np.clip(t - j * kb + 1, 0, m[j]).sum()
     per_row = (mask.astype(np.int64) * pair).sum()
     return int(4 * head_dim * per_row)
 

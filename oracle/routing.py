@@ -25,6 +25,14 @@ before the softmax (Z_ij = -inf, so P_ij = 0 and the softmax runs over the
 i+1 blocks j <= i), and "all blocks" in step 6 means those i+1 blocks.  The
 attention of a causal model additionally keeps only keys s <= t for query t
 (attention.attend with causal=True).
+
+Query and key blocks may differ in size (block for queries, key_block for
+keys): Qbar pools query blocks of `block` tokens, Kbar key blocks of
+`key_block` tokens, and Z, P, the ranking and the selection run over the
+nbk = ceil(N / key_block) key blocks of every query block.  Under causal
+routing key block j is eligible for query block i when it starts at or
+before the last token of query block i (j * key_block <= (i+1) * block - 1);
+with equal sizes that is j <= i.
 """
 from __future__ import annotations
 
@@ -60,7 +68,7 @@ def pool_blocks(x: np.ndarray, block: int) -> np.ndarray:
 
 
 def block_scores(qbar: np.ndarray, kbar: np.ndarray, scale: float) -> np.ndarray:
-    """Z = scale * Qbar Kbar^T per (b, h): [B, H, nb, nb]."""
+    """Z = scale * Qbar Kbar^T per (b, h): [B, H, nbq, nbk]."""
     return scale * np.matmul(qbar, np.swapaxes(kbar, -1, -2))
 
 
@@ -97,10 +105,19 @@ def top_p_select(prob: np.ndarray, top_p: float, valid=None):
     return order, cum, row_cnt
 
 
-def causal_cut(scores: np.ndarray) -> np.ndarray:
-    """Block-level causal cut: Z_ij = -inf for key blocks after the query block (j > i)."""
-    nb = scores.shape[-1]
-    future = np.arange(nb)[None, :] > np.arange(scores.shape[-2])[:, None]
+def causal_eligible(nbq: int, nbk: int, block: int, key_block: int) -> np.ndarray:
+    """Eligible key blocks per query block under causal routing: key block j
+    is eligible for query block i iff j * key_block <= (i+1) * block - 1."""
+    last = (np.arange(nbq, dtype=np.int64) + 1) * block - 1
+    return np.minimum(nbk, last // key_block + 1)
+
+
+def causal_cut(scores: np.ndarray, valid=None) -> np.ndarray:
+    """Block-level causal cut: Z_ij = -inf for key blocks after the query
+    block, j >= valid_i (valid_i = i + 1 when not given: equal block sizes)."""
+    nbq, nbk = scores.shape[-2], scores.shape[-1]
+    v = np.arange(1, nbq + 1) if valid is None else np.asarray(valid)
+    future = np.arange(nbk)[None, :] >= v[:, None]
     return np.where(future, -np.inf, scores)
 
 
@@ -121,21 +138,25 @@ class RouteResult:
 
 
 def route(q: np.ndarray, k: np.ndarray, block: int, top_p: float, scale: float | None = None,
-          causal: bool = False) -> RouteResult:
+          causal: bool = False, key_block: int | None = None) -> RouteResult:
     """Full top-p routing of one batch. q, k: [B, H, N, d] (any float dtype, upcast to fp64).
-    With `causal`, row i only considers key blocks j <= i (module docstring)."""
+    With `causal`, row i only considers the eligible key blocks (module docstring);
+    key_block (default: block) is the key block size."""
+    kb = block if key_block is None else key_block
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     d = q.shape[-1]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     qbar = pool_blocks(q, block)
-    kbar = pool_blocks(k, block)
+    kbar = pool_blocks(k, kb)
     scores = block_scores(qbar, kbar, scale)
-    nb = scores.shape[-1]
+    nbq, nb = scores.shape[-2], scores.shape[-1]
     if causal:
-        scores = causal_cut(scores)
-        valid = np.broadcast_to(np.arange(1, nb + 1, dtype=np.int64), scores.shape[:-1]).copy()
+        elig = causal_eligible(nbq, nb, block, kb) if kb != block else None
+        scores = causal_cut(scores, elig)
+        per_row = np.arange(1, nbq + 1, dtype=np.int64) if elig is None else elig
+        valid = np.broadcast_to(per_row, scores.shape[:-1]).copy()
     else:
         valid = np.full(scores.shape[:-1], nb, dtype=np.int64)
     prob = softmax_rows(scores)
@@ -148,7 +169,7 @@ def route(q: np.ndarray, k: np.ndarray, block: int, top_p: float, scale: float |
     B, H = prob.shape[:2]
     for b in range(B):
         for h in range(H):
-            for i in range(nb):
+            for i in range(nbq):
                 sel = np.nonzero(mask[b, h, i])[0]
                 row_idx[b, h, i, : sel.size] = sel
     head_cnt = row_cnt.sum(axis=-1)

@@ -49,7 +49,7 @@ class Augmented:
 def augment(prob, mask, row_cnt, valid, group: int, window_items: int, num_workers: int) -> Augmented:
     """Slack-aware augmentation of a routed selection.
 
-    prob [B,H,nb,nb] fp64 block probabilities, mask [B,H,nb,nb] the top-p
+    prob [B,H,nb,nbk] fp64 block probabilities, mask [B,H,nb,nbk] the top-p
     selection, row_cnt [B,H,nb] its counts, valid [B,H,nb] (or None) the
     eligible blocks per row; group = query blocks per work item; window_items
     = items per scheduling window (0: one window); num_workers = W.
@@ -57,8 +57,9 @@ def augment(prob, mask, row_cnt, valid, group: int, window_items: int, num_worke
     prob = np.asarray(prob, dtype=np.float64)
     mask = np.asarray(mask).astype(np.uint8)
     rc = np.asarray(row_cnt, dtype=np.int64)
-    B, H, nb = rc.shape
-    valid = np.full((B, H, nb), nb, dtype=np.int64) if valid is None else np.asarray(valid, dtype=np.int64)
+    B, H, nb = rc.shape                       # nb query blocks per head
+    nbk = mask.shape[-1]                      # key blocks per row
+    valid = np.full((B, H, nb), nbk, dtype=np.int64) if valid is None else np.asarray(valid, dtype=np.int64)
     ng = -(-nb // group)
 
     costs = group_costs(rc, group)
@@ -68,7 +69,7 @@ def augment(prob, mask, row_cnt, valid, group: int, window_items: int, num_worke
     slack = makespan - load
 
     # Every eligible unselected (unit, key block) pair with its worker and value.
-    eligible = np.arange(nb)[None, None, None, :] < valid[..., None]
+    eligible = np.arange(nbk)[None, None, None, :] < valid[..., None]
     cand = eligible & (mask == 0)
     b_, h_, i_, j_ = np.nonzero(cand)
     unit = (b_ * H + h_) * nb + i_
@@ -85,7 +86,7 @@ def augment(prob, mask, row_cnt, valid, group: int, window_items: int, num_worke
     new_mask = mask.copy()
     new_mask[b_[take], h_[take], i_[take], j_[take]] = 1
     new_cnt = new_mask.astype(np.int64).sum(-1)
-    row_idx = np.full((B, H, nb, nb), -1, dtype=np.int32)
+    row_idx = np.full((B, H, nb, nbk), -1, dtype=np.int32)
     for b in range(B):
         for h in range(H):
             for i in range(nb):

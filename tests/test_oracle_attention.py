@@ -144,3 +144,18 @@ def test_weights_sum_to_one_via_lse():
     for t in range(N):
         w = np.exp(logits[t, : t + 1] - lse[0, 0, t])
         assert abs(w.sum() - 1.0) < 1e-13 and (w >= 0).all()
+
+
+
+@pytest.mark.parametrize("bq,bk", [(16, 32), (32, 16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mixed_blocks_gather_equals_masked_logits(bq, bk, causal):
+    rng = np.random.default_rng(40 + bq)
+    q, k, v = (rng.standard_normal((1, 2, 90, 8)) for _ in range(3))
+    nbq, nbk = -(-90 // bq), -(-90 // bk)
+    mask = (rng.random((1, 2, nbq, nbk)) < 0.6).astype(np.uint8)
+    mask[..., 0] = 1                               # every query keeps at least key block 0
+    o1, l1 = oracle.attend(q, k, v, bq, mask=mask, causal=causal, key_block=bk)
+    o2, l2 = oracle.attend_dense_masked_logits(q, k, v, bq, mask=mask, causal=causal, key_block=bk)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)

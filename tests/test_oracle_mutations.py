@@ -121,13 +121,13 @@ def test_wrong_log_base_caught(monkeypatch):
 
 
 def test_missing_causal_cut_caught(monkeypatch):
-    _patch(monkeypatch, rt, "causal_cut", lambda z: z)
+    _patch(monkeypatch, rt, "causal_cut", lambda z, valid=None: z)
     with pytest.raises(AssertionError):
         tr.test_causal_route_never_looks_ahead(0.5)
 
 
 def test_causal_cut_off_by_one_caught(monkeypatch):
-    def late_cut(z):
+    def late_cut(z, valid=None):
         nb = z.shape[-1]
         ahead = np.arange(nb)[None, :] > np.arange(nb)[:, None] + 1
         return np.where(ahead, -np.inf, z)
@@ -144,7 +144,7 @@ def test_causal_cut_after_softmax_caught(monkeypatch):
         prob = orig(z)
         nb = z.shape[-1]
         return np.where(np.arange(nb)[None, :] > np.arange(nb)[:, None], 0.0, prob)
-    _patch(monkeypatch, rt, "causal_cut", lambda z: z)
+    _patch(monkeypatch, rt, "causal_cut", lambda z, valid=None: z)
     _patch(monkeypatch, rt, "softmax_rows", cut_after)
     with pytest.raises(AssertionError):
         tr.test_causal_route_against_brute_force()
@@ -181,3 +181,13 @@ def test_sasa_candidates_from_all_rows_caught(monkeypatch):
     monkeypatch.setattr(sa, "lpt_assign", one_worker_rows)
     with pytest.raises(AssertionError):
         ts.test_hand_example_three_workers_ties()
+
+
+def test_mixed_block_eligibility_off_by_one_caught(monkeypatch):
+    # a key block counted eligible only when it ends (not starts) before the query block's last token
+    def strict(nbq, nbk, block, key_block):
+        last = (np.arange(nbq, dtype=np.int64) + 1) * block - 1
+        return np.maximum(1, np.minimum(nbk, (last + 1) // key_block))
+    _patch(monkeypatch, rt, "causal_eligible", strict)
+    with pytest.raises(AssertionError):
+        tr.test_mixed_blocks_causal_route_against_token_brute_force(8, 16)

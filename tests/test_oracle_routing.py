@@ -278,3 +278,62 @@ def test_causal_executed_flops_closed_form():
     full = np.tril(np.ones((nb, nb), dtype=np.uint8))
     assert oracle.executed_flops(full, N, block, d, causal=True) == oracle.dense_flops(1, 1, N, d, causal=True)
     assert oracle.executed_flops(np.ones((nb, nb)), N, block, d) == oracle.dense_flops(1, 1, N, d)
+
+
+
+# ------------------------------------------------- query block != key block ---
+
+@pytest.mark.parametrize("bq,bk", [(16, 8), (8, 16), (16, 16)])
+def test_mixed_blocks_route_against_brute_force(bq, bk):
+    rng = np.random.default_rng(20 + bq + bk)
+    B, H, N, d = 1, 2, 70, 6                      # ragged tails for every block size
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d)) + q * 0.4
+    nbq, nbk = oracle.num_blocks(N, bq), oracle.num_blocks(N, bk)
+    for p in (0.5, 0.9):
+        r = oracle.route(q, k, bq, p, key_block=bk)
+        assert r.mask.shape == (B, H, nbq, nbk)
+        for h in range(H):
+            qb = [np.mean(q[0, h, i * bq:min(N, (i + 1) * bq)], axis=0) for i in range(nbq)]
+            kb = [np.mean(k[0, h, j * bk:min(N, (j + 1) * bk)], axis=0) for j in range(nbk)]
+            for i in range(nbq):
+                z = np.array([sum(qb[i][c] * kb[j][c] for c in range(d)) for j in range(nbk)]) / math.sqrt(d)
+                want = _brute_force_topp(scipy.special.softmax(z), p)
+                assert set(np.nonzero(r.mask[0, h, i])[0].tolist()) == want
+                assert r.row_idx[0, h, i, :len(want)].tolist() == sorted(want)
+
+
+@pytest.mark.parametrize("bq,bk", [(16, 8), (8, 16), (16, 32)])
+def test_mixed_blocks_causal_route_against_token_brute_force(bq, bk):
+    # Key block j is eligible for query block i iff some key of j is at or
+    # before some query of i, checked over token positions.
+    rng = np.random.default_rng(30 + bq + bk)
+    B, H, N, d = 1, 2, 75, 5
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    nbq, nbk = oracle.num_blocks(N, bq), oracle.num_blocks(N, bk)
+    elig = np.array([[any(s <= t for t in range(i * bq, min(N, (i + 1) * bq))
+                          for s in range(j * bk, min(N, (j + 1) * bk))) for j in range(nbk)] for i in range(nbq)])
+    for p in (0.6, 1.0):
+        r = oracle.route(q, k, bq, p, causal=True, key_block=bk)
+        assert (r.valid[0, 0] == elig.sum(1)).all()
+        assert not (r.mask[0] & ~elig[None]).any()
+        for h in range(H):
+            qb = [np.mean(q[0, h, i * bq:min(N, (i + 1) * bq)], axis=0) for i in range(nbq)]
+            kb = [np.mean(k[0, h, j * bk:min(N, (j + 1) * bk)], axis=0) for j in range(nbk)]
+            for i in range(nbq):
+                js = np.nonzero(elig[i])[0]
+                z = np.array([sum(qb[i][c] * kb[j][c] for c in range(d)) for j in js]) / math.sqrt(d)
+                want = {int(js[x]) for x in _brute_force_topp(scipy.special.softmax(z), p)}
+                assert set(np.nonzero(r.mask[0, h, i])[0].tolist()) == want, (p, h, i)
+
+
+@pytest.mark.parametrize("bq,bk", [(16, 8), (8, 16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mixed_blocks_flops_against_token_pairs(bq, bk, causal):
+    N, d = 45, 4
+    nbq, nbk = oracle.num_blocks(N, bq), oracle.num_blocks(N, bk)
+    mask = (np.random.default_rng(bq * bk).random((nbq, nbk)) < 0.5).astype(np.uint8)
+    pairs = sum(1 for t in range(N) for s in range(N)
+                if mask[t // bq, s // bk] and (not causal or s <= t))
+    assert oracle.executed_flops(mask, N, bq, d, causal, key_block=bk) == 4 * d * pairs
