@@ -16,8 +16,9 @@
  *                    causal): dense attention is the p = 1 case.
  *
  * With causal == 1 (decoder models) every call keeps to the causal order:
- * routing considers only key blocks j <= i for query block i, and the
- * attention calls keep only keys s <= t for query token t.
+ * routing considers only the key blocks that start at or before the last
+ * token of query block i (j <= i when key_block == block), and the attention
+ * calls keep only keys s <= t for query token t.
  *
  * Sources.  Top-p routing: FVAttn review page, section 1 (Key Terms, "Top-p
  * routing") and section 3 (Method): per query block, key blocks are taken by
@@ -35,10 +36,13 @@
  *   The caller owns every buffer; the library allocates no memory and keeps
  *   no state between calls other than cached device properties.
  * - Tensors are contiguous, row-major.  q, k, v, o: [B, H, N, d], element
- *   type `dtype` (bf16 or fp32), 16-byte aligned.  Block i of a sequence
- *   covers tokens [i*block, min((i+1)*block, N)); nb = ceil(N / block); the
- *   last block may hold fewer than `block` tokens.  Unit u = (b*H + h)*nb + i
- *   names query block i of head h of batch b; U = B*H*nb units.
+ *   type `dtype` (bf16 or fp32), 16-byte aligned.  Query block i of a
+ *   sequence covers tokens [i*block, min((i+1)*block, N)); nb = ceil(N /
+ *   block); the last block may hold fewer than `block` tokens.  Key blocks
+ *   are the same with key_block (default: block): nbk = ceil(N / key_block).
+ *   Unit u = (b*H + h)*nb + i names query block i of head h of batch b;
+ *   U = B*H*nb units.  Per-row outputs (mask, row_idx, block_prob) have nbk
+ *   entries per unit.
  * - All work is enqueued on `stream` (a hipStream_t; NULL is the default
  *   stream) and the calls return before it completes.  No call synchronises
  *   with the host; route -> schedule -> sparse_fwd on one stream need no
@@ -64,7 +68,7 @@
 extern "C" {
 #endif
 
-#define ATTN_TBS_ABI_VERSION 2
+#define ATTN_TBS_ABI_VERSION 3
 
 /* Status codes. */
 #define ATTN_OK            0
@@ -93,11 +97,13 @@ typedef struct attn_problem {
   int32_t heads;     /* H >= 1 */
   int32_t seq_len;   /* N >= 1 */
   int32_t head_dim;  /* d: 64 or 128 */
-  int32_t block;     /* block size for routing and for query/key tiles: 64 or 128 */
+  int32_t block;     /* query block size (routing rows, query tiles): 64 or 128 */
   int32_t dtype;     /* ATTN_DTYPE_BF16 or ATTN_DTYPE_F32 */
   int32_t causal;    /* 0 or 1: causal routing and causal attention (keys s <= t) */
   int32_t flags;     /* ATTN_FLAG_* bits, 0 for none */
   double scale;      /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  int32_t key_block; /* key block size (routing columns, selection unit): 64 or 128; 0 selects block */
+  int32_t reserved;  /* must be 0 */
 } attn_problem;
 
 /* ABI version of the loaded library (ATTN_TBS_ABI_VERSION when it was built). */
@@ -136,36 +142,40 @@ int32_t attn_num_workers(const attn_problem* problem, int32_t op);
 
 /* Top-p block routing.
  *
- * Per (b, h): Qbar_i = mean of q over the valid tokens of block i, Kbar_j
- * likewise; Z_ij = scale * <Qbar_i, Kbar_j>; P_i. = softmax_j(Z_i.).  Key
- * blocks are ranked by P descending, equal P by smaller index; row i keeps
- * the shortest ranked prefix whose cumulative probability is >= top_p
- * (all nb blocks when top_p >= 1).  Pooling, scores, softmax and the cut are
+ * Per (b, h): Qbar_i = mean of q over the valid tokens of query block i,
+ * Kbar_j = mean of k over the valid tokens of key block j (key_block tokens);
+ * Z_ij = scale * <Qbar_i, Kbar_j>; P_i. = softmax_j(Z_i.) over the nbk key
+ * blocks.  Key blocks are ranked by P descending, equal P by smaller index;
+ * row i keeps the shortest ranked prefix whose cumulative probability is
+ * >= top_p (all nbk blocks when top_p >= 1).  Pooling, scores, softmax and the cut are
  * evaluated in fp64, so the decisions are those of exact arithmetic up to
  * fp64 rounding.
  *
- * Causal routing (causal == 1): row i only considers the key blocks j <= i.
- * The others are cut before the softmax (Z_ij = -inf, P_ij = 0), so P_i. is a
- * softmax over the i+1 eligible scores, the ranking and the cut run over
- * those blocks only, and top_p >= 1 selects all i+1 of them.  The routing
+ * Causal routing (causal == 1): row i only considers the eligible key
+ * blocks, those with j * key_block <= (i+1) * block - 1 (the blocks j <= i
+ * when key_block == block); there are e_i = min(nbk, ((i+1)*block - 1) /
+ * key_block + 1) of them.  The others are cut before the softmax (Z_ij =
+ * -inf, P_ij = 0), so P_i. is a softmax over the e_i eligible scores, the
+ * ranking and the cut run over those blocks only, and top_p >= 1 selects
+ * all of them.  The routing
  * pages state top-p routing for full attention; cutting the future blocks
  * before the softmax is the reading this library takes for decoders.
  *
  *   q, k      [B,H,N,d] dtype, read only.
  *   top_p     in (0, 1].
- *   mask      [B,H,nb,nb] uint8 out: 1 where key block j is selected for row i.
+ *   mask      [B,H,nb,nbk] uint8 out: 1 where key block j is selected for row i.
  *   row_cnt   [B,H,nb] int32 out: k_i, number of selected key blocks (>= 1).
- *   row_idx   [B,H,nb,nb] int32 out: the first row_cnt entries of each row are
+ *   row_idx   [B,H,nb,nbk] int32 out: the first row_cnt entries of each row are
  *             the selected key blocks in ascending order; the next entries,
- *             up to the number of eligible blocks (nb, or i+1 under causal
+ *             up to the number of eligible blocks (nbk, or e_i under causal
  *             routing), are the unselected eligible blocks in rank order
  *             (P descending, equal P by smaller index), which attn_augment
  *             reads; entries after those are not written.
  *   head_cnt  [B,H] int32 out: sum over i of row_cnt (overwritten, not added to).
- *   block_prob [B,H,nb,nb] double out, nullable: the block probabilities P
+ *   block_prob [B,H,nb,nbk] double out, nullable: the block probabilities P
  *             (0 for key blocks cut by causal routing).
  *   ws        workspace of attn_workspace_bytes(problem, ATTN_OP_ROUTE) bytes.
- * Requires nb <= 1024. */
+ * Requires nbk <= 1024. */
 int32_t attn_route(const attn_problem* problem, const void* q, const void* k, double top_p,
                    uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                    double* block_prob, void* ws, size_t ws_bytes, void* stream);
@@ -198,7 +208,7 @@ int32_t attn_route(const attn_problem* problem, const void* q, const void* k, do
  *                serves load-balance reports and attn_augment.
  *   worker_load  [num_workers] int64 out, nullable: summed cost per worker
  *                under that assignment.
- * Requires nb <= 1024 and num_workers <= 4096. */
+ * Requires nbk <= 1024 and num_workers <= 4096. */
 int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32_t head_window,
                       int32_t num_workers, int32_t* work_list, int32_t* worker_of, int64_t* worker_load,
                       void* ws, size_t ws_bytes, void* stream);
@@ -218,7 +228,7 @@ int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32
  * worker's modelled load exceeds M.  Updates the routing outputs in place;
  * call attn_schedule again for a work list over the new counts.
  *
- *   block_prob   [B,H,nb,nb] double, from attn_route (block_prob output).
+ *   block_prob   [B,H,nb,nbk] double, from attn_route (block_prob output).
  *   worker_of    [B*H*ceil(nb/G)] int32, worker_load [num_workers] int64:
  *                from attn_schedule's LPT model with the same num_workers.
  *   num_workers  1 .. 4096.
@@ -229,7 +239,7 @@ int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32
  *   added        [num_workers] int32 out, nullable: blocks added per worker.
  *   ws           attn_workspace_bytes(problem, ATTN_OP_AUGMENT) bytes; the
  *                control block is not touched.
- * Honours causal (eligible blocks j <= i).  Requires nb <= 1024. */
+ * Honours causal (the eligible blocks of routing).  Requires nbk <= 1024. */
 int32_t attn_augment(const attn_problem* problem, const double* block_prob, const int32_t* worker_of,
                      const int64_t* worker_load, int32_t num_workers, uint8_t* mask, int32_t* row_cnt,
                      int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, size_t ws_bytes,
@@ -246,8 +256,9 @@ int32_t attn_augment(const attn_problem* problem, const double* block_prob, cons
  * softmax in fp32; o is written in dtype (bf16 round-to-nearest-even).
  *
  *   q, k, v    [B,H,N,d] dtype.
- *   row_cnt    [U] int32, row_idx [U, nb] int32 as written by attn_route
- *              (indices in [0, nb); the library clamps out-of-range values).
+ *   row_cnt    [U] int32, row_idx [U, nbk] int32 as written by attn_route
+ *              (key-block indices in [0, nbk); the library clamps
+ *              out-of-range values).
  *   work_list  [B*H*ceil(nb/G)] int32, nullable: work-item order (from
  *              attn_schedule); NULL processes items in natural order.
  *   o          [B,H,N,d] dtype out.  A unit whose row_cnt is 0 gets o = 0.
@@ -255,10 +266,10 @@ int32_t attn_augment(const attn_problem* problem, const double* block_prob, cons
  *   ws         attn_workspace_bytes(problem, ATTN_OP_SPARSE_FWD) bytes, control
  *              block zero on entry (see attn_workspace_bytes).
  * With causal == 1, only keys s <= t enter the sums for query token t (the
- * lists come from causal routing, so they hold blocks j <= i; a listed block
- * j > i contributes no keys, and a unit left with no keys gets o = 0 and
- * lse = -inf).
- * Requires nb <= 2048. */
+ * lists come from causal routing, so they hold eligible blocks; a listed
+ * block entirely after the query block contributes no keys, and a unit left
+ * with no keys gets o = 0 and lse = -inf).
+ * Requires nbk <= 2048. */
 int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                         const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
                         void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
@@ -267,7 +278,8 @@ int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* 
  * Same arithmetic, layouts and workspace rules as attn_sparse_fwd; with
  * causal the query blocks with the most keys are processed first.  Equals,
  * bit for bit, attn_sparse_fwd with every block selected (causal == 0) or
- * with every block j <= i selected (causal == 1). */
+ * with every eligible block selected (causal == 1), for any key_block.  The
+ * key block size does not enter the dense result. */
 int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                        void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 

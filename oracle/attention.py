@@ -12,6 +12,9 @@ For each query t with allowed key set A_t and logits l_s = scale * <Q_t, K_s>:
     mu    = max_{s in A_t} l_s
     O_t   = sum_{s in A_t} exp(l_s - mu) V_s / sum_{s in A_t} exp(l_s - mu)
     LSE_t = mu + ln sum_{s in A_t} exp(l_s - mu)          (natural log)
+A query with no allowed key (empty A_t: no selected key block, or, under a
+causal mask, selected key blocks that all start after it) gets O_t = 0 and
+LSE_t = -inf, the values of the empty sums; the pages leave this case open.
 """
 from __future__ import annotations
 
@@ -30,16 +33,20 @@ def _allowed_keys(mask_row, n_tokens: int, block: int) -> np.ndarray:
 
 def _attend_rows(q_rows, q_pos, k_h, v_h, keys, scale, causal):
     """Attention of a few query rows over an explicit key index set."""
+    n = q_rows.shape[0]
+    if keys.size == 0:
+        return np.zeros((n, v_h.shape[1])), np.full(n, -np.inf)
     kk = k_h[keys]
     vv = v_h[keys]
     logits = scale * (q_rows @ kk.T)
     if causal:
         logits = np.where(keys[None, :] <= q_pos[:, None], logits, -np.inf)
-    mu = np.max(logits, axis=1, keepdims=True)
+    has = np.isfinite(logits).any(axis=1)                  # rows with at least one allowed key
+    mu = np.max(np.where(has[:, None], logits, 0.0), axis=1, keepdims=True)
     w = np.exp(logits - mu)
     denom = np.sum(w, axis=1, keepdims=True)
-    out = (w @ vv) / denom
-    lse = mu[:, 0] + np.log(denom[:, 0])
+    out = np.where(has[:, None], (w @ vv) / np.where(has[:, None], denom, 1.0), 0.0)
+    lse = np.where(has, mu[:, 0] + np.log(np.where(has, denom[:, 0], 1.0)), -np.inf)
     return out, lse
 
 
@@ -113,9 +120,10 @@ def attend_dense_masked_logits(q, k, v, block: int, mask=None, scale: float | No
             if causal:
                 allowed &= np.arange(N)[None, :] <= np.arange(N)[:, None]
             logits = np.where(allowed, logits, -np.inf)
-            mu = logits.max(axis=1, keepdims=True)
+            has = allowed.any(axis=1)
+            mu = np.where(has[:, None], logits, 0.0).max(axis=1, keepdims=True)
             w = np.exp(logits - mu)
             den = w.sum(axis=1, keepdims=True)
-            o[b, h] = (w @ v[b, h]) / den
-            lse[b, h] = mu[:, 0] + np.log(den[:, 0])
+            o[b, h] = np.where(has[:, None], (w @ v[b, h]) / np.where(has[:, None], den, 1.0), 0.0)
+            lse[b, h] = np.where(has, mu[:, 0] + np.log(np.where(has, den[:, 0], 1.0)), -np.inf)
     return o, lse

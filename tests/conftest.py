@@ -15,3 +15,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_collection_modifyitems(config, items):
+    # Bring up the GPU runtime once, in the main thread, before the first test
+    # (and its timeout timer thread) starts, when GPU tests were collected.
+    if not any(item.get_closest_marker("gpu") for item in items):
+        return
+    import torch
+    if torch.cuda.is_available():
+        torch.cuda.init()

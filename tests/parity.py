@@ -7,7 +7,8 @@ row count and the ascending index list.
 
 Attention: GPU outputs (bf16 or fp32, upcast exactly) are compared element by
 element with the fp64 oracle on query blocks whose masks agree: max abs error
-<= 2e-2 for bf16 inputs and <= 1e-4 for fp32 inputs.  LSE uses 2e-3 / 1e-4.
+<= 2e-2 for bf16 inputs and <= 1e-4 for fp32 inputs.  LSE uses 2e-3 / 1e-4;
+a query without allowed keys must be -inf on both sides (and O = 0).
 """
 from __future__ import annotations
 
@@ -25,21 +26,23 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def oracle_route_per_head(q: torch.Tensor, k: torch.Tensor, block: int, top_p: float, scale=None, causal=False):
+def oracle_route_per_head(q: torch.Tensor, k: torch.Tensor, block: int, top_p: float, scale=None, causal=False,
+                          key_block=None):
     """Oracle routing head by head (bounded host memory at full sizes).
 
     Returns mask, row_cnt, row_idx, head_cnt and the ambiguity map, [B,H,...].
     """
     B, H, N, d = q.shape
     nb = -(-N // block)
-    mask = np.zeros((B, H, nb, nb), dtype=np.uint8)
-    amb = np.zeros((B, H, nb, nb), dtype=bool)
+    nbk = -(-N // (key_block or block))
+    mask = np.zeros((B, H, nb, nbk), dtype=np.uint8)
+    amb = np.zeros((B, H, nb, nbk), dtype=bool)
     row_cnt = np.zeros((B, H, nb), dtype=np.int64)
-    row_idx = np.full((B, H, nb, nb), -1, dtype=np.int32)
+    row_idx = np.full((B, H, nb, nbk), -1, dtype=np.int32)
     for b in range(B):
         for h in range(H):
             r = oracle.route(to64(q[b:b + 1, h:h + 1]), to64(k[b:b + 1, h:h + 1]), block, top_p, scale,
-                             causal=causal)
+                             causal=causal, key_block=key_block)
             mask[b, h] = r.mask[0, 0]
             row_cnt[b, h] = r.row_cnt[0, 0]
             row_idx[b, h] = r.row_idx[0, 0]
@@ -68,7 +71,7 @@ def compare_route(gpu_route, ref) -> dict:
     return dict(rows_agree=rows_agree, ambiguous_mismatches=int(diff.sum()))
 
 
-def compare_units(o_gpu, lse_gpu, q, k, v, block, units, mask, dtype, scale=None, causal=False):
+def compare_units(o_gpu, lse_gpu, q, k, v, block, units, mask, dtype, scale=None, causal=False, key_block=None):
     """Compare GPU output rows of `units` with the oracle, head by head.
 
     Returns (max_o_err, max_lse_err)."""
@@ -81,14 +84,17 @@ def compare_units(o_gpu, lse_gpu, q, k, v, block, units, mask, dtype, scale=None
         sl = (slice(b, b + 1), slice(h, h + 1))
         m = None if mask is None else mask[b:b + 1, h:h + 1]
         ref = oracle.attend_units(to64(q[sl]), to64(k[sl]), to64(v[sl]), block, [(0, 0, i) for i in blocks],
-                                  mask=m, scale=scale, causal=causal)
+                                  mask=m, scale=scale, causal=causal, key_block=key_block)
         o64 = to64(o_gpu[sl])[0, 0]
         l64 = to64(lse_gpu[sl])[0, 0] if lse_gpu is not None else None
         for (_, _, i), (ro, rl) in ref.items():
             lo, hi = i * block, min(N, (i + 1) * block)
             emax = max(emax, float(np.max(np.abs(o64[lo:hi] - ro))))
             if l64 is not None:
-                lmax = max(lmax, float(np.max(np.abs(l64[lo:hi] - rl))))
+                gl, ol = l64[lo:hi], rl
+                both_empty = np.isneginf(gl) & np.isneginf(ol)          # queries without keys: -inf on both sides
+                d = np.where(both_empty, 0.0, np.abs(np.where(both_empty, 0.0, gl) - np.where(both_empty, 0.0, ol)))
+                lmax = max(lmax, float(np.max(d)))
     assert emax <= O_TOL[dtype], f"max |O - O_ref| = {emax:.3e} > {O_TOL[dtype]}"
     if lse_gpu is not None:
         assert lmax <= LSE_TOL[dtype], f"max |LSE - LSE_ref| = {lmax:.3e} > {LSE_TOL[dtype]}"

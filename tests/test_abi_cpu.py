@@ -32,16 +32,17 @@ def test_exports_every_declared_symbol():
                           "attn_dense_fwd"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 2
+    assert L.attn_abi_version() == 3
 
 
-def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0):
-    return tbs.Problem(B, H, N, d, block, dtype, causal, flags, scale)
+def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0, key_block=0, reserved=0):
+    return tbs.Problem(B, H, N, d, block, dtype, causal, flags, scale, key_block, reserved)
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(tbs.Problem) == 40
+    assert ctypes.sizeof(tbs.Problem) == 48
     assert tbs.Problem.scale.offset == 32
+    assert tbs.Problem.key_block.offset == 40 and tbs.Problem.reserved.offset == 44
 
 
 def test_group_size():
@@ -59,6 +60,8 @@ def test_workspace_sizes():
     p = _problem()
     nb = 512
     assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_ROUTE) == 256 + 2 * 8 * 40 * nb * 128
+    pk = _problem(block=128, key_block=64)
+    assert L.attn_workspace_bytes(ctypes.byref(pk), tbs.OP_ROUTE) == 256 + 8 * 40 * (256 + 512) * 128
     assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_SCHEDULE) == 256
     assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_SPARSE_FWD) == 256
     p.flags = tbs.FLAG_PROFILE_WORKERS
@@ -78,7 +81,8 @@ def _route(p, top_p=0.9, q=FAKE, k=FAKE, ws=WS, ws_bytes=1 << 40, mask=FAKE, rc=
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), 1), (dict(H=-1), 1), (dict(N=0), 1), (dict(d=96), 2), (dict(d=0), 1), (dict(block=32), 2),
     (dict(dtype=7), 1), (dict(causal=2), 1), (dict(flags=8), 1), (dict(scale=-1.0), 1),
-    (dict(scale=math.inf), 1), (dict(N=64 * 1025), 2),
+    (dict(scale=math.inf), 1), (dict(N=64 * 1025), 2), (dict(key_block=96), 2), (dict(key_block=-64), 1),
+    (dict(reserved=1), 1), (dict(block=128, key_block=64, N=64 * 1025), 2),
 ])
 def test_route_rejects_bad_problem(kw, code):
     assert _route(_problem(**kw)) == code

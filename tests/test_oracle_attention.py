@@ -159,3 +159,26 @@ def test_mixed_blocks_gather_equals_masked_logits(bq, bk, causal):
     o2, l2 = oracle.attend_dense_masked_logits(q, k, v, bq, mask=mask, causal=causal, key_block=bk)
     np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
     np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+
+def test_queries_without_allowed_keys_get_zero_and_neg_inf():
+    # Causal attention with query blocks of 32 over key blocks of 16: query
+    # block 1 (tokens 32..63) listing only key block 3 (tokens 48..63) leaves
+    # tokens 32..47 without keys; tokens 48..63 see keys 48..t.
+    rng = np.random.default_rng(50)
+    q, k, v = (rng.standard_normal((1, 1, 64, 4)) for _ in range(3))
+    mask = np.zeros((1, 1, 2, 4), dtype=np.uint8)
+    mask[0, 0, 0, 0] = 1
+    mask[0, 0, 1, 3] = 1
+    o, lse = oracle.attend(q, k, v, 32, mask=mask, causal=True, key_block=16)
+    assert (o[0, 0, 32:48] == 0).all() and np.isneginf(lse[0, 0, 32:48]).all()
+    for t in range(48, 64):
+        keys = np.arange(48, t + 1)
+        lg = (q[0, 0, t] @ k[0, 0, keys].T) / 2.0
+        w = np.exp(lg - lg.max())
+        np.testing.assert_allclose(o[0, 0, t], (w @ v[0, 0, keys]) / w.sum(), rtol=1e-12, atol=1e-13)
+    o2, lse2 = oracle.attend_dense_masked_logits(q, k, v, 32, mask=mask, causal=True, key_block=16)
+    np.testing.assert_array_equal(o2[0, 0, 32:48], 0.0)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+    assert (np.isneginf(lse2) == np.isneginf(lse)).all()

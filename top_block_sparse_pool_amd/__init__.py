@@ -58,11 +58,23 @@ class Problem(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("flags", ctypes.c_int32),
         ("scale", ctypes.c_double),
+        ("key_block", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     @property
     def num_blocks(self) -> int:
+        """Query blocks per sequence, nb."""
         return -(-self.seq_len // self.block)
+
+    @property
+    def kblock(self) -> int:
+        return self.key_block or self.block
+
+    @property
+    def num_key_blocks(self) -> int:
+        """Key blocks per sequence, nbk (entries per row of the routing outputs)."""
+        return -(-self.seq_len // self.kblock)
 
     @property
     def units(self) -> int:
@@ -152,12 +164,12 @@ def _require_device(*ts):
 
 
 def make_problem(q: torch.Tensor, block: int, causal: bool = False, scale: Optional[float] = None,
-                 flags: int = 0) -> Problem:
+                 flags: int = 0, key_block: Optional[int] = None) -> Problem:
     if q.dim() != 4:
         raise ValueError(f"q must be [B, H, N, d], got shape {tuple(q.shape)}")
     B, H, N, d = q.shape
     return Problem(B, H, N, d, block, _dtype_code(q.dtype), int(bool(causal)), flags,
-                   0.0 if scale is None else float(scale))
+                   0.0 if scale is None else float(scale), int(key_block or 0), 0)
 
 
 def workspace_bytes(problem: Problem, op: Optional[int] = None) -> int:
@@ -181,30 +193,30 @@ def num_workers(problem: Problem, op: int = OP_SPARSE_FWD) -> int:
 class Route:
     problem: Problem
     top_p: float
-    mask: torch.Tensor       # [B,H,nb,nb] uint8
+    mask: torch.Tensor       # [B,H,nb,nbk] uint8
     row_cnt: torch.Tensor    # [B,H,nb] int32
-    row_idx: torch.Tensor    # [B,H,nb,nb] int32 (prefix of row_cnt entries valid)
+    row_idx: torch.Tensor    # [B,H,nb,nbk] int32 (selected prefix of row_cnt entries, then the ranked tail)
     head_cnt: torch.Tensor   # [B,H] int32
-    block_prob: Optional[torch.Tensor] = None   # [B,H,nb,nb] float64
+    block_prob: Optional[torch.Tensor] = None   # [B,H,nb,nbk] float64
 
 
 def route(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: Optional[float] = None,
           ws: Optional[torch.Tensor] = None, return_prob: bool = False, out: Optional[Route] = None,
-          causal: bool = False) -> Route:
+          causal: bool = False, key_block: Optional[int] = None) -> Route:
     """attn_route: block pooling, scores, softmax and top-p cut (all on the GPU)."""
     _require_device(q, k)
     if k.shape != q.shape or k.dtype != q.dtype:
         raise ValueError("q and k must share shape and dtype")
-    pr = make_problem(q, block, causal=causal, scale=scale)
-    B, H, nb = pr.batch, pr.heads, pr.num_blocks
+    pr = make_problem(q, block, causal=causal, scale=scale, key_block=key_block)
+    B, H, nb, nbk = pr.batch, pr.heads, pr.num_blocks, pr.num_key_blocks
     dev = q.device
     if out is None:
         out = Route(pr, float(top_p),
-                    torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev),
+                    torch.empty((B, H, nb, nbk), dtype=torch.uint8, device=dev),
                     torch.empty((B, H, nb), dtype=torch.int32, device=dev),
-                    torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, nb, nbk), dtype=torch.int32, device=dev),
                     torch.empty((B, H), dtype=torch.int32, device=dev),
-                    torch.empty((B, H, nb, nb), dtype=torch.float64, device=dev) if return_prob else None)
+                    torch.empty((B, H, nb, nbk), dtype=torch.float64, device=dev) if return_prob else None)
     out.problem, out.top_p = pr, float(top_p)
     if ws is None:
         ws = workspace(pr, dev, OP_ROUTE)
@@ -272,10 +284,10 @@ def _out_tensors(q, o, lse, want_lse):
 
 def sparse_fwd(q, k, v, row_cnt, row_idx, block: int, work_list=None, scale: Optional[float] = None,
                ws: Optional[torch.Tensor] = None, o=None, lse=None, want_lse: bool = True, flags: int = 0,
-               causal: bool = False):
+               causal: bool = False, key_block: Optional[int] = None):
     """attn_sparse_fwd: attention of each query block over its selected key blocks."""
     _require_device(q, k, v, row_cnt, row_idx, work_list)
-    pr = make_problem(q, block, causal=causal, scale=scale, flags=flags)
+    pr = make_problem(q, block, causal=causal, scale=scale, flags=flags, key_block=key_block)
     o, lse = _out_tensors(q, o, lse, want_lse)
     if ws is None:
         ws = workspace(pr, q.device, OP_SPARSE_FWD)
@@ -300,22 +312,22 @@ def dense_fwd(q, k, v, block: int, causal: bool = False, scale: Optional[float] 
 def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] = None,
                      ws: Optional[torch.Tensor] = None, want_lse: bool = True,
                      head_window: int = DEFAULT_HEAD_WINDOW, causal: bool = False, sasa: bool = False,
-                     num_workers: int = 0):
+                     num_workers: int = 0, key_block: Optional[int] = None):
     """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list).
 
     With sasa=True: route -> schedule with the LPT model -> augment -> schedule
     again over the augmented counts -> sparse_fwd."""
-    pr = make_problem(q, block, causal=causal, scale=scale)
+    pr = make_problem(q, block, causal=causal, scale=scale, key_block=key_block)
     if ws is None:
         ws = workspace(pr, q.device)
-    r = route(q, k, top_p, block, scale=scale, ws=ws, causal=causal, return_prob=sasa)
+    r = route(q, k, top_p, block, scale=scale, ws=ws, causal=causal, return_prob=sasa, key_block=key_block)
     if sasa:
         _, worker_of, worker_load = schedule(pr, r.row_cnt, ws, head_window=head_window,
                                              num_workers=num_workers, lpt=True)
         augment(pr, r, worker_of, worker_load, ws, want_added=False)
     wl = schedule(pr, r.row_cnt, ws, head_window=head_window)
     o, lse = sparse_fwd(q, k, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
-                        want_lse=want_lse, causal=causal)
+                        want_lse=want_lse, causal=causal, key_block=key_block)
     return o, lse, r, wl
 
 

@@ -62,6 +62,10 @@ int32_t check_problem(const attn_problem* pr, tbs::Shape* s) {
     return fail(ATTN_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", pr->head_dim);
   if (pr->block != 64 && pr->block != 128)
     return fail(ATTN_E_UNSUPPORTED, "block %d unsupported (64 or 128)", pr->block);
+  if (pr->key_block < 0 || pr->reserved != 0)
+    return fail(ATTN_E_INVALID, "key_block must be >= 0 and reserved 0 (got %d, %d)", pr->key_block, pr->reserved);
+  const int kb = pr->key_block ? pr->key_block : pr->block;
+  if (kb != 64 && kb != 128) return fail(ATTN_E_UNSUPPORTED, "key_block %d unsupported (64 or 128)", kb);
   const long long nb = (static_cast<long long>(pr->seq_len) + pr->block - 1) / pr->block;
   const long long units = static_cast<long long>(pr->batch) * pr->heads * nb;
   if (units > 0x3fffffffLL) return fail(ATTN_E_UNSUPPORTED, "batch*heads*blocks = %lld too large", units);
@@ -73,6 +77,8 @@ int32_t check_problem(const attn_problem* pr, tbs::Shape* s) {
   s->d = pr->head_dim;
   s->block = pr->block;
   s->nb = static_cast<int>(nb);
+  s->kb = kb;
+  s->nbk = (pr->seq_len + kb - 1) / kb;
   s->dtype = pr->dtype;
   s->causal = pr->causal;
   s->flags = pr->flags;
@@ -81,7 +87,7 @@ int32_t check_problem(const attn_problem* pr, tbs::Shape* s) {
 }
 
 size_t route_bytes(const tbs::Shape& s) {
-  return tbs::kCtrlBytes + 2 * sizeof(double) * static_cast<size_t>(s.B) * s.H * s.nb * s.d;
+  return tbs::kCtrlBytes + sizeof(double) * static_cast<size_t>(s.B) * s.H * (s.nb + s.nbk) * s.d;
 }
 
 size_t fwd_bytes(const tbs::Shape& s) {
@@ -173,8 +179,8 @@ TBS_EXPORT int32_t attn_route(const attn_problem* problem, const void* q, const 
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
-  if (s.nb > kMaxRouteBlocks)
-    return fail(ATTN_E_UNSUPPORTED, "attn_route: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
+  if (s.nbk > kMaxRouteBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_route: %d key blocks per sequence exceed %d", s.nbk, kMaxRouteBlocks);
   if (!(top_p > 0.0 && top_p <= 1.0)) return fail(ATTN_E_INVALID, "top_p must be in (0, 1] (got %g)", top_p);
   if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k"))) return st;
   if (!mask) return fail(ATTN_E_INVALID, "mask is NULL");
@@ -186,7 +192,7 @@ TBS_EXPORT int32_t attn_route(const attn_problem* problem, const void* q, const 
 
   auto* base = static_cast<unsigned char*>(ws) + tbs::kCtrlBytes;
   auto* qbar = reinterpret_cast<double*>(base);
-  auto* kbar_t = qbar + static_cast<size_t>(s.B) * s.H * s.nb * s.d;
+  auto* kbar_t = qbar + static_cast<size_t>(s.B) * s.H * s.nb * s.d;   // [B,H,d,nbk]
   auto strm = static_cast<hipStream_t>(stream);
   hipError_t e = tbs::launch_pool(s, q, k, qbar, kbar_t, head_cnt, strm);
   if (e != hipSuccess) return device_status(e, "attn_route pool launch");
@@ -200,8 +206,8 @@ TBS_EXPORT int32_t attn_schedule(const attn_problem* problem, const int32_t* row
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
-  if (s.nb > kMaxRouteBlocks)
-    return fail(ATTN_E_UNSUPPORTED, "attn_schedule: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
+  if (s.nbk > kMaxRouteBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_schedule: %d key blocks per sequence exceed %d", s.nbk, kMaxRouteBlocks);
   if (head_window < 0) return fail(ATTN_E_INVALID, "head_window must be >= 0 (got %d)", head_window);
   if (num_workers < 0 || num_workers > kMaxWorkers)
     return fail(ATTN_E_INVALID, "num_workers must be in [0, %d] (got %d)", kMaxWorkers, num_workers);
@@ -229,8 +235,8 @@ TBS_EXPORT int32_t attn_augment(const attn_problem* problem, const double* block
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
-  if (s.nb > kMaxRouteBlocks)
-    return fail(ATTN_E_UNSUPPORTED, "attn_augment: %d blocks per sequence exceed %d", s.nb, kMaxRouteBlocks);
+  if (s.nbk > kMaxRouteBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_augment: %d key blocks per sequence exceed %d", s.nbk, kMaxRouteBlocks);
   if (num_workers < 1 || num_workers > kMaxWorkers)
     return fail(ATTN_E_INVALID, "num_workers must be in [1, %d] (got %d)", kMaxWorkers, num_workers);
   if (!block_prob || !aligned(block_prob, 8)) return fail(ATTN_E_INVALID, "block_prob is NULL or not 8-byte aligned");
@@ -283,8 +289,8 @@ TBS_EXPORT int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, c
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
-  if (s.nb > kMaxSparseBlocks)
-    return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd: %d blocks per sequence exceed %d", s.nb, kMaxSparseBlocks);
+  if (s.nbk > kMaxSparseBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd: %d key blocks per sequence exceed %d", s.nbk, kMaxSparseBlocks);
   if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(row_idx, "row_idx", false)) ||
       (st = check_i32(work_list, "work_list", true)))
     return st;

@@ -95,16 +95,17 @@ __global__ __launch_bounds__(kCsrThreads) void aug_csr_kernel(const int32_t* __r
   }
 }
 
-// Candidates a .. a + kAugCache - 1 of a row's ranked tail into its cache.
+// Candidates a .. a + kAugCache - 1 of a row's ranked tail into its cache
+// (rows of nbk key-block entries).
 __device__ __forceinline__ void aug_refill(AugRow* st, const int32_t* __restrict__ row_idx,
-                                           const double* __restrict__ block_prob, int nb) {
-  const long long rb = static_cast<long long>(st->u) * nb;
+                                           const double* __restrict__ block_prob, int nbk) {
+  const long long rb = static_cast<long long>(st->u) * nbk;
   const int a = st->a, k = st->k, rem = st->rem;
   // All index loads, then all probability loads, then the stores: the state
   // may live in global memory, so stores between loads would serialise them.
   int jv[kAugCache];
 #pragma unroll
-  for (int c = 0; c < kAugCache; ++c) jv[c] = a + c < rem ? min(max(row_idx[rb + k + a + c], 0), nb - 1) : 0;
+  for (int c = 0; c < kAugCache; ++c) jv[c] = a + c < rem ? min(max(row_idx[rb + k + a + c], 0), nbk - 1) : 0;
   double pv[kAugCache];
 #pragma unroll
   for (int c = 0; c < kAugCache; ++c) pv[c] = a + c < rem ? block_prob[rb + jv[c]] : 0.0;
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(kWave) void aug_merge_kernel(const double* __restri
                                                           const int32_t* __restrict__ row_cnt,
                                                           const int32_t* __restrict__ row_idx,
                                                           const int64_t* __restrict__ worker_load, int W, int nb,
-                                                          int causal, const int32_t* __restrict__ off,
+                                                          int nbk, int bq, int bk, int causal,
+                                                          const int32_t* __restrict__ off,
                                                           const int32_t* __restrict__ rows,
                                                           AugRow* __restrict__ gstate,
                                                           int32_t* __restrict__ aug_add,
@@ -150,7 +152,8 @@ __global__ __launch_bounds__(kWave) void aug_merge_kernel(const double* __restri
     AugRow* s = st + r;
     const int u = rows[r0 + r];
     const int i = u % nb;
-    const int nv = causal ? i + 1 : nb;
+    // Causal routing: key blocks that start at or before the query block's last token.
+    const int nv = causal ? min(nbk, ((i + 1) * bq - 1) / bk + 1) : nbk;
     s->u = u;
     s->k = min(max(row_cnt[u], 0), nv);
     s->rem = nv - s->k;
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(kWave) void aug_merge_kernel(const double* __restri
     for (int r = lane; r < nr; r += kWave) st[r].a = st[r].rem;
     picks = total;
   } else if (slack > 0) {
-    for (int r = lane; r < nr; r += kWave) aug_refill(st + r, row_idx, block_prob, nb);
+    for (int r = lane; r < nr; r += kWave) aug_refill(st + r, row_idx, block_prob, nbk);
     // Best head among this lane's rows; only the lane that owned the last
     // winner rescans.
     long long bk = -1;
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(kWave) void aug_merge_kernel(const double* __restri
       if (bk == k && bu == u) {
         AugRow* s = st + br;
         s->a += 1;
-        if (s->a % kAugCache == 0 && s->a < s->rem) aug_refill(s, row_idx, block_prob, nb);
+        if (s->a % kAugCache == 0 && s->a < s->rem) aug_refill(s, row_idx, block_prob, nbk);
         rescan();
       }
     }
@@ -217,12 +220,12 @@ __global__ __launch_bounds__(kWave) void aug_merge_kernel(const double* __restri
 // them is unchanged.
 constexpr int kRebuildWaves = 4;
 __global__ __launch_bounds__(kRebuildWaves * kWave) void aug_rebuild_kernel(const int32_t* __restrict__ aug_add,
-                                                                            int U, int nb,
+                                                                            int U, int nb, int nbk,
                                                                             uint8_t* __restrict__ mask,
                                                                             int32_t* __restrict__ row_cnt,
                                                                             int32_t* __restrict__ row_idx,
                                                                             int32_t* __restrict__ head_cnt) {
-  __shared__ unsigned bits[kRebuildWaves][32];   // nb <= 1024
+  __shared__ unsigned bits[kRebuildWaves][32];   // nbk <= 1024
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int u = blockIdx.x * kRebuildWaves + wave;
@@ -235,10 +238,10 @@ __global__ __launch_bounds__(kRebuildWaves * kWave) void aug_rebuild_kernel(cons
   if (lane < 32) bw[lane] = 0u;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  int32_t* ri = row_idx + static_cast<long long>(u) * nb;
-  uint8_t* mr = mask + static_cast<long long>(u) * nb;
+  int32_t* ri = row_idx + static_cast<long long>(u) * nbk;
+  uint8_t* mr = mask + static_cast<long long>(u) * nbk;
   for (int x = lane; x < n; x += kWave) {
-    const int j = min(max(ri[x], 0), nb - 1);
+    const int j = min(max(ri[x], 0), nbk - 1);
     atomicOr(&bw[j >> 5], 1u << (j & 31));
     if (x >= k) mr[j] = 1;
   }
@@ -294,12 +297,13 @@ hipError_t launch_augment(const Shape& s, const double* block_prob, const int32_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(aug_merge_kernel, dim3(num_workers), dim3(kWave), 0, stream, block_prob, row_cnt, row_idx,
-                     worker_load, num_workers, s.nb, s.causal ? 1 : 0, off, rows, gstate, aug_add, added);
+                     worker_load, num_workers, s.nb, s.nbk, s.block, s.kb, s.causal ? 1 : 0, off, rows, gstate,
+                     aug_add, added);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned blocks = static_cast<unsigned>((U + kRebuildWaves - 1) / kRebuildWaves);
   hipLaunchKernelGGL(aug_rebuild_kernel, dim3(blocks), dim3(kRebuildWaves * kWave), 0, stream, aug_add,
-                     static_cast<int>(U), s.nb, mask, row_cnt, row_idx, head_cnt);
+                     static_cast<int>(U), s.nb, s.nbk, mask, row_cnt, row_idx, head_cnt);
   return hipGetLastError();
 }
 

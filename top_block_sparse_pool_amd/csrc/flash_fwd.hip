@@ -63,7 +63,8 @@ struct FwdParams {
   unsigned long long* prof;
   int BH;
   int N;
-  int nb;
+  int nb;             // query blocks per (b, h)
+  int nbk;            // key blocks per (b, h): entries of a row_idx row
   int U;              // work items in the queue (query-block groups)
   int G;              // query blocks per work item
   int ng;             // work items per (b, h) = ceil(nb / G)
@@ -71,8 +72,9 @@ struct FwdParams {
   float scale_log2;   // scale * log2(e)
 };
 
-// Unit bookkeeping shared by both kernels.
-template <int BQ, int MODE>
+// Unit bookkeeping of the fp32 kernel: query blocks of BQ rows, listed key
+// blocks of BK keys.
+template <int BQ, int BK, int MODE>
 struct UnitInfo {
   int bh, i, ntiles;
   const int32_t* list;
@@ -90,13 +92,13 @@ struct UnitInfo {
       bh = u / p.nb;
       i = u - bh * p.nb;
     }
-    constexpr int SPB = BQ / kKeyTile;   // key tiles per block
+    constexpr int SPB = BK / kKeyTile;   // key tiles per key block
     if (fwd_listed(MODE)) {
-      const int cnt = min(max(p.row_cnt[u], 0), p.nb);
-      list = p.row_idx + static_cast<long long>(u) * p.nb;
+      const int cnt = min(max(p.row_cnt[u], 0), p.nbk);
+      list = p.row_idx + static_cast<long long>(u) * p.nbk;
       ntiles = cnt * SPB;
-      if (SPB > 1 && cnt > 0 && list[cnt - 1] >= p.nb - 1) {
-        const int tail = p.N - (p.nb - 1) * BQ;
+      if (SPB > 1 && cnt > 0 && list[cnt - 1] >= p.nbk - 1) {
+        const int tail = p.N - (p.nbk - 1) * BK;
         ntiles = (cnt - 1) * SPB + (tail + kKeyTile - 1) / kKeyTile;
       }
     } else if (MODE == kDense) {
@@ -110,9 +112,9 @@ struct UnitInfo {
 
   __device__ __forceinline__ int key0(const FwdParams& p, int t) const {
     if (fwd_listed(MODE)) {
-      constexpr int SPB = BQ / kKeyTile;
-      const int jb = min(max(list[t / SPB], 0), p.nb - 1);
-      return jb * BQ + (t % SPB) * kKeyTile;
+      constexpr int SPB = BK / kKeyTile;
+      const int jb = min(max(list[t / SPB], 0), p.nbk - 1);
+      return jb * BK + (t % SPB) * kKeyTile;
     }
     return t * kKeyTile;
   }
@@ -295,7 +297,7 @@ struct GroupInfo {
 // must land by the end of step 2t+1, two steps ahead of their first use.
 constexpr int kWaves = 8;
 
-template <int D, int BQ, int MODE>
+template <int D, int BQ, int BK, int MODE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_bf16_pp(
     FwdParams p) {
   constexpr int G = 256 / BQ;           // query blocks per work item
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int NT = kWaves * 64;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = kKeyTile * ROWB;
-  constexpr int SPB = BQ / kKeyTile;    // key tiles per key block
+  constexpr int SPB = BK / kKeyTile;    // key tiles per key block (BK keys)
   constexpr int NS = D / 16;            // k-steps of S^T
   constexpr int NO = D / 32;            // 32-dim tiles of O^T
   // LDS: K stage 0, K stage 1, V stage 0, V stage 1.
@@ -376,15 +378,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // a bit per member block saying whether that block selected it.
     int nt;
     if (fwd_listed(MODE)) {
-      const int nwords = (p.nb + 31) / 32;
+      const int nwords = (p.nbk + 31) / 32;
       for (int x = tid; x < G * kMaxListWords; x += NT) s_bm[x] = 0u;
       __syncthreads();
       for (int m = 0; m < gi.gsz; ++m) {
         const long long u = static_cast<long long>(gi.bh) * p.nb + gi.i0 + m;
-        const int cnt = min(max(p.row_cnt[u], 0), p.nb);
-        const int32_t* lst = p.row_idx + u * p.nb;
+        const int cnt = min(max(p.row_cnt[u], 0), p.nbk);
+        const int32_t* lst = p.row_idx + u * p.nbk;
         for (int x = tid; x < cnt; x += NT) {
-          const int j = min(max(lst[x], 0), p.nb - 1);
+          const int j = min(max(lst[x], 0), p.nbk - 1);
           atomicOr(&s_bm[m * kMaxListWords + (j >> 5)], 1u << (j & 31));
         }
       }
@@ -420,8 +422,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       __syncthreads();
       const int nl = s_nlist;
       nt = nl * SPB;
-      if (SPB > 1 && nl > 0 && s_lj[nl - 1] == p.nb - 1) {
-        const int tail = p.N - (p.nb - 1) * BQ;
+      if (SPB > 1 && nl > 0 && s_lj[nl - 1] == p.nbk - 1) {
+        const int tail = p.N - (p.nbk - 1) * BK;
         nt = (nl - 1) * SPB + (tail + kKeyTile - 1) / kKeyTile;
       }
     } else if (MODE == kDense) {
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       nt = (min(p.N, (gi.i0 + gi.gsz) * BQ) + kKeyTile - 1) / kKeyTile;
     }
     auto tile_key0 = [&](int t) __attribute__((always_inline)) -> int {
-      if (fwd_listed(MODE)) return __builtin_amdgcn_readfirstlane(s_lj[t / SPB]) * BQ + (t % SPB) * kKeyTile;
+      if (fwd_listed(MODE)) return __builtin_amdgcn_readfirstlane(s_lj[t / SPB]) * BK + (t % SPB) * kKeyTile;
       return t * kKeyTile;
     };
     // Under a causal mask a wave skips tiles whose keys all follow its 32
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
 // ---------------------------------------------------------------- fp32 ---
 
-template <int D, int BQ, int MODE>
+template <int D, int BQ, int BK, int MODE>
 __global__ __launch_bounds__(BQ * 2) void flash_fwd_f32(FwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
@@ -721,7 +723,7 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_f32(FwdParams p) {
     __syncthreads();
     if (qpos >= p.U) break;
 
-    UnitInfo<BQ, MODE> ui;
+    UnitInfo<BQ, BK, MODE> ui;
     ui.decode(p, qpos);
     const long long head_off = static_cast<long long>(ui.bh) * p.N * D;
     const int q0w = ui.i * BQ + wave * 32;
@@ -849,33 +851,44 @@ constexpr int group_for(int dtype, int block) { return dtype == 0 ? 256 / block 
 
 // Every variant is instantiated explicitly: referencing a kernel template
 // only through a function-pointer table does not always emit its host stub.
-#define TBS_INSTANTIATE(D, BQ)                                          \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, kSparse>(FwdParams); \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, kDense>(FwdParams);  \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, kCausal>(FwdParams); \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, kSparseCausal>(FwdParams); \
-  template __global__ void flash_fwd_f32<D, BQ, kSparse>(FwdParams);                  \
-  template __global__ void flash_fwd_f32<D, BQ, kDense>(FwdParams);                   \
-  template __global__ void flash_fwd_f32<D, BQ, kCausal>(FwdParams);                  \
-  template __global__ void flash_fwd_f32<D, BQ, kSparseCausal>(FwdParams);
-TBS_INSTANTIATE(128, 64)
-TBS_INSTANTIATE(128, 128)
-TBS_INSTANTIATE(64, 64)
-TBS_INSTANTIATE(64, 128)
+#define TBS_INSTANTIATE(D, BQ, BKX)                                                    \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kSparse>(FwdParams);           \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kDense>(FwdParams);            \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kCausal>(FwdParams);           \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kSparseCausal>(FwdParams);     \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BKX, kSparse>(FwdParams);          \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BKX, kSparseCausal>(FwdParams);    \
+  template __global__ void flash_fwd_f32<D, BQ, BQ, kSparse>(FwdParams);               \
+  template __global__ void flash_fwd_f32<D, BQ, BQ, kDense>(FwdParams);                \
+  template __global__ void flash_fwd_f32<D, BQ, BQ, kCausal>(FwdParams);               \
+  template __global__ void flash_fwd_f32<D, BQ, BQ, kSparseCausal>(FwdParams);         \
+  template __global__ void flash_fwd_f32<D, BQ, BKX, kSparse>(FwdParams);              \
+  template __global__ void flash_fwd_f32<D, BQ, BKX, kSparseCausal>(FwdParams);
+TBS_INSTANTIATE(128, 64, 128)
+TBS_INSTANTIATE(128, 128, 64)
+TBS_INSTANTIATE(64, 64, 128)
+TBS_INSTANTIATE(64, 128, 64)
 #undef TBS_INSTANTIATE
 
-template <int D, int BQ>
+// Key blocks enter only the listed modes; dense and causal take BK = BQ.
+template <int D, int BQ, int BK>
 KernelFn pick_mode(int dtype, int mode) {
-  static const KernelFn bf16_fns[4] = {flash_fwd_bf16_pp<D, BQ, kSparse>, flash_fwd_bf16_pp<D, BQ, kDense>,
-                                       flash_fwd_bf16_pp<D, BQ, kCausal>, flash_fwd_bf16_pp<D, BQ, kSparseCausal>};
-  static const KernelFn f32_fns[4] = {flash_fwd_f32<D, BQ, kSparse>, flash_fwd_f32<D, BQ, kDense>,
-                                      flash_fwd_f32<D, BQ, kCausal>, flash_fwd_f32<D, BQ, kSparseCausal>};
+  static const KernelFn bf16_fns[4] = {flash_fwd_bf16_pp<D, BQ, BK, kSparse>, flash_fwd_bf16_pp<D, BQ, BQ, kDense>,
+                                       flash_fwd_bf16_pp<D, BQ, BQ, kCausal>,
+                                       flash_fwd_bf16_pp<D, BQ, BK, kSparseCausal>};
+  static const KernelFn f32_fns[4] = {flash_fwd_f32<D, BQ, BK, kSparse>, flash_fwd_f32<D, BQ, BQ, kDense>,
+                                      flash_fwd_f32<D, BQ, BQ, kCausal>, flash_fwd_f32<D, BQ, BK, kSparseCausal>};
   return dtype == 0 ? bf16_fns[mode] : f32_fns[mode];
 }
 
+template <int D>
+KernelFn pick_blocks(const Shape& s, int mode) {
+  if (s.block == 128) return s.kb == 128 ? pick_mode<D, 128, 128>(s.dtype, mode) : pick_mode<D, 128, 64>(s.dtype, mode);
+  return s.kb == 128 ? pick_mode<D, 64, 128>(s.dtype, mode) : pick_mode<D, 64, 64>(s.dtype, mode);
+}
+
 KernelFn pick_kernel(const Shape& s, int mode) {
-  if (s.d == 128) return s.block == 128 ? pick_mode<128, 128>(s.dtype, mode) : pick_mode<128, 64>(s.dtype, mode);
-  return s.block == 128 ? pick_mode<64, 128>(s.dtype, mode) : pick_mode<64, 64>(s.dtype, mode);
+  return s.d == 128 ? pick_blocks<128>(s, mode) : pick_blocks<64>(s, mode);
 }
 
 }  // namespace
@@ -922,6 +935,7 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
   p.BH = s.B * s.H;
   p.N = s.N;
   p.nb = s.nb;
+  p.nbk = s.nbk;
   p.G = group_size(s);
   p.ng = (s.nb + p.G - 1) / p.G;
   p.U = static_cast<int>(work_items(s));

@@ -9,12 +9,19 @@
 namespace tbs {
 
 struct Shape {
-  int B, H, N, d, block, nb;
+  int B, H, N, d, block, nb;   // query blocks: size and count
+  int kb, nbk;                 // key blocks: size and count
   int dtype;      // 0 bf16, 1 f32
   int causal;
   int flags;
   double scale;   // resolved (never 0)
   long long units() const { return static_cast<long long>(B) * H * nb; }
+  // Key blocks eligible for query block i under causal routing: those that
+  // start at or before the query block's last token.
+  int causal_valid(int i) const {
+    const long long e = (static_cast<long long>(i + 1) * block - 1) / kb + 1;
+    return e < nbk ? static_cast<int>(e) : nbk;
+  }
 };
 
 // Forward modes: a per-row block list (sparse), all keys (dense), all keys

@@ -54,21 +54,26 @@ __device__ __forceinline__ void load_chunk_f64<float>(const float* src, double* 
   for (int e = 0; e < 4; ++e) out[e] = static_cast<double>(w[e]);
 }
 
-// Block mean of Q (tensor 0) or K (tensor 1) over the valid tokens of block i.
+// Block mean of Q over the valid tokens of query block i (workgroups
+// 0 .. BH*nbq-1) or of K over key block j (the next BH*nbk workgroups).
 template <typename T, int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
     const T* __restrict__ q, const T* __restrict__ k, double* __restrict__ qbar,
-    double* __restrict__ kbar_t, int32_t* __restrict__ head_cnt, int BH, int N, int nb, int block) {
+    double* __restrict__ kbar_t, int32_t* __restrict__ head_cnt, int BH, int N, int nbq, int bq, int nbk,
+    int bk) {
   constexpr int E = 16 / sizeof(T);           // elements per 16-byte chunk
   constexpr int C = D / E;                    // chunks per token row
   constexpr int R = kPoolThreads / C;         // token rows per pass
   __shared__ double red[R][D];
 
   const long long wg = blockIdx.x;
-  const int i = static_cast<int>(wg % nb);
-  const long long tb = wg / nb;
-  const int bh = static_cast<int>(tb % BH);
-  const int tensor = static_cast<int>(tb / BH);
+  const long long nq = static_cast<long long>(BH) * nbq;
+  const int tensor = wg < nq ? 0 : 1;
+  const long long wl = tensor == 0 ? wg : wg - nq;
+  const int nb = tensor == 0 ? nbq : nbk;
+  const int block = tensor == 0 ? bq : bk;
+  const int i = static_cast<int>(wl % nb);
+  const int bh = static_cast<int>(wl / nb);
   const T* x = (tensor == 0 ? q : k) + static_cast<long long>(bh) * N * D;
   const int lo = i * block;
   const int n = min(block, N - lo);
@@ -254,7 +259,8 @@ __device__ void select_row(const double* __restrict__ zr, int nb, int nv, double
 template <int D, int R, int E>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ qbar, const double* __restrict__ kbar_t, double scale, double top_p,
-    int nb, int causal, int tiles_per_head, uint8_t* __restrict__ mask, int32_t* __restrict__ row_cnt,
+    int nbq, int nbk, int bq, int bk, int causal, int tiles_per_head, uint8_t* __restrict__ mask,
+    int32_t* __restrict__ row_cnt,
     int32_t* __restrict__ row_idx, int32_t* __restrict__ head_cnt, double* __restrict__ block_prob) {
   constexpr int NP = 64 * E;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -264,21 +270,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int wave = tid / kWave;
   const int bh = blockIdx.x / tiles_per_head;
   const int i0 = (blockIdx.x % tiles_per_head) * R;
-  const int rows = min(R, nb - i0);
+  const int rows = min(R, nbq - i0);
 
   // Phase 1: Z[r][j] = scale * <Qbar_{i0+r}, Kbar_j> in fp64.
-  const double* kt = kbar_t + static_cast<long long>(bh) * D * nb;
-  const double* qb = qbar + static_cast<long long>(bh) * nb * D;
+  const double* kt = kbar_t + static_cast<long long>(bh) * D * nbk;
+  const double* qb = qbar + static_cast<long long>(bh) * nbq * D;
   for (int j = tid; j < NP; j += kSelThreads) {
     double acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    if (j < nb) {
+    if (j < nbk) {
       for (int c = 0; c < D; ++c) {
-        const double kv = kt[static_cast<long long>(c) * nb + j];
+        const double kv = kt[static_cast<long long>(c) * nbk + j];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const int ir = min(i0 + r, nb - 1);
+          const int ir = min(i0 + r, nbq - 1);
           acc[r] = fma(qb[static_cast<long long>(ir) * D + c], kv, acc[r]);
         }
       }
@@ -293,9 +299,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   // Phase 2: one wave per row.
   for (int r = wave; r < rows; r += kSelWaves) {
-    const long long row = static_cast<long long>(bh) * nb + i0 + r;
-    const int nv = causal ? i0 + r + 1 : nb;
-    select_row<E>(z + r * NP, nb, nv, top_p, row, bh, flags + wave * NP, mask, row_cnt, row_idx, head_cnt,
+    const long long row = static_cast<long long>(bh) * nbq + i0 + r;
+    // Causal routing: key blocks that start at or before the query block's last token.
+    const int nv = causal ? min(nbk, ((i0 + r + 1) * bq - 1) / bk + 1) : nbk;
+    select_row<E>(z + r * NP, nbk, nv, top_p, row, bh, flags + wave * NP, mask, row_cnt, row_idx, head_cnt,
                   block_prob);
   }
 }
@@ -316,10 +323,10 @@ hipError_t launch_select_t(const Shape& s, const double* qbar, const double* kba
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  const int tiles = (s.nb + R - 1) / R;
+  const int tiles = (s.nb + R - 1) / R;   // query-block rows per head, R per workgroup
   const long long grid = static_cast<long long>(s.B) * s.H * tiles;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSelThreads), smem, stream, qbar, kbar_t,
-                     s.scale, top_p, s.nb, s.causal ? 1 : 0, tiles, mask, row_cnt, row_idx, head_cnt, block_prob);
+                     s.scale, top_p, s.nb, s.nbk, s.block, s.kb, s.causal ? 1 : 0, tiles, mask, row_cnt, row_idx, head_cnt, block_prob);
   return hipGetLastError();
 }
 
@@ -327,7 +334,7 @@ template <int D>
 hipError_t launch_select_d(const Shape& s, const double* qbar, const double* kbar_t, double top_p,
                            uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                            double* block_prob, hipStream_t stream) {
-  const int np = next_pow2(s.nb < 64 ? 64 : s.nb);
+  const int np = next_pow2(s.nbk < 64 ? 64 : s.nbk);
   switch (np) {
     case 64: return launch_select_t<D, 16, 1>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
     case 128: return launch_select_t<D, 16, 2>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
@@ -342,26 +349,26 @@ hipError_t launch_select_d(const Shape& s, const double* qbar, const double* kba
 hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qbar, double* kbar_t,
                        int32_t* head_cnt, hipStream_t stream) {
   const int BH = s.B * s.H;
-  const long long grid = 2LL * BH * s.nb;
+  const long long grid = static_cast<long long>(BH) * (s.nb + s.nbk);
   dim3 g(static_cast<unsigned>(grid)), b(kPoolThreads);
   if (s.dtype == 0) {
     auto qq = static_cast<const unsigned short*>(q);
     auto kk = static_cast<const unsigned short*>(k);
     if (s.d == 128)
       hipLaunchKernelGGL((pool_kernel<unsigned short, 128>), g, b, 0, stream, qq, kk, qbar, kbar_t,
-                         head_cnt, BH, s.N, s.nb, s.block);
+                         head_cnt, BH, s.N, s.nb, s.block, s.nbk, s.kb);
     else
       hipLaunchKernelGGL((pool_kernel<unsigned short, 64>), g, b, 0, stream, qq, kk, qbar, kbar_t,
-                         head_cnt, BH, s.N, s.nb, s.block);
+                         head_cnt, BH, s.N, s.nb, s.block, s.nbk, s.kb);
   } else {
     auto qq = static_cast<const float*>(q);
     auto kk = static_cast<const float*>(k);
     if (s.d == 128)
       hipLaunchKernelGGL((pool_kernel<float, 128>), g, b, 0, stream, qq, kk, qbar, kbar_t, head_cnt,
-                         BH, s.N, s.nb, s.block);
+                         BH, s.N, s.nb, s.block, s.nbk, s.kb);
     else
       hipLaunchKernelGGL((pool_kernel<float, 64>), g, b, 0, stream, qq, kk, qbar, kbar_t, head_cnt,
-                         BH, s.N, s.nb, s.block);
+                         BH, s.N, s.nb, s.block, s.nbk, s.kb);
   }
   return hipGetLastError();
 }

@@ -41,21 +41,23 @@ constexpr int kSchedThreads = 256;
 constexpr int kSchedWaves = kSchedThreads / kWave;
 constexpr int kMaxCost = 4096;  // a work item holds at most 4 blocks of <= 1024 key blocks
 constexpr int kCostBits = 13;   // costs are in [0, 4096]
-// LDS histogram: one row of G * nb + 1 counters per wave.
+// LDS histogram: one row of G * nbk + 1 counters per wave.
 constexpr size_t sched_lds_bytes(int maxc) { return sizeof(int) * kSchedWaves * (maxc + 1); }
 
-// Cost of work item g: the summed selected-block counts of its query blocks.
-__device__ __forceinline__ int item_cost(const int32_t* __restrict__ row_cnt, int g, int nb, int G, int ng) {
+// Cost of work item g: the summed selected-key-block counts of its query
+// blocks (nb query blocks and nbk key blocks per head).
+__device__ __forceinline__ int item_cost(const int32_t* __restrict__ row_cnt, int g, int nb, int nbk, int G,
+                                         int ng) {
   const int bh = g / ng;
   const int i0 = (g - bh * ng) * G;
   const int gsz = min(G, nb - i0);
   int c = 0;
-  for (int m = 0; m < gsz; ++m) c += min(max(row_cnt[static_cast<long long>(bh) * nb + i0 + m], 0), nb);
+  for (int m = 0; m < gsz; ++m) c += min(max(row_cnt[static_cast<long long>(bh) * nb + i0 + m], 0), nbk);
   return c;
 }
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ row_cnt,
-                                                                 int items, int nb, int G, int ng,
+                                                                 int items, int nb, int nbk, int G, int ng,
                                                                  int window_items,
                                                                  int32_t* __restrict__ work_list,
                                                                  uint32_t* __restrict__ ctrl) {
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
-  const int maxc = G * nb;
+  const int maxc = G * nbk;
   const int ncost = maxc + 1;   // cost values 0..maxc
   auto cnt = [&](int w, int c) -> int& { return sched_hist[w * ncost + c]; };
 
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   const int chunk = (w1 - w0 + kSchedWaves - 1) / kSchedWaves;
   const int ubeg = min(w1, w0 + wave * chunk);
   const int uend = min(w1, ubeg + chunk);
-  for (int u = ubeg + lane; u < uend; u += kWave) atomicAdd(&cnt(wave, item_cost(row_cnt, u, nb, G, ng)), 1);
+  for (int u = ubeg + lane; u < uend; u += kWave) atomicAdd(&cnt(wave, item_cost(row_cnt, u, nb, nbk, G, ng)), 1);
   __syncthreads();
 
   // Position x = 0..ncost-1 enumerates costs in descending order (c = maxc - x).
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   for (int base = ubeg; base < uend; base += kWave) {
     const int u = base + lane;
     const bool valid = u < uend;
-    const int c = valid ? item_cost(row_cnt, u, nb, G, ng) : 0;
+    const int c = valid ? item_cost(row_cnt, u, nb, nbk, G, ng) : 0;
     uint64_t same = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < kCostBits; ++b) {
@@ -182,7 +184,7 @@ constexpr int kLptChunk = 8192;   // work-list entries staged in LDS per round
 template <int R>
 __global__ __launch_bounds__(kLptThreads) void lpt_kernel(const int32_t* __restrict__ row_cnt,
                                                           const int32_t* __restrict__ work_list, int items, int nb,
-                                                          int G, int ng, int W, int32_t* __restrict__ worker_of,
+                                                          int nbk, int G, int ng, int W, int32_t* __restrict__ worker_of,
                                                           int64_t* __restrict__ worker_load) {
   __shared__ unsigned short s_cost[kLptChunk];
   __shared__ int s_id[kLptChunk];
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(kLptThreads) void lpt_kernel(const int32_t* __restr
     for (int x = tid; x < n; x += kLptThreads) {
       const int u = min(max(work_list[c0 + x], 0), items - 1);
       s_id[x] = u;
-      s_cost[x] = static_cast<unsigned short>(item_cost(row_cnt, u, nb, G, ng));
+      s_cost[x] = static_cast<unsigned short>(item_cost(row_cnt, u, nb, nbk, G, ng));
     }
     __syncthreads();
     if (wave != 0) continue;
@@ -251,13 +253,14 @@ hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int head_wind
   const int items = BH * ng;
   const int hw = (head_window <= 0 || head_window > BH) ? BH : head_window;
   const int windows = (BH + hw - 1) / hw;
-  const int maxc = G * s.nb;
+  const int maxc = G * s.nbk;
   if (maxc > kMaxCost) return hipErrorInvalidValue;
   const size_t lds = sched_lds_bytes(maxc);
   const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(schedule_kernel),
                                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(schedule_kernel, dim3(windows), dim3(kSchedThreads), lds, stream, row_cnt, items, s.nb, G, ng,
+  hipLaunchKernelGGL(schedule_kernel, dim3(windows), dim3(kSchedThreads), lds, stream, row_cnt, items, s.nb, s.nbk,
+                     G, ng,
                      hw * ng, work_list, ctrl);
   return hipGetLastError();
 }
@@ -270,7 +273,7 @@ hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* wor
   auto kern = num_workers <= 64 ? lpt_kernel<1>
              : num_workers <= 256 ? lpt_kernel<4>
              : num_workers <= 1024 ? lpt_kernel<16> : lpt_kernel<64>;
-  hipLaunchKernelGGL(kern, dim3(1), dim3(kLptThreads), 0, stream, row_cnt, work_list, items, s.nb, G, ng,
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kLptThreads), 0, stream, row_cnt, work_list, items, s.nb, s.nbk, G, ng,
                      num_workers, worker_of, worker_load);
   return hipGetLastError();
 }
