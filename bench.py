@@ -63,13 +63,22 @@ def measured_traffic(workload: str):
         return None
 
 
-def executed_flops(mask: np.ndarray, n_tokens: int, block: int, head_dim: int, causal: bool = False) -> int:
-    nb = mask.shape[-1]
-    n = np.minimum(block, n_tokens - np.arange(nb) * block).astype(np.int64)
+def executed_flops(mask: np.ndarray, n_tokens: int, block: int, head_dim: int, causal: bool = False,
+                   key_block: int | None = None) -> int:
+    """4 * d * allowed (query, key) token pairs of the selected block pairs."""
+    kb = key_block or block
+    nbq, nbk = mask.shape[-2], mask.shape[-1]
+    n = np.minimum(block, n_tokens - np.arange(nbq) * block).astype(np.int64)
+    m = np.minimum(kb, n_tokens - np.arange(nbk) * kb).astype(np.int64)
     if not causal:
-        per_row = mask.astype(np.int64) @ n            # [..., nb]: sum over selected j of n_j
+        per_row = mask.astype(np.int64) @ m            # [..., nbq]: sum over selected j of m_j
         return int(4 * head_dim * int((per_row * n).sum()))
-    pairs = np.tril(np.outer(n, n), -1) + np.diag(n * (n + 1) // 2)   # allowed token pairs per block pair
+    # allowed pairs of query block i and key block j: sum over its queries t of #{s in block j: s <= t}
+    pairs = np.zeros((nbq, nbk), dtype=np.int64)
+    starts = np.arange(nbk, dtype=np.int64) * kb
+    for i in range(nbq):
+        t = np.arange(i * block, i * block + n[i], dtype=np.int64)
+        pairs[i] = np.clip(t[:, None] - starts[None, :] + 1, 0, m[None, :]).sum(0)
     return int(4 * head_dim * int((mask.astype(np.int64) * pairs).sum()))
 
 
@@ -81,6 +90,8 @@ def parse():
     ap.add_argument("--workload", default="video-32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--causal", action="store_true", help="causal routing and causal attention")
+    ap.add_argument("--block", type=int, default=None, help="query block size (default: the workload's)")
+    ap.add_argument("--key-block", type=int, default=None, help="key block size (default: the query block size)")
     ap.add_argument("--sasa", action="store_true",
                     help="slack-aware augmentation in the step: LPT model, attn_augment, a second schedule")
     ap.add_argument("--head-window", type=int, default=None, help="heads per scheduling window (default: library's)")
@@ -95,7 +106,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False):
+def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False, block=None, key_block=None):
     """Time the fp64 oracle on a bounded sample: routing of one head and the
     attention of randomly chosen query blocks of that head."""
     import torch
@@ -109,27 +120,30 @@ def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False):
     sl = (slice(0, 1), slice(h, h + 1))
     q64, k64, v64 = (t[sl].cpu().to(torch.float64).numpy() for t in (q, k, v))
     t0 = time.perf_counter()
-    r = oracle.route(q64, k64, w.block, w.top_p, causal=causal)
+    block = block or w.block
+    kb = key_block or block
+    nbq = -(-w.seq_len // block)
+    r = oracle.route(q64, k64, block, w.top_p, causal=causal, key_block=kb)
     t_route = time.perf_counter() - t0
     rng = np.random.default_rng(seed)
-    order = rng.permutation(w.num_blocks)
+    order = rng.permutation(nbq)
     done, flops, t_attn = 0, 0, 0.0
-    while done < len(order) and t_attn + t_route * (done / w.num_blocks) < target_s:
+    while done < len(order) and t_attn + t_route * (done / nbq) < target_s:
         i = int(order[done])
         t0 = time.perf_counter()
-        oracle.attend_units(q64, k64, v64, w.block, [(0, 0, i)], mask=r.mask, causal=causal)
+        oracle.attend_units(q64, k64, v64, block, [(0, 0, i)], mask=r.mask, causal=causal, key_block=kb)
         t_attn += time.perf_counter() - t0
         row = np.zeros_like(r.mask[0, 0])
         row[i] = r.mask[0, 0, i]
-        flops += executed_flops(row, w.seq_len, w.block, w.head_dim, causal)
+        flops += executed_flops(row, w.seq_len, block, w.head_dim, causal, kb)
         done += 1
-    t_total = t_attn + t_route * (done / w.num_blocks)
+    t_total = t_attn + t_route * (done / nbq)
     return {
         "value": flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"fp64 oracle on head 0 of {w.name}{' (causal)' if causal else ''}: routing of all {w.num_blocks} query blocks "
+        "sample": (f"fp64 oracle on head 0 of {w.name}{' (causal)' if causal else ''}: routing of all {nbq} query blocks "
                    f"({t_route:.2f} s, charged pro rata) + masked attention of {done} random query blocks "
                    f"({t_attn:.2f} s); value = their executed FLOPs / charged time"),
         "ms_per_query_block": 1e3 * t_total / max(done, 1),
@@ -160,15 +174,18 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     causal = bool(args.causal)
-    pr = tbs.make_problem(q, w.block, causal=causal)
+    blk = args.block or w.block
+    kb = args.key_block or blk
+    pr = tbs.make_problem(q, blk, causal=causal, key_block=kb)
     ws = tbs.workspace(pr, dev)
-    B, H, nb, N, d = w.batch, w.heads, w.num_blocks, w.seq_len, w.head_dim
+    B, H, N, d = w.batch, w.heads, w.seq_len, w.head_dim
+    nb, nbk = pr.num_blocks, pr.num_key_blocks
     route_out = tbs.Route(pr, w.top_p,
-                          torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev),
+                          torch.empty((B, H, nb, nbk), dtype=torch.uint8, device=dev),
                           torch.empty((B, H, nb), dtype=torch.int32, device=dev),
-                          torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
+                          torch.empty((B, H, nb, nbk), dtype=torch.int32, device=dev),
                           torch.empty((B, H), dtype=torch.int32, device=dev),
-                          torch.empty((B, H, nb, nb), dtype=torch.float64, device=dev) if args.sasa else None)
+                          torch.empty((B, H, nb, nbk), dtype=torch.float64, device=dev) if args.sasa else None)
     work_list = torch.empty(pr.items, dtype=torch.int32, device=dev)
     n_workers = torch.cuda.get_device_properties(dev).multi_processor_count
     worker_of = torch.empty(pr.items, dtype=torch.int32, device=dev)
@@ -185,7 +202,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        tbs.route(q, k, w.top_p, w.block, ws=ws, out=route_out, causal=causal)
+        tbs.route(q, k, w.top_p, blk, ws=ws, out=route_out, causal=causal, key_block=kb)
         if ev is not None:
             ev[1].record()
         if args.sasa:
@@ -193,8 +210,8 @@ def main():
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         if ev is not None:
             ev[2].record()
-        tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, w.block, work_list=work_list, ws=ws,
-                       o=o, lse=lse, causal=causal)
+        tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, blk, work_list=work_list, ws=ws,
+                       o=o, lse=lse, causal=causal, key_block=kb)
         if ev is not None:
             ev[3].record()
 
@@ -213,10 +230,14 @@ def main():
     t_fwd = np.array([e[2].elapsed_time(e[3]) for e in events])
 
     mask = route_out.mask.cpu().numpy()
-    flops = executed_flops(mask, N, w.block, d, causal)
+    flops = executed_flops(mask, N, blk, d, causal, kb)
     dense_flops = 4 * B * H * d * (N * (N + 1) // 2 if causal else N * N)
     # fraction of the eligible block pairs selected (the lower triangle under causal routing)
-    density = float(mask.sum() / (B * H * (nb * (nb + 1) // 2 if causal else nb * nb)))
+    if causal:
+        elig = np.minimum(nbk, ((np.arange(nb) + 1) * blk - 1) // kb + 1)
+        density = float(mask.sum() / (B * H * int(elig.sum())))
+    else:
+        density = float(mask.sum() / (B * H * nb * nbk))
     ms_step = 1e3 * wall / args.steps
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (t_fwd.mean() * 1e-3) / 1e12
@@ -237,10 +258,10 @@ def main():
     lif = {"workers": int(W), "query_blocks_per_item": int(G), "static_partition": float(static.max() / static.mean()),
            "longest_first_lpt": float(lpt.max() / lpt.mean())}
     # measured per-workgroup busy time of the persistent kernel
-    prp = tbs.make_problem(q, w.block, causal=causal, flags=tbs.FLAG_PROFILE_WORKERS)
+    prp = tbs.make_problem(q, blk, causal=causal, flags=tbs.FLAG_PROFILE_WORKERS, key_block=kb)
     wsp = tbs.workspace(prp, dev)
-    tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, w.block, work_list=work_list, ws=wsp, o=o,
-                   lse=lse, flags=tbs.FLAG_PROFILE_WORKERS, causal=causal)
+    tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, blk, work_list=work_list, ws=wsp, o=o,
+                   lse=lse, flags=tbs.FLAG_PROFILE_WORKERS, causal=causal, key_block=kb)
     torch.cuda.synchronize()
     nw = tbs.num_workers(prp, tbs.OP_SPARSE_FWD)
     stamps = wsp[256:256 + 16 * nw].view(torch.int64).view(nw, 2).cpu().numpy()
@@ -270,12 +291,12 @@ def main():
     dense = None
     if not args.no_dense:
         od = torch.empty_like(q)
-        tbs.dense_fwd(q, k, v, w.block, causal=causal, ws=ws, o=od, want_lse=False)
+        tbs.dense_fwd(q, k, v, blk, causal=causal, ws=ws, o=od, want_lse=False)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.dense_reps):
-            tbs.dense_fwd(q, k, v, w.block, causal=causal, ws=ws, o=od, want_lse=False)
+            tbs.dense_fwd(q, k, v, blk, causal=causal, ws=ws, o=od, want_lse=False)
         e1.record()
         torch.cuda.synchronize()
         t_dense = e0.elapsed_time(e1) / args.dense_reps
@@ -289,10 +310,10 @@ def main():
         # The same routing without augmentation, for the retained mass and the forward time before SASA.
         plain = tbs.Route(pr, w.top_p, torch.empty_like(route_out.mask), torch.empty_like(route_out.row_cnt),
                           torch.empty_like(route_out.row_idx), torch.empty_like(route_out.head_cnt))
-        tbs.route(q, k, w.top_p, w.block, ws=ws, out=plain, causal=causal)
+        tbs.route(q, k, w.top_p, blk, ws=ws, out=plain, causal=causal, key_block=kb)
         wl0 = tbs.schedule(pr, plain.row_cnt, ws, head_window=hw)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        tbs.route(q, k, w.top_p, w.block, ws=ws, out=route_out, causal=causal)
+        tbs.route(q, k, w.top_p, blk, ws=ws, out=route_out, causal=causal, key_block=kb)
         ev[0].record()
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True, work_list=work_list,
                      worker_of=worker_of, worker_load=worker_load)
@@ -302,8 +323,8 @@ def main():
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         ev[3].record()
         for _ in range(3):
-            tbs.sparse_fwd(q, k, v, plain.row_cnt, plain.row_idx, w.block, work_list=wl0, ws=ws, o=o, lse=lse,
-                           causal=causal)
+            tbs.sparse_fwd(q, k, v, plain.row_cnt, plain.row_idx, blk, work_list=wl0, ws=ws, o=o, lse=lse,
+                           causal=causal, key_block=kb)
         ev[4].record()
         torch.cuda.synchronize()
         prob = route_out.block_prob.cpu().numpy()
@@ -324,7 +345,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed, causal)
+        cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed, causal, blk, kb)
 
     out = {
         "metric": METRIC,
@@ -339,7 +360,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d, "block": w.block,
+        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d, "block": blk,
+                   "key_block": kb,
                    "top_p": w.top_p, "causal": causal, "sasa": bool(args.sasa), "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
                    "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
         "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
@@ -349,7 +371,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": f"flash_fwd_bf16_pp ({'sparse causal' if causal else 'sparse'})",
                      "achieved": fwd_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": fwd_tflops / BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(w.name + ("-causal" if causal else ""))},
+                     "traffic": measured_traffic(w.name + ("-causal" if causal else "")
+                                                 + ("" if (blk, kb) == (w.block, w.block) else f"-b{blk}k{kb}"))},
         "dense_same_shape": dense,
         "cold_cache": cold,
         "load_imbalance": lif,

@@ -17,3 +17,13 @@ def test_bench_flops_equal_oracle(N, block, causal):
         mask = mask * np.tril(np.ones((nb, nb), dtype=np.uint8))
     want = sum(oracle.executed_flops(mask[b, h], N, block, 128, causal) for b in range(2) for h in range(3))
     assert bench.executed_flops(mask, N, block, 128, causal) == want
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,bq,bk", [(1000, 128, 64), (1300, 64, 128), (5, 128, 64)])
+def test_bench_flops_mixed_blocks_equal_oracle(N, bq, bk, causal):
+    rng = np.random.default_rng(N + bq)
+    nbq, nbk = oracle.num_blocks(N, bq), oracle.num_blocks(N, bk)
+    mask = (rng.random((1, 2, nbq, nbk)) < 0.4).astype(np.uint8)
+    want = sum(oracle.executed_flops(mask[0, h], N, bq, 64, causal, key_block=bk) for h in range(2))
+    assert bench.executed_flops(mask, N, bq, 64, causal, bk) == want
