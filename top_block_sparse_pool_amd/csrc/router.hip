@@ -10,9 +10,11 @@
 // Kernels:
 //   pool_kernel    one workgroup per (tensor, b, h, block): block means in fp64
 //                  (HBM-bound: reads Q and K once).
-//   select_kernel  one workgroup per (b, h, R query blocks): fp64 scores for R
-//                  rows against all key blocks (pooled K read transposed so
-//                  that lanes read consecutive key blocks); then one wave per
+//   select_kernel  one workgroup per (b, h, R = 8 query blocks): fp64 scores
+//                  for R rows against all key blocks (the R pooled query rows
+//                  staged in LDS and read as broadcasts, pooled K read
+//                  transposed so that lanes read consecutive key blocks, eight
+//                  loads in flight per thread); then one wave per
 //                  row: a max/sum softmax, a register bitonic sort by
 //                  (P desc, index asc), a fixed-order prefix sum to find the
 //                  cut, and the outputs -- no workgroup barriers per row.
@@ -265,7 +267,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   constexpr int NP = 64 * E;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   double* z = reinterpret_cast<double*>(smem_raw);                           // [R][NP]
-  unsigned char* flags = smem_raw + sizeof(double) * R * NP;                 // [waves][NP]
+  double* qs = z + R * NP;                                                   // [R][D]
+  unsigned char* flags = reinterpret_cast<unsigned char*>(qs + R * D);       // [waves][NP]
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int bh = blockIdx.x / tiles_per_head;
@@ -275,18 +278,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // Phase 1: Z[r][j] = scale * <Qbar_{i0+r}, Kbar_j> in fp64.
   const double* kt = kbar_t + static_cast<long long>(bh) * D * nbk;
   const double* qb = qbar + static_cast<long long>(bh) * nbq * D;
+  // The workgroup's R pooled query rows in LDS (read back as broadcasts).
+  for (int x = tid; x < R * D; x += kSelThreads) qs[x] = qb[static_cast<long long>(min(i0 + x / D, nbq - 1)) * D + x % D];
+  __syncthreads();
+  constexpr int CU = 8;   // pooled-K loads in flight per thread
   for (int j = tid; j < NP; j += kSelThreads) {
     double acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0;
     if (j < nbk) {
-      for (int c = 0; c < D; ++c) {
-        const double kv = kt[static_cast<long long>(c) * nbk + j];
+      for (int c0 = 0; c0 < D; c0 += CU) {
+        double kv[CU];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int ir = min(i0 + r, nbq - 1);
-          acc[r] = fma(qb[static_cast<long long>(ir) * D + c], kv, acc[r]);
-        }
+        for (int u = 0; u < CU; ++u) kv[u] = kt[static_cast<long long>(c0 + u) * nbk + j];
+#pragma unroll
+        for (int u = 0; u < CU; ++u)
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] = fma(qs[r * D + c0 + u], kv[u], acc[r]);
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) z[r * NP + j] = scale * acc[r];
@@ -318,7 +326,7 @@ hipError_t launch_select_t(const Shape& s, const double* qbar, const double* kba
                            uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                            double* block_prob, hipStream_t stream) {
   constexpr int NP = 64 * E;
-  const size_t smem = sizeof(double) * static_cast<size_t>(R) * NP + static_cast<size_t>(kSelWaves) * NP;
+  const size_t smem = sizeof(double) * static_cast<size_t>(R) * (NP + D) + static_cast<size_t>(kSelWaves) * NP;
   auto kern = select_kernel<D, R, E>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
@@ -336,10 +344,10 @@ hipError_t launch_select_d(const Shape& s, const double* qbar, const double* kba
                            double* block_prob, hipStream_t stream) {
   const int np = next_pow2(s.nbk < 64 ? 64 : s.nbk);
   switch (np) {
-    case 64: return launch_select_t<D, 16, 1>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
-    case 128: return launch_select_t<D, 16, 2>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
-    case 256: return launch_select_t<D, 16, 4>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
-    case 512: return launch_select_t<D, 16, 8>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+    case 64: return launch_select_t<D, 8, 1>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+    case 128: return launch_select_t<D, 8, 2>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+    case 256: return launch_select_t<D, 8, 4>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
+    case 512: return launch_select_t<D, 8, 8>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
     default: return launch_select_t<D, 8, 16>(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, stream);
   }
 }
