@@ -27,8 +27,10 @@ What it computes, and where the definitions come from:
 * work accounting (``flops``): executed attention FLOPs for a block mask.
 * slack-aware augmentation (``sasa``): workers of the LPT model whose load is
   below the makespan add the highest-probability unselected blocks of their
-  own rows, up to their slack -- FVAttn review, section 1 (Key Terms, "Slack-
-  Aware Sparse Augmentation") and section 3 (Method).
+  own rows, up to their slack; or every row of a work item takes the blocks
+  of the item's union (the idle wave-steps inside the item) -- FVAttn
+  review, section 1 (Key Terms, "Slack-Aware Sparse Augmentation") and
+  section 3 (Method).
 
 All arithmetic is float64 (inputs are upcast exactly from bf16/fp32).  Nothing
 is blocked, fused or reordered beyond what the definitions state.  Every
@@ -40,7 +42,7 @@ from .routing import (block_sizes, num_blocks, pool_blocks, block_scores, softma
 from .attention import attend, attend_units, attend_dense_masked_logits
 from .schedule import group_costs, work_list, lpt_assign, static_partition_loads, load_imbalance
 from .flops import executed_flops, dense_flops
-from .sasa import Augmented, augment, retained_mass
+from .sasa import Augmented, augment, UnionFilled, union_fill, retained_mass
 
 __all__ = [
     "block_sizes", "num_blocks", "pool_blocks", "block_scores", "softmax_rows",
@@ -48,5 +50,5 @@ __all__ = [
     "attend", "attend_units", "attend_dense_masked_logits",
     "group_costs", "work_list", "lpt_assign", "static_partition_loads", "load_imbalance",
     "executed_flops", "dense_flops",
-    "Augmented", "augment", "retained_mass",
+    "Augmented", "augment", "UnionFilled", "union_fill", "retained_mass",
 ]

@@ -22,6 +22,16 @@ The pages describe ranks that are GPUs.  The reading taken for one GPU:
   (P desc, unit asc, j asc).  Inside one row that is the routing rank order,
   so every row's selection stays a prefix of its ranking.  An added block
   costs one unit, like a selected one: L_w + added_w <= M.
+
+A second reading works at the granularity of a work item instead of a
+worker (``union_fill``): the attention kernel of this implementation runs a
+work item of G query blocks as one sequence of key tiles, the union of the
+G rows' selections, and a wave whose own row did not select a tile idles
+through that step.  Those idle wave-steps are slack inside the item; filling
+them costs no extra step.  So each row adds every eligible block of its
+item's union that it did not select (all of them: they are free, so the
+value order does not matter), which leaves every item's union, and with it
+the kernel's work, unchanged.
 """
 from __future__ import annotations
 
@@ -95,6 +105,49 @@ def augment(prob, mask, row_cnt, valid, group: int, window_items: int, num_worke
     added_pw = np.bincount(wk[take], minlength=num_workers).astype(np.int64)
     return Augmented(new_mask, new_cnt, row_idx, new_cnt.sum(-1), new_cnt - rc, worker_of, load,
                      slack.astype(np.int64), added_pw, makespan)
+
+
+@dataclasses.dataclass
+class UnionFilled:
+    mask: np.ndarray        # [B,H,nb,nbk] uint8
+    row_cnt: np.ndarray     # [B,H,nb] int64
+    row_idx: np.ndarray     # [B,H,nb,nbk] int32: ascending selection, then the remaining eligible
+                            # blocks in the routing rank order, then -1
+    head_cnt: np.ndarray    # [B,H] int64
+    added: np.ndarray       # [B,H,nb] int64
+
+
+def union_fill(mask, order, valid, group: int) -> UnionFilled:
+    """Work-item slack filling: row i of item g = (i // group) selects every
+    eligible block (j < valid_i) that any row of the item selected.
+
+    mask [B,H,nb,nbk] the selection, order [B,H,nb,nbk] the routing rank
+    order of each row (P desc, j asc), valid [B,H,nb] (or None: all) the
+    eligible blocks per row.
+    """
+    mask = np.asarray(mask).astype(np.uint8)
+    B, H, nb, nbk = mask.shape
+    valid = np.full((B, H, nb), nbk, dtype=np.int64) if valid is None else np.asarray(valid, dtype=np.int64)
+    new = mask.copy()
+    for i0 in range(0, nb, group):
+        members = range(i0, min(nb, i0 + group))
+        union = np.zeros((B, H, nbk), dtype=bool)
+        for i in members:
+            union |= mask[:, :, i].astype(bool)
+        for i in members:
+            eligible = np.arange(nbk)[None, None, :] < valid[:, :, i, None]
+            new[:, :, i] = (union & eligible).astype(np.uint8) | mask[:, :, i]
+    cnt = new.astype(np.int64).sum(-1)
+    row_idx = np.full((B, H, nb, nbk), -1, dtype=np.int32)
+    order = np.asarray(order)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                sel = np.nonzero(new[b, h, i])[0]
+                rest = [int(j) for j in order[b, h, i] if j < valid[b, h, i] and not new[b, h, i, j]]
+                row_idx[b, h, i, :sel.size] = sel
+                row_idx[b, h, i, sel.size:sel.size + len(rest)] = rest
+    return UnionFilled(new, cnt, row_idx, cnt.sum(-1), cnt - mask.astype(np.int64).sum(-1))
 
 
 def retained_mass(prob, mask) -> np.ndarray:

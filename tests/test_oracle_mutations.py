@@ -191,3 +191,10 @@ def test_mixed_block_eligibility_off_by_one_caught(monkeypatch):
     _patch(monkeypatch, rt, "causal_eligible", strict)
     with pytest.raises(AssertionError):
         tr.test_mixed_blocks_causal_route_against_token_brute_force(8, 16)
+
+
+def test_union_fill_wrong_group_caught(monkeypatch):
+    orig = sa.union_fill
+    monkeypatch.setattr(oracle, "union_fill", lambda mask, order, valid, group: orig(mask, order, valid, 2 * group))
+    with pytest.raises(AssertionError):
+        ts.test_union_fill_against_brute_force(2, False)

@@ -128,3 +128,47 @@ def test_windows_change_only_the_list():
     a2 = oracle.augment(r.prob, r.mask, r.row_cnt, r.valid, G, 2 * ng, 6)
     for a in (a1, a2):
         assert (a.load + a.added_per_worker).max() == a.makespan
+
+
+# ------------------------------------------------ work-item slack (union fill) ---
+
+def test_union_fill_hand_example():
+    # G = 2: rows 0 and 1 form item 0, rows 2 and 3 item 1.
+    prob, mask, rc = _hand_case()
+    order = np.argsort(-prob, axis=-1, kind="stable")
+    u = oracle.union_fill(mask, order, None, 2)
+    assert u.mask[0, 0].tolist() == [[1, 1, 0, 0], [1, 1, 0, 0], [1, 1, 1, 0], [1, 1, 1, 0]]
+    assert u.added[0, 0].tolist() == [0, 1, 0, 2]
+    # row 3: selection {0, 1, 2} ascending, then its remaining block 3
+    assert u.row_idx[0, 0, 3].tolist() == [0, 1, 2, 3]
+    # row 1 (P = [.0625, .5, .25, .1875]): selection {0, 1}, then 2 and 3 by rank
+    assert u.row_idx[0, 0, 1].tolist() == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_union_fill_against_brute_force(G, causal):
+    r = _routed(3 + G, H=3, N=700, block=64, p=0.6, causal=causal)
+    u = oracle.union_fill(r.mask, r.order, r.valid, G)
+    B, H, nb, nbk = r.mask.shape
+    for h in range(H):
+        for i in range(nb):
+            g0 = (i // G) * G
+            union = set()
+            for m in range(g0, min(nb, g0 + G)):
+                union |= set(np.nonzero(r.mask[0, h, m])[0].tolist())
+            want = {j for j in union if j < r.valid[0, h, i]}
+            assert set(np.nonzero(u.mask[0, h, i])[0].tolist()) == want
+            k = len(want)
+            assert u.row_idx[0, h, i, :k].tolist() == sorted(want)
+            ranked = [int(j) for j in r.order[0, h, i] if j < r.valid[0, h, i] and j not in want]
+            assert u.row_idx[0, h, i, k:k + len(ranked)].tolist() == ranked
+            assert (u.row_idx[0, h, i, k + len(ranked):] == -1).all()
+    assert (u.mask >= r.mask).all()
+    # the union of every item, and so the attention kernel's tiles, is unchanged
+    for i0 in range(0, nb, G):
+        assert (u.mask[:, :, i0:i0 + G].any(2) == r.mask[:, :, i0:i0 + G].any(2)).all()
+    assert (u.head_cnt == u.row_cnt.sum(-1)).all()
+    assert (oracle.retained_mass(r.prob, u.mask) >= oracle.retained_mass(r.prob, r.mask)).all()
+    if G == 1:
+        assert u.added.sum() == 0
