@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--key-block", type=int, default=None, help="key block size (default: the query block size)")
     ap.add_argument("--sasa", action="store_true",
                     help="slack-aware augmentation in the step: LPT model, attn_augment, a second schedule")
+    ap.add_argument("--sasa-union", action="store_true",
+                    help="slack filling inside work items in the step (attn_augment_union after the route)")
     ap.add_argument("--head-window", type=int, default=None, help="heads per scheduling window (default: library's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -185,7 +187,8 @@ def main():
                           torch.empty((B, H, nb), dtype=torch.int32, device=dev),
                           torch.empty((B, H, nb, nbk), dtype=torch.int32, device=dev),
                           torch.empty((B, H), dtype=torch.int32, device=dev),
-                          torch.empty((B, H, nb, nbk), dtype=torch.float64, device=dev) if args.sasa else None)
+                          torch.empty((B, H, nb, nbk), dtype=torch.float64, device=dev)
+                          if (args.sasa or args.sasa_union) else None)
     work_list = torch.empty(pr.items, dtype=torch.int32, device=dev)
     n_workers = torch.cuda.get_device_properties(dev).multi_processor_count
     worker_of = torch.empty(pr.items, dtype=torch.int32, device=dev)
@@ -207,6 +210,8 @@ def main():
             ev[1].record()
         if args.sasa:
             sasa_steps()
+        if args.sasa_union:
+            tbs.augment_union(pr, route_out)
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         if ev is not None:
             ev[2].record()
@@ -343,6 +348,36 @@ def main():
                 "sparse_fwd_ms_after": float(t_fwd.mean())}
         del plain
 
+    sasa_union = None
+    if args.sasa_union:
+        plain = tbs.Route(pr, w.top_p, torch.empty_like(route_out.mask), torch.empty_like(route_out.row_cnt),
+                          torch.empty_like(route_out.row_idx), torch.empty_like(route_out.head_cnt))
+        tbs.route(q, k, w.top_p, blk, ws=ws, out=plain, causal=causal, key_block=kb)
+        wl0 = tbs.schedule(pr, plain.row_cnt, ws, head_window=hw)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        tbs.route(q, k, w.top_p, blk, ws=ws, out=route_out, causal=causal, key_block=kb)
+        ev[0].record()
+        tbs.augment_union(pr, route_out)
+        ev[1].record()
+        for _ in range(3):
+            tbs.sparse_fwd(q, k, v, plain.row_cnt, plain.row_idx, blk, work_list=wl0, ws=ws, o=o, lse=lse,
+                           causal=causal, key_block=kb)
+        ev[2].record()
+        torch.cuda.synchronize()
+        prob = route_out.block_prob.cpu().numpy()
+        m0 = plain.mask.cpu().numpy()
+        m1 = route_out.mask.cpu().numpy()
+        mass0, mass1 = (prob * m0).sum(-1), (prob * m1).sum(-1)
+        f0 = executed_flops(m0, N, blk, d, causal, kb)
+        t0 = ev[1].elapsed_time(ev[2]) / 3
+        sasa_union = {"blocks_before": int(m0.sum()), "blocks_added": int(m1.sum() - m0.sum()),
+                      "mean_retained_mass_before": float(mass0.mean()), "mean_retained_mass_after": float(mass1.mean()),
+                      "min_retained_mass_before": float(mass0.min()), "min_retained_mass_after": float(mass1.min()),
+                      "augment_ms": ev[0].elapsed_time(ev[1]),
+                      "sparse_fwd_ms_before": t0, "sparse_fwd_tflops_before": f0 / (t0 * 1e-3) / 1e12,
+                      "sparse_fwd_ms_after": float(t_fwd.mean()), "sparse_fwd_tflops_after": fwd_tflops}
+        del plain
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed, causal, blk, kb)
@@ -362,7 +397,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d, "block": blk,
                    "key_block": kb,
-                   "top_p": w.top_p, "causal": causal, "sasa": bool(args.sasa), "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
+                   "top_p": w.top_p, "causal": causal, "sasa": bool(args.sasa), "sasa_union": bool(args.sasa_union),
+                   "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
                    "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
         "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
                          "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),
@@ -378,6 +414,7 @@ def main():
         "load_imbalance": lif,
         "cpu_baseline": cpu,
         "sasa": sasa,
+        "sasa_union": sasa_union,
         "input_generation_s": gen_s,
     }
     print(json.dumps(out))

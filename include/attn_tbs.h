@@ -245,6 +245,24 @@ int32_t attn_augment(const attn_problem* problem, const double* block_prob, cons
                      int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* Slack-aware augmentation inside work items.
+ *
+ * The attention kernel runs a work item (G query blocks, see
+ * attn_group_size) as one sequence of key tiles, the union of the G rows'
+ * selections; a wave whose row did not select a tile idles through that
+ * step.  That idle time is slack inside the item (FVAttn review page,
+ * section 1, "Slack-Aware Sparse Augmentation": extra high-value blocks in
+ * the slack).  This call fills it: every row selects every block of its
+ * item's union that is eligible for it (all blocks, or those allowed by
+ * causal routing).  The union of every item, and so the attention kernel's
+ * tiles, stay the same.  mask, row_cnt, row_idx and head_cnt are updated in
+ * place: row_idx keeps the new selection ascending, followed by the row's
+ * remaining eligible blocks in their routing rank order.  row_idx must hold
+ * attn_route's ranked tail.  No workspace.  With G = 1 (fp32) it changes
+ * nothing.  Requires nbk <= 1024. */
+int32_t attn_augment_union(const attn_problem* problem, uint8_t* mask, int32_t* row_cnt, int32_t* row_idx,
+                           int32_t* head_cnt, void* stream);
+
 /* Block-sparse attention forward, one persistent kernel launch.
  *
  * For each unit (b, h, i) and each query token t of block i, over the key

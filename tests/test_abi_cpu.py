@@ -28,8 +28,8 @@ def test_exports_every_declared_symbol():
     L = tbs.lib()
     names = _declared_functions()
     assert set(names) == {"attn_abi_version", "attn_last_error", "attn_workspace_bytes", "attn_num_workers",
-                          "attn_group_size", "attn_route", "attn_schedule", "attn_augment", "attn_sparse_fwd",
-                          "attn_dense_fwd"}
+                          "attn_group_size", "attn_route", "attn_schedule", "attn_augment", "attn_augment_union",
+                          "attn_sparse_fwd", "attn_dense_fwd"}
     for n in names:
         assert hasattr(L, n), n
     assert L.attn_abi_version() == 3
@@ -151,3 +151,14 @@ def test_augment_validation():
     assert aug(pr=_problem(N=64 * 1025)) == 2
     assert aug(wsb=1000) == 3 and aug(ws=None) == 3
     assert "workspace" in L.attn_last_error().decode()
+
+
+def test_augment_union_validation():
+    L = tbs.lib()
+    D = ctypes.c_void_p(0x10000)
+    p = _problem()
+    assert L.attn_augment_union(None, D, D, D, D, None) == 1
+    assert L.attn_augment_union(ctypes.byref(p), None, D, D, D, None) == 1
+    assert L.attn_augment_union(ctypes.byref(p), D, ctypes.c_void_p(0x10002), D, D, None) == 1
+    assert L.attn_augment_union(ctypes.byref(p), D, D, D, None, None) == 1
+    assert L.attn_augment_union(ctypes.byref(_problem(N=64 * 1025)), D, D, D, D, None) == 2

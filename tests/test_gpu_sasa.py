@@ -142,3 +142,40 @@ def test_sparse_attention_with_sasa_end_to_end():
     print(f"  mean retained mass {mass0:.4f} -> {mass1:.4f}, {int(ref.added.sum())} blocks added", flush=True)
     units = [(0, h, i) for h in range(4) for i in (0, 7, pr.num_blocks - 1)]
     compare_units(o, lse, q, k, v, w.block, units, ref.mask, q.dtype)
+
+
+UNION = [
+    (custom_workload(1, 4, 2000, 128, 64, "bf16", 0.8, wid=540), False, None),   # G = 4
+    (custom_workload(2, 3, 1500, 128, 128, "bf16", 0.7, wid=541), False, None),  # G = 2
+    (custom_workload(1, 4, 2000, 128, 64, "bf16", 0.8, wid=542), True, None),    # causal
+    (custom_workload(1, 3, 1000, 128, 128, "bf16", 0.8, wid=543), True, 64),     # causal, key blocks of 64
+    (custom_workload(1, 2, 600, 64, 64, "f32", 0.7, wid=544), False, None),      # G = 1: nothing changes
+]
+
+
+@pytest.mark.parametrize("w,causal,kb", UNION, ids=lambda x: getattr(x, "name", str(x)))
+def test_augment_union_matches_oracle(w, causal, kb):
+    q, k, v = _inputs(w)
+    pr = tbs.make_problem(q, w.block, causal=causal, key_block=kb)
+    ws = tbs.workspace(pr, DEV)
+    r = tbs.route(q, k, w.top_p, w.block, ws=ws, causal=causal, key_block=kb)
+    mask0 = r.mask.cpu().numpy()
+    tbs.augment_union(pr, r)
+    wl = tbs.schedule(pr, r.row_cnt, ws)
+    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws, causal=causal,
+                            key_block=kb)
+    torch.cuda.synchronize()
+    rr = oracle.route(to64(q), to64(k), w.block, w.top_p, causal=causal, key_block=kb)
+    assert (mask0 == rr.mask).all(), "routing differs on an ambiguous block; exact comparison not possible"
+    ref = oracle.union_fill(rr.mask, rr.order, rr.valid, pr.group)
+    assert (r.mask.cpu().numpy() == ref.mask).all()
+    assert (r.row_cnt.cpu().numpy() == ref.row_cnt).all()
+    assert (r.head_cnt.cpu().numpy() == ref.head_cnt).all()
+    ri = r.row_idx.cpu().numpy()
+    written = ref.row_idx >= 0                     # selection and ranked tail; entries after them are not written
+    assert (ri[written] == ref.row_idx[written]).all()
+    print(f"  {int(ref.added.sum())} blocks added to {int(rr.mask.sum())}", flush=True)
+    rng = np.random.default_rng(2)
+    units = [(b, h, int(i)) for b in range(pr.batch) for h in range(pr.heads)
+             for i in rng.choice(pr.num_blocks, size=min(3, pr.num_blocks), replace=False)]
+    compare_units(o, lse, q, k, v, w.block, units, ref.mask, q.dtype, causal=causal, key_block=kb)

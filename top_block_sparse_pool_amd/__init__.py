@@ -128,6 +128,8 @@ def lib() -> ctypes.CDLL:
     L.attn_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_augment.restype = i32
     L.attn_augment.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_augment_union.restype = i32
+    L.attn_augment_union.argtypes = [P, vp, vp, vp, vp, vp]
     _lib = L
     return L
 
@@ -273,6 +275,15 @@ def augment(problem: Problem, r: Route, worker_of: torch.Tensor, worker_load: to
     return added
 
 
+def augment_union(problem: Problem, r: Route) -> Route:
+    """attn_augment_union: every row takes the eligible blocks of its work
+    item's union (the idle wave-steps inside the item), in place."""
+    _require_device(r.mask, r.row_cnt, r.row_idx, r.head_cnt)
+    _check(lib().attn_augment_union(ctypes.byref(problem), _ptr(r.mask), _ptr(r.row_cnt), _ptr(r.row_idx),
+                                    _ptr(r.head_cnt), _stream()))
+    return r
+
+
 def _out_tensors(q, o, lse, want_lse):
     B, H, N, d = q.shape
     if o is None:
@@ -333,5 +344,5 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
 
 __all__ = [
     "lib", "AttnError", "Problem", "Route", "make_problem", "workspace", "workspace_bytes", "num_workers",
-    "route", "schedule", "augment", "sparse_fwd", "dense_fwd", "sparse_attention", "LIB_PATH",
+    "route", "schedule", "augment", "augment_union", "sparse_fwd", "dense_fwd", "sparse_attention", "LIB_PATH",
 ]

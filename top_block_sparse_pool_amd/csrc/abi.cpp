@@ -253,6 +253,22 @@ TBS_EXPORT int32_t attn_augment(const attn_problem* problem, const double* block
   return device_status(e, "attn_augment launch");
 }
 
+TBS_EXPORT int32_t attn_augment_union(const attn_problem* problem, uint8_t* mask, int32_t* row_cnt,
+                                      int32_t* row_idx, int32_t* head_cnt, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if (s.nbk > kMaxRouteBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_augment_union: %d key blocks per sequence exceed %d", s.nbk,
+                kMaxRouteBlocks);
+  if (!mask) return fail(ATTN_E_INVALID, "mask is NULL");
+  if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(row_idx, "row_idx", false)) ||
+      (st = check_i32(head_cnt, "head_cnt", false)))
+    return st;
+  hipError_t e = tbs::launch_augment_union(s, mask, row_cnt, row_idx, head_cnt, static_cast<hipStream_t>(stream));
+  return device_status(e, "attn_augment_union launch");
+}
+
 namespace {
 int32_t run_fwd(const tbs::Shape& s, int mode, const void* q, const void* k, const void* v,
                 const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list, void* o, float* lse,

@@ -24,6 +24,12 @@
 //                      and a row's cache is refilled every 16 picks.
 //   aug_rebuild_kernel one wave per row that gained blocks: the ascending
 //                      list of the new selection, mask bits, counts.
+//   aug_union_kernel   slack inside a work item (attn_augment_union): one
+//                      workgroup per item, one wave per member row.  The
+//                      attention kernel runs an item as the union of its rows'
+//                      key tiles and a wave idles on the tiles its row did not
+//                      select; every row takes the eligible blocks of the
+//                      union, so the item's tiles, and its time, stay the same.
 #include "device_common.h"
 #include "launch.h"
 
@@ -268,7 +274,104 @@ __global__ __launch_bounds__(kRebuildWaves * kWave) void aug_rebuild_kernel(cons
   }
 }
 
+// Row of one member: old entries (selected blocks ascending, then the ranked
+// tail) are read into registers first, the item's union is built in LDS,
+// then the row is rewritten: union blocks below the row's eligible count in
+// ascending order, then the old tail without them (rank order kept).
+constexpr int kUnionPerLane = 16;   // nbk <= 1024
+__global__ __launch_bounds__(4 * kWave) void aug_union_kernel(uint8_t* __restrict__ mask,
+                                                              int32_t* __restrict__ row_cnt,
+                                                              int32_t* __restrict__ row_idx,
+                                                              int32_t* __restrict__ head_cnt, int nb, int nbk,
+                                                              int bq, int bk, int causal, int G, int ng) {
+  __shared__ unsigned uni[32];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = blockIdx.x;
+  const int bh = g / ng;
+  const int i0 = (g - bh * ng) * G;
+  const int gsz = min(G, nb - i0);
+  const bool active = wave < gsz;
+  const int i = i0 + wave;
+  const long long u = static_cast<long long>(bh) * nb + i;
+  if (threadIdx.x < 32) uni[threadIdx.x] = 0u;
+  __syncthreads();
+  int k = 0, nv = 0;
+  int ent[kUnionPerLane];
+  if (active) {
+    nv = causal ? min(nbk, ((i + 1) * bq - 1) / bk + 1) : nbk;
+    k = min(max(row_cnt[u], 0), nv);
+#pragma unroll
+    for (int e = 0; e < kUnionPerLane; ++e) {
+      const int pos = lane * kUnionPerLane + e;
+      ent[e] = pos < nv ? min(max(row_idx[u * nbk + pos], 0), nbk - 1) : 0;
+      if (pos < k) atomicOr(&uni[ent[e] >> 5], 1u << (ent[e] & 31));
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  // New selection: union blocks j < nv, ascending (lane w < 32 owns word w).
+  unsigned word = lane < 32 ? uni[lane] : 0u;
+  const int lo = lane * 32;
+  if (lo >= nv) word = 0u;
+  else if (nv - lo < 32) word &= (1u << (nv - lo)) - 1u;
+  const int c = __popc(word);
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  const int kn = __shfl(incl, kWave - 1, kWave);
+  // Old tail entries that stay unselected, counted per lane (blocked layout).
+  int keep = 0;
+#pragma unroll
+  for (int e = 0; e < kUnionPerLane; ++e) {
+    const int pos = lane * kUnionPerLane + e;
+    const int j = ent[e];
+    if (pos >= k && pos < nv && !((uni[j >> 5] >> (j & 31)) & 1u)) ++keep;
+  }
+  int kincl = keep;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(kincl, o, kWave);
+    if (lane >= o) kincl += y;
+  }
+  int32_t* ri = row_idx + u * nbk;
+  uint8_t* mr = mask + u * nbk;
+  int pos = incl - c;
+  unsigned wv = word;
+  while (wv) {
+    const int b = __ffs(wv) - 1;
+    wv &= wv - 1;
+    ri[pos++] = lo + b;
+    mr[lo + b] = 1;
+  }
+  int tp = kn + kincl - keep;
+#pragma unroll
+  for (int e = 0; e < kUnionPerLane; ++e) {
+    const int p2 = lane * kUnionPerLane + e;
+    const int j = ent[e];
+    if (p2 >= k && p2 < nv && !((uni[j >> 5] >> (j & 31)) & 1u)) ri[tp++] = j;
+  }
+  if (lane == 0) {
+    row_cnt[u] = kn;
+    atomicAdd(head_cnt + bh, kn - k);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_augment_union(const Shape& s, uint8_t* mask, int32_t* row_cnt, int32_t* row_idx,
+                                int32_t* head_cnt, hipStream_t stream) {
+  const int G = group_size(s);
+  const int ng = (s.nb + G - 1) / G;
+  const long long items = static_cast<long long>(s.B) * s.H * ng;
+  if (G < 1 || G > 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(aug_union_kernel, dim3(static_cast<unsigned>(items)), dim3(G * kWave), 0, stream, mask,
+                     row_cnt, row_idx, head_cnt, s.nb, s.nbk, s.block, s.kb, s.causal ? 1 : 0, G, ng);
+  return hipGetLastError();
+}
 
 size_t augment_ws_bytes(const Shape& s, int num_workers) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };

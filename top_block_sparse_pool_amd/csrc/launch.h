@@ -52,6 +52,9 @@ hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* wor
 // rebuilt lists of the rows that gained blocks.  Workspace bytes after the
 // control block, for up to 4096 workers.
 size_t augment_ws_bytes(const Shape& s, int num_workers);
+// Work-item slack: every row takes the eligible blocks of its item's union.
+hipError_t launch_augment_union(const Shape& s, uint8_t* mask, int32_t* row_cnt, int32_t* row_idx,
+                                int32_t* head_cnt, hipStream_t stream);
 hipError_t launch_augment(const Shape& s, const double* block_prob, const int32_t* worker_of,
                           const int64_t* worker_load, int num_workers, uint8_t* mask, int32_t* row_cnt,
                           int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, hipStream_t stream);
