@@ -163,7 +163,7 @@ def main():
     from workloads import get_workload, make_inputs
 
     w = get_workload(args.workload)
-    hw = tbs.DEFAULT_HEAD_WINDOW if args.head_window is None else args.head_window
+    hw = None if args.head_window is None else args.head_window
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
@@ -180,6 +180,8 @@ def main():
     kb = args.key_block or blk
     pr = tbs.make_problem(q, blk, causal=causal, key_block=kb)
     ws = tbs.workspace(pr, dev)
+    if hw is None:
+        hw = tbs.default_head_window(pr)
     B, H, N, d = w.batch, w.heads, w.seq_len, w.head_dim
     nb, nbk = pr.num_blocks, pr.num_key_blocks
     route_out = tbs.Route(pr, w.top_p,
@@ -273,6 +275,29 @@ def main():
     busy = (stamps[:, 1] - stamps[:, 0]).astype(np.float64)
     lif["measured_workgroups"] = int(nw)
     lif["measured_busy_max_over_mean"] = float(busy.max() / busy.mean())
+    # Processing orders of the same lists: natural item order (what a plain
+    # grid launch approximates), pure longest-first (one window) and the
+    # head-windowed longest-first list of the step.
+    _, _, lpt_pure = tbs.schedule(pr, route_out.row_cnt, ws, head_window=0, lpt=True)
+    wl_pure = tbs.schedule(pr, route_out.row_cnt, ws, head_window=0)
+    torch.cuda.synchronize()
+    lp = lpt_pure.cpu().numpy()
+    lif["longest_first_lpt_one_window"] = float(lp.max() / lp.mean())
+
+    def time_fwd(wl, reps=3):
+        tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, blk, work_list=wl, ws=ws, o=o, lse=lse,
+                       causal=causal, key_block=kb)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, blk, work_list=wl, ws=ws, o=o, lse=lse,
+                           causal=causal, key_block=kb)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    order_ms = {"natural_order": time_fwd(None), "longest_first_one_window": time_fwd(wl_pure),
+                "step_list": time_fwd(work_list), "step_list_head_window": hw}
 
     # Cold caches: a 512 MB buffer is written before every step (outside the
     # timed events), evicting L2 and the MALL, so Q, K and V come from HBM.
@@ -412,6 +437,7 @@ def main():
         "dense_same_shape": dense,
         "cold_cache": cold,
         "load_imbalance": lif,
+        "sparse_fwd_ms_by_order": order_ms,
         "cpu_baseline": cpu,
         "sasa": sasa,
         "sasa_union": sasa_union,

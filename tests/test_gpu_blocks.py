@@ -51,7 +51,7 @@ def test_mixed_blocks_path_matches_oracle(w, kb, causal):
         assert not (r.mask.cpu().numpy() * (np.arange(nbk)[None, :] >= e[:, None])).any()
     G = pr.group
     want_wl = oracle.work_list(oracle.group_costs(r.row_cnt.cpu().numpy(), G),
-                               tbs.DEFAULT_HEAD_WINDOW * -(-nb // G))
+                               tbs.default_head_window(pr) * -(-nb // G))
     assert (wl.cpu().numpy() == want_wl).all()
     units = [(b, h, i) for b in range(pr.batch) for h in range(pr.heads) for i in range(nb)
              if cmp["rows_agree"][b, h, i]]

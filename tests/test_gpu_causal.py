@@ -58,7 +58,7 @@ def test_causal_sparse_path_matches_oracle(w):
     print(f"  ambiguous mismatches: {cmp['ambiguous_mismatches']}", flush=True)
     G = pr.group
     want_wl = oracle.work_list(oracle.group_costs(r.row_cnt.cpu().numpy(), G),
-                               tbs.DEFAULT_HEAD_WINDOW * -(-nb // G))
+                               tbs.default_head_window(pr) * -(-nb // G))
     assert (wl.cpu().numpy() == want_wl).all()
     units = [(b, h, i) for b in range(pr.batch) for h in range(pr.heads) for i in range(nb)
              if cmp["rows_agree"][b, h, i]]

@@ -58,7 +58,7 @@ def test_largest_routing_size():
     ref = oracle_route_per_head(q, k, w.block, w.top_p)
     cmp = compare_route(r, ref)
     assert (wl.cpu().numpy() == oracle.work_list(oracle.group_costs(r.row_cnt.cpu().numpy(), pr.group),
-                                                 tbs.DEFAULT_HEAD_WINDOW * -(-1024 // pr.group))).all()
+                                                 tbs.default_head_window(pr) * -(-1024 // pr.group))).all()
     units = [(0, h, i) for h in range(2) for i in (0, 511, 1023) if cmp["rows_agree"][0, h, i]]
     e, le = compare_units(o, lse, q, k, v, w.block, units, ref["mask"], q.dtype)
     print(f"  ambiguous mismatches {cmp['ambiguous_mismatches']}; max |O err| {e:.3e}", flush=True)

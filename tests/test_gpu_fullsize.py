@@ -45,7 +45,7 @@ def test_full_size_sparse_workload(name):
     cmp = compare_route(r, ref)
     costs = r.row_cnt.cpu().numpy()
     G = pr.group
-    want_wl = oracle.work_list(oracle.group_costs(costs, G), tbs.DEFAULT_HEAD_WINDOW * -(-pr.num_blocks // G))
+    want_wl = oracle.work_list(oracle.group_costs(costs, G), tbs.default_head_window(pr) * -(-pr.num_blocks // G))
     assert (wl.cpu().numpy() == want_wl).all()
     density = costs.sum() / (pr.units * pr.num_blocks)
     print(f"  mask ok (ambiguous mismatches {cmp['ambiguous_mismatches']}), density {density:.3f}", flush=True)

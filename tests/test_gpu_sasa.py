@@ -135,7 +135,7 @@ def test_sparse_attention_with_sasa_end_to_end():
     rr = _oracle_route(q, k, w.block, w.top_p, False)
     G = pr.group
     ng = -(-pr.num_blocks // G)
-    ref = oracle.augment(rr.prob, rr.mask, rr.row_cnt, rr.valid, G, tbs.DEFAULT_HEAD_WINDOW * ng, 16)
+    ref = oracle.augment(rr.prob, rr.mask, rr.row_cnt, rr.valid, G, tbs.default_head_window(pr) * ng, 16)
     assert (r.mask.cpu().numpy() == ref.mask).all()
     mass0 = oracle.retained_mass(rr.prob, rr.mask).mean()
     mass1 = oracle.retained_mass(rr.prob, ref.mask).mean()

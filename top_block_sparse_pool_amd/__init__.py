@@ -37,6 +37,18 @@ OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD, OP_AUGMENT = 0, 1, 2, 3, 4
 FLAG_PROFILE_WORKERS = 1
 CTRL_BYTES = 256
 DEFAULT_HEAD_WINDOW = 4
+# Head windows keep the K/V of the heads that run together cache-resident;
+# past this many K+V bytes per head they no longer fit and only cost balance.
+HEAD_WINDOW_MAX_KV_BYTES = 32 << 20
+
+
+def default_head_window(problem: "Problem") -> int:
+    """Heads per scheduling window used when none is given: DEFAULT_HEAD_WINDOW
+    while one head's K and V fit in HEAD_WINDOW_MAX_KV_BYTES, else 0 (a single
+    longest-first list over all heads)."""
+    elem = 2 if problem.dtype == ATTN_DTYPE_BF16 else 4
+    kv = 2 * problem.seq_len * problem.head_dim * elem
+    return DEFAULT_HEAD_WINDOW if kv <= HEAD_WINDOW_MAX_KV_BYTES else 0
 
 _STATUS_NAMES = {1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_WORKSPACE", 4: "ATTN_E_DEVICE"}
 
@@ -228,13 +240,16 @@ def route(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: Opt
     return out
 
 
-def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, head_window: int = DEFAULT_HEAD_WINDOW,
+def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, head_window: Optional[int] = None,
              num_workers: int = 0, lpt: bool = False, work_list: Optional[torch.Tensor] = None,
              worker_of: Optional[torch.Tensor] = None, worker_load: Optional[torch.Tensor] = None):
     """attn_schedule: longest-first work list inside windows of `head_window`
-    heads (0: one window); with lpt=True also the greedy LPT assignment
-    (worker_of, worker_load), for load-balance reports and augment()."""
+    heads (0: one window; None: default_head_window(problem)); with lpt=True
+    also the greedy LPT assignment (worker_of, worker_load), for load-balance
+    reports and augment()."""
     _require_device(row_cnt, ws)
+    if head_window is None:
+        head_window = default_head_window(problem)
     dev = row_cnt.device
     n_items = problem.items
     if work_list is None:
@@ -322,7 +337,7 @@ def dense_fwd(q, k, v, block: int, causal: bool = False, scale: Optional[float] 
 
 def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] = None,
                      ws: Optional[torch.Tensor] = None, want_lse: bool = True,
-                     head_window: int = DEFAULT_HEAD_WINDOW, causal: bool = False, sasa: bool = False,
+                     head_window: Optional[int] = None, causal: bool = False, sasa: bool = False,
                      num_workers: int = 0, key_block: Optional[int] = None):
     """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list).
 
@@ -343,6 +358,6 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
 
 
 __all__ = [
-    "lib", "AttnError", "Problem", "Route", "make_problem", "workspace", "workspace_bytes", "num_workers",
+    "lib", "AttnError", "Problem", "Route", "make_problem", "default_head_window", "workspace", "workspace_bytes", "num_workers",
     "route", "schedule", "augment", "augment_union", "sparse_fwd", "dense_fwd", "sparse_attention", "LIB_PATH",
 ]
