@@ -118,6 +118,15 @@ def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False, block=None,
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
+    host = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            names = [ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")]
+        sockets = len({ln for ln in open("/proc/cpuinfo") if ln.startswith("physical id")}) or 1
+        if names:
+            host = f"{names[0]} ({len(names)} hardware threads visible, {sockets} socket(s))"
+    except OSError:
+        pass
     h = 0
     sl = (slice(0, 1), slice(h, h + 1))
     q64, k64, v64 = (t[sl].cpu().to(torch.float64).numpy() for t in (q, k, v))
@@ -149,6 +158,7 @@ def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False, block=None,
                    f"({t_route:.2f} s, charged pro rata) + masked attention of {done} random query blocks "
                    f"({t_attn:.2f} s); value = their executed FLOPs / charged time"),
         "ms_per_query_block": 1e3 * t_total / max(done, 1),
+        "host": host,
     }
 
 
@@ -235,6 +245,7 @@ def main():
     t_route = np.array([e[0].elapsed_time(e[1]) for e in events])
     t_sched = np.array([e[1].elapsed_time(e[2]) for e in events])
     t_fwd = np.array([e[2].elapsed_time(e[3]) for e in events])
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in events])
 
     mask = route_out.mask.cpu().numpy()
     flops = executed_flops(mask, N, blk, d, causal, kb)
@@ -427,7 +438,8 @@ def main():
                    "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
         "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
                          "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),
-                         "sparse_fwd_mean": float(t_fwd.mean()), "sparse_fwd_median": float(np.median(t_fwd))},
+                         "sparse_fwd_mean": float(t_fwd.mean()), "sparse_fwd_median": float(np.median(t_fwd)),
+                         "step_events_mean": float(t_step.mean()), "step_events_median": float(np.median(t_step))},
         "sparse_fwd_tflops": fwd_tflops,
         "roofline": {"bound": "mfma", "kernel": f"flash_fwd_bf16_pp ({'sparse causal' if causal else 'sparse'})",
                      "achieved": fwd_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
