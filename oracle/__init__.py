@@ -31,8 +31,15 @@ What it computes, and where the definitions come from:
   of the item's union (the idle wave-steps inside the item) -- FVAttn
   review, section 1 (Key Terms, "Slack-Aware Sparse Augmentation") and
   section 3 (Method).
+* FP8 quantisation (``fp8``): OCP E4M3 codes of Q (one scale per token) and
+  K (one scale per 64-token tile), scales from each group's largest
+  magnitude, every decision in fp32 -- the ParaAttention/HunyuanVideo post,
+  section on FP8 dynamic quantisation (format and groups are readings).  The
+  fp8 attention path is exact attention on the dequantised Q and K.
 
-All arithmetic is float64 (inputs are upcast exactly from bf16/fp32).  Nothing
+All arithmetic is float64 (inputs are upcast exactly from bf16/fp32), except
+that the fp8 quantiser rounds its intermediate steps to fp32 explicitly, as
+its definition states.  Nothing
 is blocked, fused or reordered beyond what the definitions state.  Every
 function is pinned by the CPU tests against brute force, closed forms,
 library special cases or invariants.
@@ -43,6 +50,7 @@ from .attention import attend, attend_units, attend_dense_masked_logits
 from .schedule import group_costs, work_list, lpt_assign, static_partition_loads, load_imbalance
 from .flops import executed_flops, dense_flops
 from .sasa import Augmented, augment, UnionFilled, union_fill, retained_mass
+from . import fp8
 
 __all__ = [
     "block_sizes", "num_blocks", "pool_blocks", "block_scores", "softmax_rows",
@@ -51,4 +59,5 @@ __all__ = [
     "group_costs", "work_list", "lpt_assign", "static_partition_loads", "load_imbalance",
     "executed_flops", "dense_flops",
     "Augmented", "augment", "UnionFilled", "union_fill", "retained_mass",
+    "fp8",
 ]

@@ -4,7 +4,9 @@ a reversed tie rule, a dropped scale, an off-by-one causal mask, a wrong log
 base, a wrong sort direction, and a causal block cut that is missing, off by
 one, or applied after the softmax instead of before it; and an augmentation
 that takes the lowest-probability candidates, measures slack from the mean
-load, or draws candidates from every worker's rows."""
+load, or draws candidates from every worker's rows; an E4M3 exponent bias off by
+one, ties rounded away from zero, K scaled per token instead of per tile, and
+an inverted dequantisation scale."""
 import numpy as np
 import pytest
 
@@ -198,3 +200,41 @@ def test_union_fill_wrong_group_caught(monkeypatch):
     monkeypatch.setattr(oracle, "union_fill", lambda mask, order, valid, group: orig(mask, order, valid, 2 * group))
     with pytest.raises(AssertionError):
         ts.test_union_fill_against_brute_force(2, False)
+
+
+# ------------------------------------------------------------------ fp8 ---
+
+import oracle.fp8 as f8        # noqa: E402
+import test_oracle_fp8 as tf   # noqa: E402
+
+
+def test_e4m3_exponent_bias_off_by_one_caught(monkeypatch):
+    orig = f8.e4m3_value
+    monkeypatch.setattr(f8, "e4m3_value", lambda c: orig(c) * 2.0)
+    with pytest.raises(AssertionError):
+        tf.test_e4m3_closed_form_codes()
+
+
+def test_e4m3_ties_away_from_zero_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(f8, "_round_half_even", lambda x: np.floor(x + 0.5))
+    with pytest.raises(AssertionError):
+        tf.test_quantize_hand_example(golden_dir)
+    with pytest.raises(AssertionError):
+        tf.test_e4m3_encode_matches_torch_rounding()
+
+
+def test_k_scaled_per_token_caught(monkeypatch):
+    def per_token(k, tile=f8.QUANT_TILE):
+        k = np.asarray(k, dtype=np.float64)
+        amax = np.abs(k).max(axis=-1)
+        return f8.quantize_groups(k, amax[..., None]), f8.group_factors(amax[:, :, ::tile])[1].astype(np.float32)
+    monkeypatch.setattr(f8, "quantize_k", per_token)
+    with pytest.raises(AssertionError):
+        tf.test_quantize_group_scaling_and_locality()
+
+
+def test_scale_inverted_caught(monkeypatch, golden_dir):
+    orig = f8.group_factors
+    monkeypatch.setattr(f8, "group_factors", lambda a: (orig(a)[0], orig(a)[0]))
+    with pytest.raises(AssertionError):
+        tf.test_quantize_hand_example(golden_dir)
