@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define ATTN_TBS_ABI_VERSION 3
+#define ATTN_TBS_ABI_VERSION 4
 
 /* Status codes. */
 #define ATTN_OK            0
@@ -300,6 +300,53 @@ int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* 
  * key block size does not enter the dense result. */
 int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                        void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* FP8 (E4M3) path
+ * ---------------
+ * Source: ParaAttention/HunyuanVideo post (WaveSpeed), section on FP8 dynamic
+ * quantisation: activations are quantised to FP8 at run time so that the
+ * products run on 8-bit matrix units.  The post fixes neither format nor
+ * granularity; this library takes OCP E4M3 (largest magnitude 448, round to
+ * nearest even), one scale per query token and one per 64-token tile of keys,
+ * and quantises only Q and K: the S = Q K^T product runs on gfx950's fp8
+ * matrix instructions while V, the softmax weights (bf16) and O stay as in
+ * attn_sparse_fwd.  The result is, up to fp32 rounding, exact attention on
+ * the dequantised Q and K: q_t = code * q_scale[t], k_s = code * k_scale[s/64].
+ * These calls take bf16 problems with head_dim 128 (ATTN_E_UNSUPPORTED
+ * otherwise); routing (attn_route) keeps reading the bf16 Q and K. */
+
+/* Dynamic E4M3 quantisation of Q and K.  For each group (a query token's d
+ * values; the d values of up to 64 tokens of keys, tile tau holding tokens
+ * 64 tau .. min(64 tau + 64, N) - 1 of a (b, h)) with largest magnitude a,
+ * in correctly rounded fp32: inv = 448 / a, code = E4M3(clamp(x * inv, -448,
+ * 448)) rounded to nearest even (the sign bit kept, so a negative value that
+ * rounds to zero gives 0x80), scale = a / 448; a = 0 gives scale 0 and zero
+ * codes.
+ *
+ *   q, k     [B,H,N,128] bf16, read only.
+ *   q8, k8   [B,H,N,128] uint8 out: E4M3 codes, 16-byte aligned.
+ *   q_scale  [B,H,N] float out: per-token Q scales.
+ *   k_scale  [B,H,ceil(N/64)] float out: per-tile K scales.
+ * One kernel launch; reads Q and K once. */
+int32_t attn_quantize_qk_fp8(const attn_problem* problem, const void* q, const void* k, uint8_t* q8,
+                             float* q_scale, uint8_t* k8, float* k_scale, void* stream);
+
+/* attn_sparse_fwd with Q and K as E4M3 codes and scales (from
+ * attn_quantize_qk_fp8).  The logit of query t and key s is
+ * scale * q_scale[t] * k_scale[s/64] * sum_c code_q[t][c] * code_k[s][c], the
+ * sum of code products accumulated in fp32 by the matrix unit; everything
+ * else (lists, work list, masks, causal rule, outputs, workspace) is as in
+ * attn_sparse_fwd.  v and o are bf16. */
+int32_t attn_sparse_fwd_fp8(const attn_problem* problem, const uint8_t* q8, const float* q_scale,
+                            const uint8_t* k8, const float* k_scale, const void* v, const int32_t* row_cnt,
+                            const int32_t* row_idx, const int32_t* work_list, void* o, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* attn_dense_fwd with fp8 Q and K (same logits as attn_sparse_fwd_fp8); equals
+ * attn_sparse_fwd_fp8 with every (eligible) block selected, bit for bit. */
+int32_t attn_dense_fwd_fp8(const attn_problem* problem, const uint8_t* q8, const float* q_scale,
+                           const uint8_t* k8, const float* k_scale, const void* v, void* o, float* lse, void* ws,
+                           size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

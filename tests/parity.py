@@ -22,7 +22,9 @@ O_TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
 LSE_TOL = {torch.bfloat16: 2e-3, torch.float32: 1e-4}
 
 
-def to64(t: torch.Tensor) -> np.ndarray:
+def to64(t) -> np.ndarray:
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64, copy=False)
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 

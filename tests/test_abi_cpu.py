@@ -21,7 +21,7 @@ WS = ctypes.c_void_p(0x20000)
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\S.*?\b(attn_[a-z_]+)\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\S.*?\b(attn_[a-z0-9_]+)\(", text, flags=re.M)))
 
 
 def test_exports_every_declared_symbol():
@@ -29,10 +29,11 @@ def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"attn_abi_version", "attn_last_error", "attn_workspace_bytes", "attn_num_workers",
                           "attn_group_size", "attn_route", "attn_schedule", "attn_augment", "attn_augment_union",
-                          "attn_sparse_fwd", "attn_dense_fwd"}
+                          "attn_sparse_fwd", "attn_dense_fwd", "attn_quantize_qk_fp8", "attn_sparse_fwd_fp8",
+                          "attn_dense_fwd_fp8"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 3
+    assert L.attn_abi_version() == 4
 
 
 def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0, key_block=0, reserved=0):
@@ -162,3 +163,30 @@ def test_augment_union_validation():
     assert L.attn_augment_union(ctypes.byref(p), D, ctypes.c_void_p(0x10002), D, D, None) == 1
     assert L.attn_augment_union(ctypes.byref(p), D, D, D, None, None) == 1
     assert L.attn_augment_union(ctypes.byref(_problem(N=64 * 1025)), D, D, D, D, None) == 2
+
+
+def test_fp8_validation():
+    L = tbs.lib()
+    D = ctypes.c_void_p(0x10000)
+    p = _problem()
+
+    def quant(pr=p, q=D, k=D, q8=D, qs=D, k8=D, ks=D):
+        return L.attn_quantize_qk_fp8(ctypes.byref(pr) if pr is not None else None, q, k, q8, qs, k8, ks, None)
+    assert quant(pr=None) == 1
+    assert quant(pr=_problem(d=64)) == 2 and "head_dim" in L.attn_last_error().decode()
+    assert quant(pr=_problem(dtype=1)) == 2
+    assert quant(q=None) == 1 and quant(k8=ctypes.c_void_p(0x10008)) == 1
+    assert quant(qs=None) == 1 and quant(ks=ctypes.c_void_p(0x10002)) == 1
+
+    def sfwd(pr=p, q8=D, qs=D, k8=D, ks=D, v=D, rc=D, ri=D, wl=None, o=D, lse=None, ws=WS, wsb=1 << 20):
+        return L.attn_sparse_fwd_fp8(ctypes.byref(pr), q8, qs, k8, ks, v, rc, ri, wl, o, lse, ws, wsb, None)
+    assert sfwd(pr=_problem(d=64)) == 2 and sfwd(pr=_problem(dtype=1)) == 2
+    assert sfwd(qs=None) == 1 and sfwd(ks=None) == 1 and sfwd(q8=ctypes.c_void_p(0x10004)) == 1
+    assert sfwd(rc=None) == 1 and sfwd(ri=ctypes.c_void_p(0x10002)) == 1 and sfwd(v=None) == 1
+    assert sfwd(wsb=16) == 3
+    assert sfwd(pr=_problem(N=64 * 2049)) == 2
+
+    def dfwd(pr=p, q8=D, qs=D, k8=D, ks=D, v=D, o=D, lse=None, ws=WS, wsb=1 << 20):
+        return L.attn_dense_fwd_fp8(ctypes.byref(pr), q8, qs, k8, ks, v, o, lse, ws, wsb, None)
+    assert dfwd(pr=_problem(d=64)) == 2 and dfwd(qs=None) == 1 and dfwd(o=None) == 1
+    assert dfwd(lse=ctypes.c_void_p(0x10001)) == 1 and dfwd(ws=None) == 3

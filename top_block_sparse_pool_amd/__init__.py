@@ -142,6 +142,12 @@ def lib() -> ctypes.CDLL:
     L.attn_augment.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_augment_union.restype = i32
     L.attn_augment_union.argtypes = [P, vp, vp, vp, vp, vp]
+    L.attn_quantize_qk_fp8.restype = i32
+    L.attn_quantize_qk_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_sparse_fwd_fp8.restype = i32
+    L.attn_sparse_fwd_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_dense_fwd_fp8.restype = i32
+    L.attn_dense_fwd_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -335,14 +341,80 @@ def dense_fwd(q, k, v, block: int, causal: bool = False, scale: Optional[float] 
     return o, lse
 
 
+FP8_TILE = 64   # keys per K scale of the fp8 path
+
+
+@dataclasses.dataclass
+class QuantizedQK:
+    q8: torch.Tensor        # [B,H,N,d] uint8 E4M3 codes
+    q_scale: torch.Tensor   # [B,H,N] float32, one per token
+    k8: torch.Tensor        # [B,H,N,d] uint8 E4M3 codes
+    k_scale: torch.Tensor   # [B,H,ceil(N/64)] float32, one per 64-token tile
+
+
+def quantize_qk_fp8(q: torch.Tensor, k: torch.Tensor, block: int = 64, out: Optional[QuantizedQK] = None,
+                    key_block: Optional[int] = None) -> QuantizedQK:
+    """attn_quantize_qk_fp8: E4M3 codes of Q (scale per token) and K (scale per 64-token tile)."""
+    _require_device(q, k)
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must share shape and dtype")
+    pr = make_problem(q, block, key_block=key_block)
+    B, H, N, d = q.shape
+    if out is None:
+        dev = q.device
+        out = QuantizedQK(torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+                          torch.empty((B, H, N), dtype=torch.float32, device=dev),
+                          torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+                          torch.empty((B, H, -(-N // FP8_TILE)), dtype=torch.float32, device=dev))
+    _check(lib().attn_quantize_qk_fp8(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(out.q8), _ptr(out.q_scale),
+                                      _ptr(out.k8), _ptr(out.k_scale), _stream()))
+    return out
+
+
+def _fp8_problem(qk: QuantizedQK, v: torch.Tensor, block: int, causal: bool, scale, flags, key_block):
+    _require_device(qk.q8, qk.q_scale, qk.k8, qk.k_scale, v)
+    if qk.q8.shape != v.shape or qk.k8.shape != v.shape:
+        raise ValueError("q8, k8 and v must share the shape [B, H, N, d]")
+    return make_problem(v, block, causal=causal, scale=scale, flags=flags, key_block=key_block)
+
+
+def sparse_fwd_fp8(qk: QuantizedQK, v, row_cnt, row_idx, block: int, work_list=None,
+                   scale: Optional[float] = None, ws: Optional[torch.Tensor] = None, o=None, lse=None,
+                   want_lse: bool = True, flags: int = 0, causal: bool = False, key_block: Optional[int] = None):
+    """attn_sparse_fwd_fp8: sparse_fwd with E4M3 Q and K (S = Q K^T on fp8 MFMA)."""
+    _require_device(row_cnt, row_idx, work_list)
+    pr = _fp8_problem(qk, v, block, causal, scale, flags, key_block)
+    o, lse = _out_tensors(v, o, lse, want_lse)
+    if ws is None:
+        ws = workspace(pr, v.device, OP_SPARSE_FWD)
+    _check(lib().attn_sparse_fwd_fp8(ctypes.byref(pr), _ptr(qk.q8), _ptr(qk.q_scale), _ptr(qk.k8), _ptr(qk.k_scale),
+                                     _ptr(v), _ptr(row_cnt), _ptr(row_idx), _ptr(work_list), _ptr(o), _ptr(lse),
+                                     _ptr(ws), ws.numel(), _stream()))
+    return o, lse
+
+
+def dense_fwd_fp8(qk: QuantizedQK, v, block: int, causal: bool = False, scale: Optional[float] = None,
+                  ws: Optional[torch.Tensor] = None, o=None, lse=None, want_lse: bool = True, flags: int = 0):
+    """attn_dense_fwd_fp8: dense (optionally causal) attention with E4M3 Q and K."""
+    pr = _fp8_problem(qk, v, block, causal, scale, flags, None)
+    o, lse = _out_tensors(v, o, lse, want_lse)
+    if ws is None:
+        ws = workspace(pr, v.device, OP_DENSE_FWD)
+    _check(lib().attn_dense_fwd_fp8(ctypes.byref(pr), _ptr(qk.q8), _ptr(qk.q_scale), _ptr(qk.k8), _ptr(qk.k_scale),
+                                    _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return o, lse
+
+
 def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] = None,
                      ws: Optional[torch.Tensor] = None, want_lse: bool = True,
                      head_window: Optional[int] = None, causal: bool = False, sasa: bool = False,
-                     num_workers: int = 0, key_block: Optional[int] = None):
+                     num_workers: int = 0, key_block: Optional[int] = None, fp8: bool = False):
     """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list).
 
     With sasa=True: route -> schedule with the LPT model -> augment -> schedule
-    again over the augmented counts -> sparse_fwd."""
+    again over the augmented counts -> sparse_fwd.  With fp8=True Q and K are
+    quantised to E4M3 (quantize_qk_fp8) after routing and the forward is
+    sparse_fwd_fp8; routing reads the bf16 Q and K either way."""
     pr = make_problem(q, block, causal=causal, scale=scale, key_block=key_block)
     if ws is None:
         ws = workspace(pr, q.device)
@@ -352,12 +424,18 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
                                              num_workers=num_workers, lpt=True)
         augment(pr, r, worker_of, worker_load, ws, want_added=False)
     wl = schedule(pr, r.row_cnt, ws, head_window=head_window)
-    o, lse = sparse_fwd(q, k, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
-                        want_lse=want_lse, causal=causal, key_block=key_block)
+    if fp8:
+        qk = quantize_qk_fp8(q, k, block, key_block=key_block)
+        o, lse = sparse_fwd_fp8(qk, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
+                                want_lse=want_lse, causal=causal, key_block=key_block)
+    else:
+        o, lse = sparse_fwd(q, k, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
+                            want_lse=want_lse, causal=causal, key_block=key_block)
     return o, lse, r, wl
 
 
 __all__ = [
     "lib", "AttnError", "Problem", "Route", "make_problem", "default_head_window", "workspace", "workspace_bytes", "num_workers",
     "route", "schedule", "augment", "augment_union", "sparse_fwd", "dense_fwd", "sparse_attention", "LIB_PATH",
+    "QuantizedQK", "quantize_qk_fp8", "sparse_fwd_fp8", "dense_fwd_fp8", "FP8_TILE",
 ]

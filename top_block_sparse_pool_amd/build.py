@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libattn_tbs.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["csrc/abi.cpp", "csrc/router.hip", "csrc/schedule.hip", "csrc/augment.hip", "csrc/flash_fwd.hip"]
+SOURCES = ["csrc/abi.cpp", "csrc/router.hip", "csrc/schedule.hip", "csrc/augment.hip", "csrc/quant.hip",
+           "csrc/flash_fwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [

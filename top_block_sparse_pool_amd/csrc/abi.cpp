@@ -272,10 +272,12 @@ TBS_EXPORT int32_t attn_augment_union(const attn_problem* problem, uint8_t* mask
 namespace {
 int32_t run_fwd(const tbs::Shape& s, int mode, const void* q, const void* k, const void* v,
                 const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list, void* o, float* lse,
-                void* ws, size_t ws_bytes, void* stream) {
+                void* ws, size_t ws_bytes, void* stream, const float* q_scale = nullptr,
+                const float* k_scale = nullptr) {
   int32_t st;
-  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
-      (st = check_tensor(o, "o")))
+  const bool fp8 = q_scale != nullptr;
+  if ((st = check_tensor(q, fp8 ? "q8" : "q")) || (st = check_tensor(k, fp8 ? "k8" : "k")) ||
+      (st = check_tensor(v, "v")) || (st = check_tensor(o, "o")))
     return st;
   if (lse && !aligned(lse, 4)) return fail(ATTN_E_INVALID, "lse is not 4-byte aligned");
   if ((st = check_ws(ws, ws_bytes, fwd_bytes(s)))) return st;
@@ -292,7 +294,10 @@ int32_t run_fwd(const tbs::Shape& s, int mode, const void* q, const void* k, con
   a.prof = (s.flags & ATTN_FLAG_PROFILE_WORKERS)
                ? reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(ws) + tbs::kCtrlBytes)
                : nullptr;
-  if (a.prof && tbs::fwd_workers(s, mode) > 4096)
+  a.fp8 = fp8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  if (a.prof && tbs::fwd_workers(s, mode, fp8) > 4096)
     return fail(ATTN_E_UNSUPPORTED, "worker profiling supports at most 4096 workers");
   hipError_t e = tbs::launch_fwd(s, mode, a, static_cast<hipStream_t>(stream));
   return device_status(e, "attention kernel launch");
@@ -321,4 +326,61 @@ TBS_EXPORT int32_t attn_dense_fwd(const attn_problem* problem, const void* q, co
   if (st != ATTN_OK) return st;
   return run_fwd(s, s.causal ? tbs::kCausal : tbs::kDense, q, k, v, nullptr, nullptr, nullptr, o, lse, ws,
                  ws_bytes, stream);
+}
+
+namespace {
+// The fp8 calls take bf16 problems with head_dim 128.
+int32_t check_fp8_problem(const tbs::Shape& s, const char* who) {
+  if (s.dtype != ATTN_DTYPE_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: dtype must be ATTN_DTYPE_BF16", who);
+  if (s.d != 128) return fail(ATTN_E_UNSUPPORTED, "%s: head_dim %d unsupported (128)", who, s.d);
+  return ATTN_OK;
+}
+
+int32_t check_scales(const float* q_scale, const float* k_scale) {
+  if (!q_scale || !aligned(q_scale, 4)) return fail(ATTN_E_INVALID, "q_scale is NULL or not 4-byte aligned");
+  if (!k_scale || !aligned(k_scale, 4)) return fail(ATTN_E_INVALID, "k_scale is NULL or not 4-byte aligned");
+  return ATTN_OK;
+}
+}  // namespace
+
+TBS_EXPORT int32_t attn_quantize_qk_fp8(const attn_problem* problem, const void* q, const void* k, uint8_t* q8,
+                                        float* q_scale, uint8_t* k8, float* k_scale, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if ((st = check_fp8_problem(s, "attn_quantize_qk_fp8"))) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(q8, "q8")) ||
+      (st = check_tensor(k8, "k8")) || (st = check_scales(q_scale, k_scale)))
+    return st;
+  hipError_t e = tbs::launch_quantize_qk(s, q, k, q8, q_scale, k8, k_scale, static_cast<hipStream_t>(stream));
+  return device_status(e, "attn_quantize_qk_fp8 launch");
+}
+
+TBS_EXPORT int32_t attn_sparse_fwd_fp8(const attn_problem* problem, const uint8_t* q8, const float* q_scale,
+                                       const uint8_t* k8, const float* k_scale, const void* v,
+                                       const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
+                                       void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if ((st = check_fp8_problem(s, "attn_sparse_fwd_fp8"))) return st;
+  if (s.nbk > kMaxSparseBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd_fp8: %d key blocks per sequence exceed %d", s.nbk,
+                kMaxSparseBlocks);
+  if ((st = check_scales(q_scale, k_scale)) || (st = check_i32(row_cnt, "row_cnt", false)) ||
+      (st = check_i32(row_idx, "row_idx", false)) || (st = check_i32(work_list, "work_list", true)))
+    return st;
+  return run_fwd(s, s.causal ? tbs::kSparseCausal : tbs::kSparse, q8, k8, v, row_cnt, row_idx, work_list, o, lse,
+                 ws, ws_bytes, stream, q_scale, k_scale);
+}
+
+TBS_EXPORT int32_t attn_dense_fwd_fp8(const attn_problem* problem, const uint8_t* q8, const float* q_scale,
+                                      const uint8_t* k8, const float* k_scale, const void* v, void* o, float* lse,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if ((st = check_fp8_problem(s, "attn_dense_fwd_fp8")) || (st = check_scales(q_scale, k_scale))) return st;
+  return run_fwd(s, s.causal ? tbs::kCausal : tbs::kDense, q8, k8, v, nullptr, nullptr, nullptr, o, lse, ws,
+                 ws_bytes, stream, q_scale, k_scale);
 }

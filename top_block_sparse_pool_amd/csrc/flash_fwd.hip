@@ -42,6 +42,8 @@
 // tiles; weights stay fp32.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -61,6 +63,9 @@ struct FwdParams {
   const int32_t* work_list;
   uint32_t* ctrl;
   unsigned long long* prof;
+  const float* q_scale;   // fp8 path: per-token Q scales [BH, N]
+  const float* k_scale;   // fp8 path: per-64-key-tile K scales [BH, nkt]
+  int nkt;                // fp8 path: 64-key tiles per (b, h)
   int BH;
   int N;
   int nb;             // query blocks per (b, h)
@@ -297,19 +302,22 @@ struct GroupInfo {
 // must land by the end of step 2t+1, two steps ahead of their first use.
 constexpr int kWaves = 8;
 
-template <int D, int BQ, int BK, int MODE>
+template <int D, int BQ, int BK, int MODE, bool F8>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_bf16_pp(
     FwdParams p) {
   constexpr int G = 256 / BQ;           // query blocks per work item
   constexpr int NWB = BQ / 32;          // waves per member block
   constexpr int NT = kWaves * 64;
-  constexpr int ROWB = D * 2;
+  constexpr int ROWB = D * 2;           // bytes of a V row (and of a bf16 K or Q row)
   constexpr int TILEB = kKeyTile * ROWB;
+  constexpr int ROWK = F8 ? D : ROWB;   // bytes of a K row
+  constexpr int TILEK = kKeyTile * ROWK;
   constexpr int SPB = BK / kKeyTile;    // key tiles per key block (BK keys)
-  constexpr int NS = D / 16;            // k-steps of S^T
+  constexpr int NS = F8 ? D / 64 : D / 16;   // k-steps of S^T
   constexpr int NO = D / 32;            // 32-dim tiles of O^T
+  static_assert(!F8 || D == 128, "the fp8 path takes head_dim 128");
   // LDS: K stage 0, K stage 1, V stage 0, V stage 1.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILEK + 2 * TILEB];
   __shared__ unsigned s_bm[fwd_listed(MODE) ? G * kMaxListWords : 1];
   __shared__ unsigned short s_lj[fwd_listed(MODE) ? kMaxListBlocks : 1];
   __shared__ unsigned char s_lm[fwd_listed(MODE) ? kMaxListBlocks : 1];
@@ -331,8 +339,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const unsigned char* qg_all = static_cast<const unsigned char*>(p.q);
   const unsigned char* kg_all = static_cast<const unsigned char*>(p.k);
   const unsigned char* vg_all = static_cast<const unsigned char*>(p.v);
-  TileLoader<D, kWaves> loader;
+  TileLoader<D, kWaves> loader;        // V tiles, and K tiles of the bf16 path
   loader.init(wave, lane);
+  TileLoader<F8 ? D / 2 : D, kWaves> loader8;   // K tiles of the fp8 path (D-byte rows)
+  if (F8) loader8.init(wave, lane);
   const int krow0 = swap_bits23(col);   // K operand row: bits 2 and 3 swapped
 
   // Lane byte offsets of the MFMA operands inside a K or V tile.  K (A
@@ -343,9 +353,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // chunk swizzle depends on the low four row bits only, which neither the
   // half (+32 rows) nor the key step (+16 rows) changes, so both are
   // immediate offsets.
-  unsigned koff[NS];
+  //
+  // fp8 path: K (A operand of the 32x32x64 product) holds one byte per
+  // element; for k-step s lane (h, col) supplies the 32 bytes of dims
+  // 64s + 32h .. +31 (chunks 4s + 2h and 4s + 2h + 1 of its row), and Q^T
+  // (B operand) the same dims of its query.  A and B share the assignment of
+  // dims to (lane half, byte), so the product sums every dim once.
+  unsigned koff[F8 ? 2 * NS : NS];
+  if (F8) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) koff[s] = krow0 * ROWB + (((2 * s + h) ^ chunk_swz<D>(krow0)) * 16);
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        koff[2 * s + e] = krow0 * ROWK + (((4 * s + 2 * h + e) ^ chunk_swz<D / 2>(krow0)) * 16);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = krow0 * ROWB + (((2 * s + h) ^ chunk_swz<D>(krow0)) * 16);
+  }
   unsigned voff[NO][2];
 #pragma unroll
   for (int mo = 0; mo < NO; ++mo)
@@ -367,7 +391,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     GroupInfo<BQ, G, MODE> gi;
     gi.decode(p, qpos);
     const long long head_off = static_cast<long long>(gi.bh) * p.N * ROWB;
-    const unsigned char* kg = kg_all + head_off;
+    const unsigned char* kg = kg_all + static_cast<long long>(gi.bh) * p.N * ROWK;
     const unsigned char* vg = vg_all + head_off;
     const bool active = member < gi.gsz;
     const int qblk = gi.i0 + member;
@@ -447,13 +471,34 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       return true;
     };
 
-    // Q^T as B operand: lane (h, col) holds Q[qrow][16s + 8h .. +7].
-    bf16x8 qf[NS];
+    // Q^T as B operand: lane (h, col) holds Q[qrow][16s + 8h .. +7] (bf16)
+    // or the codes of Q[qrow][64s + 32h .. +31] (fp8), with the row's scale.
+    using QFrag = typename std::conditional<F8, i32x8, bf16x8>::type;
+    QFrag qf[NS];
+    float q_sc = 1.f;
     {
-      const unsigned char* qr = qg_all + head_off + static_cast<long long>(min(qrow, p.N - 1)) * ROWB;
+      const long long qtok = static_cast<long long>(gi.bh) * p.N + min(qrow, p.N - 1);
+      if constexpr (F8) {
+        const unsigned char* qr = qg_all + qtok * D;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + (16 * s + 8 * h) * 2);
+        for (int s = 0; s < NS; ++s) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(qr + 64 * s + 32 * h);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(qr + 64 * s + 32 * h + 16);
+          qf[s] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        q_sc = p.q_scale[qtok];
+      } else {
+        const unsigned char* qr = qg_all + qtok * ROWB;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + (16 * s + 8 * h) * 2);
+      }
     }
+    // fp8 path: tile scale of the K tile whose S product this wave computed
+    // last, read with a scalar load in M(t) and used in V(t).
+    float k_sc = 1.f;
+    const float TBS_CONST* ksc_head =
+        F8 ? (const float TBS_CONST*)(p.k_scale) + static_cast<long long>(__builtin_amdgcn_readfirstlane(gi.bh)) * p.nkt
+           : nullptr;
 
     f32x16 acc_o[NO];
 #pragma unroll
@@ -478,11 +523,32 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       constexpr int VS = decltype(vs)::value;
       const bool s_on = t < nt && tile_mine(t);
       const bool pv_on = t >= 1 && t - 1 < nt && tile_mine(t - 1);
-      const TBS_LDS unsigned char* lk = lds + KS * TILEB;
-      const TBS_LDS unsigned char* lv = lds + (2 + VS) * TILEB;
+      const TBS_LDS unsigned char* lk = lds + KS * TILEK;
+      const TBS_LDS unsigned char* lv = lds + 2 * TILEK + VS * TILEB;
       constexpr int NF = 2 * NS;          // fragments of each product
       constexpr int KP = TBS_KPF < NF ? TBS_KPF : NF;
-      if (s_on) {
+      if constexpr (F8) {
+        if (s_on) {
+          k_sc = ksc_head[tile_key0(t) / kKeyTile];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+          // All NF fragments (two 16-byte reads each) are read up front.
+          i32x8 kr[NF];
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const TBS_LDS unsigned char* row = lk + (f / NS) * 32 * ROWK;
+            const u32x4 lo = *(const TBS_LDS u32x4*)(row + koff[2 * (f % NS)]);
+            const u32x4 hi = *(const TBS_LDS u32x4*)(row + koff[2 * (f % NS) + 1]);
+            kr[f] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            sacc[f / NS] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[f], qf[f % NS], sacc[f / NS], 0, 0, 0, 0,
+                                                                           0, 0);
+        }
+      } else if (s_on) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -573,6 +639,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       float mx = max3f(m4[0], m4[1], max3f(m4[2], m4[3], m4[3]));
       const float mo32 = xor32(mx);
       mx = max3f(mx, mo32, mo32);
+      // fp8 path: accumulators hold dot products of codes; f = q_sc * k_sc
+      // converts them to dot products of the dequantised rows (f > 0, so the
+      // maximum carries over).  The floors keep 0 * -inf out of masked keys
+      // when a scale is 0, in which case the codes and accumulators are 0.
+      float sl2t = sl2;
+      if constexpr (F8) {
+        constexpr float kMinNormal = 1.17549435e-38f;
+        mx *= fmaxf(q_sc * k_sc, kMinNormal);
+        sl2t = fmaxf(sl2 * fmaxf(q_sc * k_sc, kMinNormal), kMinNormal);
+      }
       // The reference maximum of a row moves only when the tile maximum
       // exceeds it by more than 2^8 in weight (any reference gives the exact
       // result; the bound keeps every weight <= 2^8).  Lanes l and l^32 hold
@@ -599,7 +675,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2, -m_b));
+            const float pv = fast_exp2(fmaf(sacc[mt][8 * t2 + e], sl2t, -m_b));
             ls[e & 3] += pv;
             pb[mt][t2][e] = static_cast<__bf16>(pv);
           }
@@ -614,10 +690,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
     // Copies started at global step 2t: K(t+1) into K stage (t+1)&1 and
     // V(t) into V stage t&1 (P = t&1); every wave issues its share.
+    auto issue_k = [&](int key0, TBS_LDS unsigned char* dst) __attribute__((always_inline)) {
+      if constexpr (F8)
+        loader8.issue_one(kg, key0, p.N, dst);
+      else
+        loader.issue_one(kg, key0, p.N, dst);
+    };
     auto issue = [&](auto pp, int t) __attribute__((always_inline)) {
       constexpr int P = decltype(pp)::value;
-      if (t + 1 < nt) loader.issue_one(kg, tile_key0(t + 1), p.N, lds + (P ^ 1) * TILEB);
-      if (t < nt) loader.issue_one(vg, tile_key0(t), p.N, lds + (2 + P) * TILEB);
+      if (t + 1 < nt) issue_k(tile_key0(t + 1), lds + (P ^ 1) * TILEK);
+      if (t < nt) loader.issue_one(vg, tile_key0(t), p.N, lds + 2 * TILEK + P * TILEB);
     };
 
     // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(nt), one
@@ -629,7 +711,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // the barrier that opens step 2t+2.  The loop is unrolled twice so the
     // LDS stages of K(t) and V(t-1) are compile-time constants.
     if (nt > 0) {
-      loader.issue_one(kg, tile_key0(0), p.N, lds);
+      issue_k(tile_key0(0), lds);
       wait_vmem();
       step_barrier();
       if (grp == 1) {
@@ -851,44 +933,63 @@ constexpr int group_for(int dtype, int block) { return dtype == 0 ? 256 / block 
 
 // Every variant is instantiated explicitly: referencing a kernel template
 // only through a function-pointer table does not always emit its host stub.
-#define TBS_INSTANTIATE(D, BQ, BKX)                                                    \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kSparse>(FwdParams);           \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kDense>(FwdParams);            \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kCausal>(FwdParams);           \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kSparseCausal>(FwdParams);     \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, BKX, kSparse>(FwdParams);          \
-  template __global__ void flash_fwd_bf16_pp<D, BQ, BKX, kSparseCausal>(FwdParams);    \
+#define TBS_INSTANTIATE(D, BQ, BKX, F8)                                                    \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kSparse, F8>(FwdParams);           \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kDense, F8>(FwdParams);            \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kCausal, F8>(FwdParams);           \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BQ, kSparseCausal, F8>(FwdParams);     \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BKX, kSparse, F8>(FwdParams);          \
+  template __global__ void flash_fwd_bf16_pp<D, BQ, BKX, kSparseCausal, F8>(FwdParams);
+#define TBS_INSTANTIATE_F32(D, BQ, BKX)                                                \
   template __global__ void flash_fwd_f32<D, BQ, BQ, kSparse>(FwdParams);               \
   template __global__ void flash_fwd_f32<D, BQ, BQ, kDense>(FwdParams);                \
   template __global__ void flash_fwd_f32<D, BQ, BQ, kCausal>(FwdParams);               \
   template __global__ void flash_fwd_f32<D, BQ, BQ, kSparseCausal>(FwdParams);         \
   template __global__ void flash_fwd_f32<D, BQ, BKX, kSparse>(FwdParams);              \
   template __global__ void flash_fwd_f32<D, BQ, BKX, kSparseCausal>(FwdParams);
-TBS_INSTANTIATE(128, 64, 128)
-TBS_INSTANTIATE(128, 128, 64)
-TBS_INSTANTIATE(64, 64, 128)
-TBS_INSTANTIATE(64, 128, 64)
+TBS_INSTANTIATE(128, 64, 128, false)
+TBS_INSTANTIATE(128, 128, 64, false)
+TBS_INSTANTIATE(64, 64, 128, false)
+TBS_INSTANTIATE(64, 128, 64, false)
+TBS_INSTANTIATE(128, 64, 128, true)
+TBS_INSTANTIATE(128, 128, 64, true)
+TBS_INSTANTIATE_F32(128, 64, 128)
+TBS_INSTANTIATE_F32(128, 128, 64)
+TBS_INSTANTIATE_F32(64, 64, 128)
+TBS_INSTANTIATE_F32(64, 128, 64)
 #undef TBS_INSTANTIATE
+#undef TBS_INSTANTIATE_F32
 
 // Key blocks enter only the listed modes; dense and causal take BK = BQ.
+// Element kinds: 0 bf16, 1 fp32, 2 bf16 with fp8 Q and K (head_dim 128).
 template <int D, int BQ, int BK>
-KernelFn pick_mode(int dtype, int mode) {
-  static const KernelFn bf16_fns[4] = {flash_fwd_bf16_pp<D, BQ, BK, kSparse>, flash_fwd_bf16_pp<D, BQ, BQ, kDense>,
-                                       flash_fwd_bf16_pp<D, BQ, BQ, kCausal>,
-                                       flash_fwd_bf16_pp<D, BQ, BK, kSparseCausal>};
+KernelFn pick_mode(int kind, int mode) {
+  static const KernelFn bf16_fns[4] = {
+      flash_fwd_bf16_pp<D, BQ, BK, kSparse, false>, flash_fwd_bf16_pp<D, BQ, BQ, kDense, false>,
+      flash_fwd_bf16_pp<D, BQ, BQ, kCausal, false>, flash_fwd_bf16_pp<D, BQ, BK, kSparseCausal, false>};
   static const KernelFn f32_fns[4] = {flash_fwd_f32<D, BQ, BK, kSparse>, flash_fwd_f32<D, BQ, BQ, kDense>,
                                       flash_fwd_f32<D, BQ, BQ, kCausal>, flash_fwd_f32<D, BQ, BK, kSparseCausal>};
-  return dtype == 0 ? bf16_fns[mode] : f32_fns[mode];
+  if (kind == 2) {
+    if constexpr (D == 128) {
+      static const KernelFn f8_fns[4] = {
+          flash_fwd_bf16_pp<D, BQ, BK, kSparse, true>, flash_fwd_bf16_pp<D, BQ, BQ, kDense, true>,
+          flash_fwd_bf16_pp<D, BQ, BQ, kCausal, true>, flash_fwd_bf16_pp<D, BQ, BK, kSparseCausal, true>};
+      return f8_fns[mode];
+    }
+    return nullptr;
+  }
+  return kind == 0 ? bf16_fns[mode] : f32_fns[mode];
 }
 
 template <int D>
-KernelFn pick_blocks(const Shape& s, int mode) {
-  if (s.block == 128) return s.kb == 128 ? pick_mode<D, 128, 128>(s.dtype, mode) : pick_mode<D, 128, 64>(s.dtype, mode);
-  return s.kb == 128 ? pick_mode<D, 64, 128>(s.dtype, mode) : pick_mode<D, 64, 64>(s.dtype, mode);
+KernelFn pick_blocks(const Shape& s, int kind, int mode) {
+  if (s.block == 128) return s.kb == 128 ? pick_mode<D, 128, 128>(kind, mode) : pick_mode<D, 128, 64>(kind, mode);
+  return s.kb == 128 ? pick_mode<D, 64, 128>(kind, mode) : pick_mode<D, 64, 64>(kind, mode);
 }
 
-KernelFn pick_kernel(const Shape& s, int mode) {
-  return s.d == 128 ? pick_blocks<128>(s, mode) : pick_blocks<64>(s, mode);
+KernelFn pick_kernel(const Shape& s, int mode, bool fp8) {
+  const int kind = fp8 ? 2 : s.dtype;
+  return s.d == 128 ? pick_blocks<128>(s, kind, mode) : pick_blocks<64>(s, kind, mode);
 }
 
 }  // namespace
@@ -907,8 +1008,9 @@ long long work_items(const Shape& s) {
   return static_cast<long long>(s.B) * s.H * ((s.nb + G - 1) / G);
 }
 
-int fwd_workers(const Shape& s, int mode) {
-  KernelFn fn = pick_kernel(s, mode);
+int fwd_workers(const Shape& s, int mode, bool fp8) {
+  KernelFn fn = pick_kernel(s, mode, fp8);
+  if (!fn) return 0;
   const int threads = fwd_threads(s);
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0) !=
@@ -932,6 +1034,9 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
   p.work_list = a.work_list;
   p.ctrl = a.ctrl;
   p.prof = reinterpret_cast<unsigned long long*>(a.prof);
+  p.q_scale = a.q_scale;
+  p.k_scale = a.k_scale;
+  p.nkt = (s.N + kKeyTile - 1) / kKeyTile;
   p.BH = s.B * s.H;
   p.N = s.N;
   p.nb = s.nb;
@@ -941,8 +1046,9 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
   p.U = static_cast<int>(work_items(s));
   p.scale = static_cast<float>(s.scale);
   p.scale_log2 = static_cast<float>(s.scale * 1.4426950408889634);
-  const int grid = fwd_workers(s, mode);
-  KernelFn fn = pick_kernel(s, mode);
+  const int grid = fwd_workers(s, mode, a.fp8);
+  KernelFn fn = pick_kernel(s, mode, a.fp8);
+  if (!fn || grid < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(fwd_threads(s)), 0, stream, p);
   return hipGetLastError();
 }

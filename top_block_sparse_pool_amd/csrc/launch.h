@@ -59,6 +59,12 @@ hipError_t launch_augment(const Shape& s, const double* block_prob, const int32_
                           const int64_t* worker_load, int num_workers, uint8_t* mask, int32_t* row_cnt,
                           int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, hipStream_t stream);
 
+// FP8 (E4M3) quantisation of Q (per token) and K (per 64-token tile) for
+// the fp8 attention path; bf16 inputs, head_dim 128.
+int quant_tiles(const Shape& s);
+hipError_t launch_quantize_qk(const Shape& s, const void* q, const void* k, uint8_t* q8, float* q_scale, uint8_t* k8,
+                              float* k_scale, hipStream_t stream);
+
 // Attention forward.
 struct FwdArgs {
   const void* q;
@@ -71,11 +77,16 @@ struct FwdArgs {
   const int32_t* work_list;
   uint32_t* ctrl;
   uint64_t* prof;
+  // fp8 path: q and k hold E4M3 codes ([B,H,N,d] bytes) with per-token Q
+  // scales [B,H,N] and per-64-key-tile K scales [B,H,ceil(N/64)].
+  bool fp8 = false;
+  const float* q_scale = nullptr;
+  const float* k_scale = nullptr;
 };
 // Query blocks per work item (G) and number of work items B*H*ceil(nb/G).
 int group_size(const Shape& s);
 long long work_items(const Shape& s);
-int fwd_workers(const Shape& s, int mode);
+int fwd_workers(const Shape& s, int mode, bool fp8 = false);
 hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t stream);
 
 int device_cu_count();
