@@ -13,7 +13,9 @@ roofline block reports the attention kernel alone against the bf16 MFMA
 peak.  The CPU baseline is the fp64 oracle timed on a bounded sample of the
 same workload on this machine's host cores.  --causal runs the same workload
 with causal routing and causal attention (executed FLOPs then count the
-allowed token pairs of diagonal blocks only).
+allowed token pairs of diagonal blocks only).  --fp8 quantises Q and K to
+E4M3 in the step (attn_quantize_qk_fp8) and runs attn_sparse_fwd_fp8; its
+roofline peak is the mix of the fp8 rate (S) and the bf16 rate (P V).
 """
 from __future__ import annotations
 
@@ -30,6 +32,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+# The fp8 kernel runs half of its products (S = K Q^T) at the fp8 rate and
+# half (O += V^T P^T) at the bf16 rate: its peak is the harmonic mix.
+FP8_QK_PEAK_TFLOPS = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
 METRIC = "executed TFLOP/s + ms/call, top-p sparse attn fwd, N=32760 H=40 d=128 bf16"
 KERNEL_SOURCES = ("top_block_sparse_pool_amd/csrc/flash_fwd.hip", "top_block_sparse_pool_amd/csrc/device_common.h")
 TRAFFIC_SUMMARY = "profiles/flash_fwd_bf16_sparse_video-32k_traffic.md"
@@ -96,6 +102,8 @@ def parse():
                     help="slack-aware augmentation in the step: LPT model, attn_augment, a second schedule")
     ap.add_argument("--sasa-union", action="store_true",
                     help="slack filling inside work items in the step (attn_augment_union after the route)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 path: Q and K quantised to E4M3 in the step, S = K Q^T on fp8 MFMA")
     ap.add_argument("--head-window", type=int, default=None, help="heads per scheduling window (default: library's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -213,6 +221,24 @@ def main():
         tbs.augment(pr, route_out, worker_of, worker_load, ws, added=added)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    fp8 = bool(args.fp8)
+    qk8 = None
+    if fp8:
+        qk8 = tbs.QuantizedQK(torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+                              torch.empty((B, H, N), dtype=torch.float32, device=dev),
+                              torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+                              torch.empty((B, H, -(-N // tbs.FP8_TILE)), dtype=torch.float32, device=dev))
+
+    def fwd(row_cnt, row_idx, wl, ws_=None, o_=None, lse_=None, flags=0):
+        ws_ = ws if ws_ is None else ws_
+        o_ = o if o_ is None else o_
+        lse_ = lse if lse_ is None else lse_
+        if fp8:
+            tbs.sparse_fwd_fp8(qk8, v, row_cnt, row_idx, blk, work_list=wl, ws=ws_, o=o_, lse=lse_, flags=flags,
+                               causal=causal, key_block=kb)
+        else:
+            tbs.sparse_fwd(q, k, v, row_cnt, row_idx, blk, work_list=wl, ws=ws_, o=o_, lse=lse_, flags=flags,
+                           causal=causal, key_block=kb)
 
     def step(ev=None):
         if ev is not None:
@@ -227,15 +253,18 @@ def main():
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         if ev is not None:
             ev[2].record()
-        tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, blk, work_list=work_list, ws=ws,
-                       o=o, lse=lse, causal=causal, key_block=kb)
+        if fp8:
+            tbs.quantize_qk_fp8(q, k, blk, out=qk8, key_block=kb)
         if ev is not None:
             ev[3].record()
+        fwd(route_out.row_cnt, route_out.row_idx, work_list)
+        if ev is not None:
+            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -244,8 +273,9 @@ def main():
     wall = time.perf_counter() - t0
     t_route = np.array([e[0].elapsed_time(e[1]) for e in events])
     t_sched = np.array([e[1].elapsed_time(e[2]) for e in events])
-    t_fwd = np.array([e[2].elapsed_time(e[3]) for e in events])
-    t_step = np.array([e[0].elapsed_time(e[3]) for e in events])
+    t_quant = np.array([e[2].elapsed_time(e[3]) for e in events])
+    t_fwd = np.array([e[3].elapsed_time(e[4]) for e in events])
+    t_step = np.array([e[0].elapsed_time(e[4]) for e in events])
 
     mask = route_out.mask.cpu().numpy()
     flops = executed_flops(mask, N, blk, d, causal, kb)
@@ -278,8 +308,7 @@ def main():
     # measured per-workgroup busy time of the persistent kernel
     prp = tbs.make_problem(q, blk, causal=causal, flags=tbs.FLAG_PROFILE_WORKERS, key_block=kb)
     wsp = tbs.workspace(prp, dev)
-    tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, blk, work_list=work_list, ws=wsp, o=o,
-                   lse=lse, flags=tbs.FLAG_PROFILE_WORKERS, causal=causal, key_block=kb)
+    fwd(route_out.row_cnt, route_out.row_idx, work_list, ws_=wsp, flags=tbs.FLAG_PROFILE_WORKERS)
     torch.cuda.synchronize()
     nw = tbs.num_workers(prp, tbs.OP_SPARSE_FWD)
     stamps = wsp[256:256 + 16 * nw].view(torch.int64).view(nw, 2).cpu().numpy()
@@ -296,13 +325,11 @@ def main():
     lif["longest_first_lpt_one_window"] = float(lp.max() / lp.mean())
 
     def time_fwd(wl, reps=3):
-        tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, blk, work_list=wl, ws=ws, o=o, lse=lse,
-                       causal=causal, key_block=kb)
+        fwd(route_out.row_cnt, route_out.row_idx, wl)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            tbs.sparse_fwd(q, k, v, route_out.row_cnt, route_out.row_idx, blk, work_list=wl, ws=ws, o=o, lse=lse,
-                           causal=causal, key_block=kb)
+            fwd(route_out.row_cnt, route_out.row_idx, wl)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
@@ -315,14 +342,14 @@ def main():
     cold = None
     if args.cold_reps > 0:
         evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold_reps)]
+        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.cold_reps)]
         for rep_ in range(args.cold_reps):
             evict.fill_(rep_ & 0xff)
             step(ce[rep_])
         torch.cuda.synchronize()
         c_route = np.array([e[0].elapsed_time(e[1]) for e in ce])
-        c_fwd = np.array([e[2].elapsed_time(e[3]) for e in ce])
-        c_step = np.array([e[0].elapsed_time(e[3]) for e in ce])
+        c_fwd = np.array([e[3].elapsed_time(e[4]) for e in ce])
+        c_step = np.array([e[0].elapsed_time(e[4]) for e in ce])
         cold = {"reps": args.cold_reps, "evict_bytes": 512 << 20, "step_ms_mean": float(c_step.mean()),
                 "route_ms_mean": float(c_route.mean()), "sparse_fwd_ms_mean": float(c_fwd.mean()),
                 "sparse_fwd_tflops": flops / (c_fwd.mean() * 1e-3) / 1e12,
@@ -332,12 +359,18 @@ def main():
     dense = None
     if not args.no_dense:
         od = torch.empty_like(q)
-        tbs.dense_fwd(q, k, v, blk, causal=causal, ws=ws, o=od, want_lse=False)
+
+        def dense_call():
+            if fp8:
+                tbs.dense_fwd_fp8(qk8, v, blk, causal=causal, ws=ws, o=od, want_lse=False)
+            else:
+                tbs.dense_fwd(q, k, v, blk, causal=causal, ws=ws, o=od, want_lse=False)
+        dense_call()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.dense_reps):
-            tbs.dense_fwd(q, k, v, blk, causal=causal, ws=ws, o=od, want_lse=False)
+            dense_call()
         e1.record()
         torch.cuda.synchronize()
         t_dense = e0.elapsed_time(e1) / args.dense_reps
@@ -364,8 +397,7 @@ def main():
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         ev[3].record()
         for _ in range(3):
-            tbs.sparse_fwd(q, k, v, plain.row_cnt, plain.row_idx, blk, work_list=wl0, ws=ws, o=o, lse=lse,
-                           causal=causal, key_block=kb)
+            fwd(plain.row_cnt, plain.row_idx, wl0)
         ev[4].record()
         torch.cuda.synchronize()
         prob = route_out.block_prob.cpu().numpy()
@@ -396,8 +428,7 @@ def main():
         tbs.augment_union(pr, route_out)
         ev[1].record()
         for _ in range(3):
-            tbs.sparse_fwd(q, k, v, plain.row_cnt, plain.row_idx, blk, work_list=wl0, ws=ws, o=o, lse=lse,
-                           causal=causal, key_block=kb)
+            fwd(plain.row_cnt, plain.row_idx, wl0)
         ev[2].record()
         torch.cuda.synchronize()
         prob = route_out.block_prob.cpu().numpy()
@@ -418,6 +449,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed, causal, blk, kb)
 
+    peak = FP8_QK_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
     out = {
         "metric": METRIC,
         "value": value,
@@ -429,22 +461,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": ("fp8e4m3+bf16" if fp8 else "bf16") if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d, "block": blk,
                    "key_block": kb,
                    "top_p": w.top_p, "causal": causal, "sasa": bool(args.sasa), "sasa_union": bool(args.sasa_union),
+                   "fp8_qk": fp8,
                    "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
                    "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
         "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
                          "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),
+                         "quantize_mean": float(t_quant.mean()), "quantize_median": float(np.median(t_quant)),
                          "sparse_fwd_mean": float(t_fwd.mean()), "sparse_fwd_median": float(np.median(t_fwd)),
                          "step_events_mean": float(t_step.mean()), "step_events_median": float(np.median(t_step))},
         "sparse_fwd_tflops": fwd_tflops,
-        "roofline": {"bound": "mfma", "kernel": f"flash_fwd_bf16_pp ({'sparse causal' if causal else 'sparse'})",
-                     "achieved": fwd_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": fwd_tflops / BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(w.name + ("-causal" if causal else "")
+        "roofline": {"bound": "mfma",
+                     "kernel": f"flash_fwd_bf16_pp ({'sparse causal' if causal else 'sparse'}{', fp8 QK' if fp8 else ''})",
+                     "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": fwd_tflops / peak,
+                     "traffic": measured_traffic(w.name + ("-causal" if causal else "") + ("-fp8" if fp8 else "")
                                                  + ("" if (blk, kb) == (w.block, w.block) else f"-b{blk}k{kb}"))},
         "dense_same_shape": dense,
         "cold_cache": cold,
