@@ -252,6 +252,32 @@ struct TileLoader {
   }
 };
 
+// Copies one float (the scale of a K tile) from `src` into LDS with a
+// buffer_load_dword ... lds issued by one wave: every lane fetches the same
+// word, so dwords dst[0..63] all receive it.  Like the tile copies it is
+// written as inline asm and waited for with the explicit vmcnt wait and
+// barrier of the copy protocol.
+__device__ __forceinline__ void copy_scale(const float* src, TBS_LDS float* dst) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(src);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32) & 0xffffu);
+  r[2] = 4u;
+  r[3] = kRsrcWord3;
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)dst);
+  const unsigned zero = 0u;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(zero), "s"(r)
+      : "memory");
+}
+
 // A work item is a group of G consecutive query blocks of one (b, h).  The
 // workgroup loads every 64-key K/V tile in the union of the group's key
 // blocks once; each wave (32 query rows of one member block) computes only
@@ -323,6 +349,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ unsigned char s_lm[fwd_listed(MODE) ? kMaxListBlocks : 1];
   __shared__ int s_unit;
   __shared__ int s_nlist;
+  __shared__ float s_ksc[F8 ? 2 : 1][64];   // fp8 path: scale of the K tile in each stage
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -493,12 +520,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + (16 * s + 8 * h) * 2);
       }
     }
-    // fp8 path: tile scale of the K tile whose S product this wave computed
-    // last, read with a scalar load in M(t) and used in V(t).
+    // fp8 path: scale of K tile t.  Wave 0 copies it into the tile's LDS
+    // stage slot together with the tile (same wait and barrier); M(t) reads
+    // it and V(t) uses it.
     float k_sc = 1.f;
-    const float TBS_CONST* ksc_head =
-        F8 ? (const float TBS_CONST*)(p.k_scale) + static_cast<long long>(__builtin_amdgcn_readfirstlane(gi.bh)) * p.nkt
-           : nullptr;
+    const float* ksc_head = F8 ? p.k_scale + static_cast<long long>(gi.bh) * p.nkt : nullptr;
 
     f32x16 acc_o[NO];
 #pragma unroll
@@ -529,7 +555,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       constexpr int KP = TBS_KPF < NF ? TBS_KPF : NF;
       if constexpr (F8) {
         if (s_on) {
-          k_sc = ksc_head[tile_key0(t) / kKeyTile];
+          k_sc = s_ksc[KS][0];
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -690,15 +716,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
     // Copies started at global step 2t: K(t+1) into K stage (t+1)&1 and
     // V(t) into V stage t&1 (P = t&1); every wave issues its share.
-    auto issue_k = [&](int key0, TBS_LDS unsigned char* dst) __attribute__((always_inline)) {
-      if constexpr (F8)
-        loader8.issue_one(kg, key0, p.N, dst);
-      else
-        loader.issue_one(kg, key0, p.N, dst);
+    auto issue_k = [&](auto stage, int key0) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage)::value;
+      if constexpr (F8) {
+        loader8.issue_one(kg, key0, p.N, lds + ST * TILEK);
+        if (wave == 0) copy_scale(ksc_head + key0 / kKeyTile, (TBS_LDS float*)&s_ksc[ST][0]);
+      } else {
+        loader.issue_one(kg, key0, p.N, lds + ST * TILEK);
+      }
     };
     auto issue = [&](auto pp, int t) __attribute__((always_inline)) {
       constexpr int P = decltype(pp)::value;
-      if (t + 1 < nt) issue_k(tile_key0(t + 1), lds + (P ^ 1) * TILEK);
+      if (t + 1 < nt) issue_k(Stage<P ^ 1>{}, tile_key0(t + 1));
       if (t < nt) loader.issue_one(vg, tile_key0(t), p.N, lds + 2 * TILEK + P * TILEB);
     };
 
@@ -711,7 +740,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // the barrier that opens step 2t+2.  The loop is unrolled twice so the
     // LDS stages of K(t) and V(t-1) are compile-time constants.
     if (nt > 0) {
-      issue_k(tile_key0(0), lds);
+      issue_k(Stage<0>{}, tile_key0(0));
       wait_vmem();
       step_barrier();
       if (grp == 1) {
