@@ -38,7 +38,9 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 FP8_QK_PEAK_TFLOPS = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
 METRIC = "executed TFLOP/s + ms/call, top-p sparse attn fwd, N=32760 H=40 d=128 bf16"
 KERNEL_SOURCES = ("top_block_sparse_pool_amd/csrc/flash_fwd.hip", "top_block_sparse_pool_amd/csrc/device_common.h")
-TRAFFIC_SUMMARY = "profiles/flash_fwd_bf16_sparse_video-32k_traffic.md"
+# rocprofv3 HBM byte summaries of the sparse kernel, by workload key.
+TRAFFIC_SUMMARIES = {"video-32k": "profiles/flash_fwd_bf16_sparse_video-32k_traffic.md",
+                     "video-32k-fp8": "profiles/flash_fwd_fp8qk_sparse_video-32k_traffic.md"}
 
 
 def kernel_source_hash() -> str:
@@ -56,7 +58,9 @@ def measured_traffic(workload: str):
     rocprofv3 summary; None unless the summary covers this workload and was
     taken on the kernel sources as they are now."""
     import re
-    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if workload not in TRAFFIC_SUMMARIES:
+        return None
+    path = os.path.join(ROOT, TRAFFIC_SUMMARIES[workload])
     if not os.path.exists(path):
         return None
     with open(path) as f:
