@@ -345,8 +345,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // LDS: K stage 0, K stage 1, V stage 0, V stage 1.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILEK + 2 * TILEB];
   __shared__ unsigned s_bm[fwd_listed(MODE) ? G * kMaxListWords : 1];
-  __shared__ unsigned short s_lj[fwd_listed(MODE) ? kMaxListBlocks : 1];
-  __shared__ unsigned char s_lm[fwd_listed(MODE) ? kMaxListBlocks : 1];
+  // Union list: key block index in the low 16 bits, member-block bits above.
+  __shared__ unsigned s_lt[fwd_listed(MODE) ? kMaxListBlocks : 1];
   __shared__ int s_unit;
   __shared__ int s_nlist;
   __shared__ float s_ksc[F8 ? 2 : 1][64];   // fp8 path: scale of the K tile in each stage
@@ -464,8 +464,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
           unsigned msk = 0u;
 #pragma unroll
           for (int m = 0; m < G; ++m) msk |= ((wm[m] >> bit) & 1u) << m;
-          s_lj[pos] = static_cast<unsigned short>(lane * 32 + bit);
-          s_lm[pos] = static_cast<unsigned char>(msk);
+          s_lt[pos] = static_cast<unsigned>(lane * 32 + bit) | (msk << 16);
           ++pos;
         }
         if (lane == 63) s_nlist = incl;
@@ -473,7 +472,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       __syncthreads();
       const int nl = s_nlist;
       nt = nl * SPB;
-      if (SPB > 1 && nl > 0 && s_lj[nl - 1] == p.nbk - 1) {
+      if (SPB > 1 && nl > 0 && static_cast<int>(s_lt[nl - 1] & 0xffffu) == p.nbk - 1) {
         const int tail = p.N - (p.nbk - 1) * BK;
         nt = (nl - 1) * SPB + (tail + kKeyTile - 1) / kKeyTile;
       }
@@ -482,20 +481,30 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     } else {
       nt = (min(p.N, (gi.i0 + gi.gsz) * BQ) + kKeyTile - 1) / kKeyTile;
     }
-    auto tile_key0 = [&](int t) __attribute__((always_inline)) -> int {
-      if (fwd_listed(MODE)) return __builtin_amdgcn_readfirstlane(s_lj[t / SPB]) * BK + (t % SPB) * kKeyTile;
+    // Per-tile facts from the tile's union-list word w (listed modes): its
+    // first key and whether this wave's block selected it.  The loop keeps
+    // the words of tiles t-1 .. t+3 in scalar registers and reads the next
+    // ones from LDS one iteration ahead, so no lookup waits on LDS.
+    auto wkey0 = [&](unsigned w, int t) __attribute__((always_inline)) -> int {
+      if (fwd_listed(MODE)) return static_cast<int>(w & 0xffffu) * BK + (t % SPB) * kKeyTile;
       return t * kKeyTile;
     };
     // Under a causal mask a wave skips tiles whose keys all follow its 32
     // query rows (the second tile of a 128-row diagonal block, for the first
     // half of its rows).
-    auto tile_mine = [&](int t) __attribute__((always_inline)) -> bool {
+    auto wmine = [&](unsigned w, int t) __attribute__((always_inline)) -> bool {
       if (!active) return false;
-      if (MODE == kSparseCausal)
-        return ((__builtin_amdgcn_readfirstlane(s_lm[t / SPB]) >> member) & 1) && tile_key0(t) < q0w + 32;
-      if (MODE == kSparse) return (__builtin_amdgcn_readfirstlane(s_lm[t / SPB]) >> member) & 1;
+      if (MODE == kSparseCausal) return ((w >> (16 + member)) & 1u) && wkey0(w, t) < q0w + 32;
+      if (MODE == kSparse) return (w >> (16 + member)) & 1u;
       if (MODE == kCausal) return t * kKeyTile < q0w + 32;
       return true;
+    };
+    auto wread = [&](int t) __attribute__((always_inline)) -> unsigned {
+      if (fwd_listed(MODE)) return s_lt[min(max(t, 0) / SPB, kMaxListBlocks - 1)];
+      return 0u;
+    };
+    auto wuni = [&](unsigned v) __attribute__((always_inline)) -> unsigned {
+      return fwd_listed(MODE) ? __builtin_amdgcn_readfirstlane(v) : 0u;
     };
 
     // Q^T as B operand: lane (h, col) holds Q[qrow][16s + 8h .. +7] (bf16)
@@ -544,11 +553,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // M(t): S(t) from K stage KS, then O^T += V^T P^T of tile t - 1 from V
     // stage VS.  All 32 A-operand fragments (16 of K, 16 of V^T) stream
     // through one ring of TBS_KPF registers, read that many MFMAs ahead.
-    auto mpart = [&](auto ks, auto vs, int t) __attribute__((always_inline)) {
+    auto mpart = [&](auto ks, auto vs, int t, unsigned w_t, unsigned w_tm1) __attribute__((always_inline)) {
       constexpr int KS = decltype(ks)::value;
       constexpr int VS = decltype(vs)::value;
-      const bool s_on = t < nt && tile_mine(t);
-      const bool pv_on = t >= 1 && t - 1 < nt && tile_mine(t - 1);
+      const bool s_on = t < nt && wmine(w_t, t);
+      const bool pv_on = t >= 1 && t - 1 < nt && wmine(w_tm1, t - 1);
       const TBS_LDS unsigned char* lk = lds + KS * TILEK;
       const TBS_LDS unsigned char* lv = lds + 2 * TILEK + VS * TILEB;
       constexpr int NF = 2 * NS;          // fragments of each product
@@ -638,9 +647,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // pb.  The whole tile (both halves) shares one reference maximum: its
     // P V product is accumulated only in M(t+1), after the rescale below has
     // been applied to everything accumulated so far.
-    auto vpart = [&](int t) __attribute__((always_inline)) {
-      if (!(t < nt && tile_mine(t))) return;
-      const int key0 = tile_key0(t);
+    auto vpart = [&](int t, unsigned w_t) __attribute__((always_inline)) {
+      if (!(t < nt && wmine(w_t, t))) return;
+      const int key0 = wkey0(w_t, t);
       const bool need_mask = (key0 + kKeyTile > p.N) || (fwd_causal(MODE) && key0 + kKeyTile - 1 > q0w);
       if (need_mask) {
         // Mask keys past the sequence end (ragged tail) and, if causal, keys
@@ -725,10 +734,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         loader.issue_one(kg, key0, p.N, lds + ST * TILEK);
       }
     };
-    auto issue = [&](auto pp, int t) __attribute__((always_inline)) {
+    auto issue = [&](auto pp, int t, unsigned w_tp1, unsigned w_t) __attribute__((always_inline)) {
       constexpr int P = decltype(pp)::value;
-      if (t + 1 < nt) issue_k(Stage<P ^ 1>{}, tile_key0(t + 1));
-      if (t < nt) loader.issue_one(vg, tile_key0(t), p.N, lds + 2 * TILEK + P * TILEB);
+      if (t + 1 < nt) issue_k(Stage<P ^ 1>{}, wkey0(w_tp1, t + 1));
+      if (t < nt) loader.issue_one(vg, wkey0(w_t, t), p.N, lds + 2 * TILEK + P * TILEB);
     };
 
     // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(nt), one
@@ -740,33 +749,41 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // the barrier that opens step 2t+2.  The loop is unrolled twice so the
     // LDS stages of K(t) and V(t-1) are compile-time constants.
     if (nt > 0) {
-      issue_k(Stage<0>{}, tile_key0(0));
+      // Union-list words of tiles t-1 .. t+3 (uniform).
+      unsigned w_m1 = 0u, w_0 = wuni(wread(0)), w_1 = wuni(wread(1)), w_2 = wuni(wread(2)), w_3 = wuni(wread(3));
+      issue_k(Stage<0>{}, wkey0(w_0, 0));
       wait_vmem();
       step_barrier();
       if (grp == 1) {
-        issue(Stage<0>{}, 0);
+        issue(Stage<0>{}, 0, w_1, w_0);
         step_barrier();
       }
       for (int t = 0;; t += 2) {
-        if (grp == 0) issue(Stage<0>{}, t);
-        mpart(Stage<0>{}, Stage<1>{}, t);
+        const unsigned pf_a = wread(t + 4), pf_b = wread(t + 5);   // tiles t+4, t+5, for the next iteration
+        if (grp == 0) issue(Stage<0>{}, t, w_1, w_0);
+        mpart(Stage<0>{}, Stage<1>{}, t, w_0, w_m1);
         if (grp == 1) wait_vmem();
         step_barrier();
         if (t == nt) break;
-        if (grp == 1) issue(Stage<1>{}, t + 1);
-        vpart(t);
+        if (grp == 1) issue(Stage<1>{}, t + 1, w_2, w_1);
+        vpart(t, w_0);
         if (grp == 0) wait_vmem();
         step_barrier();
 
-        if (grp == 0) issue(Stage<1>{}, t + 1);
-        mpart(Stage<1>{}, Stage<0>{}, t + 1);
+        if (grp == 0) issue(Stage<1>{}, t + 1, w_2, w_1);
+        mpart(Stage<1>{}, Stage<0>{}, t + 1, w_1, w_0);
         if (grp == 1) wait_vmem();
         step_barrier();
         if (t + 1 == nt) break;
-        if (grp == 1) issue(Stage<0>{}, t + 2);
-        vpart(t + 1);
+        if (grp == 1) issue(Stage<0>{}, t + 2, w_3, w_2);
+        vpart(t + 1, w_1);
         if (grp == 0) wait_vmem();
         step_barrier();
+        w_m1 = w_1;
+        w_0 = w_2;
+        w_1 = w_3;
+        w_2 = wuni(pf_a);
+        w_3 = wuni(pf_b);
       }
       if (grp == 0) step_barrier();
     }
