@@ -13,8 +13,8 @@
 //   select_kernel  one workgroup per (b, h, R = 8 query blocks): fp64 scores
 //                  for R rows against all key blocks (the R pooled query rows
 //                  staged in LDS and read as broadcasts, pooled K read
-//                  transposed so that lanes read consecutive key blocks, eight
-//                  loads in flight per thread); then one wave per
+//                  transposed so that lanes read consecutive key blocks, each
+//                  thread holding all of its key blocks' sums); then one wave per
 //                  row: a max/sum softmax, a register bitonic sort by
 //                  (P desc, index asc), a fixed-order prefix sum to find the
 //                  cut, and the outputs -- no workgroup barriers per row.
@@ -281,27 +281,40 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // The workgroup's R pooled query rows in LDS (read back as broadcasts).
   for (int x = tid; x < R * D; x += kSelThreads) qs[x] = qb[static_cast<long long>(min(i0 + x / D, nbq - 1)) * D + x % D];
   __syncthreads();
-  constexpr int CU = 8;   // pooled-K loads in flight per thread
-  for (int j = tid; j < NP; j += kSelThreads) {
-    double acc[R];
+  // Each thread accumulates all J of its key blocks (j = tid + u * threads)
+  // at once, so every broadcast read of a pooled query value feeds J FMAs;
+  // the sum over the head dimension runs in increasing order.
+  constexpr int CU = NP > 2 * kSelThreads ? 4 : 8;   // head-dimension steps per batch of pooled-K loads
+  constexpr int J = NP > kSelThreads ? NP / kSelThreads : 1;
+  if (tid < NP) {
+    double acc[J][R];
+    bool live[J];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    if (j < nbk) {
-      for (int c0 = 0; c0 < D; c0 += CU) {
-        double kv[CU];
+    for (int u = 0; u < J; ++u) {
+      live[u] = tid + u * kSelThreads < nbk;
 #pragma unroll
-        for (int u = 0; u < CU; ++u) kv[u] = kt[static_cast<long long>(c0 + u) * nbk + j];
-#pragma unroll
-        for (int u = 0; u < CU; ++u)
-#pragma unroll
-          for (int r = 0; r < R; ++r) acc[r] = fma(qs[r * D + c0 + u], kv[u], acc[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) z[r * NP + j] = scale * acc[r];
-    } else {
-#pragma unroll
-      for (int r = 0; r < R; ++r) z[r * NP + j] = -INFINITY;
+      for (int r = 0; r < R; ++r) acc[u][r] = 0.0;
     }
+    for (int c0 = 0; c0 < D; c0 += CU) {
+      double kv[J][CU];
+#pragma unroll
+      for (int u = 0; u < J; ++u)
+#pragma unroll
+        for (int c = 0; c < CU; ++c)
+          kv[u][c] = live[u] ? kt[static_cast<long long>(c0 + c) * nbk + tid + u * kSelThreads] : 0.0;
+#pragma unroll
+      for (int c = 0; c < CU; ++c)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const double qv = qs[r * D + c0 + c];
+#pragma unroll
+          for (int u = 0; u < J; ++u) acc[u][r] = fma(qv, kv[u][c], acc[u][r]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < J; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) z[r * NP + tid + u * kSelThreads] = live[u] ? scale * acc[u][r] : -INFINITY;
   }
   __syncthreads();
 
