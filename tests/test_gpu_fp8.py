@@ -192,3 +192,29 @@ def test_full_size_video_fp8_sampled():
         e, le = compare_units(o[:, sl], lse[:, sl], ref_q.q_deq, ref_q.k_deq, v[:, sl], w.block, units, ref["mask"],
                               q.dtype)
         print(f"  head {h}: {len(units)} sampled blocks, max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)
+
+
+def test_fp8_processing_order_is_bitwise_invariant():
+    # Each work item is computed by one workgroup in a fixed key order, so the
+    # natural order, the longest-first list and other head windows give the
+    # same bits.
+    w = CASES[1]
+    q, k, v = _inputs(w, seed=3)
+    pr, ws, r, qk, o, lse = _fp8_path(w, q, k, v)
+    outs = []
+    for hw in (None, 0, 1):
+        wl = None if hw is None else tbs.schedule(pr, r.row_cnt, ws, head_window=hw)
+        o2, l2 = tbs.sparse_fwd_fp8(qk, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws)
+        outs.append((o2, l2))
+    torch.cuda.synchronize()
+    for o2, l2 in outs:
+        assert torch.equal(o2, o) and torch.equal(l2, lse)
+
+
+def test_sparse_attention_fp8_wrapper_matches_the_calls():
+    w = CASES[0]
+    q, k, v = _inputs(w, seed=4)
+    o, lse, r, wl = tbs.sparse_attention(q, k, v, w.top_p, w.block, fp8=True)
+    pr, ws, r2, qk, o2, l2 = _fp8_path(w, q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(r.mask, r2.mask) and torch.equal(o, o2) and torch.equal(lse, l2)
