@@ -27,3 +27,10 @@ def test_bench_flops_mixed_blocks_equal_oracle(N, bq, bk, causal):
     mask = (rng.random((1, 2, nbq, nbk)) < 0.4).astype(np.uint8)
     want = sum(oracle.executed_flops(mask[0, h], N, bq, 64, causal, key_block=bk) for h in range(2))
     assert bench.executed_flops(mask, N, bq, 64, causal, bk) == want
+
+
+def test_fp8_peak_is_the_harmonic_mix():
+    # Half of the FLOPs at the fp8 rate and half at the bf16 rate take
+    # 0.5/5.0 + 0.5/2.5 = 0.3 ms per PFLOP, so the peak is 1/0.3 PFLOP/s.
+    assert abs(bench.FP8_QK_PEAK_TFLOPS - 1e3 / 0.3) < 1e-6
+    assert bench.BF16_PEAK_TFLOPS < bench.FP8_QK_PEAK_TFLOPS < bench.FP8_PEAK_TFLOPS

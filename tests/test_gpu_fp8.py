@@ -218,3 +218,62 @@ def test_sparse_attention_fp8_wrapper_matches_the_calls():
     pr, ws, r2, qk, o2, l2 = _fp8_path(w, q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(r.mask, r2.mask) and torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_dense_fp8_on_the_dense_workload(causal):
+    # dense-4k: iid N(0,1) inputs, H = 16, N = 4096; sampled query blocks of
+    # every head against the oracle on the dequantised operands.
+    w = WORKLOADS["dense-4k"]
+    print(f"[case] fp8 dense {w.describe()} causal={causal}", flush=True)
+    q, k, v = [t.to(DEV) for t in make_inputs(w, 0)]
+    qk = tbs.quantize_qk_fp8(q, k, w.block)
+    o, lse = tbs.dense_fwd_fp8(qk, v, w.block, causal=causal)
+    torch.cuda.synchronize()
+    ref_q = ofp8.quantize_qk(to64(q), to64(k))
+    rng = np.random.default_rng(9)
+    units = [(0, h, int(i)) for h in range(w.heads) for i in rng.integers(0, w.num_blocks, size=2)]
+    units.append((0, w.heads - 1, w.num_blocks - 1))
+    e, le = compare_units(o, lse, ref_q.q_deq, ref_q.k_deq, v, w.block, units, None, q.dtype, causal=causal)
+    print(f"  {len(units)} blocks: max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)
+
+
+def test_fp8_after_union_fill():
+    # attn_augment_union changes only the lists; the fp8 kernel then runs over
+    # the filled lists (every row of an item takes the item's union).
+    w = CASES[0]
+    q, k, v = _inputs(w, seed=5)
+    pr = tbs.make_problem(q, w.block)
+    ws = tbs.workspace(pr, DEV)
+    r = tbs.route(q, k, w.top_p, w.block, ws=ws)
+    tbs.augment_union(pr, r)
+    wl = tbs.schedule(pr, r.row_cnt, ws)
+    qk = tbs.quantize_qk_fp8(q, k, w.block)
+    o, lse = tbs.sparse_fwd_fp8(qk, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws)
+    torch.cuda.synchronize()
+    mask = r.mask.cpu().numpy()
+    ref_q = ofp8.quantize_qk(to64(q), to64(k))
+    units = [(b, h, i) for b in range(w.batch) for h in range(w.heads) for i in range(pr.num_blocks)]
+    e, le = compare_units(o, lse, ref_q.q_deq, ref_q.k_deq, v, w.block, units, mask, q.dtype)
+    print(f"  {len(units)} blocks over filled lists: max |O err| {e:.3e}", flush=True)
+
+
+def test_full_size_long_video_fp8_sampled():
+    w = WORKLOADS["video-119k"]
+    print(f"[case] fp8 {w.describe()}", flush=True)
+    q, k, v = [t.to(DEV) for t in make_inputs(w, 0)]
+    pr, ws, r, qk, o, lse = _fp8_path(w, q, k, v)
+    print("  gpu done; oracle per sampled head", flush=True)
+    rng = np.random.default_rng(13)
+    for h in (0, w.heads - 1):
+        sl = slice(h, h + 1)
+        ref = ofp8.quantize_qk(to64(q[:, sl]), to64(k[:, sl]))
+        assert np.array_equal(qk.q8[:, sl].cpu().numpy(), ref.q_codes)
+        assert np.array_equal(qk.k8[:, sl].cpu().numpy(), ref.k_codes)
+        route_ref = oracle_route_per_head(q[:, sl], k[:, sl], w.block, w.top_p)
+        agree = ~(r.mask[:, sl].cpu().numpy() != route_ref["mask"]).any(-1)
+        cand = {int(x) for x in rng.integers(0, pr.num_blocks, size=3)} | {pr.num_blocks - 1}
+        units = [(0, 0, i) for i in sorted(cand) if agree[0, 0, i]]
+        e, le = compare_units(o[:, sl], lse[:, sl], ref.q_deq, ref.k_deq, v[:, sl], w.block, units,
+                              route_ref["mask"], q.dtype)
+        print(f"  head {h}: {len(units)} sampled blocks, max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)
