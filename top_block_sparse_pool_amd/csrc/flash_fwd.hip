@@ -155,7 +155,9 @@ __device__ __forceinline__ int swap_bits23(int m) {
 template <int D>
 __device__ __forceinline__ int chunk_swz(int row) {
   if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  return ((row & 3) << 1) | ((row >> 3) & 1);
+  // 128-byte rows: two rows share a line of the 64 four-byte banks, so the
+  // rows of a 16-lane read group must differ in (row parity, chunk).
+  return (row >> 1) & 7;
 }
 
 // Copies a 64-key tile of K or V (rows key0 .. key0+63 of one head) from HBM
