@@ -16,8 +16,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define TBS_LDS __attribute__((address_space(3)))
-// Read-only global memory that the kernel reads with scalar loads.
-#define TBS_CONST __attribute__((address_space(4)))
 
 constexpr int kWave = 64;
 
