@@ -16,6 +16,11 @@ with causal routing and causal attention (executed FLOPs then count the
 allowed token pairs of diagonal blocks only).  --fp8 quantises Q and K to
 E4M3 in the step (attn_quantize_qk_fp8) and runs attn_sparse_fwd_fp8; its
 roofline peak is the mix of the fp8 rate (S) and the bf16 rate (P V).
+--share-of G measures one GPU's share of a G-way split by whole heads: all
+heads are routed, the heads go to the G GPUs longest first by their
+selected-block counts, and the step runs on the heads of the GPU with the
+largest load, at their real shape (the other GPUs and the exchange of
+heads between them are not run).
 """
 from __future__ import annotations
 
@@ -115,9 +120,59 @@ def parse():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="steps timed with a 512 MB buffer written before each (0: skip the cold measurement)")
+    ap.add_argument("--share-of", type=int, default=1,
+                    help="time one GPU's share of a head split over this many GPUs (the most loaded one)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def head_lpt(costs, num_gpus: int):
+    """Whole heads to GPUs, longest first: heads in (cost desc, id asc) order,
+    each to the GPU with the smallest load so far (ties: the lowest GPU id).
+    Returns (gpu_of [heads], load [num_gpus])."""
+    costs = np.asarray(costs, dtype=np.int64).reshape(-1)
+    order = sorted(range(costs.size), key=lambda h: (-int(costs[h]), h))
+    load = np.zeros(num_gpus, dtype=np.int64)
+    gpu_of = np.empty(costs.size, dtype=np.int64)
+    for h in order:
+        g = int(np.argmin(load))
+        gpu_of[h] = g
+        load[g] += costs[h]
+    return gpu_of, load
+
+
+def contiguous_head_loads(costs, num_gpus: int) -> np.ndarray:
+    """Loads when GPU g owns the contiguous slice of heads [g*H/G, (g+1)*H/G)."""
+    costs = np.asarray(costs, dtype=np.int64).reshape(-1)
+    n = costs.size
+    return np.array([costs[(g * n) // num_gpus:((g + 1) * n) // num_gpus].sum() for g in range(num_gpus)],
+                    dtype=np.int64)
+
+
+def take_share(tbs, q, k, v, top_p, block, key_block, causal, num_gpus):
+    """One GPU's share of a num_gpus-way split by whole heads.  All heads are
+    routed (their selected-block counts are what the GPUs would exchange),
+    head_lpt gives the heads to GPUs, and the heads of the GPU with the
+    largest load are returned as a [1, n, N, d] problem with a description."""
+    import torch
+    B, H, N, d = q.shape
+    t0 = time.perf_counter()
+    r = tbs.route(q, k, top_p, block, causal=causal, key_block=key_block)
+    costs = r.head_cnt.cpu().numpy().astype(np.int64).reshape(-1)
+    route_s = time.perf_counter() - t0
+    gpu_of, load = head_lpt(costs, num_gpus)
+    contiguous = contiguous_head_loads(costs, num_gpus)
+    rank = int(np.argmax(load))
+    heads = np.nonzero(gpu_of == rank)[0]
+    idx = torch.as_tensor(heads, device=q.device)
+    sub = [t.reshape(B * H, N, d).index_select(0, idx).unsqueeze(0).contiguous() for t in (q, k, v)]
+    info = {"gpus": num_gpus, "rank": rank, "heads": [int(h) for h in heads],
+            "head_cost": [int(costs[h]) for h in heads], "rank_loads": [int(x) for x in load],
+            "lif_head_lpt": float(load.max() / load.mean()),
+            "lif_contiguous_heads": float(contiguous.max() / contiguous.mean()),
+            "route_all_heads_s": route_s}
+    return sub[0], sub[1], sub[2], info
 
 
 def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False, block=None, key_block=None):
@@ -200,11 +255,16 @@ def main():
     causal = bool(args.causal)
     blk = args.block or w.block
     kb = args.key_block or blk
+    share = None
+    if args.share_of > 1:
+        q, k, v, share = take_share(tbs, q, k, v, w.top_p, blk, kb, causal, args.share_of)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     pr = tbs.make_problem(q, blk, causal=causal, key_block=kb)
     ws = tbs.workspace(pr, dev)
     if hw is None:
         hw = tbs.default_head_window(pr)
-    B, H, N, d = w.batch, w.heads, w.seq_len, w.head_dim
+    B, H, N, d = (int(x) for x in q.shape)
     nb, nbk = pr.num_blocks, pr.num_key_blocks
     route_out = tbs.Route(pr, w.top_p,
                           torch.empty((B, H, nb, nbk), dtype=torch.uint8, device=dev),
@@ -450,7 +510,7 @@ def main():
         del plain
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and share is None:
         cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed, causal, blk, kb)
 
     peak = FP8_QK_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
@@ -472,7 +532,9 @@ def main():
                    "top_p": w.top_p, "causal": causal, "sasa": bool(args.sasa), "sasa_union": bool(args.sasa_union),
                    "fp8_qk": fp8,
                    "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
-                   "dense_tflop": dense_flops / 1e12, "parallelism": "single GPU"},
+                   "dense_tflop": dense_flops / 1e12,
+                   "parallelism": f"one GPU's share of a {share['gpus']}-GPU split by heads" if share else "single GPU",
+                   "share": share},
         "breakdown_ms": {"route_mean": float(t_route.mean()), "route_median": float(np.median(t_route)),
                          "schedule_mean": float(t_sched.mean()), "schedule_median": float(np.median(t_sched)),
                          "quantize_mean": float(t_quant.mean()), "quantize_median": float(np.median(t_quant)),
@@ -483,7 +545,8 @@ def main():
                      "kernel": f"flash_fwd_bf16_pp ({'sparse causal' if causal else 'sparse'}{', fp8 QK' if fp8 else ''})",
                      "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": fwd_tflops / peak,
-                     "traffic": measured_traffic(w.name + ("-causal" if causal else "") + ("-fp8" if fp8 else "")
+                     "traffic": measured_traffic(w.name + (f"-share{share['gpus']}" if share else "")
+                                                 + ("-causal" if causal else "") + ("-fp8" if fp8 else "")
                                                  + ("" if (blk, kb) == (w.block, w.block) else f"-b{blk}k{kb}"))},
         "dense_same_shape": dense,
         "cold_cache": cold,
