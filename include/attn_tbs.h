@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define ATTN_TBS_ABI_VERSION 4
+#define ATTN_TBS_ABI_VERSION 5
 
 /* Status codes. */
 #define ATTN_OK            0
@@ -120,7 +120,11 @@ const char* attn_last_error(void);
  * satisfies this, and attn_schedule and every fwd call leave them zero when
  * they complete, so one zero fill at allocation is enough (attn_route and
  * attn_augment use only the bytes after it).  One workspace of the largest
- * size serves every operation. */
+ * size serves every operation.  For ATTN_OP_DENSE_FWD of a causal problem
+ * with few work items (see attn_dense_fwd) the size includes per-item part
+ * counters, which the call zeroes itself, and the parts' partial results:
+ * at most (work items + compute units) * 8 * (8 * head_dim + 128) * 4 bytes
+ * more, which depends on the current device. */
 size_t attn_workspace_bytes(const attn_problem* problem, int32_t op);
 
 /* Query blocks per work item, G.  The persistent fwd kernel processes a work
@@ -297,7 +301,16 @@ int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* 
  * causal the query blocks with the most keys are processed first.  Equals,
  * bit for bit, attn_sparse_fwd with every block selected (causal == 0) or
  * with every eligible block selected (causal == 1), for any key_block.  The
- * key block size does not enter the dense result. */
+ * key block size does not enter the dense result.
+ *
+ * Causal bf16 problems with fewer than 4 work items per compute unit whose
+ * last item holds more than half the mean work per compute unit (at least
+ * 16 key tiles of 64 keys) run their longer items as equal parts along the
+ * keys, each part's running maximum, sum and unnormalised O merged in part
+ * order by the item's last part to finish (FlashAttention review, Tiling
+ * Softmax: partial softmax results combine exactly).  The result is then
+ * deterministic and equal to the unsplit one up to fp32 rounding, not bit
+ * for bit; attn_num_workers and attn_workspace_bytes account for the parts. */
 int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                        void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 

@@ -105,3 +105,19 @@ def compare_units(o_gpu, lse_gpu, q, k, v, block, units, mask, dtype, scale=None
 
 def units_where(rows_agree, units):
     return [u for u in units if rows_agree[u]]
+
+
+def dense_causal_splits(w) -> bool:
+    """Whether attn_dense_fwd(causal) splits this bf16 workload's work items
+    along the keys: fewer than four items of 256 query rows per compute unit,
+    and a last item longer than half the mean work per compute unit (at
+    least 16 key tiles of 64 keys)."""
+    if w.dtype != "bf16":
+        return False
+    ng = -(-w.seq_len // 256)
+    items = w.batch * w.heads * ng
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = [-(-min(w.seq_len, 256 * (gi + 1)) // 64) for gi in range(ng)]
+    mean = -(-(w.batch * w.heads * sum(tiles)) // cus)
+    part = max(16, (mean + 1) // 2)
+    return items < 4 * cus and tiles[-1] > part

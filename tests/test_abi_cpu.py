@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
                           "attn_dense_fwd_fp8"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 4
+    assert L.attn_abi_version() == 5
 
 
 def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0, key_block=0, reserved=0):

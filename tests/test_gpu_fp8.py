@@ -15,7 +15,7 @@ import torch
 import oracle
 from oracle import fp8 as ofp8
 import top_block_sparse_pool_amd as tbs
-from parity import compare_route, compare_units, oracle_route_per_head, to64
+from parity import compare_route, compare_units, oracle_route_per_head, to64, dense_causal_splits
 from workloads import WORKLOADS, custom_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -136,7 +136,12 @@ def test_dense_fp8_equals_sparse_at_p1(w, causal):
     pr, ws, r, qk, o_s, l_s = _fp8_path(w, q, k, v, top_p=1.0, causal=causal)
     o_d, l_d = tbs.dense_fwd_fp8(qk, v, w.block, causal=causal, ws=ws)
     torch.cuda.synchronize()
-    assert torch.equal(o_s, o_d) and torch.equal(l_s, l_d)
+    if not (causal and dense_causal_splits(w)):
+        assert torch.equal(o_s, o_d) and torch.equal(l_s, l_d)
+    else:
+        # split items along the keys: equal to rounding (both checked against the oracle below)
+        assert (o_d.float() - o_s.float()).abs().max().item() <= 2e-2
+        assert (l_d - l_s).abs().max().item() <= 2e-3
     ref_q = ofp8.quantize_qk(to64(q), to64(k))
     units = [(b, h, i) for b in range(w.batch) for h in range(w.heads) for i in range(pr.num_blocks)]
     compare_units(o_d, l_d, ref_q.q_deq, ref_q.k_deq, v, w.block, units, None, q.dtype, causal=causal)

@@ -90,9 +90,13 @@ size_t route_bytes(const tbs::Shape& s) {
   return tbs::kCtrlBytes + sizeof(double) * static_cast<size_t>(s.B) * s.H * (s.nb + s.nbk) * s.d;
 }
 
-size_t fwd_bytes(const tbs::Shape& s) {
+// Control block, optional worker stamps, then (dense causal with split
+// items) the part counters and partial results, 256-byte aligned.
+size_t fwd_split_offset(const tbs::Shape& s) {
   return tbs::kCtrlBytes + ((s.flags & ATTN_FLAG_PROFILE_WORKERS) ? kProfileBytes : 0);
 }
+
+size_t fwd_bytes(const tbs::Shape& s, int mode) { return fwd_split_offset(s) + tbs::causal_split_bytes(s, mode); }
 
 int32_t check_tensor(const void* p, const char* name) {
   if (!p) return fail(ATTN_E_INVALID, "%s is NULL", name);
@@ -148,8 +152,8 @@ TBS_EXPORT size_t attn_workspace_bytes(const attn_problem* problem, int32_t op) 
   switch (op) {
     case ATTN_OP_ROUTE: return route_bytes(s);
     case ATTN_OP_SCHEDULE: return tbs::kCtrlBytes;
-    case ATTN_OP_SPARSE_FWD:
-    case ATTN_OP_DENSE_FWD: return fwd_bytes(s);
+    case ATTN_OP_SPARSE_FWD: return fwd_bytes(s, s.causal ? tbs::kSparseCausal : tbs::kSparse);
+    case ATTN_OP_DENSE_FWD: return fwd_bytes(s, s.causal ? tbs::kCausal : tbs::kDense);
     case ATTN_OP_AUGMENT: return tbs::augment_ws_bytes(s, kMaxWorkers);
     default: fail(ATTN_E_INVALID, "unknown op %d", op); return 0;
   }
@@ -280,7 +284,7 @@ int32_t run_fwd(const tbs::Shape& s, int mode, const void* q, const void* k, con
       (st = check_tensor(v, "v")) || (st = check_tensor(o, "o")))
     return st;
   if (lse && !aligned(lse, 4)) return fail(ATTN_E_INVALID, "lse is not 4-byte aligned");
-  if ((st = check_ws(ws, ws_bytes, fwd_bytes(s)))) return st;
+  if ((st = check_ws(ws, ws_bytes, fwd_bytes(s, mode)))) return st;
   tbs::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -297,6 +301,7 @@ int32_t run_fwd(const tbs::Shape& s, int mode, const void* q, const void* k, con
   a.fp8 = fp8;
   a.q_scale = q_scale;
   a.k_scale = k_scale;
+  a.split_ws = static_cast<unsigned char*>(ws) + fwd_split_offset(s);
   if (a.prof && tbs::fwd_workers(s, mode, fp8) > 4096)
     return fail(ATTN_E_UNSUPPORTED, "worker profiling supports at most 4096 workers");
   hipError_t e = tbs::launch_fwd(s, mode, a, static_cast<hipStream_t>(stream));

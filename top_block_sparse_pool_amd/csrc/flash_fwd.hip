@@ -47,6 +47,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace tbs {
 namespace {
 
@@ -75,6 +77,12 @@ struct FwdParams {
   int ng;             // work items per (b, h) = ceil(nb / G)
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
+  // Dense causal, split items (split_tiles > 0): the queue holds U parts of
+  // at most split_tiles key tiles; part_buf holds each part's unnormalised O,
+  // running maximum and sum, part_cnt the parts finished per item.
+  int split_tiles;
+  uint32_t* part_cnt;
+  float* part_buf;
 };
 
 // Unit bookkeeping of the fp32 kernel: query blocks of BQ rows, listed key
@@ -291,10 +299,36 @@ constexpr int kMaxListWords = kMaxListBlocks / 32;
 template <int BQ, int G, int MODE>
 struct GroupInfo {
   int bh, i0, gsz;   // head, first query block, member blocks present (1..G)
+  int g;             // work item
+  int tb, te;        // key tiles [tb, te) of this part (te: an upper bound when not split)
+  int part, nparts;  // part of the item and the item's number of parts
 
   __device__ __forceinline__ void decode(const FwdParams& p, int qpos) {
-    int g;
-    if (MODE == kCausal) {
+    tb = 0;
+    te = 0x7fffffff;
+    part = 0;
+    nparts = 1;
+    if (MODE == kCausal && p.split_tiles > 0) {
+      // Split dense causal: the queue runs item rows gi = ng-1 .. 0 (the last
+      // query blocks have the most keys); row gi holds, for every head, the
+      // ceil(tiles(gi) / split_tiles) equal parts of its item, consecutively.
+      int rem = qpos;
+      int gi = p.ng - 1;
+      int ntg = 1, npg = 1;
+      for (;; --gi) {
+        ntg = (min(p.N, (gi + 1) * G * BQ) + kKeyTile - 1) / kKeyTile;
+        npg = (ntg + p.split_tiles - 1) / p.split_tiles;
+        if (rem < p.BH * npg || gi == 0) break;
+        rem -= p.BH * npg;
+      }
+      bh = rem / npg;
+      part = rem - bh * npg;
+      nparts = npg;
+      // equal parts: lengths differ by at most one tile
+      tb = part * ntg / npg;
+      te = (part + 1) * ntg / npg;
+      g = bh * p.ng + gi;
+    } else if (MODE == kCausal) {
       // Longest first: the last query blocks of every head have the most keys.
       const int gi = p.ng - 1 - qpos / p.BH;
       bh = qpos % p.BH;
@@ -351,6 +385,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ unsigned s_lt[fwd_listed(MODE) ? kMaxListBlocks : 1];
   __shared__ int s_unit;
   __shared__ int s_nlist;
+  __shared__ int s_last;
   __shared__ float s_ksc[F8 ? 2 : 1][64];   // fp8 path: scale of the K tile in each stage
 
   const int tid = threadIdx.x;
@@ -481,15 +516,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     } else if (MODE == kDense) {
       nt = (p.N + kKeyTile - 1) / kKeyTile;
     } else {
-      nt = (min(p.N, (gi.i0 + gi.gsz) * BQ) + kKeyTile - 1) / kKeyTile;
+      nt = min((min(p.N, (gi.i0 + gi.gsz) * BQ) + kKeyTile - 1) / kKeyTile, gi.te) - gi.tb;
     }
+    const int tb = gi.tb;   // first key tile of this part (0 unless split)
     // Per-tile facts from the tile's union-list word w (listed modes): its
     // first key and whether this wave's block selected it.  The loop keeps
     // the words of tiles t-1 .. t+3 in scalar registers and reads the next
     // ones from LDS one iteration ahead, so no lookup waits on LDS.
     auto wkey0 = [&](unsigned w, int t) __attribute__((always_inline)) -> int {
       if (fwd_listed(MODE)) return static_cast<int>(w & 0xffffu) * BK + (t % SPB) * kKeyTile;
-      return t * kKeyTile;
+      return (tb + t) * kKeyTile;
     };
     // Under a causal mask a wave skips tiles whose keys all follow its 32
     // query rows (the second tile of a 128-row diagonal block, for the first
@@ -498,7 +534,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       if (!active) return false;
       if (MODE == kSparseCausal) return ((w >> (16 + member)) & 1u) && wkey0(w, t) < q0w + 32;
       if (MODE == kSparse) return (w >> (16 + member)) & 1u;
-      if (MODE == kCausal) return t * kKeyTile < q0w + 32;
+      if (MODE == kCausal) return (tb + t) * kKeyTile < q0w + 32;
       return true;
     };
     auto wread = [&](int t) __attribute__((always_inline)) -> unsigned {
@@ -792,6 +828,84 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
     // Epilogue: lane (h, col) holds O[qrow][32mo + 8j + 4h + r] in acc_o[mo][4j + r].
     const float l_tot = l_run + xor32(l_run);
+    if (MODE == kCausal && gi.nparts > 1) {
+      // A part of a split item: its O (unnormalised, relative to its own
+      // reference maximum m_run), m_run and row sum go to the part's slot;
+      // the item's last part to finish merges every part, in part order.
+      // Parts run on any XCD, whose L2 caches are not coherent with each
+      // other, so the slots are written through to memory and read past the
+      // caches (buffer stores and loads with sc0 sc1), in the lanes' own
+      // fragment order (1 KB contiguous per wave and instruction); every store
+      // has completed (vmcnt 0, then the workgroup barrier) before the part
+      // counter moves, so no fence has to write back a whole L2.
+      constexpr int PW = NO * 4 * 256 + 2 * 64;    // floats per wave: O fragments, then m and l per lane
+      constexpr int PS = kWaves * PW;              // floats per part
+      constexpr int kThrough = 17;                 // sc0 | sc1
+      auto frag = [&](long long e, int f) __attribute__((always_inline)) -> int {   // byte offset of fragment f
+        return static_cast<int>(((e * PS + wave * PW + f * 256) + lane * 4) * 4);
+      };
+      auto lanef = [&](long long e, int w) __attribute__((always_inline)) -> int {  // m (w = 0) or l (w = 1)
+        return static_cast<int>((e * PS + wave * PW + NO * 4 * 256 + w * 64 + lane) * 4);
+      };
+      const __amdgpu_buffer_rsrc_t rsrc_t = __builtin_amdgcn_make_buffer_rsrc(p.part_buf, 0, 0x7fffffff, kRsrcWord3);
+#pragma unroll
+      for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = __float_as_uint(acc_o[mo][4 * j + r]);
+          __builtin_amdgcn_raw_buffer_store_b128(ov, rsrc_t, frag(qpos, mo * 4 + j), 0, kThrough);
+        }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), rsrc_t, lanef(qpos, 0), 0, kThrough);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot), rsrc_t, lanef(qpos, 1), 0, kThrough);
+      wait_vmem();
+      __syncthreads();
+      if (tid == 0) s_last = atomicAdd(p.part_cnt + gi.g, 1u) == static_cast<unsigned>(gi.nparts - 1);
+      __syncthreads();
+      if (s_last) {
+        const long long e0 = qpos - gi.part;
+        float mm = -INFINITY;
+        for (int q = 0; q < gi.nparts; ++q)
+          mm = fmaxf(mm, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_t, lanef(e0 + q, 0), 0, kThrough)));
+        float ll = 0.f;
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc_o[mo][e] = 0.f;
+        for (int q = 0; q < gi.nparts; ++q) {
+          const float mq = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_t, lanef(e0 + q, 0), 0, kThrough));
+          const float lq = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_t, lanef(e0 + q, 1), 0, kThrough));
+          const float f = mq == -INFINITY ? 0.f : fast_exp2((mq - mm) * sl2);
+          ll += f * lq;
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const u32x4 ov = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, frag(e0 + q, mo * 4 + j), 0, kThrough);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc_o[mo][4 * j + r] += f * __uint_as_float(ov[r]);
+            }
+        }
+        const float inv = ll > 0.f ? 1.f / ll : 0.f;
+        if (active && qrow < p.N) {
+          unsigned short* orow = static_cast<unsigned short*>(p.o) +
+                                 (static_cast<long long>(gi.bh) * p.N + qrow) * D;
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              bf16x4 ov;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) ov[r] = static_cast<__bf16>(acc_o[mo][4 * j + r] * inv);
+              *reinterpret_cast<bf16x4*>(orow + 32 * mo + 8 * j + 4 * h) = ov;
+            }
+          if (h == 0 && p.lse)
+            p.lse[static_cast<long long>(gi.bh) * p.N + qrow] = ll > 0.f ? mm * p.scale + logf(ll) : -INFINITY;
+        }
+      }
+      continue;
+    }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (active && qrow < p.N) {
       unsigned short* orow = static_cast<unsigned short*>(p.o) +
@@ -1056,6 +1170,57 @@ long long work_items(const Shape& s) {
   return static_cast<long long>(s.B) * s.H * ((s.nb + G - 1) / G);
 }
 
+namespace {
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ x, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = 0u;
+}
+}  // namespace
+
+constexpr int kSplitMinTiles = 16;     // shortest part of a split item
+constexpr int kSplitItemsPerCu = 4;    // split below this many items per compute unit
+
+// Key tiles of dense causal item row gi (256 query rows).
+static long long causal_item_tiles(const Shape& s, int gi) {
+  const int G = group_size(s);
+  const long long rows = std::min<long long>(s.N, static_cast<long long>(gi + 1) * G * s.block);
+  return (rows + kKeyTile - 1) / kKeyTile;
+}
+
+int causal_split_tiles(const Shape& s, int mode) {
+  if (mode != kCausal || s.dtype != 0) return 0;
+  const int cus = device_cu_count();
+  if (work_items(s) >= static_cast<long long>(kSplitItemsPerCu) * cus) return 0;
+  // Parts of half the mean work per compute unit (at least 16 tiles), so
+  // that every compute unit takes about two: only the items longer than that
+  // are split.
+  const int G = group_size(s);
+  const int ng = (s.nb + G - 1) / G;
+  long long total = 0;
+  for (int gi = 0; gi < ng; ++gi) total += causal_item_tiles(s, gi);
+  total *= static_cast<long long>(s.B) * s.H;
+  const long long mean = (total + cus - 1) / cus;
+  const long long t = std::max<long long>(kSplitMinTiles, (mean + 1) / 2);
+  if (causal_item_tiles(s, ng - 1) <= t) return 0;
+  return static_cast<int>(t);
+}
+
+long long causal_split_entries(const Shape& s, int split_tiles) {
+  const int G = group_size(s);
+  const int ng = (s.nb + G - 1) / G;
+  long long per_head = 0;
+  for (int gi = 0; gi < ng; ++gi) per_head += (causal_item_tiles(s, gi) + split_tiles - 1) / split_tiles;
+  return per_head * s.B * s.H;
+}
+
+size_t causal_split_bytes(const Shape& s, int mode) {
+  const int t = causal_split_tiles(s, mode);
+  if (t == 0) return 0;
+  const size_t counters = (static_cast<size_t>(work_items(s)) * sizeof(uint32_t) + 255) / 256 * 256;
+  const size_t part_floats = static_cast<size_t>(kWaves) * ((s.d / 32) * 4 * 256 + 2 * 64);
+  return counters + static_cast<size_t>(causal_split_entries(s, t)) * part_floats * sizeof(float);
+}
+
 int fwd_workers(const Shape& s, int mode, bool fp8) {
   KernelFn fn = pick_kernel(s, mode, fp8);
   if (!fn) return 0;
@@ -1066,7 +1231,8 @@ int fwd_workers(const Shape& s, int mode, bool fp8) {
       per_cu < 1)
     per_cu = 1;
   const long long want = static_cast<long long>(device_cu_count()) * per_cu;
-  const long long items = work_items(s);
+  const int split = causal_split_tiles(s, mode);
+  const long long items = split ? causal_split_entries(s, split) : work_items(s);
   return static_cast<int>(want < items ? want : items);
 }
 
@@ -1094,6 +1260,21 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
   p.U = static_cast<int>(work_items(s));
   p.scale = static_cast<float>(s.scale);
   p.scale_log2 = static_cast<float>(s.scale * 1.4426950408889634);
+  p.split_tiles = causal_split_tiles(s, mode);
+  p.part_cnt = nullptr;
+  p.part_buf = nullptr;
+  if (p.split_tiles > 0) {
+    if (!a.split_ws) return hipErrorInvalidValue;
+    const long long items = work_items(s);
+    p.U = static_cast<int>(causal_split_entries(s, p.split_tiles));
+    p.part_cnt = static_cast<uint32_t*>(a.split_ws);
+    p.part_buf = reinterpret_cast<float*>(static_cast<unsigned char*>(a.split_ws) +
+                                          (static_cast<size_t>(items) * sizeof(uint32_t) + 255) / 256 * 256);
+    // The part counters start at zero on every call (the workspace region
+    // may hold another call's data).
+    const int n = static_cast<int>(items);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p.part_cnt, n);
+  }
   const int grid = fwd_workers(s, mode, a.fp8);
   KernelFn fn = pick_kernel(s, mode, a.fp8);
   if (!fn || grid < 1) return hipErrorInvalidValue;

@@ -82,11 +82,25 @@ struct FwdArgs {
   bool fp8 = false;
   const float* q_scale = nullptr;
   const float* k_scale = nullptr;
+  // Dense causal with split items: causal_split_bytes(s, mode) bytes of
+  // workspace, any contents on entry (the per-item part counters, zeroed by
+  // the call, then the parts' partial results).
+  void* split_ws = nullptr;
 };
 // Query blocks per work item (G) and number of work items B*H*ceil(nb/G).
 int group_size(const Shape& s);
 long long work_items(const Shape& s);
 int fwd_workers(const Shape& s, int mode, bool fp8 = false);
+// Dense causal work items split along the keys: parts of at most this many
+// 64-key tiles (0: no split).  Items are split when the problem holds fewer
+// than four per compute unit and its longest item is longer than half the
+// mean work per compute unit (at least 16 tiles), which is then the part
+// length, so that the items of the last query blocks do not set the makespan.
+int causal_split_tiles(const Shape& s, int mode);
+// Queue entries of the split problem (parts of every item).
+long long causal_split_entries(const Shape& s, int split_tiles);
+// Workspace bytes the split needs (0 without a split).
+size_t causal_split_bytes(const Shape& s, int mode);
 hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t stream);
 
 int device_cu_count();
