@@ -123,8 +123,8 @@ const char* attn_last_error(void);
  * size serves every operation.  For ATTN_OP_DENSE_FWD of a causal problem
  * with few work items (see attn_dense_fwd) the size includes per-item part
  * counters, which the call zeroes itself, and the parts' partial results:
- * at most (work items + compute units) * 8 * (8 * head_dim + 128) * 4 bytes
- * more, which depends on the current device. */
+ * (256 * head_dim + 1024) * 4 bytes per part, at most (work items + 2 *
+ * compute units) parts, which depends on the current device. */
 size_t attn_workspace_bytes(const attn_problem* problem, int32_t op);
 
 /* Query blocks per work item, G.  The persistent fwd kernel processes a work

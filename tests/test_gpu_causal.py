@@ -172,3 +172,29 @@ def test_dense_causal_split_items_match_oracle(w):
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
+
+
+def test_split_accounting_matches_the_rule():
+    # attn_num_workers and attn_workspace_bytes of a split dense causal
+    # problem follow the documented rule: parts of at most
+    # max(16, ceil(mean tiles per CU / 2)) tiles, equal parts per item, a
+    # slot of 256 * d + 1024 floats per queue entry (O of 256 rows, a maximum
+    # and a sum per lane of 8 waves) after 256-byte aligned part counters.
+    w = SPLIT[0]
+    q = torch.empty((w.batch, w.heads, w.seq_len, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    pr = tbs.make_problem(q, w.block, causal=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ng = -(-w.seq_len // 256)
+    tiles = [-(-min(w.seq_len, 256 * (gi + 1)) // 64) for gi in range(ng)]
+    bh = w.batch * w.heads
+    part = max(16, (-(-(bh * sum(tiles)) // cus) + 1) // 2)
+    entries = bh * sum(-(-t // part) for t in tiles)
+    assert tbs.num_workers(pr, tbs.OP_DENSE_FWD) == min(cus, entries)
+    counters = -(-(bh * ng * 4) // 256) * 256
+    slot = (256 * w.head_dim + 1024) * 4
+    assert entries <= bh * ng + 2 * cus
+    assert tbs.workspace_bytes(pr, tbs.OP_DENSE_FWD) == 256 + counters + entries * slot
+    # non-causal: no split, the control block only
+    prn = tbs.make_problem(q, w.block)
+    assert tbs.workspace_bytes(prn, tbs.OP_DENSE_FWD) == 256
+    assert tbs.num_workers(prn, tbs.OP_DENSE_FWD) == min(cus, bh * ng)
