@@ -36,18 +36,22 @@
 //   * The two waves of each SIMD alternate: one issues the MFMA part of a
 //     tile while the other runs the softmax of another.
 //   * Epilogue: O / l in fp32 -> bf16 (round to nearest even), LSE = m + ln l.
+//   * Dense causal problems with few items per compute unit run their long
+//     items as parts along the keys: each part keeps its own running
+//     maximum, sum and unnormalised O and writes them to the workspace; the
+//     item's last part to finish combines the parts (the partial results of
+//     Tiling Softmax) and writes O and LSE.
 //
 // fp32 kernel: same unit/tile/queue structure and the same transposed
 // formulation on v_mfma_f32_32x32x2_f32, operands read from padded LDS
 // tiles; weights stay fp32.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
-
-#include <algorithm>
 
 namespace tbs {
 namespace {
