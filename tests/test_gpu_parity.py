@@ -204,3 +204,33 @@ def test_worker_profile_stamps():
     stamps = ws[256:256 + 16 * W].view(torch.int64).view(W, 2).cpu()
     assert W >= 1 and (stamps[:, 1] >= stamps[:, 0]).all() and (stamps[:, 0] > 0).all()
     assert (ws[:256] == 0).all()     # queue counters left at zero
+
+
+def test_one_gpu_share_equals_the_full_problem_on_its_heads():
+    # bench.py --share-of G runs the heads that the head-level LPT gives one
+    # GPU as a problem of their own; heads are independent and the results do
+    # not depend on the processing order, so the share's masks, counts,
+    # outputs and LSE equal the full problem's rows of those heads bit for bit.
+    import bench
+    w = custom_workload(1, 8, 1500, 128, 64, "bf16", 0.9, wid=217)
+    q, k, v = _inputs(w)
+    pr = tbs.make_problem(q, w.block)
+    ws = tbs.workspace(pr, DEV)
+    r = tbs.route(q, k, w.top_p, w.block, ws=ws)
+    wl = tbs.schedule(pr, r.row_cnt, ws)
+    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws)
+    qs, ks, vs, info = bench.take_share(tbs, q, k, v, w.top_p, w.block, w.block, False, 3)
+    heads = info["heads"]
+    assert 1 <= len(heads) < w.heads and info["lif_head_lpt"] <= info["lif_contiguous_heads"] + 1e-12
+    prs = tbs.make_problem(qs, w.block)
+    wss = tbs.workspace(prs, DEV)
+    rs = tbs.route(qs, ks, w.top_p, w.block, ws=wss)
+    wls = tbs.schedule(prs, rs.row_cnt, wss)
+    os_, lses = tbs.sparse_fwd(qs, ks, vs, rs.row_cnt, rs.row_idx, w.block, work_list=wls, ws=wss)
+    torch.cuda.synchronize()
+    idx = torch.tensor(heads, device=DEV)
+    assert torch.equal(rs.mask[0], r.mask[0].index_select(0, idx))
+    assert torch.equal(rs.row_cnt[0], r.row_cnt[0].index_select(0, idx))
+    assert torch.equal(os_[0], o[0].index_select(0, idx))
+    assert torch.equal(lses[0], lse[0].index_select(0, idx))
+    assert sorted(info["head_cost"]) == sorted(int(c) for c in r.head_cnt[0].index_select(0, idx).tolist())
