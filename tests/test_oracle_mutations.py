@@ -6,7 +6,9 @@ one, or applied after the softmax instead of before it; and an augmentation
 that takes the lowest-probability candidates, measures slack from the mean
 load, or draws candidates from every worker's rows; an E4M3 exponent bias off by
 one, ties rounded away from zero, K scaled per token instead of per tile, and
-an inverted dequantisation scale."""
+an inverted dequantisation scale; and an ambiguity window whose swap-across-
+the-cut rule is dropped (whole or either half), measured against the wrong
+neighbour, or applied to near ties between any two neighbouring ranks."""
 import numpy as np
 import pytest
 
@@ -238,3 +240,73 @@ def test_scale_inverted_caught(monkeypatch, golden_dir):
     monkeypatch.setattr(f8, "group_factors", lambda a: (orig(a)[0], orig(a)[0]))
     with pytest.raises(AssertionError):
         tf.test_quantize_hand_example(golden_dir)
+
+
+# --------------------------------------------------- ambiguity window ---
+
+def _ambiguity_variant(swap_in_ref="first_out", swap_out_ref="last_in", adjacent=False):
+    """ambiguous_blocks with its swap rule changed: the selected blocks
+    measured against `swap_in_ref` and the unselected ones against
+    `swap_out_ref` (None drops that half), or (adjacent=True) any two
+    neighbouring ranks within the window flagged wherever they are."""
+    def amb(res, window=1e-5):
+        prob, order, cum = res.prob, res.order, res.cum
+        shape, nb = prob.shape, prob.shape[-1]
+        if res.top_p >= 1.0:
+            return np.zeros(shape, dtype=bool)
+        k = np.asarray(res.row_cnt)
+        valid = np.full(k.shape, nb, dtype=np.int64) if res.valid is None else np.asarray(res.valid)
+        ranked = np.take_along_axis(prob, order, axis=-1)
+        ref = {"last_in": np.take_along_axis(ranked, (k - 1)[..., None], axis=-1),
+               "first_out": np.where((k < valid)[..., None],
+                                     np.take_along_axis(ranked, np.minimum(k, nb - 1)[..., None], axis=-1),
+                                     -np.inf)}
+        excl = cum - ranked
+        near_ranked = (np.abs(excl - res.top_p) <= window) | (np.abs(cum - res.top_p) <= window)
+        near = np.zeros(shape, dtype=bool)
+        np.put_along_axis(near, order, near_ranked, axis=-1)
+        rank_of = np.empty_like(order)
+        np.put_along_axis(rank_of, order, np.broadcast_to(np.arange(nb), shape), axis=-1)
+        selected = rank_of < k[..., None]
+        eligible = np.arange(nb) < valid[..., None]
+        out = near & eligible
+        if adjacent:
+            close = np.zeros(shape, dtype=bool)
+            gap = np.abs(np.diff(ranked, axis=-1)) <= window
+            close_ranked = np.zeros(shape, dtype=bool)
+            close_ranked[..., :-1] |= gap
+            close_ranked[..., 1:] |= gap
+            np.put_along_axis(close, order, close_ranked, axis=-1)
+            return out | (close & eligible)
+        if swap_in_ref is not None:
+            out |= selected & (np.abs(prob - ref[swap_in_ref]) <= window)
+        if swap_out_ref is not None:
+            out |= ~selected & eligible & (np.abs(ref[swap_out_ref] - prob) <= window)
+        return out
+    return amb
+
+
+@pytest.mark.parametrize("variant", [
+    dict(swap_in_ref=None, swap_out_ref=None),            # swap rule dropped
+    dict(swap_in_ref=None),                               # selected half dropped
+    dict(swap_out_ref=None),                              # unselected half dropped
+    dict(swap_in_ref="last_in", swap_out_ref="first_out"),  # each half against its own side of the cut
+    dict(swap_out_ref="first_out"),                       # unselected blocks against the first unselected one
+    dict(adjacent=True),                                  # any near tie between neighbouring ranks
+])
+def test_ambiguity_swap_rule_mutants_caught(monkeypatch, golden_dir, variant):
+    _patch(monkeypatch, rt, "ambiguous_blocks", _ambiguity_variant(**variant))
+    with pytest.raises(AssertionError):
+        tr.test_ambiguity_swap_across_the_cut_golden(golden_dir)
+
+
+def test_ambiguity_variant_helper_is_faithful(golden_dir):
+    # The unmutated helper reproduces the oracle, so each mutant above differs
+    # from it by exactly the change it names.
+    tr.test_ambiguity_swap_across_the_cut_golden(golden_dir)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 2, 512, 4))
+    for p in (0.3, 0.7, 0.9):
+        r = oracle.route(q, q + 0.1 * rng.standard_normal(q.shape), 16, p)
+        for w in (1e-5, 1e-3, 3e-2):
+            np.testing.assert_array_equal(_ambiguity_variant()(r, w), oracle.ambiguous_blocks(r, w))

@@ -4,6 +4,7 @@ import itertools
 import json
 import math
 import os
+import re
 
 import numpy as np
 import pytest
@@ -193,6 +194,38 @@ def test_ambiguity_window_flags_near_cut_only():
     amb2 = oracle.ambiguous_blocks(r2, window=1e-5)
     assert amb2[0, 0, 0, 2] and amb2[0, 0, 0, 3] and not amb2[0, 0, 0, 0]
 
+
+
+def _dyadic(expr: str, eps: float) -> float:
+    """Value of a fixture entry 'a', 'a + k*eps' or 'a - eps' (exact in fp64)."""
+    m = re.fullmatch(r"\s*([0-9.]+)\s*(?:([+-])\s*(?:(\d+)\*)?eps)?\s*", expr)
+    assert m, expr
+    v = float(m.group(1))
+    if m.group(2):
+        k = int(m.group(3) or 1)
+        v = v + k * eps if m.group(2) == "+" else v - k * eps
+    return v
+
+
+def test_ambiguity_swap_across_the_cut_golden(golden_dir):
+    # Hand-worked rows in which no cumulative sum comes near p, so only the
+    # swap-across-the-cut half of the rule can flag a block.
+    g = _load(golden_dir, "ambiguity_rows.json")
+    eps = 2.0 ** -18
+    for case in g["cases"]:
+        prob = np.array([_dyadic(s, eps) for s in case["prob"]])
+        assert prob.sum() == 1.0, case["name"]
+        p = case["top_p"]
+        order, cum, cnt = oracle.top_p_select(prob[None, None, None], p)
+        sel = sorted(order[0, 0, 0, : cnt[0, 0, 0]].tolist())
+        assert sel == case["selected"], case["name"]
+        excl = cum - np.take_along_axis(prob[None, None, None], order, -1)
+        assert (np.abs(cum - p) >= 0.025).all() and (np.abs(excl - p) >= 0.025).all(), case["name"]
+        q = np.zeros((1, 1, prob.size, 2))
+        r = oracle.RouteResult(q, q, prob[None, None, None], prob[None, None, None], order, cum, cnt,
+                               None, None, None, p)
+        amb = oracle.ambiguous_blocks(r, window=g["window"])
+        assert amb[0, 0, 0].astype(int).tolist() == case["ambiguous"], case["name"]
 
 # ----------------------------------------------------------- causal routing ---
 
