@@ -58,3 +58,12 @@ def test_head_split_hand_example():
     assert gpu_of.tolist() == [0, 1, 1, 0, 1]
     assert load.tolist() == [13, 15]
     assert bench.contiguous_head_loads([9, 7, 5, 4, 3], 2).tolist() == [16, 12]
+
+
+def test_metric_names_the_shape_run():
+    # The headline string is the one built for the 32k video shape; a head
+    # share or another workload names its own shape.
+    assert bench.metric_for(32760, 40, 128, "bf16") == bench.METRIC
+    assert "H=5 " in bench.metric_for(32760, 5, 128, "bf16")
+    assert "N=118800 H=24" in bench.metric_for(118800, 24, 128, "bf16")
+    assert "causal" in bench.metric_for(32760, 40, 128, "bf16", causal=True)

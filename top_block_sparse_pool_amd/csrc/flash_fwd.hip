@@ -1278,6 +1278,10 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
     // may hold another call's data).
     const int n = static_cast<int>(items);
     hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p.part_cnt, n);
+    // A failed fill would leave the counters that pick each item's merging
+    // part undefined: report it before the attention kernel is enqueued.
+    const hipError_t ze = hipGetLastError();
+    if (ze != hipSuccess) return ze;
   }
   const int grid = fwd_workers(s, mode, a.fp8);
   KernelFn fn = pick_kernel(s, mode, a.fp8);
