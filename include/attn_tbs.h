@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define ATTN_TBS_ABI_VERSION 5
+#define ATTN_TBS_ABI_VERSION 6
 
 /* Status codes. */
 #define ATTN_OK            0
@@ -295,6 +295,24 @@ int32_t attn_augment_union(const attn_problem* problem, uint8_t* mask, int32_t* 
 int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                         const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
                         void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* attn_sparse_fwd without a workspace argument, for callers that cannot
+ * allocate device memory or hand one over: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments
+ * (minus ws / ws_bytes), arithmetic and results as attn_sparse_fwd, bit for
+ * bit.  Its only scratch -- the persistent queue's control block, 256 bytes
+ * -- lives in a file-scope device array of the library, one per GPU, held
+ * until the process ends; each call zeroes it with a fill kernel on `stream`
+ * before the attention kernel.  The call allocates nothing and needs no prior
+ * attn_schedule to reset a control block.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (for example on two
+ * streams without ordering between them) race and must not be issued.
+ * Problems whose attn_sparse_fwd workspace would exceed the array (the
+ * ATTN_FLAG_PROFILE_WORKERS flag) are rejected with ATTN_E_WORKSPACE before
+ * any HIP call.  Requires nbk <= 2048. */
+int32_t attn_sparse_fwd_noalloc(const attn_problem* problem, const void* q, const void* k, const void* v,
+                                const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
+                                void* o, float* lse, void* stream);
 
 /* Dense attention forward (every key block; causal keeps keys s <= t).
  * Same arithmetic, layouts and workspace rules as attn_sparse_fwd; with

@@ -29,11 +29,11 @@ def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"attn_abi_version", "attn_last_error", "attn_workspace_bytes", "attn_num_workers",
                           "attn_group_size", "attn_route", "attn_schedule", "attn_augment", "attn_augment_union",
-                          "attn_sparse_fwd", "attn_dense_fwd", "attn_quantize_qk_fp8", "attn_sparse_fwd_fp8",
-                          "attn_dense_fwd_fp8"}
+                          "attn_sparse_fwd", "attn_sparse_fwd_noalloc", "attn_dense_fwd", "attn_quantize_qk_fp8",
+                          "attn_sparse_fwd_fp8", "attn_dense_fwd_fp8"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 5
+    assert L.attn_abi_version() == 6
 
 
 def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0, key_block=0, reserved=0):
@@ -190,3 +190,23 @@ def test_fp8_validation():
         return L.attn_dense_fwd_fp8(ctypes.byref(pr), q8, qs, k8, ks, v, o, lse, ws, wsb, None)
     assert dfwd(pr=_problem(d=64)) == 2 and dfwd(qs=None) == 1 and dfwd(o=None) == 1
     assert dfwd(lse=ctypes.c_void_p(0x10001)) == 1 and dfwd(ws=None) == 3
+
+
+def test_sparse_fwd_noalloc_validation():
+    # Bad arguments and a problem whose workspace exceeds the static scratch
+    # (the worker-profiling flag) are rejected before any HIP call.
+    L = tbs.lib()
+    pr = _problem(N=4096, H=2)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None]
+    st = L.attn_sparse_fwd_noalloc(ctypes.byref(_problem(N=4096, H=2, flags=tbs.FLAG_PROFILE_WORKERS)), *args)
+    assert st == tbs.ATTN_E_WORKSPACE
+    assert b"static array holds 256" in L.attn_last_error()
+    st = L.attn_sparse_fwd_noalloc(ctypes.byref(pr), None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None)
+    assert st == tbs.ATTN_E_INVALID and b"q is NULL" in L.attn_last_error()
+    st = L.attn_sparse_fwd_noalloc(ctypes.byref(pr), FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None)
+    assert st == tbs.ATTN_E_INVALID and b"row_cnt" in L.attn_last_error()
+    st = L.attn_sparse_fwd_noalloc(ctypes.byref(pr), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   ctypes.c_void_p(0x10004), FAKE, None)
+    assert st == tbs.ATTN_E_INVALID and b"o is not 16-byte aligned" in L.attn_last_error()
+    st = L.attn_sparse_fwd_noalloc(ctypes.byref(_problem(d=80)), *args)
+    assert st == tbs.ATTN_E_UNSUPPORTED

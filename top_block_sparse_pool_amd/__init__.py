@@ -136,6 +136,8 @@ def lib() -> ctypes.CDLL:
     L.attn_schedule.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     L.attn_sparse_fwd.restype = i32
     L.attn_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_sparse_fwd_noalloc.restype = i32
+    L.attn_sparse_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_dense_fwd.restype = i32
     L.attn_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_augment.restype = i32
@@ -328,6 +330,20 @@ def sparse_fwd(q, k, v, row_cnt, row_idx, block: int, work_list=None, scale: Opt
     return o, lse
 
 
+def sparse_fwd_noalloc(q, k, v, row_cnt, row_idx, block: int, work_list=None, scale: Optional[float] = None,
+                       o=None, lse=None, want_lse: bool = True, flags: int = 0, causal: bool = False,
+                       key_block: Optional[int] = None):
+    """attn_sparse_fwd_noalloc: attn_sparse_fwd whose queue counters live in the
+    library's static per-GPU scratch (no workspace).  Pass o (and lse) to keep
+    the call free of allocations; calls on one GPU must not overlap."""
+    _require_device(q, k, v, row_cnt, row_idx, work_list)
+    pr = make_problem(q, block, causal=causal, scale=scale, flags=flags, key_block=key_block)
+    o, lse = _out_tensors(q, o, lse, want_lse)
+    _check(lib().attn_sparse_fwd_noalloc(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(row_cnt),
+                                         _ptr(row_idx), _ptr(work_list), _ptr(o), _ptr(lse), _stream()))
+    return o, lse
+
+
 def dense_fwd(q, k, v, block: int, causal: bool = False, scale: Optional[float] = None,
               ws: Optional[torch.Tensor] = None, o=None, lse=None, want_lse: bool = True, flags: int = 0):
     """attn_dense_fwd: dense (optionally causal) attention, the p = 1 case."""
@@ -436,6 +452,7 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
 
 __all__ = [
     "lib", "AttnError", "Problem", "Route", "make_problem", "default_head_window", "workspace", "workspace_bytes", "num_workers",
-    "route", "schedule", "augment", "augment_union", "sparse_fwd", "dense_fwd", "sparse_attention", "LIB_PATH",
+    "route", "schedule", "augment", "augment_union", "sparse_fwd", "sparse_fwd_noalloc", "dense_fwd",
+    "sparse_attention", "LIB_PATH",
     "QuantizedQK", "quantize_qk_fp8", "sparse_fwd_fp8", "dense_fwd_fp8", "FP8_TILE",
 ]

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libattn_tbs.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["csrc/abi.cpp", "csrc/router.hip", "csrc/schedule.hip", "csrc/augment.hip", "csrc/quant.hip",
-           "csrc/flash_fwd.hip"]
+           "csrc/flash_fwd.hip", "csrc/noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [

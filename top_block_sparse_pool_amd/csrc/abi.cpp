@@ -324,6 +324,40 @@ TBS_EXPORT int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, c
                  ws, ws_bytes, stream);
 }
 
+TBS_EXPORT int32_t attn_sparse_fwd_noalloc(const attn_problem* problem, const void* q, const void* k, const void* v,
+                                           const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
+                                           void* o, float* lse, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if (s.nbk > kMaxSparseBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd_noalloc: %d key blocks per sequence exceed %d", s.nbk,
+                kMaxSparseBlocks);
+  if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(row_idx, "row_idx", false)) ||
+      (st = check_i32(work_list, "work_list", true)))
+    return st;
+  const int mode = s.causal ? tbs::kSparseCausal : tbs::kSparse;
+  const size_t need = fwd_bytes(s, mode);
+  if (need > tbs::noalloc_scratch_bytes())
+    return fail(ATTN_E_WORKSPACE,
+                "attn_sparse_fwd_noalloc: the call needs %zu bytes of scratch, the static array holds %zu "
+                "(ATTN_FLAG_PROFILE_WORKERS needs a workspace: use attn_sparse_fwd)",
+                need, tbs::noalloc_scratch_bytes());
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(o, "o")))
+    return st;
+  if (lse && !aligned(lse, 4)) return fail(ATTN_E_INVALID, "lse is not 4-byte aligned");
+  void* scratch = nullptr;
+  hipError_t e = tbs::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return device_status(e, "attn_sparse_fwd_noalloc scratch lookup");
+  auto strm = static_cast<hipStream_t>(stream);
+  // The queue counters must be zero when the attention kernel starts.
+  e = tbs::noalloc_clear(scratch, tbs::noalloc_scratch_bytes(), strm);
+  if (e != hipSuccess) return device_status(e, "attn_sparse_fwd_noalloc scratch clear");
+  return run_fwd(s, mode, q, k, v, row_cnt, row_idx, work_list, o, lse, scratch, tbs::noalloc_scratch_bytes(),
+                 stream);
+}
+
 TBS_EXPORT int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                                   void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
   tbs::Shape s;

@@ -105,4 +105,11 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
 
 int device_cu_count();
 
+// Allocation-free sparse attention: the device address of this device's
+// file-scope scratch array (looked up once per device), its size, and a fill
+// kernel that zeroes it on `stream`.
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
+hipError_t noalloc_clear(void* ptr, size_t bytes, hipStream_t stream);
+
 }  // namespace tbs
