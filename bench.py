@@ -103,6 +103,72 @@ def executed_flops(mask: np.ndarray, n_tokens: int, block: int, head_dim: int, c
     return int(4 * head_dim * int((mask.astype(np.int64) * pairs).sum()))
 
 
+def union_tiles(mask: np.ndarray, n_tokens: int, block: int, key_block: int, group: int) -> int:
+    """64-key tiles the attention kernel stages per launch: for every work item
+    (`group` consecutive query blocks of one head) the union of its rows'
+    selected key blocks, each key block holding key_block/64 tiles (the last
+    block only the tiles its keys reach)."""
+    nbq, nbk = mask.shape[-2], mask.shape[-1]
+    rows = mask.reshape(-1, nbq, nbk).astype(bool)
+    ng = -(-nbq // group)
+    pad = np.zeros((rows.shape[0], ng * group, nbk), dtype=bool)
+    pad[:, :nbq] = rows
+    union = pad.reshape(rows.shape[0], ng, group, nbk).any(axis=2)          # [heads, items, nbk]
+    per_block = np.full(nbk, key_block // 64, dtype=np.int64)
+    per_block[-1] = -(-(n_tokens - (nbk - 1) * key_block) // 64)
+    return int((union.astype(np.int64) * per_block).sum())
+
+
+def summarize_counters(fetch_db: str, write_db: str, kernel: str, calib_mib: int, first: int) -> dict:
+    """HBM bytes per launch of `kernel` from two rocprofv3 counter databases
+    (one FETCH_SIZE pass, one WRITE_SIZE pass of the same bench command with
+    --copy-calibration-mib): each counter (KiB) is scaled by the bytes a plain
+    copy of calib_mib MiB moves over what the counter reads for it, and
+    averaged over the kernel's first `first` dispatches (the warm-up and timed
+    steps of the run)."""
+    import sqlite3
+
+    def read(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select dispatch_id, kernel_name, sum(value) from counters_collection "
+                           "where counter_name = ? group by dispatch_id order by dispatch_id", (counter,)).fetchall()
+        con.close()
+        copy = [v for _, name, v in rows if "copyBuffer" in name and v > 0.25 * calib_mib * 1024]
+        if not copy:
+            raise ValueError(f"{db}: no calibration copy of {calib_mib} MiB found")
+        vals = [v for _, name, v in rows if kernel in name][:first]
+        if not vals:
+            raise ValueError(f"{db}: no dispatch of a kernel named like {kernel!r}")
+        factor = calib_mib * 1024.0 / copy[0]
+        return float(np.mean(vals)) * 1024.0 * factor, factor, len(vals), (min(vals), max(vals))
+
+    fetch, ff, nf, fr = read(fetch_db, "FETCH_SIZE")
+    write, wf, nw, wr = read(write_db, "WRITE_SIZE")
+    return {"fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write, "fetch_scale": ff, "write_scale": wf,
+            "dispatches": min(nf, nw), "fetch_kib_range": fr, "write_kib_range": wr}
+
+
+def summarize_trace(db: str, kernel: str, warmup: int, steps: int) -> dict:
+    """Per-kernel dispatch durations (microseconds) from a rocprofv3 kernel-trace
+    database, and the mean over the `steps` timed dispatches of `kernel` that
+    follow its `warmup` first ones (the timed steps of a bench.py run)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration from kernels order by start").fetchall()
+    con.close()
+    per = {}
+    for name, dur in rows:
+        per.setdefault(name, []).append(dur / 1e3)
+    table = sorted(((n, len(v), float(np.mean(v)), float(np.min(v)), float(np.max(v))) for n, v in per.items()),
+                   key=lambda r: -r[1] * r[2])
+    hits = [v for n, v in per.items() if kernel in n]
+    if not hits:
+        raise ValueError(f"{db}: no dispatch of a kernel named like {kernel!r}")
+    timed = hits[0][warmup:warmup + steps]
+    return {"table": table, "timed_mean_us": float(np.mean(timed)), "timed_min_us": float(np.min(timed)),
+            "timed_max_us": float(np.max(timed)), "timed_dispatches": len(timed)}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +196,17 @@ def parse():
                     help="time one GPU's share of a head split over this many GPUs (the most loaded one)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print the HBM bytes per launch of the sparse attention kernel from two rocprofv3 "
+                         "counter databases (FETCH_SIZE and WRITE_SIZE passes of a run with "
+                         "--copy-calibration-mib) and exit; needs no GPU")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DB",
+                    help="print per-kernel durations from a rocprofv3 --kernel-trace database and the mean of the "
+                         "timed sparse-kernel dispatches (after --warmup, --steps of them) and exit; needs no GPU")
+    ap.add_argument("--counter-kernel", default="flash_fwd_bf16_pp<128, 64, 64, 0, false>",
+                    help="kernel name fragment for --summarize-counters and --summarize-trace")
+    ap.add_argument("--counter-dispatches", type=int, default=3,
+                    help="first dispatches of the kernel averaged by --summarize-counters (warm-up + steps)")
     return ap.parse_args()
 
 
@@ -237,6 +314,30 @@ def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False, block=None,
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        res = summarize_trace(args.summarize_trace, args.counter_kernel, args.warmup, args.steps)
+        print("| kernel | calls | avg (us) | min (us) | max (us) |")
+        print("|---|---|---|---|---|")
+        for name, n, avg, lo, hi in res["table"]:
+            short = name.replace("(anonymous namespace)::", "").split("(")[0] if "<" not in name else \
+                name.replace("(anonymous namespace)::", "").split(">(")[0] + ">"
+            print(f"| {short} | {n} | {avg:.1f} | {lo:.1f} | {hi:.1f} |")
+        print(f"\ntimed dispatches of {args.counter_kernel} ({res['timed_dispatches']} after {args.warmup} "
+              f"warm-up): {res['timed_mean_us']:.1f} us average ({res['timed_min_us']:.1f} .. {res['timed_max_us']:.1f})")
+        return
+    if args.summarize_counters:
+        res = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.counter_kernel,
+                                 args.copy_calibration_mib or 1024, args.counter_dispatches)
+        print(f"- workload: {args.workload}{'-fp8' if args.fp8 else ''}")
+        print(f"- kernel_source_sha256: {kernel_source_hash()}")
+        print(f"- fetch_bytes_per_launch: {res['fetch_bytes_per_launch']:.6e}")
+        print(f"- write_bytes_per_launch: {res['write_bytes_per_launch']:.6e}")
+        print(f"- fetch_scale: {res['fetch_scale']:.5f}")
+        print(f"- write_scale: {res['write_scale']:.5f}")
+        print(f"- dispatches_averaged: {res['dispatches']}")
+        print(f"- fetch_kib_range: {res['fetch_kib_range'][0]:.0f} .. {res['fetch_kib_range'][1]:.0f}")
+        print(f"- write_kib_range: {res['write_kib_range'][0]:.0f} .. {res['write_kib_range'][1]:.0f}")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by head across GPUs, which this build does not run)", file=sys.stderr)
@@ -519,6 +620,24 @@ def main():
     if not args.no_cpu_baseline and share is None:
         cpu = cpu_baseline(q, k, v, w, mask, args.cpu_seconds, args.seed, causal, blk, kb)
 
+    # Bytes the attention kernel moves: the algorithmic bytes (Q, K, V read and
+    # O written once) and the K/V tiles it stages into LDS (every tile of
+    # every work item's union, counted from the routed lists), beside the
+    # HBM bytes the counters measured.
+    tiles = union_tiles(mask, N, blk, kb, G)
+    tile_bytes = 64 * d * (1 if fp8 else 2) + 64 * d * 2
+    elems = B * H * N * d
+    # bf16: Q, K, V read and O written, 2 bytes each; fp8: Q and K codes 1 byte
+    # and their scales; LSE 4 bytes per token either way
+    alg_bytes = (elems * 8 if not fp8 else elems * 6 + B * H * N * 4 + B * H * (-(-N // 64)) * 4) + B * H * N * 4
+    traffic_key = (w.name + (f"-share{share['gpus']}" if share else "") + ("-causal" if causal else "")
+                   + ("-fp8" if fp8 else "") + ("" if (blk, kb) == (w.block, w.block) else f"-b{blk}k{kb}"))
+    traffic = measured_traffic(traffic_key)
+    traffic_detail = {"union_tiles": tiles, "staged_kv_bytes": tiles * tile_bytes,
+                      "algorithmic_bytes": alg_bytes,
+                      "hbm_bytes_measured": traffic,
+                      "hbm_over_algorithmic": None if traffic is None else traffic / alg_bytes,
+                      "staged_over_algorithmic": tiles * tile_bytes / alg_bytes}
     peak = FP8_QK_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
     # The metric string names the shape and precision actually run; only the
     # headline run (video-32k, whole problem, bf16, its own routing settings)
@@ -558,9 +677,8 @@ def main():
                      "kernel": f"flash_fwd_bf16_pp ({'sparse causal' if causal else 'sparse'}{', fp8 QK' if fp8 else ''})",
                      "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": fwd_tflops / peak,
-                     "traffic": measured_traffic(w.name + (f"-share{share['gpus']}" if share else "")
-                                                 + ("-causal" if causal else "") + ("-fp8" if fp8 else "")
-                                                 + ("" if (blk, kb) == (w.block, w.block) else f"-b{blk}k{kb}"))},
+                     "traffic": traffic},
+        "traffic_detail": traffic_detail,
         "dense_same_shape": dense,
         "cold_cache": cold,
         "load_imbalance": lif,

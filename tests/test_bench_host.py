@@ -67,3 +67,60 @@ def test_metric_names_the_shape_run():
     assert "H=5 " in bench.metric_for(32760, 5, 128, "bf16")
     assert "N=118800 H=24" in bench.metric_for(118800, 24, 128, "bf16")
     assert "causal" in bench.metric_for(32760, 40, 128, "bf16", causal=True)
+
+
+def test_union_tiles_counts_item_unions():
+    # 5 query blocks of 64 over 3 key blocks of 128 (last one 40 keys: 1 tile),
+    # items of 2 query blocks: {0,1}, {2,3}, {4}.
+    mask = np.array([[1, 0, 0],
+                     [0, 1, 0],
+                     [1, 0, 1],
+                     [1, 0, 0],
+                     [0, 0, 1]], dtype=np.uint8)[None, None]
+    N = 2 * 128 + 40
+    # item 0: blocks 0,1 -> 2 + 2 tiles; item 1: blocks 0,2 -> 2 + 1; item 2: block 2 -> 1
+    assert bench.union_tiles(mask, N, 64, 128, 2) == 8
+    # one block per item: the per-row sum
+    assert bench.union_tiles(mask, N, 64, 128, 1) == 2 + 2 + 3 + 2 + 1
+
+
+def test_summarize_counters_scales_by_the_copy(tmp_path):
+    import sqlite3
+
+    def db(path, counter, copy_kib, kernel_kib):
+        con = sqlite3.connect(path)
+        con.execute("create table counters_collection (dispatch_id int, kernel_name text, counter_name text, "
+                    "value real)")
+        rows = [(1, "__amd_rocclr_copyBuffer", counter, copy_kib)]
+        rows += [(2 + i, "void ns::flash_fwd_bf16_pp<128, 64, 64, 0, false>(P)", counter, v)
+                 for i, v in enumerate(kernel_kib)]
+        rows += [(9, "void ns::other(P)", counter, 5.0)]
+        con.executemany("insert into counters_collection values (?, ?, ?, ?)", rows)
+        con.commit()
+        con.close()
+        return str(path)
+
+    f = db(tmp_path / "f.db", "FETCH_SIZE", 512 * 1024, [1000.0, 3000.0, 2000.0, 9999.0])
+    w = db(tmp_path / "w.db", "WRITE_SIZE", 1024 * 1024, [10.0, 30.0, 20.0, 99.0])
+    res = bench.summarize_counters(f, w, "flash_fwd_bf16_pp<128, 64, 64, 0, false>", 1024, 3)
+    assert res["fetch_scale"] == 2.0 and res["write_scale"] == 1.0
+    assert res["fetch_bytes_per_launch"] == 2000.0 * 1024 * 2.0      # mean of the first three, scaled
+    assert res["write_bytes_per_launch"] == 20.0 * 1024
+
+
+def test_summarize_trace_timed_dispatches(tmp_path):
+    import sqlite3
+    path = str(tmp_path / "t.db")
+    con = sqlite3.connect(path)
+    con.execute("create table kernels (name text, start int, duration int)")
+    durs = [900, 800, 100, 200, 300, 400, 5000]            # 2 warm-up, 4 timed, then other launches
+    con.executemany("insert into kernels values (?, ?, ?)",
+                    [("void ns::flash_fwd_bf16_pp<128, 64, 64, 0, false>(P)", i, d * 1000) for i, d in enumerate(durs)]
+                    + [("ns::schedule_kernel(int)", 100 + i, 7000) for i in range(3)])
+    con.commit()
+    con.close()
+    res = bench.summarize_trace(path, "flash_fwd_bf16_pp<128, 64, 64, 0, false>", 2, 4)
+    assert res["timed_dispatches"] == 4 and res["timed_mean_us"] == 250.0
+    assert res["timed_min_us"] == 100.0 and res["timed_max_us"] == 400.0
+    names = [r[0] for r in res["table"]]
+    assert len(names) == 2 and res["table"][0][1] == 7
