@@ -6,9 +6,13 @@ counted and returned.  Rows whose masks agree must also agree exactly on the
 row count and the ascending index list.
 
 Attention: GPU outputs (bf16 or fp32, upcast exactly) are compared element by
-element with the fp64 oracle on query blocks whose masks agree: max abs error
-<= 2e-2 for bf16 inputs and <= 1e-4 for fp32 inputs.  LSE uses 2e-3 / 1e-4;
-a query without allowed keys must be -inf on both sides (and O = 0).
+element with the fp64 oracle evaluated on the GPU's own mask (which equals the
+oracle's mask except inside the window, so a row whose selection differs by an
+ambiguous block is still checked, against the attention its selection defines):
+max abs error <= 2e-2 for bf16 inputs and <= 1e-4 for fp32 inputs.  LSE uses
+2e-3 / 1e-4; a query without allowed keys must be -inf on both sides (and O = 0).
+Sampled units are extended by every query block whose mask row differs from the
+oracle's (routed_units).
 """
 from __future__ import annotations
 
@@ -70,7 +74,13 @@ def compare_route(gpu_route, ref) -> dict:
     assert (got[rows_agree] == want[rows_agree]).all(), "index lists differ on agreeing rows"
     hc = gpu_route.head_cnt.cpu().numpy().astype(np.int64)
     assert (hc == rc.sum(-1)).all(), "head counts are not the sum of row counts"
-    return dict(rows_agree=rows_agree, ambiguous_mismatches=int(diff.sum()))
+    return dict(rows_agree=rows_agree, ambiguous_mismatches=int(diff.sum()), gpu_mask=mask)
+
+
+def routed_units(units, cmp) -> list:
+    """`units` plus every query block whose GPU mask row differs from the oracle's."""
+    extra = {tuple(int(x) for x in u) for u in np.argwhere(~cmp["rows_agree"])}
+    return sorted({tuple(int(x) for x in u) for u in units} | extra)
 
 
 def compare_units(o_gpu, lse_gpu, q, k, v, block, units, mask, dtype, scale=None, causal=False, key_block=None):
@@ -101,10 +111,6 @@ def compare_units(o_gpu, lse_gpu, q, k, v, block, units, mask, dtype, scale=None
     if lse_gpu is not None:
         assert lmax <= LSE_TOL[dtype], f"max |LSE - LSE_ref| = {lmax:.3e} > {LSE_TOL[dtype]}"
     return emax, lmax
-
-
-def units_where(rows_agree, units):
-    return [u for u in units if rows_agree[u]]
 
 
 def dense_causal_splits(w) -> bool:

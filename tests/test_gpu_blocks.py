@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import top_block_sparse_pool_amd as tbs
-from parity import compare_route, compare_units, oracle_route_per_head, to64
+from parity import compare_route, compare_units, oracle_route_per_head, routed_units, to64
 from workloads import WORKLOADS, custom_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -53,9 +53,9 @@ def test_mixed_blocks_path_matches_oracle(w, kb, causal):
     want_wl = oracle.work_list(oracle.group_costs(r.row_cnt.cpu().numpy(), G),
                                tbs.default_head_window(pr) * -(-nb // G))
     assert (wl.cpu().numpy() == want_wl).all()
-    units = [(b, h, i) for b in range(pr.batch) for h in range(pr.heads) for i in range(nb)
-             if cmp["rows_agree"][b, h, i]]
-    err, lerr = compare_units(o, lse, q, k, v, w.block, units, ref["mask"], q.dtype, causal=causal, key_block=kb)
+    units = [(b, h, i) for b in range(pr.batch) for h in range(pr.heads) for i in range(nb)]
+    err, lerr = compare_units(o, lse, q, k, v, w.block, units, cmp["gpu_mask"], q.dtype, causal=causal,
+                              key_block=kb)
     print(f"  {len(units)} blocks: max |O err| {err:.3e}, |LSE err| {lerr:.3e}", flush=True)
 
 
@@ -122,6 +122,7 @@ def test_mixed_blocks_full_size_video_sample():
     units = []
     for h in range(0, w.heads, 3):
         cand = {0, pr.num_blocks - 1, int(np.argmax(rc[0, h])), int(rng.integers(pr.num_blocks))}
-        units += [(0, h, i) for i in sorted(cand) if cmp["rows_agree"][0, h, i]]
-    e, le = compare_units(o, lse, q, k, v, bq, units, ref["mask"], q.dtype, key_block=kb)
+        units += [(0, h, i) for i in sorted(cand)]
+    units = routed_units(units, cmp)
+    e, le = compare_units(o, lse, q, k, v, bq, units, cmp["gpu_mask"], q.dtype, key_block=kb)
     print(f"  {len(units)} sampled blocks: max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import top_block_sparse_pool_amd as tbs
-from parity import compare_route, compare_units, oracle_route_per_head, dense_causal_splits
+from parity import compare_route, compare_units, dense_causal_splits, oracle_route_per_head, routed_units
 from workloads import WORKLOADS, custom_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -60,9 +60,8 @@ def test_causal_sparse_path_matches_oracle(w):
     want_wl = oracle.work_list(oracle.group_costs(r.row_cnt.cpu().numpy(), G),
                                tbs.default_head_window(pr) * -(-nb // G))
     assert (wl.cpu().numpy() == want_wl).all()
-    units = [(b, h, i) for b in range(pr.batch) for h in range(pr.heads) for i in range(nb)
-             if cmp["rows_agree"][b, h, i]]
-    e, le = compare_units(o, lse, q, k, v, w.block, units, ref["mask"], q.dtype, causal=True)
+    units = [(b, h, i) for b in range(pr.batch) for h in range(pr.heads) for i in range(nb)]
+    e, le = compare_units(o, lse, q, k, v, w.block, units, cmp["gpu_mask"], q.dtype, causal=True)
     print(f"  max |O err| {e:.3e}  max |LSE err| {le:.3e} over {len(units)} blocks", flush=True)
     o2, lse2 = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, ws=ws, causal=True)
     torch.cuda.synchronize()
@@ -138,8 +137,9 @@ def test_causal_full_size_video_sample():
     units = []
     for h in range(0, w.heads, 3):
         cand = {0, nb - 1, int(np.argmax(rc[0, h])), int(rng.integers(nb))}
-        units += [(0, h, i) for i in sorted(cand) if cmp["rows_agree"][0, h, i]]
-    e, le = compare_units(o, lse, q, k, v, w.block, units, ref["mask"], q.dtype, causal=True)
+        units += [(0, h, i) for i in sorted(cand)]
+    units = routed_units(units, cmp)
+    e, le = compare_units(o, lse, q, k, v, w.block, units, cmp["gpu_mask"], q.dtype, causal=True)
     print(f"  {len(units)} sampled blocks: max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)
 
 

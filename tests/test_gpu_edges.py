@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import top_block_sparse_pool_amd as tbs
-from parity import compare_route, compare_units, oracle_route_per_head, to64
+from parity import compare_route, compare_units, oracle_route_per_head, routed_units, to64
 from workloads import custom_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -59,8 +59,8 @@ def test_largest_routing_size():
     cmp = compare_route(r, ref)
     assert (wl.cpu().numpy() == oracle.work_list(oracle.group_costs(r.row_cnt.cpu().numpy(), pr.group),
                                                  tbs.default_head_window(pr) * -(-1024 // pr.group))).all()
-    units = [(0, h, i) for h in range(2) for i in (0, 511, 1023) if cmp["rows_agree"][0, h, i]]
-    e, le = compare_units(o, lse, q, k, v, w.block, units, ref["mask"], q.dtype)
+    units = routed_units([(0, h, i) for h in range(2) for i in (0, 511, 1023)], cmp)
+    e, le = compare_units(o, lse, q, k, v, w.block, units, cmp["gpu_mask"], q.dtype)
     print(f"  ambiguous mismatches {cmp['ambiguous_mismatches']}; max |O err| {e:.3e}", flush=True)
 
 
