@@ -14,7 +14,7 @@ peak.  The CPU baseline is the fp64 oracle timed on a bounded sample of the
 same workload on this machine's host cores.  --causal runs the same workload
 with causal routing and causal attention (executed FLOPs then count the
 allowed token pairs of diagonal blocks only).  --fp8 quantises Q and K to
-E4M3 in the step (attn_quantize_qk_fp8) and runs attn_sparse_fwd_fp8; its
+E4M3 in the step's routing pass (attn_route_fp8) and runs attn_sparse_fwd_fp8; its
 roofline peak is the mix of the fp8 rate (S) and the bf16 rate (P V).
 --share-of G measures one GPU's share of a G-way split by whole heads: all
 heads are routed, the heads go to the G GPUs longest first by their
@@ -414,7 +414,11 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        tbs.route(q, k, w.top_p, blk, ws=ws, out=route_out, causal=causal, key_block=kb)
+        if fp8:
+            # routing and E4M3 quantisation of Q and K in one read of Q and K
+            tbs.route_fp8(q, k, w.top_p, blk, ws=ws, out=route_out, qk_out=qk8, causal=causal, key_block=kb)
+        else:
+            tbs.route(q, k, w.top_p, blk, ws=ws, out=route_out, causal=causal, key_block=kb)
         if ev is not None:
             ev[1].record()
         if args.sasa:
@@ -424,8 +428,6 @@ def main():
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
         if ev is not None:
             ev[2].record()
-        if fp8:
-            tbs.quantize_qk_fp8(q, k, blk, out=qk8, key_block=kb)
         if ev is not None:
             ev[3].record()
         fwd(route_out.row_cnt, route_out.row_idx, work_list)

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define ATTN_TBS_ABI_VERSION 6
+#define ATTN_TBS_ABI_VERSION 7
 
 /* Status codes. */
 #define ATTN_OK            0
@@ -344,7 +344,8 @@ int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k
  * attn_sparse_fwd.  The result is, up to fp32 rounding, exact attention on
  * the dequantised Q and K: q_t = code * q_scale[t], k_s = code * k_scale[s/64].
  * These calls take bf16 problems with head_dim 128 (ATTN_E_UNSUPPORTED
- * otherwise); routing (attn_route) keeps reading the bf16 Q and K. */
+ * otherwise); routing keeps reading the bf16 Q and K (attn_route, or
+ * attn_route_fp8, which also quantises them in the same pass). */
 
 /* Dynamic E4M3 quantisation of Q and K.  For each group (a query token's d
  * values; the d values of up to 64 tokens of keys, tile tau holding tokens
@@ -361,6 +362,17 @@ int32_t attn_dense_fwd(const attn_problem* problem, const void* q, const void* k
  * One kernel launch; reads Q and K once. */
 int32_t attn_quantize_qk_fp8(const attn_problem* problem, const void* q, const void* k, uint8_t* q8,
                              float* q_scale, uint8_t* k8, float* k_scale, void* stream);
+
+/* attn_route and attn_quantize_qk_fp8 in one pass over Q and K: the block
+ * means, scores, softmax and top-p cut of attn_route (the same mask, lists,
+ * counts and block probabilities, bit for bit) and the E4M3 codes and scales
+ * of attn_quantize_qk_fp8 (bit for bit), with each element of Q and K read
+ * from HBM once by a kernel that pools and quantises the same registers.
+ * Arguments as in the two calls; bf16 problems with head_dim 128
+ * (ATTN_E_UNSUPPORTED otherwise); ws as for attn_route. */
+int32_t attn_route_fp8(const attn_problem* problem, const void* q, const void* k, double top_p, uint8_t* mask,
+                       int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt, double* block_prob, uint8_t* q8,
+                       float* q_scale, uint8_t* k8, float* k_scale, void* ws, size_t ws_bytes, void* stream);
 
 /* attn_sparse_fwd with Q and K as E4M3 codes and scales (from
  * attn_quantize_qk_fp8).  The logit of query t and key s is

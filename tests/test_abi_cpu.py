@@ -30,10 +30,10 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"attn_abi_version", "attn_last_error", "attn_workspace_bytes", "attn_num_workers",
                           "attn_group_size", "attn_route", "attn_schedule", "attn_augment", "attn_augment_union",
                           "attn_sparse_fwd", "attn_sparse_fwd_noalloc", "attn_dense_fwd", "attn_quantize_qk_fp8",
-                          "attn_sparse_fwd_fp8", "attn_dense_fwd_fp8"}
+                          "attn_route_fp8", "attn_sparse_fwd_fp8", "attn_dense_fwd_fp8"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 6
+    assert L.attn_abi_version() == 7
 
 
 def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0, key_block=0, reserved=0):
@@ -210,3 +210,21 @@ def test_sparse_fwd_noalloc_validation():
     assert st == tbs.ATTN_E_INVALID and b"o is not 16-byte aligned" in L.attn_last_error()
     st = L.attn_sparse_fwd_noalloc(ctypes.byref(_problem(d=80)), *args)
     assert st == tbs.ATTN_E_UNSUPPORTED
+
+
+def test_route_fp8_validation():
+    L = tbs.lib()
+    args = [FAKE, FAKE, ctypes.c_double(0.9), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, WS,
+            ctypes.c_size_t(1 << 30), None]
+    assert L.attn_route_fp8(ctypes.byref(_problem(d=64)), *args) == tbs.ATTN_E_UNSUPPORTED
+    assert L.attn_route_fp8(ctypes.byref(_problem(dtype=1)), *args) == tbs.ATTN_E_UNSUPPORTED
+    bad = list(args)
+    bad[8] = None                                                     # q8
+    assert L.attn_route_fp8(ctypes.byref(_problem(N=4096)), *bad) == tbs.ATTN_E_INVALID
+    assert b"q8" in L.attn_last_error()
+    bad = list(args)
+    bad[2] = ctypes.c_double(1.5)                                     # top_p
+    assert L.attn_route_fp8(ctypes.byref(_problem(N=4096)), *bad) == tbs.ATTN_E_INVALID
+    small = list(args)
+    small[13] = ctypes.c_size_t(64)                                   # workspace too small
+    assert L.attn_route_fp8(ctypes.byref(_problem(N=4096)), *small) == tbs.ATTN_E_WORKSPACE

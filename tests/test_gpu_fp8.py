@@ -287,3 +287,56 @@ def test_full_size_long_video_fp8_sampled():
         units = [(0, 0, i) for i in sorted(cand)]
         e, le = compare_units(o[:, sl], lse[:, sl], ref.q_deq, ref.k_deq, v[:, sl], w.block, units, gmask, q.dtype)
         print(f"  head {h}: {len(units)} sampled blocks, max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)
+
+
+ROUTE_FP8_CASES = [
+    (custom_workload(1, 3, 1000, 128, 64, "bf16", 0.9, wid=540), None, False),     # ragged tail of 40
+    (custom_workload(2, 2, 1300, 128, 128, "bf16", 0.9, wid=541), None, False),    # block 128, tail 20
+    (custom_workload(1, 2, 1100, 128, 128, "bf16", 0.85, wid=542), 64, False),     # 128-row blocks over 64 keys
+    (custom_workload(1, 2, 1100, 128, 64, "bf16", 0.85, wid=543), 128, True),      # 64 over 128, causal
+    (custom_workload(1, 2, 64, 128, 64, "bf16", 0.5, wid=544), None, False),       # one block
+    (custom_workload(1, 1, 5, 128, 64, "bf16", 0.9, wid=545), None, True),         # N < block
+]
+
+
+@pytest.mark.parametrize("w,kb,causal", ROUTE_FP8_CASES, ids=lambda x: getattr(x, "name", str(x)))
+def test_route_fp8_equals_route_then_quantize(w, kb, causal):
+    # One read of Q and K gives the routing of attn_route and the codes of
+    # attn_quantize_qk_fp8, bit for bit.
+    q, k, v = _inputs(w)
+    pr = tbs.make_problem(q, w.block, causal=causal, key_block=kb)
+    ws = tbs.workspace(pr, DEV)
+    r0 = tbs.route(q, k, w.top_p, w.block, ws=ws, return_prob=True, causal=causal, key_block=kb)
+    qk0 = tbs.quantize_qk_fp8(q, k, w.block, key_block=kb)
+    torch.cuda.synchronize()
+    r1, qk1 = tbs.route_fp8(q, k, w.top_p, w.block, ws=ws, return_prob=True, causal=causal, key_block=kb)
+    torch.cuda.synchronize()
+    for a, b in [(r0.mask, r1.mask), (r0.row_cnt, r1.row_cnt), (r0.head_cnt, r1.head_cnt),
+                 (r0.block_prob, r1.block_prob), (qk0.q8, qk1.q8), (qk0.k8, qk1.k8),
+                 (qk0.q_scale, qk1.q_scale), (qk0.k_scale, qk1.k_scale)]:
+        assert torch.equal(a, b)
+    rc = r0.row_cnt.cpu().numpy()
+    valid = np.arange(pr.num_key_blocks)[None, None, None, :] < rc[..., None]
+    if not causal:
+        assert torch.equal(r0.row_idx, r1.row_idx)
+    else:
+        assert (np.where(valid, r0.row_idx.cpu().numpy(), -1) == np.where(valid, r1.row_idx.cpu().numpy(), -1)).all()
+    # and the routing itself against the oracle
+    compare_route(r1, oracle_route_per_head(q, k, w.block, w.top_p, causal=causal, key_block=kb))
+
+
+def test_route_fp8_full_size_video():
+    w = WORKLOADS["video-32k"]
+    print(f"[case] route_fp8 {w.describe()}", flush=True)
+    q, k, v = [t.to(DEV) for t in make_inputs(w, 0)]
+    pr = tbs.make_problem(q, w.block)
+    ws = tbs.workspace(pr, DEV)
+    r0 = tbs.route(q, k, w.top_p, w.block, ws=ws, return_prob=True)
+    qk0 = tbs.quantize_qk_fp8(q, k, w.block)
+    torch.cuda.synchronize()
+    r1, qk1 = tbs.route_fp8(q, k, w.top_p, w.block, ws=ws, return_prob=True)
+    torch.cuda.synchronize()
+    for a, b in [(r0.mask, r1.mask), (r0.row_cnt, r1.row_cnt), (r0.row_idx, r1.row_idx), (r0.head_cnt, r1.head_cnt),
+                 (r0.block_prob, r1.block_prob), (qk0.q8, qk1.q8), (qk0.k8, qk1.k8), (qk0.q_scale, qk1.q_scale),
+                 (qk0.k_scale, qk1.k_scale)]:
+        assert torch.equal(a, b)

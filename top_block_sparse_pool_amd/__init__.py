@@ -146,6 +146,8 @@ def lib() -> ctypes.CDLL:
     L.attn_augment_union.argtypes = [P, vp, vp, vp, vp, vp]
     L.attn_quantize_qk_fp8.restype = i32
     L.attn_quantize_qk_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_route_fp8.restype = i32
+    L.attn_route_fp8.argtypes = [P, vp, vp, dbl, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_sparse_fwd_fp8.restype = i32
     L.attn_sparse_fwd_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_dense_fwd_fp8.restype = i32
@@ -387,6 +389,45 @@ def quantize_qk_fp8(q: torch.Tensor, k: torch.Tensor, block: int = 64, out: Opti
     return out
 
 
+def _new_quantized(q: torch.Tensor) -> QuantizedQK:
+    B, H, N, d = q.shape
+    dev = q.device
+    return QuantizedQK(torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+                       torch.empty((B, H, N), dtype=torch.float32, device=dev),
+                       torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+                       torch.empty((B, H, -(-N // FP8_TILE)), dtype=torch.float32, device=dev))
+
+
+def route_fp8(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: Optional[float] = None,
+              ws: Optional[torch.Tensor] = None, return_prob: bool = False, out: Optional[Route] = None,
+              qk_out: Optional[QuantizedQK] = None, causal: bool = False, key_block: Optional[int] = None):
+    """attn_route_fp8: attn_route and attn_quantize_qk_fp8 in one read of Q and K.
+    Returns (Route, QuantizedQK)."""
+    _require_device(q, k)
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must share shape and dtype")
+    pr = make_problem(q, block, causal=causal, scale=scale, key_block=key_block)
+    B, H, nb, nbk = pr.batch, pr.heads, pr.num_blocks, pr.num_key_blocks
+    dev = q.device
+    if out is None:
+        out = Route(pr, float(top_p),
+                    torch.empty((B, H, nb, nbk), dtype=torch.uint8, device=dev),
+                    torch.empty((B, H, nb), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, nb, nbk), dtype=torch.int32, device=dev),
+                    torch.empty((B, H), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, nb, nbk), dtype=torch.float64, device=dev) if return_prob else None)
+    out.problem, out.top_p = pr, float(top_p)
+    if qk_out is None:
+        qk_out = _new_quantized(q)
+    if ws is None:
+        ws = workspace(pr, dev, OP_ROUTE)
+    _check(lib().attn_route_fp8(ctypes.byref(pr), _ptr(q), _ptr(k), float(top_p), _ptr(out.mask), _ptr(out.row_cnt),
+                                _ptr(out.row_idx), _ptr(out.head_cnt), _ptr(out.block_prob), _ptr(qk_out.q8),
+                                _ptr(qk_out.q_scale), _ptr(qk_out.k8), _ptr(qk_out.k_scale), _ptr(ws), ws.numel(),
+                                _stream()))
+    return out, qk_out
+
+
 def _fp8_problem(qk: QuantizedQK, v: torch.Tensor, block: int, causal: bool, scale, flags, key_block):
     _require_device(qk.q8, qk.q_scale, qk.k8, qk.k_scale, v)
     if qk.q8.shape != v.shape or qk.k8.shape != v.shape:
@@ -428,20 +469,23 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
     """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list).
 
     With sasa=True: route -> schedule with the LPT model -> augment -> schedule
-    again over the augmented counts -> sparse_fwd.  With fp8=True Q and K are
-    quantised to E4M3 (quantize_qk_fp8) after routing and the forward is
-    sparse_fwd_fp8; routing reads the bf16 Q and K either way."""
+    again over the augmented counts -> sparse_fwd.  With fp8=True the routing
+    pass also quantises Q and K to E4M3 (route_fp8: one read of Q and K) and the
+    forward is sparse_fwd_fp8; routing reads the bf16 Q and K either way."""
     pr = make_problem(q, block, causal=causal, scale=scale, key_block=key_block)
     if ws is None:
         ws = workspace(pr, q.device)
-    r = route(q, k, top_p, block, scale=scale, ws=ws, causal=causal, return_prob=sasa, key_block=key_block)
+    if fp8:
+        r, qk = route_fp8(q, k, top_p, block, scale=scale, ws=ws, causal=causal, return_prob=sasa,
+                          key_block=key_block)
+    else:
+        r = route(q, k, top_p, block, scale=scale, ws=ws, causal=causal, return_prob=sasa, key_block=key_block)
     if sasa:
         _, worker_of, worker_load = schedule(pr, r.row_cnt, ws, head_window=head_window,
                                              num_workers=num_workers, lpt=True)
         augment(pr, r, worker_of, worker_load, ws, want_added=False)
     wl = schedule(pr, r.row_cnt, ws, head_window=head_window)
     if fp8:
-        qk = quantize_qk_fp8(q, k, block, key_block=key_block)
         o, lse = sparse_fwd_fp8(qk, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
                                 want_lse=want_lse, causal=causal, key_block=key_block)
     else:
@@ -454,5 +498,5 @@ __all__ = [
     "lib", "AttnError", "Problem", "Route", "make_problem", "default_head_window", "workspace", "workspace_bytes", "num_workers",
     "route", "schedule", "augment", "augment_union", "sparse_fwd", "sparse_fwd_noalloc", "dense_fwd",
     "sparse_attention", "LIB_PATH",
-    "QuantizedQK", "quantize_qk_fp8", "sparse_fwd_fp8", "dense_fwd_fp8", "FP8_TILE",
+    "QuantizedQK", "quantize_qk_fp8", "route_fp8", "sparse_fwd_fp8", "dense_fwd_fp8", "FP8_TILE",
 ]

@@ -395,6 +395,36 @@ TBS_EXPORT int32_t attn_quantize_qk_fp8(const attn_problem* problem, const void*
   return device_status(e, "attn_quantize_qk_fp8 launch");
 }
 
+TBS_EXPORT int32_t attn_route_fp8(const attn_problem* problem, const void* q, const void* k, double top_p,
+                                  uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
+                                  double* block_prob, uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  tbs::Shape s;
+  int32_t st = check_problem(problem, &s);
+  if (st != ATTN_OK) return st;
+  if ((st = check_fp8_problem(s, "attn_route_fp8"))) return st;
+  if (s.nbk > kMaxRouteBlocks)
+    return fail(ATTN_E_UNSUPPORTED, "attn_route_fp8: %d key blocks per sequence exceed %d", s.nbk, kMaxRouteBlocks);
+  if (!(top_p > 0.0 && top_p <= 1.0)) return fail(ATTN_E_INVALID, "top_p must be in (0, 1] (got %g)", top_p);
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(q8, "q8")) ||
+      (st = check_tensor(k8, "k8")) || (st = check_scales(q_scale, k_scale)))
+    return st;
+  if (!mask) return fail(ATTN_E_INVALID, "mask is NULL");
+  if ((st = check_i32(row_cnt, "row_cnt", false)) || (st = check_i32(row_idx, "row_idx", false)) ||
+      (st = check_i32(head_cnt, "head_cnt", false)))
+    return st;
+  if (block_prob && !aligned(block_prob, 8)) return fail(ATTN_E_INVALID, "block_prob is not 8-byte aligned");
+  if ((st = check_ws(ws, ws_bytes, route_bytes(s)))) return st;
+  auto* base = static_cast<unsigned char*>(ws) + tbs::kCtrlBytes;
+  auto* qbar = reinterpret_cast<double*>(base);
+  auto* kbar_t = qbar + static_cast<size_t>(s.B) * s.H * s.nb * s.d;
+  auto strm = static_cast<hipStream_t>(stream);
+  hipError_t e = tbs::launch_pool_quant(s, q, k, qbar, kbar_t, head_cnt, q8, q_scale, k8, k_scale, strm);
+  if (e != hipSuccess) return device_status(e, "attn_route_fp8 pool launch");
+  e = tbs::launch_select(s, qbar, kbar_t, top_p, mask, row_cnt, row_idx, head_cnt, block_prob, strm);
+  return device_status(e, "attn_route_fp8 select launch");
+}
+
 TBS_EXPORT int32_t attn_sparse_fwd_fp8(const attn_problem* problem, const uint8_t* q8, const float* q_scale,
                                        const uint8_t* k8, const float* k_scale, const void* v,
                                        const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,

@@ -38,6 +38,12 @@ constexpr size_t kCtrlBytes = 256;
 // zeroes head_cnt; then scores, softmax, top-p cut and outputs.
 hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qbar, double* kbar_t,
                        int32_t* head_cnt, hipStream_t stream);
+// Pooling of bf16 Q and K (head_dim 128) fused with their E4M3 quantisation
+// (the same codes and scales as launch_quantize_qk, the same means as
+// launch_pool), reading each element once.
+hipError_t launch_pool_quant(const Shape& s, const void* q, const void* k, double* qbar, double* kbar_t,
+                             int32_t* head_cnt, uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
+                             hipStream_t stream);
 hipError_t launch_select(const Shape& s, const double* qbar, const double* kbar_t, double top_p,
                          uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                          double* block_prob, hipStream_t stream);

@@ -20,6 +20,7 @@
 // per-token maxima reduce over the row's lanes with shuffles, the tile
 // maximum over the workgroup through LDS.
 #include "device_common.h"
+#include "e4m3.h"
 #include "launch.h"
 
 namespace tbs {
@@ -27,37 +28,10 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 constexpr int kQuantTile = 64;
-constexpr float kE4M3Max = 448.0f;
 
 __device__ __forceinline__ void load_bf16x8(const unsigned short* src, float* out) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    out[2 * j] = __uint_as_float(w[j] << 16);
-    out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-  }
+  bf16x8_to_f32(*reinterpret_cast<const u32x4*>(src), out);
 }
-
-// Eight codes of x * inv, packed little-endian (element 0 in the low byte).
-// v_cvt_pk_fp8_f32 rounds to nearest even; the clamp keeps every input in
-// the finite E4M3 range.
-__device__ __forceinline__ u32x2 encode8(const float* x, float inv) {
-  float y[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(x[e] * inv, -kE4M3Max), kE4M3Max);
-  u32x2 r;
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    int v = 0;
-    v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * w], y[4 * w + 1], v, false);
-    v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * w + 2], y[4 * w + 3], v, true);
-    r[w] = static_cast<unsigned>(v);
-  }
-  return r;
-}
-
-__device__ __forceinline__ float group_inv(float a) { return a > 0.f ? __fdiv_rn(kE4M3Max, a) : 0.f; }
-__device__ __forceinline__ float group_scale(float a) { return a > 0.f ? __fdiv_rn(a, kE4M3Max) : 0.f; }
 
 template <int D>
 __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
@@ -94,8 +68,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
 #pragma unroll
     for (int off = 1; off < C; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, kWave));
     if (valid) {
-      *reinterpret_cast<u32x2*>(q8 + (base + row) * D + c * 8) = encode8(x, group_inv(a));
-      if (c == 0) q_scale[base + row] = group_scale(a);
+      *reinterpret_cast<u32x2*>(q8 + (base + row) * D + c * 8) = e4m3_encode8(x, e4m3_group_inv(a));
+      if (c == 0) q_scale[base + row] = e4m3_group_scale(a);
     }
   }
 
@@ -120,13 +94,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_qk_kernel(
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kQuantThreads / kWave; ++w) a = fmaxf(a, red[w]);
-  const float inv = group_inv(a);
+  const float inv = e4m3_group_inv(a);
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
     const int row = lo + r0 + pass * RP;
-    if (row < N) *reinterpret_cast<u32x2*>(k8 + (base + row) * D + c * 8) = encode8(xk[pass], inv);
+    if (row < N) *reinterpret_cast<u32x2*>(k8 + (base + row) * D + c * 8) = e4m3_encode8(xk[pass], inv);
   }
-  if (tid == 0) k_scale[bh * nkt + tile] = group_scale(a);
+  if (tid == 0) k_scale[bh * nkt + tile] = e4m3_group_scale(a);
 }
 
 }  // namespace

@@ -8,8 +8,12 @@
 // fp64 so the selection matches exact arithmetic up to fp64 rounding.
 //
 // Kernels:
-//   pool_kernel    one workgroup per (tensor, b, h, block): block means in fp64
-//                  (HBM-bound: reads Q and K once).
+//   pool_qk_kernel one workgroup per (b, h, span of 64 or 128 tokens) of bf16
+//                  Q and K: block means in fp64 (HBM-bound: reads Q and K
+//                  once, every load of a thread in flight at once), and for
+//                  the fp8 path the E4M3 codes and scales of the same rows.
+//   pool_kernel    the same means for fp32 inputs, one workgroup per
+//                  (tensor, b, h, block).
 //   select_kernel  one workgroup per (b, h, R = 8 query blocks): fp64 scores
 //                  for R rows against all key blocks (the R pooled query rows
 //                  staged in LDS and read as broadcasts, pooled K read
@@ -27,6 +31,7 @@
 #include <math.h>
 
 #include "device_common.h"
+#include "e4m3.h"
 #include "launch.h"
 
 namespace tbs {
@@ -109,6 +114,204 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
     for (int x2 = tid; x2 < BH; x2 += kPoolThreads) head_cnt[x2] = 0;
 }
 
+// Block means of bf16 Q and K over one span of SPAN tokens of one (b, h) per
+// workgroup (SPAN = the larger of the query and key block sizes, so every
+// block lies in one span), and with QUANT the E4M3 codes and scales of the
+// same rows (one scale per query token, one per 64-token key tile), from one
+// read of each element.
+//
+// Summation order (fp64, fixed): per 64-token tile, a thread adds its rows
+// r0, r0 + RP, ... of one 16-byte column chunk; the row groups of a wave
+// combine by xor shuffles (the same sum in every lane, fp64 addition being
+// commutative); the four waves add in wave order; a 128-token block adds its
+// two tiles in order.  The mean divides by the block's valid tokens.
+template <int D, int SPAN, bool QUANT>
+__global__ __launch_bounds__(kPoolThreads) void pool_qk_kernel(
+    const unsigned short* __restrict__ q, const unsigned short* __restrict__ k, double* __restrict__ qbar,
+    double* __restrict__ kbar_t, int32_t* __restrict__ head_cnt, uint8_t* __restrict__ q8,
+    float* __restrict__ q_scale, uint8_t* __restrict__ k8, float* __restrict__ k_scale, int BH, int N, int nbq,
+    int bq, int nbk, int bk, int nspan, int nkt) {
+  constexpr int C = D / 8;                    // 16-byte chunks per token row
+  constexpr int RP = kPoolThreads / C;        // rows per pass (16 for d = 128, 32 for d = 64)
+  constexpr int P = 64 / RP;                  // passes per 64-token tile
+  constexpr int T = SPAN / 64;                // tiles per span
+  constexpr int NW = kPoolThreads / kWave;
+  static_assert(!QUANT || D == 128, "the fp8 path takes head_dim 128");
+  __shared__ double red[NW][2][T][D];
+  __shared__ float kmax_s[NW][T];
+
+  const int bh = blockIdx.x / nspan;
+  const int t0 = (blockIdx.x % nspan) * SPAN;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int c = tid % C;
+  const int r0 = tid / C;
+  const long long base = static_cast<long long>(bh) * N;
+
+  // Every load first: P rows of each tile, Q and K.
+  u32x4 xq[T][P], xk[T][P];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp) {
+      const int row = t0 + 64 * t + r0 + RP * pp;
+      const bool valid = row < N;
+      const long long off = (base + (valid ? row : 0)) * D + c * 8;
+      xq[t][pp] = valid ? *reinterpret_cast<const u32x4*>(q + off) : u32x4{0u, 0u, 0u, 0u};
+      xk[t][pp] = valid ? *reinterpret_cast<const u32x4*>(k + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+  // Column sums of each tile: over the thread's rows, then the wave's row
+  // groups; lanes of the first row group write their chunk.
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int ten = 0; ten < 2; ++ten) {
+      double acc[8];
+#pragma unroll
+      for (int pp = 0; pp < P; ++pp) {
+        float x[8];
+        bf16x8_to_f32(ten == 0 ? xq[t][pp] : xk[t][pp], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = pp == 0 ? static_cast<double>(x[e]) : acc[e] + static_cast<double>(x[e]);
+      }
+#pragma unroll
+      for (int off = C; off < kWave; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
+      if (lane < C)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][ten][t][c * 8 + e] = acc[e];
+    }
+
+  if constexpr (QUANT) {
+    // E4M3: a scale per query row (over the row's C lanes), one per K tile.
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float km = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < P; ++pp) {
+        const int row = t0 + 64 * t + r0 + RP * pp;
+        float x[8];
+        bf16x8_to_f32(xq[t][pp], x);
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
+#pragma unroll
+        for (int off = 1; off < C; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, kWave));
+        if (row < N) {
+          *reinterpret_cast<u32x2*>(q8 + (base + row) * D + c * 8) = e4m3_encode8(x, e4m3_group_inv(a));
+          if (c == 0) q_scale[base + row] = e4m3_group_scale(a);
+        }
+        bf16x8_to_f32(xk[t][pp], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) km = fmaxf(km, fabsf(x[e]));
+      }
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) km = fmaxf(km, __shfl_xor(km, off, kWave));
+      if (lane == 0) kmax_s[wave][t] = km;
+    }
+  }
+  __syncthreads();
+
+  if constexpr (QUANT) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int tile = (t0 + 64 * t) / 64;
+      if (tile >= nkt) continue;
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) a = fmaxf(a, kmax_s[w][t]);
+      const float inv = e4m3_group_inv(a);
+#pragma unroll
+      for (int pp = 0; pp < P; ++pp) {
+        const int row = t0 + 64 * t + r0 + RP * pp;
+        if (row < N) {
+          float x[8];
+          bf16x8_to_f32(xk[t][pp], x);
+          *reinterpret_cast<u32x2*>(k8 + (base + row) * D + c * 8) = e4m3_encode8(x, inv);
+        }
+      }
+      if (tid == 0) k_scale[static_cast<long long>(bh) * nkt + tile] = e4m3_group_scale(a);
+    }
+  }
+
+  // Block means: tile sums over the waves in order, blocks of 128 tokens
+  // adding their two tiles.
+  if (tid < 2 * D) {
+    const int ten = tid / D;
+    const int col = tid % D;
+    double ts[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      double s = red[0][ten][t][col];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) s += red[w][ten][t][col];
+      ts[t] = s;
+    }
+    const int blk = ten == 0 ? bq : bk;
+    const int nb = ten == 0 ? nbq : nbk;
+    if (blk == 64) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int i = (t0 + 64 * t) / 64;
+        if (i >= nb) continue;
+        const double mean = ts[t] / static_cast<double>(min(64, N - 64 * i));
+        if (ten == 0)
+          qbar[(static_cast<long long>(bh) * nb + i) * D + col] = mean;
+        else
+          kbar_t[(static_cast<long long>(bh) * D + col) * nb + i] = mean;
+      }
+    } else {
+      const int i = t0 / 128;
+      double s = ts[0];
+#pragma unroll
+      for (int t = 1; t < T; ++t) s += ts[t];
+      const double mean = s / static_cast<double>(min(128, N - 128 * i));
+      if (ten == 0)
+        qbar[(static_cast<long long>(bh) * nb + i) * D + col] = mean;
+      else
+        kbar_t[(static_cast<long long>(bh) * D + col) * nb + i] = mean;
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int x2 = tid; x2 < BH; x2 += kPoolThreads) head_cnt[x2] = 0;
+}
+
+// Value of lane (lane ^ LX) for a 32-bit register, with VALU lane moves instead
+// of an LDS permute: DPP quad permutations (1, 2), two row shifts and a select
+// (4), a row rotation by half a row (8), and the gfx950 row swaps (16, 32).
+template <int LX>
+__device__ __forceinline__ unsigned xor_lane(unsigned v) {
+  const unsigned lane = __lane_id();
+  if constexpr (LX == 1) {
+    return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (LX == 2) {
+    return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (LX == 4) {
+    const unsigned up = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false);   // row_shr:4 (lane - 4)
+    const unsigned dn = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0xF, false);   // row_shl:4 (lane + 4)
+    return (lane & 4) ? up : dn;
+  } else if constexpr (LX == 8) {
+    return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (LX == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(LX == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+template <int LX>
+__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v) {
+  const unsigned lo = xor_lane<LX>(static_cast<unsigned>(v));
+  const unsigned hi = xor_lane<LX>(static_cast<unsigned>(v >> 32));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
 // "a before b" in the ranking: larger probability first, then smaller index.
 // Probabilities are non-negative doubles, which order like their bit
 // patterns; padding elements (P = 0, index >= nb) rank after every real block.
@@ -176,8 +379,16 @@ __device__ void select_row(const double* __restrict__ zr, int nb, int nv, double
         const int lx = j / E;   // partner lane distance
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-          const unsigned long long ok = __shfl_xor(key[i], lx, kWave);
-          const int oi = __shfl_xor(idx[i], lx, kWave);
+          unsigned long long ok;
+          int oi;
+          switch (lx) {
+            case 1: ok = xor_lane64<1>(key[i]); oi = static_cast<int>(xor_lane<1>(idx[i])); break;
+            case 2: ok = xor_lane64<2>(key[i]); oi = static_cast<int>(xor_lane<2>(idx[i])); break;
+            case 4: ok = xor_lane64<4>(key[i]); oi = static_cast<int>(xor_lane<4>(idx[i])); break;
+            case 8: ok = xor_lane64<8>(key[i]); oi = static_cast<int>(xor_lane<8>(idx[i])); break;
+            case 16: ok = xor_lane64<16>(key[i]); oi = static_cast<int>(xor_lane<16>(idx[i])); break;
+            default: ok = xor_lane64<32>(key[i]); oi = static_cast<int>(xor_lane<32>(idx[i])); break;
+          }
           const int pos = base + i;
           const bool lower = (pos & j) == 0;
           const bool up = (pos & k) == 0;
@@ -367,6 +578,34 @@ hipError_t launch_select_d(const Shape& s, const double* qbar, const double* kba
 
 }  // namespace
 
+namespace {
+template <int D, int SPAN, bool QUANT>
+void launch_pool_qk_t(const Shape& s, const unsigned short* q, const unsigned short* k, double* qbar, double* kbar_t,
+                      int32_t* head_cnt, uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
+                      hipStream_t stream) {
+  const int BH = s.B * s.H;
+  const int nspan = (s.N + SPAN - 1) / SPAN;
+  const int nkt = (s.N + 63) / 64;
+  const long long grid = static_cast<long long>(BH) * nspan;
+  hipLaunchKernelGGL((pool_qk_kernel<D, SPAN, QUANT>), dim3(static_cast<unsigned>(grid)), dim3(kPoolThreads), 0,
+                     stream, q, k, qbar, kbar_t, head_cnt, q8, q_scale, k8, k_scale, BH, s.N, s.nb, s.block, s.nbk,
+                     s.kb, nspan, nkt);
+}
+}  // namespace
+
+hipError_t launch_pool_quant(const Shape& s, const void* q, const void* k, double* qbar, double* kbar_t,
+                             int32_t* head_cnt, uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
+                             hipStream_t stream) {
+  auto qq = static_cast<const unsigned short*>(q);
+  auto kk = static_cast<const unsigned short*>(k);
+  if (s.dtype != 0 || s.d != 128) return hipErrorInvalidValue;
+  if (s.block == 128 || s.kb == 128)
+    launch_pool_qk_t<128, 128, true>(s, qq, kk, qbar, kbar_t, head_cnt, q8, q_scale, k8, k_scale, stream);
+  else
+    launch_pool_qk_t<128, 64, true>(s, qq, kk, qbar, kbar_t, head_cnt, q8, q_scale, k8, k_scale, stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qbar, double* kbar_t,
                        int32_t* head_cnt, hipStream_t stream) {
   const int BH = s.B * s.H;
@@ -375,12 +614,18 @@ hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qba
   if (s.dtype == 0) {
     auto qq = static_cast<const unsigned short*>(q);
     auto kk = static_cast<const unsigned short*>(k);
-    if (s.d == 128)
-      hipLaunchKernelGGL((pool_kernel<unsigned short, 128>), g, b, 0, stream, qq, kk, qbar, kbar_t,
-                         head_cnt, BH, s.N, s.nb, s.block, s.nbk, s.kb);
-    else
-      hipLaunchKernelGGL((pool_kernel<unsigned short, 64>), g, b, 0, stream, qq, kk, qbar, kbar_t,
-                         head_cnt, BH, s.N, s.nb, s.block, s.nbk, s.kb);
+    const bool wide = s.block == 128 || s.kb == 128;
+    if (s.d == 128) {
+      if (wide)
+        launch_pool_qk_t<128, 128, false>(s, qq, kk, qbar, kbar_t, head_cnt, nullptr, nullptr, nullptr, nullptr, stream);
+      else
+        launch_pool_qk_t<128, 64, false>(s, qq, kk, qbar, kbar_t, head_cnt, nullptr, nullptr, nullptr, nullptr, stream);
+    } else {
+      if (wide)
+        launch_pool_qk_t<64, 128, false>(s, qq, kk, qbar, kbar_t, head_cnt, nullptr, nullptr, nullptr, nullptr, stream);
+      else
+        launch_pool_qk_t<64, 64, false>(s, qq, kk, qbar, kbar_t, head_cnt, nullptr, nullptr, nullptr, nullptr, stream);
+    }
   } else {
     auto qq = static_cast<const float*>(q);
     auto kk = static_cast<const float*>(k);
