@@ -91,6 +91,10 @@ extern "C" {
 /* Problem flags. */
 #define ATTN_FLAG_PROFILE_WORKERS 1  /* fwd calls record per-worker start/end
                                         times in the workspace (see below) */
+#define ATTN_FLAG_NO_SPLIT        2  /* fwd calls run every work item whole,
+                                        never as parts along the keys: results
+                                        then do not depend on the number of
+                                        compute units (see attn_sparse_fwd) */
 
 typedef struct attn_problem {
   int32_t batch;     /* B >= 1 */
@@ -291,6 +295,20 @@ int32_t attn_augment_union(const attn_problem* problem, uint8_t* mask, int32_t* 
  * lists come from causal routing, so they hold eligible blocks; a listed
  * block entirely after the query block contributes no keys, and a unit left
  * with no keys gets o = 0 and lse = -inf).
+ *
+ * Problems with few work items (bf16, fewer than 4 items of 256 query rows
+ * per compute unit and at most 1024 items, e.g. one GPU's share of a few
+ * heads) run as equal shares of their union key tiles: two small kernels on
+ * `stream` count each item's union tiles from the lists, lay the items end
+ * to end in item order and cut the sequence into one chunk of equal length
+ * (within a tile) per persistent workgroup, so an item crossing a cut runs
+ * as parts on several workgroups.  Each part's running maximum, sum and
+ * unnormalised O are merged in part order by the item's last part to finish
+ * (FlashAttention review, Tiling Softmax).  The result is deterministic,
+ * independent of work_list, and equal to the unsplit one up to fp32
+ * rounding; attn_workspace_bytes accounts for the parts (work_items +
+ * 2 * CUs slots of partial results).  ATTN_FLAG_NO_SPLIT
+ * runs every item whole (then an all-ones mask gives attn_dense_fwd's bits).
  * Requires nbk <= 2048. */
 int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* k, const void* v,
                         const int32_t* row_cnt, const int32_t* row_idx, const int32_t* work_list,
@@ -300,7 +318,9 @@ int32_t attn_sparse_fwd(const attn_problem* problem, const void* q, const void* 
  * allocate device memory or hand one over: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation.  Same arguments
  * (minus ws / ws_bytes), arithmetic and results as attn_sparse_fwd, bit for
- * bit.  Its only scratch -- the persistent queue's control block, 256 bytes
+ * bit, except that every work item runs whole: where attn_sparse_fwd splits
+ * the items of a small problem along the keys, the results agree up to fp32
+ * rounding.  Its only scratch -- the persistent queue's control block, 256 bytes
  * -- lives in a file-scope device array of the library, one per GPU, held
  * until the process ends; each call zeroes it with a fill kernel on `stream`
  * before the attention kernel.  The call allocates nothing and needs no prior
@@ -318,10 +338,13 @@ int32_t attn_sparse_fwd_noalloc(const attn_problem* problem, const void* q, cons
  * Same arithmetic, layouts and workspace rules as attn_sparse_fwd; with
  * causal the query blocks with the most keys are processed first.  Equals,
  * bit for bit, attn_sparse_fwd with every block selected (causal == 0) or
- * with every eligible block selected (causal == 1), for any key_block.  The
- * key block size does not enter the dense result.
+ * with every eligible block selected (causal == 1), for any key_block, when
+ * neither call splits its work items (ATTN_FLAG_NO_SPLIT on both calls makes
+ * sure of it), and up to fp32 rounding otherwise.  The key block size does
+ * not enter the dense result.
  *
- * Causal bf16 problems with fewer than 4 work items per compute unit whose
+ * Causal bf16 problems (unless ATTN_FLAG_NO_SPLIT) with fewer than 4 work
+ * items per compute unit whose
  * last item holds more than half the mean work per compute unit (at least
  * 16 key tiles of 64 keys) run their longer items as equal parts along the
  * keys, each part's running maximum, sum and unnormalised O merged in part
@@ -386,7 +409,8 @@ int32_t attn_sparse_fwd_fp8(const attn_problem* problem, const uint8_t* q8, cons
                             size_t ws_bytes, void* stream);
 
 /* attn_dense_fwd with fp8 Q and K (same logits as attn_sparse_fwd_fp8); equals
- * attn_sparse_fwd_fp8 with every (eligible) block selected, bit for bit. */
+ * attn_sparse_fwd_fp8 with every (eligible) block selected, bit for bit, when
+ * neither call splits its work items (see attn_dense_fwd). */
 int32_t attn_dense_fwd_fp8(const attn_problem* problem, const uint8_t* q8, const float* q_scale,
                            const uint8_t* k8, const float* k_scale, const void* v, void* o, float* lse, void* ws,
                            size_t ws_bytes, void* stream);

@@ -66,8 +66,9 @@ def test_mixed_blocks_p1_equals_dense_bitwise(w, kb, causal):
     pr = tbs.make_problem(q, w.block, causal=causal, key_block=kb)
     ws = tbs.workspace(pr, DEV)
     r = tbs.route(q, k, 1.0, w.block, ws=ws, causal=causal, key_block=kb)
-    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, ws=ws, causal=causal, key_block=kb)
-    od, lsed = tbs.dense_fwd(q, k, v, w.block, causal=causal, ws=ws)
+    ns = tbs.FLAG_NO_SPLIT   # both calls run every work item whole
+    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, ws=ws, causal=causal, key_block=kb, flags=ns)
+    od, lsed = tbs.dense_fwd(q, k, v, w.block, causal=causal, ws=ws, flags=ns)
     torch.cuda.synchronize()
     nb, nbk = pr.num_blocks, pr.num_key_blocks
     want = np.ones((nb, nbk), dtype=np.uint8)

@@ -86,7 +86,7 @@ def test_quantize_special_values(golden_dir):
     assert (((sub & 0x78) == 0) & ((sub & 0x07) != 0)).any(), "expected subnormal codes in the test input"
 
 
-def _fp8_path(w, q, k, v, top_p=None, causal=False, key_block=None, ws=None):
+def _fp8_path(w, q, k, v, top_p=None, causal=False, key_block=None, ws=None, flags=0):
     p = w.top_p if top_p is None else top_p
     pr = tbs.make_problem(q, w.block, causal=causal, key_block=key_block)
     ws = tbs.workspace(pr, DEV) if ws is None else ws
@@ -94,7 +94,7 @@ def _fp8_path(w, q, k, v, top_p=None, causal=False, key_block=None, ws=None):
     wl = tbs.schedule(pr, r.row_cnt, ws)
     qk = tbs.quantize_qk_fp8(q, k, w.block, key_block=key_block)
     o, lse = tbs.sparse_fwd_fp8(qk, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws, causal=causal,
-                                key_block=key_block)
+                                key_block=key_block, flags=flags)
     torch.cuda.synchronize()
     return pr, ws, r, qk, o, lse
 
@@ -133,7 +133,11 @@ def test_sparse_fp8_mixed_blocks(kb):
 @pytest.mark.parametrize("w", CASES[:3], ids=lambda w: w.name)
 def test_dense_fp8_equals_sparse_at_p1(w, causal):
     q, k, v = _inputs(w, seed=1)
-    pr, ws, r, qk, o_s, l_s = _fp8_path(w, q, k, v, top_p=1.0, causal=causal)
+    ns = tbs.FLAG_NO_SPLIT   # both calls run every work item whole
+    pr, ws, r, qk, o_s, l_s = _fp8_path(w, q, k, v, top_p=1.0, causal=causal, flags=ns)
+    o_d, l_d = tbs.dense_fwd_fp8(qk, v, w.block, causal=causal, ws=ws, flags=ns)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_d) and torch.equal(l_s, l_d)
     o_d, l_d = tbs.dense_fwd_fp8(qk, v, w.block, causal=causal, ws=ws)
     torch.cuda.synchronize()
     if not (causal and dense_causal_splits(w)):

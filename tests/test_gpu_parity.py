@@ -160,8 +160,9 @@ def test_sparse_p1_equals_dense_bitwise():
     ws = tbs.workspace(pr, DEV)
     r = tbs.route(q, k, 1.0, w.block, ws=ws)
     wl = tbs.schedule(pr, r.row_cnt, ws)
-    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws)
-    od, lsed = tbs.dense_fwd(q, k, v, w.block, ws=ws)
+    ns = tbs.FLAG_NO_SPLIT   # both calls run every work item whole
+    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws, flags=ns)
+    od, lsed = tbs.dense_fwd(q, k, v, w.block, ws=ws, flags=ns)
     torch.cuda.synchronize()
     assert (r.mask == 1).all() and (r.row_cnt == r.mask.shape[-1]).all()
     assert torch.equal(o, od) and torch.equal(lse, lsed)
@@ -209,7 +210,9 @@ def test_one_gpu_share_equals_the_full_problem_on_its_heads():
     # bench.py --share-of G runs the heads that the head-level LPT gives one
     # GPU as a problem of their own; heads are independent and the results do
     # not depend on the processing order, so the share's masks, counts,
-    # outputs and LSE equal the full problem's rows of those heads bit for bit.
+    # outputs and LSE equal the full problem's rows of those heads bit for bit
+    # when neither call splits its work items along their keys (both are
+    # small enough that the default calls do; those agree to rounding).
     import bench
     w = custom_workload(1, 8, 1500, 128, 64, "bf16", 0.9, wid=217)
     q, k, v = _inputs(w)
@@ -217,7 +220,8 @@ def test_one_gpu_share_equals_the_full_problem_on_its_heads():
     ws = tbs.workspace(pr, DEV)
     r = tbs.route(q, k, w.top_p, w.block, ws=ws)
     wl = tbs.schedule(pr, r.row_cnt, ws)
-    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws)
+    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws, flags=tbs.FLAG_NO_SPLIT)
+    o_sp, lse_sp = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, w.block, work_list=wl, ws=ws)
     qs, ks, vs, info = bench.take_share(tbs, q, k, v, w.top_p, w.block, w.block, False, 3)
     heads = info["heads"]
     assert 1 <= len(heads) < w.heads and info["lif_head_lpt"] <= info["lif_contiguous_heads"] + 1e-12
@@ -225,11 +229,17 @@ def test_one_gpu_share_equals_the_full_problem_on_its_heads():
     wss = tbs.workspace(prs, DEV)
     rs = tbs.route(qs, ks, w.top_p, w.block, ws=wss)
     wls = tbs.schedule(prs, rs.row_cnt, wss)
-    os_, lses = tbs.sparse_fwd(qs, ks, vs, rs.row_cnt, rs.row_idx, w.block, work_list=wls, ws=wss)
+    os_, lses = tbs.sparse_fwd(qs, ks, vs, rs.row_cnt, rs.row_idx, w.block, work_list=wls, ws=wss,
+                               flags=tbs.FLAG_NO_SPLIT)
+    os_sp, lses_sp = tbs.sparse_fwd(qs, ks, vs, rs.row_cnt, rs.row_idx, w.block, work_list=wls, ws=wss)
     torch.cuda.synchronize()
     idx = torch.tensor(heads, device=DEV)
     assert torch.equal(rs.mask[0], r.mask[0].index_select(0, idx))
     assert torch.equal(rs.row_cnt[0], r.row_cnt[0].index_select(0, idx))
     assert torch.equal(os_[0], o[0].index_select(0, idx))
     assert torch.equal(lses[0], lse[0].index_select(0, idx))
+    for a, b in ((o_sp, o), (os_sp, os_)):
+        assert (a.float() - b.float()).abs().max().item() <= 2e-2
+    for a, b in ((lse_sp, lse), (lses_sp, lses)):
+        assert (a - b).abs().max().item() <= 2e-3
     assert sorted(info["head_cost"]) == sorted(int(c) for c in r.head_cnt[0].index_select(0, idx).tolist())

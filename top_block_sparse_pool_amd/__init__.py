@@ -35,6 +35,7 @@ ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_DEVICE = 0
 ATTN_DTYPE_BF16, ATTN_DTYPE_F32 = 0, 1
 OP_ROUTE, OP_SCHEDULE, OP_SPARSE_FWD, OP_DENSE_FWD, OP_AUGMENT = 0, 1, 2, 3, 4
 FLAG_PROFILE_WORKERS = 1
+FLAG_NO_SPLIT = 2        # run every work item whole (no split along the keys)
 CTRL_BYTES = 256
 DEFAULT_HEAD_WINDOW = 4
 # Head windows keep the K/V of the heads that run together cache-resident;

@@ -55,7 +55,8 @@ int32_t check_problem(const attn_problem* pr, tbs::Shape* s) {
   if (pr->dtype != ATTN_DTYPE_BF16 && pr->dtype != ATTN_DTYPE_F32)
     return fail(ATTN_E_INVALID, "dtype must be ATTN_DTYPE_BF16 or ATTN_DTYPE_F32 (got %d)", pr->dtype);
   if (pr->causal != 0 && pr->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
-  if (pr->flags & ~ATTN_FLAG_PROFILE_WORKERS) return fail(ATTN_E_INVALID, "unknown flag bits 0x%x", pr->flags);
+  if (pr->flags & ~(ATTN_FLAG_PROFILE_WORKERS | ATTN_FLAG_NO_SPLIT))
+    return fail(ATTN_E_INVALID, "unknown flag bits 0x%x", pr->flags);
   if (!(pr->scale >= 0.0) || !std::isfinite(pr->scale))
     return fail(ATTN_E_INVALID, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
   if (pr->head_dim != 64 && pr->head_dim != 128)
@@ -330,6 +331,7 @@ TBS_EXPORT int32_t attn_sparse_fwd_noalloc(const attn_problem* problem, const vo
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
+  s.flags |= ATTN_FLAG_NO_SPLIT;   // every work item runs whole: no parts to keep
   if (s.nbk > kMaxSparseBlocks)
     return fail(ATTN_E_UNSUPPORTED, "attn_sparse_fwd_noalloc: %d key blocks per sequence exceed %d", s.nbk,
                 kMaxSparseBlocks);
@@ -453,3 +455,5 @@ TBS_EXPORT int32_t attn_dense_fwd_fp8(const attn_problem* problem, const uint8_t
   return run_fwd(s, s.causal ? tbs::kCausal : tbs::kDense, q8, k8, v, nullptr, nullptr, nullptr, o, lse, ws,
                  ws_bytes, stream, q_scale, k_scale);
 }
+
+static_assert(ATTN_FLAG_NO_SPLIT == tbs::kFlagNoSplit, "flag values of the header and the launchers agree");

@@ -87,6 +87,13 @@ struct FwdParams {
   int split_tiles;
   uint32_t* part_cnt;
   float* part_buf;
+  // Listed modes with split items: the entries written by the planning
+  // kernels ({item, part, parts, first tile | end tile << 16}), their number,
+  // and the first entry of every workgroup (workgroup w runs entries
+  // starts[w] .. starts[w + 1] - 1 in order; no shared queue).
+  const int4* entries;
+  const int* n_entries;
+  const int* starts;
 };
 
 // Unit bookkeeping of the fp32 kernel: query blocks of BQ rows, listed key
@@ -332,6 +339,16 @@ struct GroupInfo {
       tb = part * ntg / npg;
       te = (part + 1) * ntg / npg;
       g = bh * p.ng + gi;
+    } else if (fwd_listed(MODE) && p.entries) {
+      // Split sparse items: the entry names the item, the part and its range
+      // of the item's union tiles.
+      const int4 en = p.entries[qpos];
+      g = min(max(en.x, 0), p.U - 1);
+      part = en.y;
+      nparts = max(en.z, 1);
+      tb = en.w & 0xffff;
+      te = static_cast<int>(static_cast<unsigned>(en.w) >> 16);
+      bh = g / p.ng;
     } else if (MODE == kCausal) {
       // Longest first: the last query blocks of every head have the most keys.
       const int gi = p.ng - 1 - qpos / p.BH;
@@ -449,12 +466,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       voff[mo][hf] = row * ROWB + ((dim >> 3) ^ chunk_swz<D>(row)) * 16 + (dim & 7) * 2;
     }
 
+  // Queue length: the work items, or (split sparse items) the entries the
+  // planning kernels wrote, of which this workgroup runs its own range.
+  const bool own_range = fwd_listed(MODE) && p.starts != nullptr;
+  const int n_queue = own_range ? *p.n_entries : p.U;
+  int next = own_range ? p.starts[blockIdx.x] : 0;
+  const int last = own_range ? min(p.starts[blockIdx.x + 1], n_queue) : 0;
   for (;;) {
-    if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
-    __syncthreads();
-    const int qpos = s_unit;
-    __syncthreads();
-    if (qpos >= p.U) break;
+    int qpos;
+    if (own_range) {
+      // every wave is done with the previous item's LDS before it is reused
+      __syncthreads();
+      qpos = next++;
+      if (qpos >= last) break;
+    } else {
+      if (tid == 0) s_unit = static_cast<int>(atomicAdd(p.ctrl, 1u));
+      __syncthreads();
+      qpos = s_unit;
+      __syncthreads();
+      if (qpos >= n_queue) break;
+    }
 
     GroupInfo<BQ, G, MODE> gi;
     gi.decode(p, qpos);
@@ -517,6 +548,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         const int tail = p.N - (p.nbk - 1) * BK;
         nt = (nl - 1) * SPB + (tail + kKeyTile - 1) / kKeyTile;
       }
+      nt = max(min(nt, gi.te) - gi.tb, 0);   // a part runs union tiles [tb, te)
     } else if (MODE == kDense) {
       nt = (p.N + kKeyTile - 1) / kKeyTile;
     } else {
@@ -528,7 +560,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     // the words of tiles t-1 .. t+3 in scalar registers and reads the next
     // ones from LDS one iteration ahead, so no lookup waits on LDS.
     auto wkey0 = [&](unsigned w, int t) __attribute__((always_inline)) -> int {
-      if (fwd_listed(MODE)) return static_cast<int>(w & 0xffffu) * BK + (t % SPB) * kKeyTile;
+      if (fwd_listed(MODE)) return static_cast<int>(w & 0xffffu) * BK + ((tb + t) % SPB) * kKeyTile;
       return (tb + t) * kKeyTile;
     };
     // Under a causal mask a wave skips tiles whose keys all follow its 32
@@ -542,7 +574,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       return true;
     };
     auto wread = [&](int t) __attribute__((always_inline)) -> unsigned {
-      if (fwd_listed(MODE)) return s_lt[min(max(t, 0) / SPB, kMaxListBlocks - 1)];
+      if (fwd_listed(MODE)) return s_lt[min(max(tb + t, 0) / SPB, kMaxListBlocks - 1)];
       return 0u;
     };
     auto wuni = [&](unsigned v) __attribute__((always_inline)) -> unsigned {
@@ -832,7 +864,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
     // Epilogue: lane (h, col) holds O[qrow][32mo + 8j + 4h + r] in acc_o[mo][4j + r].
     const float l_tot = l_run + xor32(l_run);
-    if (MODE == kCausal && gi.nparts > 1) {
+    if ((MODE == kCausal || fwd_listed(MODE)) && gi.nparts > 1) {
       // A part of a split item: its O (unnormalised, relative to its own
       // reference maximum m_run), m_run and row sum go to the part's slot;
       // the item's last part to finish merges every part, in part order.
@@ -1174,15 +1206,131 @@ long long work_items(const Shape& s) {
   return static_cast<long long>(s.B) * s.H * ((s.nb + G - 1) / G);
 }
 
+constexpr int kSplitMinTiles = 16;     // shortest part of a split item
+constexpr int kSplitItemsPerCu = 4;    // split below this many items per compute unit
+constexpr int kPlanThreads = 1024;     // split sparse problems hold at most this many items
+constexpr int kPlanMaxWorkers = 1024;  // and run on at most this many workgroups
+
 namespace {
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ x, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) x[i] = 0u;
 }
-}  // namespace
 
-constexpr int kSplitMinTiles = 16;     // shortest part of a split item
-constexpr int kSplitItemsPerCu = 4;    // split below this many items per compute unit
+// Union tile count of every work item of a listed problem: the key blocks its
+// rows select, OR'ed into an LDS bitmap, each holding kb/64 key tiles (the
+// last block only the tiles its keys reach) -- the tiles the attention kernel
+// runs for the item.
+__global__ __launch_bounds__(256) void item_tiles_kernel(const int32_t* __restrict__ row_cnt,
+                                                         const int32_t* __restrict__ row_idx, int nb, int nbk,
+                                                         int kb, int N, int ng, int G, int* __restrict__ item_tiles) {
+  __shared__ unsigned bm[kMaxListWords];
+  const int g = blockIdx.x;
+  const int bh = g / ng;
+  const int i0 = (g - bh * ng) * G;
+  const int gsz = min(G, nb - i0);
+  const int nwords = (nbk + 31) / 32;
+  const int tid = threadIdx.x;
+  for (int x = tid; x < nwords; x += 256) bm[x] = 0u;
+  __syncthreads();
+  for (int m = 0; m < gsz; ++m) {
+    const long long u = static_cast<long long>(bh) * nb + i0 + m;
+    const int cnt = min(max(row_cnt[u], 0), nbk);
+    const int32_t* lst = row_idx + u * nbk;
+    for (int x = tid; x < cnt; x += 256) {
+      const int j = min(max(lst[x], 0), nbk - 1);
+      atomicOr(&bm[j >> 5], 1u << (j & 31));
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    int c = 0;
+    for (int x = tid; x < nwords; x += kWave) c += __popc(bm[x]);
+    c = wave_sum_i32(c);
+    if (tid == 0) {
+      const int spb = kb / kKeyTile;
+      int tiles = c * spb;
+      if (spb > 1 && c > 0 && ((bm[(nbk - 1) >> 5] >> ((nbk - 1) & 31)) & 1u))
+        tiles = (c - 1) * spb + (N - (nbk - 1) * kb + kKeyTile - 1) / kKeyTile;
+      item_tiles[g] = tiles;
+    }
+  }
+}
+
+// Inclusive prefix sum over the kPlanThreads threads of one workgroup (every
+// thread calls it; s_w holds one int per wave).  Returns the thread's
+// inclusive sum and sets *total to the workgroup's sum.
+__device__ __forceinline__ long long plan_scan(long long x, long long* s_w, long long* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  long long incl = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const long long y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) s_w[wv] = incl;
+  __syncthreads();
+  long long base = 0, all = 0;
+  for (int w = 0; w < kPlanThreads / kWave; ++w) {
+    if (w < wv) base += s_w[w];
+    all += s_w[w];
+  }
+  *total = all;
+  return base + incl;
+}
+
+// Work of a split sparse problem, cut into equal shares (one workgroup, one
+// thread per item).  The items' union tiles are laid end to end in item
+// order (so the parts, and the results, do not depend on a work list) and
+// the sequence is cut into `workers`
+// contiguous chunks of C = ceil(total / workers) tiles; worker w runs chunk
+// w.  An item crossing a chunk boundary becomes several parts (consecutive
+// entries, {item, part, parts, first tile | end tile << 16}); an item without
+// tiles is one entry of the chunk its position falls in.  starts[w] is the
+// first entry of worker w (starts[workers] = number of entries); the per-item
+// part counters are zeroed.
+__global__ __launch_bounds__(kPlanThreads) void split_plan_kernel(const int* __restrict__ item_tiles, int items,
+                                                                  int workers, int4* __restrict__ entries,
+                                                                  int* __restrict__ n_entries,
+                                                                  int* __restrict__ starts,
+                                                                  uint32_t* __restrict__ part_cnt) {
+  __shared__ long long s_w[kPlanThreads / kWave];
+  __shared__ int s_chunk[kPlanThreads + kPlanMaxWorkers];
+  const int t = threadIdx.x;
+  const bool live = t < items;
+  const int g = t;
+  const long long tiles = live ? item_tiles[g] : 0;
+  long long total = 0;
+  const long long s0 = plan_scan(tiles, s_w, &total) - tiles;    // first tile of the item in the sequence
+  const long long e0 = s0 + tiles;
+  const long long C = total > 0 ? (total + workers - 1) / workers : 1;
+  const int cfirst = static_cast<int>(min(s0 / C, static_cast<long long>(workers - 1)));
+  const int parts = !live ? 0 : tiles == 0 ? 1 : static_cast<int>((e0 - 1) / C - s0 / C + 1);
+  long long n = 0;
+  const int off0 = static_cast<int>(plan_scan(parts, s_w, &n) - parts);
+  for (int q = 0; q < parts; ++q) {
+    const long long lo = q == 0 ? s0 : (cfirst + q) * C;
+    const long long hi = min(e0, (cfirst + q + 1) * C);
+    const int tb = static_cast<int>(lo - s0);
+    const int te = static_cast<int>(hi - s0);
+    entries[off0 + q] = make_int4(g, q, parts, tb | (te << 16));
+    s_chunk[off0 + q] = cfirst + q;
+  }
+  if (live) part_cnt[g] = 0u;
+  __syncthreads();
+  // Entries are in chunk order: worker c starts at the first entry whose
+  // chunk is c or later.
+  const int ne = static_cast<int>(n);
+  for (int e = t; e <= ne; e += kPlanThreads) {
+    const int lo = e == 0 ? 0 : s_chunk[e - 1] + 1;
+    const int hi = e == ne ? workers : s_chunk[e];
+    for (int c = lo; c <= hi; ++c) starts[c] = e;
+  }
+  if (t == 0) n_entries[0] = ne;
+}
+}  // namespace
 
 // Key tiles of dense causal item row gi (256 query rows).
 static long long causal_item_tiles(const Shape& s, int gi) {
@@ -1192,7 +1340,7 @@ static long long causal_item_tiles(const Shape& s, int gi) {
 }
 
 int causal_split_tiles(const Shape& s, int mode) {
-  if (mode != kCausal || s.dtype != 0) return 0;
+  if (mode != kCausal || s.dtype != 0 || (s.flags & kFlagNoSplit)) return 0;
   const int cus = device_cu_count();
   if (work_items(s) >= static_cast<long long>(kSplitItemsPerCu) * cus) return 0;
   // Parts of half the mean work per compute unit (at least 16 tiles), so
@@ -1217,12 +1365,52 @@ long long causal_split_entries(const Shape& s, int split_tiles) {
   return per_head * s.B * s.H;
 }
 
+bool sparse_split(const Shape& s, int mode) {
+  if (!fwd_listed(mode) || s.dtype != 0 || (s.flags & kFlagNoSplit)) return false;
+  // entries hold tile indices of an item in 16 bits
+  if ((s.N + kKeyTile - 1) / kKeyTile >= (1 << 16)) return false;
+  const long long items = work_items(s);
+  return items < static_cast<long long>(kSplitItemsPerCu) * device_cu_count() && items <= kPlanThreads &&
+         device_cu_count() <= kPlanMaxWorkers / 2;
+}
+
+namespace {
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+size_t part_bytes(const Shape& s) {
+  return static_cast<size_t>(kWaves) * ((s.d / 32) * 4 * 256 + 2 * 64) * sizeof(float);
+}
+// Split sparse problems run on at most 2 workgroups per compute unit; each
+// chunk boundary cuts at most one item, so there are at most items + workers
+// entries.
+long long sparse_split_max_workers() { return 2LL * device_cu_count(); }
+long long sparse_split_max_entries(const Shape& s) { return work_items(s) + sparse_split_max_workers(); }
+
+// Workspace of a split sparse problem: part counters, entry count, item tile
+// counts, workgroup starts, entries, then the parts' partial results.
+struct SparseSplitLayout {
+  size_t counters, n_entries, item_tiles, starts, entries, parts, total;
+};
+SparseSplitLayout sparse_split_layout(const Shape& s) {
+  SparseSplitLayout l;
+  const size_t items = static_cast<size_t>(work_items(s));
+  const size_t maxe = static_cast<size_t>(sparse_split_max_entries(s));
+  l.counters = 0;
+  l.n_entries = align256(items * sizeof(uint32_t));
+  l.item_tiles = l.n_entries + 256;
+  l.starts = l.item_tiles + align256(items * sizeof(int));
+  l.entries = l.starts + align256((static_cast<size_t>(sparse_split_max_workers()) + 1) * sizeof(int));
+  l.parts = l.entries + align256(maxe * sizeof(int4));
+  l.total = l.parts + maxe * part_bytes(s);
+  return l;
+}
+}  // namespace
+
 size_t causal_split_bytes(const Shape& s, int mode) {
+  if (sparse_split(s, mode)) return sparse_split_layout(s).total;
   const int t = causal_split_tiles(s, mode);
   if (t == 0) return 0;
-  const size_t counters = (static_cast<size_t>(work_items(s)) * sizeof(uint32_t) + 255) / 256 * 256;
-  const size_t part_floats = static_cast<size_t>(kWaves) * ((s.d / 32) * 4 * 256 + 2 * 64);
-  return counters + static_cast<size_t>(causal_split_entries(s, t)) * part_floats * sizeof(float);
+  const size_t counters = align256(static_cast<size_t>(work_items(s)) * sizeof(uint32_t));
+  return counters + static_cast<size_t>(causal_split_entries(s, t)) * part_bytes(s);
 }
 
 int fwd_workers(const Shape& s, int mode, bool fp8) {
@@ -1235,6 +1423,8 @@ int fwd_workers(const Shape& s, int mode, bool fp8) {
       per_cu < 1)
     per_cu = 1;
   const long long want = static_cast<long long>(device_cu_count()) * per_cu;
+  // split sparse problems: the entry count is known on the device only
+  if (sparse_split(s, mode)) return static_cast<int>(std::min(want, sparse_split_max_workers()));
   const int split = causal_split_tiles(s, mode);
   const long long items = split ? causal_split_entries(s, split) : work_items(s);
   return static_cast<int>(want < items ? want : items);
@@ -1267,7 +1457,35 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
   p.split_tiles = causal_split_tiles(s, mode);
   p.part_cnt = nullptr;
   p.part_buf = nullptr;
-  if (p.split_tiles > 0) {
+  p.entries = nullptr;
+  p.n_entries = nullptr;
+  p.starts = nullptr;
+  const int grid = fwd_workers(s, mode, a.fp8);
+  if (sparse_split(s, mode)) {
+    // Split sparse items: union tile counts per item, then the queue of parts.
+    if (!a.split_ws) return hipErrorInvalidValue;
+    const SparseSplitLayout l = sparse_split_layout(s);
+    auto* ws = static_cast<unsigned char*>(a.split_ws);
+    p.part_cnt = reinterpret_cast<uint32_t*>(ws + l.counters);
+    int* n_entries = reinterpret_cast<int*>(ws + l.n_entries);
+    int* item_tiles = reinterpret_cast<int*>(ws + l.item_tiles);
+    int* starts = reinterpret_cast<int*>(ws + l.starts);
+    int4* entries = reinterpret_cast<int4*>(ws + l.entries);
+    p.part_buf = reinterpret_cast<float*>(ws + l.parts);
+    p.entries = entries;
+    p.n_entries = n_entries;
+    p.starts = starts;
+    if (grid < 1 || grid > sparse_split_max_workers()) return hipErrorInvalidValue;
+    const int items = static_cast<int>(work_items(s));
+    hipLaunchKernelGGL(item_tiles_kernel, dim3(items), dim3(256), 0, stream, a.row_cnt, a.row_idx, s.nb, s.nbk, s.kb,
+                       s.N, p.ng, p.G, item_tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, item_tiles, items, grid, entries,
+                       n_entries, starts, p.part_cnt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (p.split_tiles > 0) {
     if (!a.split_ws) return hipErrorInvalidValue;
     const long long items = work_items(s);
     p.U = static_cast<int>(causal_split_entries(s, p.split_tiles));
@@ -1283,7 +1501,6 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
     const hipError_t ze = hipGetLastError();
     if (ze != hipSuccess) return ze;
   }
-  const int grid = fwd_workers(s, mode, a.fp8);
   KernelFn fn = pick_kernel(s, mode, a.fp8);
   if (!fn || grid < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(fwd_threads(s)), 0, stream, p);

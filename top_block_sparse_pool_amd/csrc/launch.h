@@ -31,6 +31,9 @@ enum FwdMode { kSparse = 0, kDense = 1, kCausal = 2, kSparseCausal = 3 };
 constexpr bool fwd_listed(int m) { return m == kSparse || m == kSparseCausal; }
 constexpr bool fwd_causal(int m) { return m == kCausal || m == kSparseCausal; }
 
+// Problem flag: run every work item whole (no split along the keys).
+constexpr int kFlagNoSplit = 2;
+
 // Control block at workspace offset 0 (bytes [0, 256)): queue counters.
 constexpr size_t kCtrlBytes = 256;
 
@@ -88,9 +91,9 @@ struct FwdArgs {
   bool fp8 = false;
   const float* q_scale = nullptr;
   const float* k_scale = nullptr;
-  // Dense causal with split items: causal_split_bytes(s, mode) bytes of
-  // workspace, any contents on entry (the per-item part counters, zeroed by
-  // the call, then the parts' partial results).
+  // Split items (dense causal or sparse): causal_split_bytes(s, mode) bytes
+  // of workspace, any contents on entry (per-item part counters, zeroed by
+  // the call, the sparse plan, then the parts' partial results).
   void* split_ws = nullptr;
 };
 // Query blocks per work item (G) and number of work items B*H*ceil(nb/G).
@@ -105,7 +108,14 @@ int fwd_workers(const Shape& s, int mode, bool fp8 = false);
 int causal_split_tiles(const Shape& s, int mode);
 // Queue entries of the split problem (parts of every item).
 long long causal_split_entries(const Shape& s, int split_tiles);
-// Workspace bytes the split needs (0 without a split).
+// Sparse (listed) bf16 problems with fewer than 4 work items per compute
+// unit (and at most 1024) run as equal shares of their union tiles: the
+// items laid end to end in item order, cut into one chunk per persistent
+// workgroup (planned on the device from the routed lists), items crossing a
+// cut merged like the dense causal parts.  kFlagNoSplit turns both splits
+// off.
+bool sparse_split(const Shape& s, int mode);
+// Workspace bytes a split needs (0 without a split).
 size_t causal_split_bytes(const Shape& s, int mode);
 hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t stream);
 
