@@ -25,12 +25,12 @@ What it computes, and where the definitions come from:
   factor (max over mean) -- FVAttn review, section 1 (Runtime Load
   Balancing) and section 3 (load imbalance factor).
 * work accounting (``flops``): executed attention FLOPs for a block mask.
-* slack-aware augmentation (``sasa``): workers of the LPT model whose load is
-  below the makespan add the highest-probability unselected blocks of their
-  own rows, up to their slack; or every row of a work item takes the blocks
-  of the item's union (the idle wave-steps inside the item) -- FVAttn
-  review, section 1 (Key Terms, "Slack-Aware Sparse Augmentation") and
-  section 3 (Method).
+* slack-aware augmentation (``sasa``): priced in the key tiles the attention
+  kernel runs, every row of a work item takes the blocks of the item's union
+  (free), and workers of a batched longest-first model whose load is below
+  the makespan buy the most valuable blocks outside the union of their last
+  item with their slack; or the union fill alone -- FVAttn review, section 1
+  (Key Terms, "Slack-Aware Sparse Augmentation") and section 3 (Method).
 * FP8 quantisation (``fp8``): OCP E4M3 codes of Q (one scale per token) and
   K (one scale per 64-token tile), scales from each group's largest
   magnitude, every decision in fp32 -- the ParaAttention/HunyuanVideo post,
@@ -47,9 +47,9 @@ library special cases or invariants.
 from .routing import (block_sizes, num_blocks, pool_blocks, block_scores, softmax_rows,
                       top_p_select, causal_eligible, causal_cut, route, ambiguous_blocks, RouteResult)
 from .attention import attend, attend_units, attend_dense_masked_logits
-from .schedule import group_costs, work_list, lpt_assign, static_partition_loads, load_imbalance
+from .schedule import group_costs, work_list, lpt_assign, lpt_batched, static_partition_loads, load_imbalance
 from .flops import executed_flops, dense_flops
-from .sasa import Augmented, augment, UnionFilled, union_fill, retained_mass
+from .sasa import Augmented, augment, UnionFilled, union_fill, retained_mass, item_unions, block_tiles
 from . import fp8
 
 __all__ = [

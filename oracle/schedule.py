@@ -16,11 +16,15 @@ selected key blocks.
   pages; they are this implementation's way of keeping the query blocks that
   run together on the K/V of a few heads.
 * work items: the attention kernel of this implementation processes G
-  consecutive query blocks of one head together (G = 2 for bf16 with 64-row
-  blocks); an item costs the summed counts of its blocks, item id
+  consecutive query blocks of one head together (256 query rows: G = 4 for
+  bf16 with 64-row blocks, 2 with 128-row blocks); for the work list an item
+  costs the summed counts of its blocks, item id
   g = (b*H + h)*ceil(nb/G) + i//G.
 * greedy longest-processing-time (LPT): in work-list order, each unit goes to
   the worker with the least load so far, ties to the lowest worker id.
+  ``lpt_batched`` takes the list W positions at a time: the workers ranked
+  by (load, id) before the batch take its items in that rank order (one
+  each), so every choice of a batch can be made in parallel.
 * "before": a contiguous static partition of the natural unit order, worker w
   taking units [floor(w*U/W), floor((w+1)*U/W)) -- the analogue of each rank
   owning a fixed group of whole heads.
@@ -72,6 +76,30 @@ def lpt_assign(costs, order, num_workers: int):
         load[w] = l + costs[u]
         heapq.heappush(heap, (int(load[w]), w))
     return worker_of, load
+
+
+def lpt_batched(costs, order, num_workers: int):
+    """Longest-first assignment in batches of num_workers list positions.
+
+    Before each batch the workers are ranked by (load asc, id asc); the r-th
+    item of the batch goes to the r-th ranked worker, so a batch gives every
+    worker at most one item and all of a batch's choices can be made at once.
+    Returns (worker_of [U], worker_load [W], last_item [W]): last_item[w] is
+    the item of the latest batch that reached w (-1: none).
+    """
+    costs = np.asarray(costs, dtype=np.int64).reshape(-1)
+    order = np.asarray(order, dtype=np.int64).reshape(-1)
+    load = np.zeros(num_workers, dtype=np.int64)
+    worker_of = np.full(costs.size, -1, dtype=np.int64)
+    last_item = np.full(num_workers, -1, dtype=np.int64)
+    for b in range(0, order.size, num_workers):
+        ranked = sorted(range(num_workers), key=lambda w: (int(load[w]), w))
+        for r, g in enumerate(order[b:b + num_workers]):
+            w = ranked[r]
+            worker_of[g] = w
+            load[w] += costs[g]
+            last_item[w] = g
+    return worker_of, load, last_item
 
 
 def static_partition_loads(costs, num_workers: int) -> np.ndarray:

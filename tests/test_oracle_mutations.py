@@ -2,9 +2,11 @@
 catch each one: a transposed operand, a wrong divisor, an exclusive threshold,
 a reversed tie rule, a dropped scale, an off-by-one causal mask, a wrong log
 base, a wrong sort direction, and a causal block cut that is missing, off by
-one, or applied after the softmax instead of before it; and an augmentation
-that takes the lowest-probability candidates, measures slack from the mean
-load, or draws candidates from every worker's rows; an E4M3 exponent bias off by
+one, or applied after the softmax instead of before it; an augmentation that
+buys the lowest-value blocks, values a block by one row or by the largest
+row, breaks ties the wrong way, assigns items with the sequential LPT,
+spends slack on a worker's first item, rounds its budget up, or prices
+blocks instead of tiles; an E4M3 exponent bias off by
 one, ties rounded away from zero, K scaled per token instead of per tile, and
 an inverted dequantisation scale; and an ambiguity window whose swap-across-
 the-cut rule is dropped (whole or either half), measured against the wrong
@@ -154,37 +156,69 @@ def test_causal_cut_after_softmax_caught(monkeypatch):
         tr.test_causal_route_against_brute_force()
 
 
-def test_sasa_lowest_probability_first_caught(monkeypatch):
-    orig = sa.augment
-
-    def low_first(prob, *a, **k):
-        return orig(-np.asarray(prob), *a, **k)
-    monkeypatch.setattr(oracle, "augment", low_first)
+def test_sasa_lowest_value_first_caught(monkeypatch):
+    monkeypatch.setattr(sa, "buy_order", lambda value, j: (value, j))
     with pytest.raises(AssertionError):
-        ts.test_brute_force_added_blocks_carry_max_mass(0, 400, 1, 6)
+        ts.test_brute_force_bought_blocks_carry_max_mass(1, 400, 2, 5, False)
 
 
-def test_sasa_slack_from_mean_caught(monkeypatch):
-    orig_lpt = sa.lpt_assign
-
-    def mean_makespan(costs, order, W):
-        worker_of, load = orig_lpt(costs, order, W)
-        # a wrong slack: measured from the mean load (raise every load to the max minus the mean)
-        return worker_of, load - (load.max() - int(load.mean()))
-    monkeypatch.setattr(sa, "lpt_assign", mean_makespan)
+def test_sasa_first_row_value_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(sa, "block_value", lambda p_rows, v_rows, j: float(p_rows[0][j]) if j < v_rows[0] else 0.0)
     with pytest.raises(AssertionError):
-        ts.test_hand_example_two_workers()
+        ts.test_golden_union_priced_example(golden_dir)
 
 
-def test_sasa_candidates_from_all_rows_caught(monkeypatch):
-    orig_lpt = sa.lpt_assign
-
-    def one_worker_rows(costs, order, W):
-        worker_of, load = orig_lpt(costs, order, W)
-        return np.zeros_like(worker_of), load          # every row counted as worker 0's
-    monkeypatch.setattr(sa, "lpt_assign", one_worker_rows)
+def test_sasa_largest_row_value_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(sa, "block_value",
+                        lambda p_rows, v_rows, j: max(float(p[j]) if j < nv else 0.0 for p, nv in zip(p_rows, v_rows)))
     with pytest.raises(AssertionError):
-        ts.test_hand_example_three_workers_ties()
+        ts.test_golden_union_priced_example(golden_dir)
+
+
+def test_sasa_reversed_tie_rule_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(sa, "buy_order", lambda value, j: (-value, -j))
+    with pytest.raises(AssertionError):
+        ts.test_golden_union_priced_example(golden_dir)
+
+
+def test_sasa_sequential_lpt_caught(monkeypatch, golden_dir):
+    def sequential(costs, order, W):
+        worker_of, load = oracle.lpt_assign(costs, order, W)
+        last = np.full(W, -1, dtype=np.int64)
+        for g in order:
+            last[worker_of[g]] = g
+        return worker_of, load, last
+    monkeypatch.setattr(sa, "lpt_batched", sequential)
+    with pytest.raises(AssertionError):
+        ts.test_golden_union_priced_example(golden_dir)
+
+
+def test_sasa_slack_on_first_item_caught(monkeypatch):
+    orig = sa.lpt_batched
+
+    def first_item(costs, order, W):
+        worker_of, load, _ = orig(costs, order, W)
+        first = np.full(W, -1, dtype=np.int64)
+        for g in reversed(np.asarray(order).tolist()):
+            first[worker_of[g]] = g
+        return worker_of, load, first
+    monkeypatch.setattr(sa, "lpt_batched", first_item)
+    with pytest.raises(AssertionError):
+        ts.test_assignment_unchanged_and_makespan_kept(4, 64, 1000, False)
+
+
+def test_sasa_budget_rounded_up_caught(monkeypatch):
+    monkeypatch.setattr(sa, "budget_blocks", lambda slack, per_block: -(-slack // per_block))
+    with pytest.raises(AssertionError):
+        ts.test_assignment_unchanged_and_makespan_kept(24, 128, 1064, False)
+
+
+def test_sasa_priced_in_blocks_caught(monkeypatch):
+    # every key block priced at one tile, the kernel's 128-key blocks included
+    monkeypatch.setattr(sa, "block_tiles", lambda nbk, n_tokens, key_block: np.ones(nbk, dtype=np.int64))
+    monkeypatch.setattr(sa, "budget_blocks", lambda slack, per_block: slack)
+    with pytest.raises(AssertionError):
+        ts.test_assignment_unchanged_and_makespan_kept(8, 128, 1000, False)
 
 
 def test_mixed_block_eligibility_off_by_one_caught(monkeypatch):

@@ -1,10 +1,14 @@
-"""Pins for the slack-aware augmentation oracle: a hand-worked example with
-ties, brute force over candidate subsets (the added blocks carry the most
-probability a worker's slack can buy), and invariants (makespan kept, every
-row stays a prefix of its ranking, nothing added without slack or
-candidates, causal eligibility)."""
+"""Pins for the slack-aware augmentation oracle: a hand-worked example
+(tests/golden/sasa_union_priced.json) with a batch that a sequential LPT
+would assign differently, a tie and values that differ from one row's;
+the batched LPT against the sequential one where they must agree; brute
+force over candidate subsets (the bought blocks carry the most retained
+mass the slack can buy); the assignment unchanged after augmentation with
+the makespan kept; every row holding its item's union."""
 import itertools
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -25,109 +29,195 @@ def _hand_case():
     return prob, mask, mask.sum(-1)
 
 
-def test_hand_example_two_workers():
-    # costs [2, 1, 3, 1]; list 2, 0, 1, 3; LPT: 2->w0 (3), 0->w1 (2), 1->w1 (3),
-    # 3->w0 (tie 3/3, lowest id) -> loads [4, 3], M = 4, slack [0, 1].
-    # w1 holds rows 0 and 1; its best candidate is row 1, block 2 (P = 0.25).
-    prob, mask, rc = _hand_case()
-    a = oracle.augment(prob, mask, rc, None, 1, 0, 2)
-    assert a.load.tolist() == [4, 3] and a.makespan == 4 and a.slack.tolist() == [0, 1]
-    assert a.worker_of.tolist() == [1, 1, 0, 0]
-    assert a.added[0, 0].tolist() == [0, 1, 0, 0]
-    assert a.mask[0, 0, 1].tolist() == [0, 1, 1, 0]
-    assert a.row_idx[0, 0, 1].tolist() == [1, 2, -1, -1]
-    assert a.head_cnt[0, 0] == 8
+def _golden(golden_dir):
+    with open(os.path.join(golden_dir, "sasa_union_priced.json")) as f:
+        gd = json.load(f)
+    sh = gd["shape"]
+    prob = np.array(gd["prob_32nds"], dtype=np.float64)[None] / 32.0
+    H, nb = sh["H"], sh["nb"]
+    mask = np.zeros((1, H, nb, nb), dtype=np.uint8)
+    for h in range(H):
+        for i in range(nb):
+            mask[0, h, i, gd["selected"][h][i]] = 1
+    # rank order of every row: P descending, equal P by the smaller block
+    order = np.array([[[sorted(range(nb), key=lambda j: (-prob[0, h, i, j], j)) for i in range(nb)]
+                       for h in range(H)]])
+    return gd, sh, prob, mask, order
 
 
-def test_hand_example_three_workers_ties():
-    # LPT: 2->w0 (3), 0->w1 (2), 1->w2 (1), 3->w2 (2): loads [3, 2, 2], slack [0, 1, 1].
-    # w1 (row 0): blocks 2 and 3 tie at 0.125 -> the smaller index, 2.
-    # w2 (rows 1, 3): row 1 block 2 and row 3 block 3 tie at 0.25 -> the smaller row, 1.
-    prob, mask, rc = _hand_case()
-    a = oracle.augment(prob, mask, rc, None, 1, 0, 3)
-    assert a.slack.tolist() == [0, 1, 1]
-    assert a.added[0, 0].tolist() == [1, 1, 0, 0]
-    assert a.mask[0, 0, 0].tolist() == [1, 1, 1, 0]
-    assert a.mask[0, 0, 1].tolist() == [0, 1, 1, 0]
-    assert a.mask[0, 0, 3].tolist() == [0, 0, 1, 0]
+def _run_golden(golden_dir):
+    gd, sh, prob, mask, order = _golden(golden_dir)
+    return gd, oracle.augment(prob, mask, order, gd["work_list"], None, sh["group"], sh["workers"],
+                              sh["n_tokens"], sh["key_block"])
 
 
-def _routed(seed, B=1, H=2, N=300, d=8, block=64, p=0.6, causal=False):
+def test_golden_union_priced_example(golden_dir):
+    gd, a = _run_golden(golden_dir)
+    ex = gd["expected"]
+    assert a.worker_of.tolist() == ex["worker_of"]
+    assert a.load.tolist() == ex["load"] and a.makespan == ex["makespan"]
+    assert a.slack.tolist() == ex["slack"] and a.last_item.tolist() == ex["last_item"]
+    assert a.paid.tolist() == ex["paid"] and a.paid_tiles.tolist() == ex["paid"]
+    assert a.mask[0].tolist() == ex["mask"]
+    assert a.row_cnt[0].tolist() == ex["row_cnt"]
+    assert a.head_cnt[0].tolist() == ex["head_cnt"]
+    assert a.row_idx[0].tolist() == ex["row_idx"]
+
+
+# ------------------------------------------------------------ batched LPT ---
+
+@pytest.mark.parametrize("seed", range(4))
+def test_lpt_batched_single_batch_is_lpt(seed):
+    # At most W items: one batch, the items in list order to the workers in id
+    # order, which is what the sequential greedy does from all-zero loads.
+    rng = np.random.default_rng(seed)
+    W = int(rng.integers(3, 40))
+    n = int(rng.integers(1, W + 1))
+    costs = rng.integers(1, 50, size=n)
+    order = rng.permutation(n)
+    wb, lb, last = oracle.lpt_batched(costs, order, W)
+    ws, ls = oracle.lpt_assign(costs, order, W)
+    assert wb.tolist() == ws.tolist() and lb.tolist() == ls.tolist()
+    assert wb[order].tolist() == list(range(n))
+    assert last.tolist() == [int(order[w]) if w < n else -1 for w in range(W)]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_lpt_batched_batches(seed):
+    rng = np.random.default_rng(10 + seed)
+    W = int(rng.integers(2, 12))
+    n = int(rng.integers(W, 6 * W))
+    costs = rng.integers(0, 30, size=n)
+    order = rng.permutation(n)
+    wo, load, last = oracle.lpt_batched(costs, order, W)
+    assert (np.bincount(wo, weights=costs, minlength=W) == load).all()
+    for b in range(0, n, W):
+        batch = wo[order[b:b + W]]
+        assert len(set(batch.tolist())) == batch.size          # one item per worker and batch
+    for w in range(W):
+        mine = [p for p in range(n) if wo[order[p]] == w]
+        assert last[w] == (order[mine[-1]] if mine else -1)
+    # equal costs: a round robin, loads within one item of each other
+    wo2, l2, _ = oracle.lpt_batched(np.full(n, 7), order, W)
+    assert l2.max() - l2.min() <= 7
+
+
+# ------------------------------------------------- union-priced augmentation ---
+
+def _routed(seed, B=1, H=2, N=300, d=8, block=64, p=0.6, causal=False, key_block=None):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, H, N, d)) * 2
     k = rng.standard_normal((B, H, N, d)) * 2
-    return oracle.route(q, k, block, p, causal=causal)
+    return oracle.route(q, k, block, p, causal=causal, key_block=key_block)
+
+
+def _augment(r, G, W, N, kb, window=0):
+    order = oracle.work_list(oracle.group_costs(r.row_cnt, G), window)
+    return oracle.augment(r.prob, r.mask, r.order, order, r.valid, G, W, N, kb)
+
+
+def _mass_gain(prob, valid, rows, S):
+    """Retained-mass gain of giving the blocks S to the rows (b, h, i), each
+    where eligible, computed from masks."""
+    gain = 0.0
+    for (b, h, i) in rows:
+        m = np.zeros(prob.shape[-1], dtype=bool)
+        for j in S:
+            if j < valid[b, h, i]:
+                m[j] = True
+        gain += float(oracle.retained_mass(prob[b, h, i], m))
+    return gain
 
 
 @pytest.mark.parametrize("seed", range(6))
-@pytest.mark.parametrize("N,G,W", [(400, 1, 6), (320, 1, 4), (500, 2, 5)])
-def test_brute_force_added_blocks_carry_max_mass(seed, N, G, W):
-    r = _routed(seed, N=N, p=0.3 + 0.1 * seed)
-    a = oracle.augment(r.prob, r.mask, r.row_cnt, r.valid, G, 0, W)
-    nb = r.mask.shape[-1]
+@pytest.mark.parametrize("N,G,W,causal", [(400, 2, 5, False), (512, 4, 3, False), (640, 4, 4, True), (300, 1, 6, False)])
+def test_brute_force_bought_blocks_carry_max_mass(seed, N, G, W, causal):
+    r = _routed(seed, N=N, p=0.3 + 0.1 * seed, causal=causal)
+    B, H, nb, nbk = r.mask.shape
+    valid = r.valid if r.valid is not None else np.full((B, H, nb), nbk)
+    a = _augment(r, G, W, N, 64)
     ng = -(-nb // G)
+    old = oracle.item_unions(r.mask, G)
     for w in range(W):
-        rows = [(h, i) for h in range(2) for i in range(nb) if a.worker_of[h * ng + i // G] == w]
-        cands = [(h, i, j) for (h, i) in rows for j in range(nb) if not r.mask[0, h, i, j]]
-        kk = min(int(a.slack[w]), len(cands))
-        added = [(h, i, j) for (h, i, j) in cands if a.mask[0, h, i, j]]
-        assert len(added) == kk == a.added_per_worker[w]
-        if kk == 0 or len(cands) > 16:
+        g = int(a.last_item[w])
+        if g < 0:
+            assert a.paid[w] == 0
             continue
-        best = max(math.fsum(r.prob[0, h, i, j] for (h, i, j) in sub)
-                   for sub in itertools.combinations(cands, kk))
-        got = math.fsum(r.prob[0, h, i, j] for (h, i, j) in added)
-        assert got >= best * (1 - 1e-15)
+        bh, gi = divmod(g, ng)
+        b, h = divmod(bh, H)
+        rows = [(b, h, i) for i in range(gi * G, min(nb, (gi + 1) * G))]
+        nv = max(int(valid[x]) for x in rows)
+        cands = [j for j in range(nv) if not old[g, j]]
+        bought = [j for j in range(nbk) if a.union[g, j] and not old[g, j]]
+        kk = min(int(a.slack[w]), len(cands))
+        assert len(bought) == kk == a.paid[w]
+        if kk == 0 or math.comb(len(cands), kk) > 5000:
+            continue
+        best = max(_mass_gain(r.prob, valid, rows, S) for S in itertools.combinations(cands, kk))
+        assert _mass_gain(r.prob, valid, rows, bought) >= best * (1 - 1e-15)
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("W", [1, 4, 16, 64])
-def test_invariants(W, causal):
-    r = _routed(10 + W, B=1, H=3, N=1000, block=64, p=0.7, causal=causal)
+@pytest.mark.parametrize("W,kb,N", [(1, 64, 1000), (4, 64, 1000), (16, 64, 1000), (64, 64, 1000),
+                                    (8, 128, 1000), (24, 128, 1064)])
+def test_assignment_unchanged_and_makespan_kept(W, kb, N, causal):
+    # N = 1064 with 128-key blocks: a ragged last key block of one tile, so
+    # some slacks are odd
+    r = _routed(10 + W, B=1, H=3, N=N, block=64, p=0.3, causal=causal, key_block=kb)
     G = 4
-    a = oracle.augment(r.prob, r.mask, r.row_cnt, r.valid, G, 0, W)
-    new_load = a.load + a.added_per_worker
-    assert new_load.max() == a.makespan                       # the makespan is kept
+    a = _augment(r, G, W, N, kb)
+    tiles = oracle.block_tiles(r.mask.shape[-1], N, kb)
+    new_costs = (a.union * tiles).sum(-1)
+    old_costs = (oracle.item_unions(r.mask, G) * tiles).sum(-1)
+    order = oracle.work_list(oracle.group_costs(r.row_cnt, G), 0)
+    # priced in the tiles the kernel runs: the same assignment, every worker
+    # grown by the tiles it bought, none past the makespan
+    wo2, load2, last2 = oracle.lpt_batched(new_costs, order, W)
+    assert wo2.tolist() == a.worker_of.tolist() and last2.tolist() == a.last_item.tolist()
+    assert (load2 == a.load + a.paid_tiles).all() and load2.max() == a.makespan
+    assert (a.paid * (kb // 64) >= a.paid_tiles).all()
+    assert ((a.slack - a.paid * (kb // 64)) >= 0).all()
+    # only last items grew
+    grown = np.nonzero(new_costs != old_costs)[0]
+    assert set(grown.tolist()) <= set(int(g) for g in a.last_item if g >= 0)
     if W == 1:
-        assert a.added.sum() == 0
-    assert (a.mask >= r.mask).all() and (a.added >= 0).all()
-    assert (a.row_cnt == r.row_cnt + a.added).all()
-    assert (a.head_cnt == a.row_cnt.sum(-1)).all()
-    # every row is still the first row_cnt blocks of its ranking
-    ranked_sel = np.take_along_axis(a.mask, r.order, -1)
-    want = (np.arange(a.mask.shape[-1]) < a.row_cnt[..., None]).astype(np.uint8)
-    assert (ranked_sel == want).all()
-    assert (oracle.retained_mass(r.prob, a.mask) >= oracle.retained_mass(r.prob, r.mask)).all()
-    if causal:
-        nb = a.mask.shape[-1]
-        assert not (a.mask * np.triu(np.ones((nb, nb), dtype=np.uint8), 1)).any()
-    # a worker with slack left over has no candidate left
-    nb = a.mask.shape[-1]
+        assert a.paid.sum() == 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_take_their_item_union(causal):
+    r = _routed(21, B=1, H=3, N=900, block=64, p=0.5, causal=causal)
+    G = 4
+    a = _augment(r, G, 7, 900, 64)
+    B, H, nb, nbk = r.mask.shape
     ng = -(-nb // G)
-    left = a.slack - a.added_per_worker
-    for w in np.nonzero(left > 0)[0]:
-        items = np.nonzero(a.worker_of == w)[0]
-        for g in items:
-            bh, i0 = divmod(int(g), ng)
-            rows = a.row_cnt.reshape(-1, nb)[bh, i0 * G:(i0 + 1) * G]
-            vrows = r.valid.reshape(-1, nb)[bh, i0 * G:(i0 + 1) * G]
-            assert (rows == vrows).all()
+    valid = r.valid if r.valid is not None else np.full((B, H, nb), nbk)
+    for h in range(H):
+        for i in range(nb):
+            g = h * ng + i // G
+            want = {j for j in np.nonzero(a.union[g])[0].tolist() if j < valid[0, h, i]}
+            assert set(np.nonzero(a.mask[0, h, i])[0].tolist()) == want
+            k = len(want)
+            assert a.row_idx[0, h, i, :k].tolist() == sorted(want)
+            ranked = [int(j) for j in r.order[0, h, i] if j < valid[0, h, i] and j not in want]
+            assert a.row_idx[0, h, i, k:k + len(ranked)].tolist() == ranked
+            assert (a.row_idx[0, h, i, k + len(ranked):] == -1).all()
+    assert (a.mask >= r.mask).all()
+    assert (a.row_cnt == r.mask.sum(-1) + a.added).all() and (a.head_cnt == a.row_cnt.sum(-1)).all()
+    assert (oracle.retained_mass(r.prob, a.mask) >= oracle.retained_mass(r.prob, r.mask)).all()
+    # a worker whose budget outlasted its candidates left its last item full
+    for w in range(7):
+        g = int(a.last_item[w])
+        if g >= 0 and a.slack[w] > a.paid[w]:
+            bh, gi = divmod(g, ng)
+            nv = max(int(valid[0, bh, i]) for i in range(gi * G, min(nb, (gi + 1) * G)))
+            assert a.union[g, :nv].all()
 
 
-def test_nothing_to_add_at_p_one():
+def test_nothing_to_buy_at_p_one():
     r = _routed(3, p=1.0)
-    a = oracle.augment(r.prob, r.mask, r.row_cnt, r.valid, 2, 0, 5)
-    assert a.added.sum() == 0 and (a.mask == 1).all()
-
-
-def test_windows_change_only_the_list():
-    r = _routed(4, H=4, N=640, p=0.6)
-    G = 2
-    ng = -(-r.mask.shape[-1] // G)
-    a1 = oracle.augment(r.prob, r.mask, r.row_cnt, r.valid, G, 0, 6)
-    a2 = oracle.augment(r.prob, r.mask, r.row_cnt, r.valid, G, 2 * ng, 6)
-    for a in (a1, a2):
-        assert (a.load + a.added_per_worker).max() == a.makespan
+    a = _augment(r, 2, 5, 300, 64)
+    assert a.paid.sum() == 0 and a.added.sum() == 0 and (a.mask == 1).all()
 
 
 # ------------------------------------------------ work-item slack (union fill) ---
