@@ -49,7 +49,7 @@ from .routing import (block_sizes, num_blocks, pool_blocks, block_scores, softma
 from .attention import attend, attend_units, attend_dense_masked_logits
 from .schedule import group_costs, work_list, lpt_assign, lpt_batched, static_partition_loads, load_imbalance
 from .flops import executed_flops, dense_flops
-from .sasa import Augmented, augment, UnionFilled, union_fill, retained_mass, item_unions, block_tiles
+from .sasa import Augmented, augment, UnionFilled, union_fill, retained_mass, item_unions, block_tiles, item_costs
 from . import fp8
 
 __all__ = [

@@ -8,34 +8,35 @@ high-value blocks to improve quality.
 
 The pages describe ranks that are GPUs and price work in blocks.  The
 readings taken for one GPU, priced in what the attention kernel of this
-implementation actually runs:
+implementation runs:
 
 * a work item (G consecutive query blocks of one head) runs as one sequence
-  of 64-key tiles: the union of its rows' selected key blocks, a key block
-  holding key_block/64 tiles (the last block only the tiles its keys reach).
-  An item costs its union tiles.
+  of 64-key tiles, the union of its rows' selected key blocks (a key block
+  holds key_block/64 tiles, the last block only the tiles its keys reach);
+  every tile costs a fixed part and each row that selected it computes it.
+  With row-tiles as the unit, an item costs
+      F * (union tiles) + (row tiles),
+  F = tile_fixed (a measured constant of the kernel, an input here).
 * ranks are the W workers of a longest-first assignment of the items in
   work-list order, made in batches (``schedule.lpt_batched``); the slack of
-  worker w is s_w = M - L_w, with L_w its load and M = max_w L_w.
-* a block that is already in its item's union costs nothing: every row of an
-  item takes every block of the union that is eligible for it (j < valid_i).
-  A block outside the union costs one key block of tiles (key_block/64,
-  also for a ragged last block), and once paid for it is in the union, so
-  every row of the item for which it is eligible takes it.
+  worker w is s_w = M - L_w, with L_w its cost and M = max_w L_w.
 * worker w spends its slack on its last item (the one of the latest batch
-  that reached it): extra tiles there leave every other choice of the
+  that reached it): extra cost there leaves every other choice of the
   batched assignment, and of a list schedule, unchanged (a worker that took
   no later item keeps taking none when its load grows), so no worker ends
-  after M.  It buys floor(s_w / (key_block/64)) key blocks.
-* the value of key block j for item g is the sum of its rows' routing
-  probabilities P_ij over the rows for which j is eligible, added in member
-  order from 0.0 (the pages name no other measure of a block's value).  With
-  one price per block, taking the candidates in the order (value desc, j asc)
-  maximises the value the budget buys.
+  after M.
+* its candidates are the (row, key block) pairs of that item whose block is
+  eligible for the row and not selected by it; the value of a pair is the
+  row's routing probability of the block (the pages name no other measure
+  of a block's value).  Candidates go in the order (value desc, row asc,
+  block asc); a pair costs the block's tiles t_j, plus F * t_j when its
+  block is in neither the item's union nor an earlier pair of the order.
+  The worker buys the longest prefix of that order whose total cost is at
+  most s_w.
 
-``union_fill`` is the same with no slack: every row takes the eligible
-blocks of its item's union, which leaves every union, and the kernel's work,
-unchanged.
+``union_fill`` gives every row of a work item the blocks of the item's
+union that are eligible for it (the union, and the number of tiles, stay the
+same; the row-tiles grow).
 """
 from __future__ import annotations
 
@@ -68,24 +69,29 @@ def block_tiles(nbk: int, n_tokens: int, key_block: int) -> np.ndarray:
     return t
 
 
-def block_value(p_rows, valid_rows, j: int) -> float:
-    """Value of key block j for an item: P of the item's rows (in member
-    order) for which j is eligible, added from 0.0."""
-    v = 0.0
-    for p, nv in zip(p_rows, valid_rows):
-        if j < nv:
-            v += float(p[j])
-    return v
+def buy_order(value, row: int, j: int):
+    """Sort key of a candidate pair: value descending, then row, then block."""
+    return (-value, row, j)
 
 
-def buy_order(value, j: int):
-    """Sort key of a candidate: value descending, then block ascending."""
-    return (-value, j)
+def pair_cost(tiles_j: int, opens: bool, tile_fixed: int) -> int:
+    """Row-tiles of giving a row key block j: its tiles, plus the fixed part
+    of every tile when the block is not yet in the item's union."""
+    return tiles_j * (1 + (tile_fixed if opens else 0))
 
 
-def budget_blocks(slack: int, per_block: int) -> int:
-    """Key blocks a slack of `slack` tiles buys at per_block tiles each."""
-    return slack // per_block
+def item_costs(mask, group: int, n_tokens: int, key_block: int, tile_fixed: int) -> np.ndarray:
+    """F * (union tiles) + (row tiles) of every work item."""
+    mask = np.asarray(mask) != 0
+    B, H, nb, nbk = mask.shape
+    tiles = block_tiles(nbk, n_tokens, key_block)
+    ng = -(-nb // group)
+    row_tiles = (mask * tiles).sum(-1).reshape(B * H, nb)
+    per_item = np.zeros((B * H, ng), dtype=np.int64)
+    for i in range(nb):
+        per_item[:, i // group] += row_tiles[:, i]
+    union_tiles = (item_unions(mask, group) * tiles).sum(-1)
+    return tile_fixed * union_tiles + per_item.reshape(-1)
 
 
 @dataclasses.dataclass
@@ -97,30 +103,34 @@ class Augmented:
     head_cnt: np.ndarray    # [B,H] int64
     added: np.ndarray       # [B,H,nb] int64, blocks added per row
     worker_of: np.ndarray   # [items] int64, worker of each work item
-    load: np.ndarray        # [W] int64, union tiles per worker before augmentation
+    load: np.ndarray        # [W] int64, cost per worker before augmentation
     last_item: np.ndarray   # [W] int64, the item that takes the worker's slack (-1: none)
     slack: np.ndarray       # [W] int64, M - load
-    paid: np.ndarray        # [W] int64, key blocks bought per worker
-    paid_tiles: np.ndarray  # [W] int64, tiles they hold
+    paid: np.ndarray        # [W] int64, pairs bought per worker
+    paid_cost: np.ndarray   # [W] int64, their cost
     makespan: int
-    union: np.ndarray       # [items, nbk] bool, every item's union after augmentation
 
 
 def _fill(mask, unions, order, valid, group: int):
     """Row i of item g selects its own blocks and every block of unions[g]
-    eligible for it; row_idx lists the selection ascending, then the row's
-    other eligible blocks in the rank order `order`, then -1."""
+    eligible for it; row_idx as in _rebuild."""
     mask = np.asarray(mask).astype(np.uint8)
     B, H, nb, nbk = mask.shape
-    ng = -(-nb // group)
     valid = np.full((B, H, nb), nbk, dtype=np.int64) if valid is None else np.asarray(valid, dtype=np.int64)
-    order = np.asarray(order)
+    ng = -(-nb // group)
     new = mask.copy()
     uni = np.asarray(unions).reshape(B, H, ng, nbk)
     for i in range(nb):
         eligible = np.arange(nbk)[None, None, :] < valid[:, :, i, None]
         new[:, :, i] |= (uni[:, :, i // group] & eligible).astype(np.uint8)
     cnt = new.astype(np.int64).sum(-1)
+    return new, cnt, _rebuild(new, np.asarray(order), valid)
+
+
+def _rebuild(new, order, valid):
+    """row_idx of a selection: ascending selected blocks, then the row's other
+    eligible blocks in the rank order `order`, then -1."""
+    B, H, nb, nbk = new.shape
     row_idx = np.full((B, H, nb, nbk), -1, dtype=np.int32)
     for b in range(B):
         for h in range(H):
@@ -129,18 +139,19 @@ def _fill(mask, unions, order, valid, group: int):
                 rest = [int(j) for j in order[b, h, i] if j < valid[b, h, i] and not new[b, h, i, j]]
                 row_idx[b, h, i, :sel.size] = sel
                 row_idx[b, h, i, sel.size:sel.size + len(rest)] = rest
-    return new, cnt, row_idx
+    return row_idx
 
 
 def augment(prob, mask, order, work_order, valid, group: int, num_workers: int, n_tokens: int,
-            key_block: int) -> Augmented:
-    """Slack-aware augmentation priced in union tiles.
+            key_block: int, tile_fixed: int) -> Augmented:
+    """Slack-aware augmentation priced in row-tiles.
 
     prob [B,H,nb,nbk] fp64 block probabilities; mask [B,H,nb,nbk] the
     selection; order [B,H,nb,nbk] each row's routing rank order (P desc, j
     asc); work_order the work list (item ids); valid [B,H,nb] (or None) the
     eligible blocks per row; group = query blocks per work item; num_workers
-    = W; n_tokens and key_block give the tiles of each key block.
+    = W; n_tokens and key_block give the tiles of each key block; tile_fixed
+    = F, the fixed cost of a tile in row-tiles.
     """
     prob = np.asarray(prob, dtype=np.float64)
     mask = np.asarray(mask).astype(np.uint8)
@@ -148,40 +159,42 @@ def augment(prob, mask, order, work_order, valid, group: int, num_workers: int, 
     ng = -(-nb // group)
     valid = np.full((B, H, nb), nbk, dtype=np.int64) if valid is None else np.asarray(valid, dtype=np.int64)
     tiles = block_tiles(nbk, n_tokens, key_block)
-    per_block = key_block // 64
 
     union = item_unions(mask, group)
-    costs = (union * tiles[None, :]).sum(-1)
+    costs = item_costs(mask, group, n_tokens, key_block, tile_fixed)
     worker_of, load, last_item = lpt_batched(costs, work_order, num_workers)
     makespan = int(load.max()) if load.size else 0
     slack = makespan - load
 
-    new_union = union.copy()
+    new = mask.copy()
     paid = np.zeros(num_workers, dtype=np.int64)
-    paid_tiles = np.zeros(num_workers, dtype=np.int64)
+    paid_cost = np.zeros(num_workers, dtype=np.int64)
     for w in range(num_workers):
         g = int(last_item[w])
-        budget = budget_blocks(int(slack[w]), per_block)
-        if g < 0 or budget == 0:
+        if g < 0 or slack[w] <= 0:
             continue
         bh, gi = divmod(g, ng)
         b, h = divmod(bh, H)
-        members = list(range(gi * group, min(nb, (gi + 1) * group)))
-        p_rows = [prob[b, h, i] for i in members]
-        v_rows = [int(valid[b, h, i]) for i in members]
-        nv = max(v_rows)
-        cands = [j for j in range(nv) if not union[g, j]]
-        value = {j: block_value(p_rows, v_rows, j) for j in cands}
-        take = sorted(cands, key=lambda j: buy_order(value[j], j))[:budget]
-        for j in take:
-            new_union[g, j] = True
-        paid[w] = len(take)
-        paid_tiles[w] = int(sum(int(tiles[j]) for j in take))
+        cands = [(i, j) for i in range(gi * group, min(nb, (gi + 1) * group))
+                 for j in range(int(valid[b, h, i])) if not mask[b, h, i, j]]
+        cands.sort(key=lambda c: buy_order(float(prob[b, h, c[0], c[1]]), c[0], c[1]))
+        opened = union[g].copy()
+        spent = 0
+        for i, j in cands:
+            c = pair_cost(int(tiles[j]), not opened[j], tile_fixed)
+            if spent + c > slack[w]:
+                break
+            spent += c
+            opened[j] = True
+            new[b, h, i, j] = 1
+            paid[w] += 1
+        paid_cost[w] = spent
 
-    new_mask, cnt, row_idx = _fill(mask, new_union, order, valid, group)
+    cnt = new.astype(np.int64).sum(-1)
+    row_idx = _rebuild(new, order, valid)
     added = cnt - mask.astype(np.int64).sum(-1)
-    return Augmented(new_mask, cnt, row_idx, cnt.sum(-1), added, worker_of, load, last_item,
-                     slack.astype(np.int64), paid, paid_tiles, makespan, new_union)
+    return Augmented(new, cnt, row_idx, cnt.sum(-1), added, worker_of, load, last_item,
+                     slack.astype(np.int64), paid, paid_cost, makespan)
 
 
 @dataclasses.dataclass

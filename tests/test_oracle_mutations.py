@@ -3,10 +3,11 @@ catch each one: a transposed operand, a wrong divisor, an exclusive threshold,
 a reversed tie rule, a dropped scale, an off-by-one causal mask, a wrong log
 base, a wrong sort direction, and a causal block cut that is missing, off by
 one, or applied after the softmax instead of before it; an augmentation that
-buys the lowest-value blocks, values a block by one row or by the largest
-row, breaks ties the wrong way, assigns items with the sequential LPT,
-spends slack on a worker's first item, rounds its budget up, or prices
-blocks instead of tiles; an E4M3 exponent bias off by
+buys the lowest-value pairs, breaks ties the wrong way, drops the fixed cost
+of a tile, charges it for every pair, passes over a pair it cannot afford
+instead of stopping, assigns items with the sequential LPT, spends slack on
+a worker's first item, prices items in union tiles only, or prices a key
+block as one tile; an E4M3 exponent bias off by
 one, ties rounded away from zero, K scaled per token instead of per tile, and
 an inverted dequantisation scale; and an ambiguity window whose swap-across-
 the-cut rule is dropped (whole or either half), measured against the wrong
@@ -157,28 +158,63 @@ def test_causal_cut_after_softmax_caught(monkeypatch):
 
 
 def test_sasa_lowest_value_first_caught(monkeypatch):
-    monkeypatch.setattr(sa, "buy_order", lambda value, j: (value, j))
+    monkeypatch.setattr(sa, "buy_order", lambda value, row, j: (value, row, j))
     with pytest.raises(AssertionError):
-        ts.test_brute_force_bought_blocks_carry_max_mass(1, 400, 2, 5, False)
-
-
-def test_sasa_first_row_value_caught(monkeypatch, golden_dir):
-    monkeypatch.setattr(sa, "block_value", lambda p_rows, v_rows, j: float(p_rows[0][j]) if j < v_rows[0] else 0.0)
-    with pytest.raises(AssertionError):
-        ts.test_golden_union_priced_example(golden_dir)
-
-
-def test_sasa_largest_row_value_caught(monkeypatch, golden_dir):
-    monkeypatch.setattr(sa, "block_value",
-                        lambda p_rows, v_rows, j: max(float(p[j]) if j < nv else 0.0 for p, nv in zip(p_rows, v_rows)))
-    with pytest.raises(AssertionError):
-        ts.test_golden_union_priced_example(golden_dir)
+        ts.test_purchase_is_the_longest_affordable_prefix(1, 400, 2, 5, False, 64, 3)
 
 
 def test_sasa_reversed_tie_rule_caught(monkeypatch, golden_dir):
-    monkeypatch.setattr(sa, "buy_order", lambda value, j: (-value, -j))
+    monkeypatch.setattr(sa, "buy_order", lambda value, row, j: (-value, -row, -j))
     with pytest.raises(AssertionError):
-        ts.test_golden_union_priced_example(golden_dir)
+        ts.test_golden_slack_purchase_example(golden_dir)
+
+
+def test_sasa_fixed_tile_cost_dropped_caught(monkeypatch):
+    monkeypatch.setattr(sa, "pair_cost", lambda tiles_j, opens, tile_fixed: tiles_j)
+    with pytest.raises(AssertionError):
+        ts.test_purchase_is_the_longest_affordable_prefix(1, 400, 2, 5, False, 64, 3)
+
+
+def test_sasa_every_pair_opens_a_tile_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(sa, "pair_cost", lambda tiles_j, opens, tile_fixed: tiles_j * (1 + tile_fixed))
+    with pytest.raises(AssertionError):
+        ts.test_golden_slack_purchase_example(golden_dir)
+
+
+def test_sasa_skips_instead_of_stopping_caught(monkeypatch, golden_dir):
+    # a purchase that passes over a pair it cannot afford and goes on
+    orig_cost = sa.pair_cost
+    orig_augment = sa.augment
+
+    def patched(prob, mask, order, work_order, valid, group, W, n_tokens, key_block, tile_fixed):
+        prob = np.asarray(prob, dtype=np.float64)
+        mask0 = np.asarray(mask).astype(np.uint8)
+        res = orig_augment(prob, mask0, order, work_order, valid, group, W, n_tokens, key_block, tile_fixed)
+        B, H, nb, nbk = mask0.shape
+        ng = -(-nb // group)
+        tiles = sa.block_tiles(nbk, n_tokens, key_block)
+        union = sa.item_unions(mask0, group)
+        new = mask0.copy()
+        for w in range(W):
+            g = int(res.last_item[w])
+            if g < 0 or res.slack[w] <= 0:
+                continue
+            bh, gi = divmod(g, ng)
+            b, h = divmod(bh, H)
+            cands = sorted(((i, j) for i in range(gi * group, min(nb, (gi + 1) * group)) for j in range(nbk)
+                            if not mask0[b, h, i, j]), key=lambda c: (-prob[b, h, c[0], c[1]], c[0], c[1]))
+            opened, spent = union[g].copy(), 0
+            for i, j in cands:
+                c = orig_cost(int(tiles[j]), not opened[j], tile_fixed)
+                if spent + c <= res.slack[w]:
+                    spent += c
+                    opened[j] = True
+                    new[b, h, i, j] = 1
+        res.mask = new
+        return res
+    monkeypatch.setattr(oracle, "augment", patched)
+    with pytest.raises(AssertionError):
+        ts.test_golden_slack_purchase_example(golden_dir)
 
 
 def test_sasa_sequential_lpt_caught(monkeypatch, golden_dir):
@@ -190,7 +226,7 @@ def test_sasa_sequential_lpt_caught(monkeypatch, golden_dir):
         return worker_of, load, last
     monkeypatch.setattr(sa, "lpt_batched", sequential)
     with pytest.raises(AssertionError):
-        ts.test_golden_union_priced_example(golden_dir)
+        ts.test_golden_slack_purchase_example(golden_dir)
 
 
 def test_sasa_slack_on_first_item_caught(monkeypatch):
@@ -204,21 +240,21 @@ def test_sasa_slack_on_first_item_caught(monkeypatch):
         return worker_of, load, first
     monkeypatch.setattr(sa, "lpt_batched", first_item)
     with pytest.raises(AssertionError):
-        ts.test_assignment_unchanged_and_makespan_kept(4, 64, 1000, False)
+        ts.test_assignment_unchanged_and_makespan_kept(4, 64, 1000, 3, False)
 
 
-def test_sasa_budget_rounded_up_caught(monkeypatch):
-    monkeypatch.setattr(sa, "budget_blocks", lambda slack, per_block: -(-slack // per_block))
+def test_sasa_items_priced_in_union_tiles_only_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(sa, "item_costs", lambda mask, group, n_tokens, key_block, tile_fixed: (
+        sa.item_unions(mask, group) * sa.block_tiles(np.asarray(mask).shape[-1], n_tokens, key_block)).sum(-1))
     with pytest.raises(AssertionError):
-        ts.test_assignment_unchanged_and_makespan_kept(24, 128, 1064, False)
+        ts.test_golden_slack_purchase_example(golden_dir)
 
 
-def test_sasa_priced_in_blocks_caught(monkeypatch):
+def test_sasa_blocks_priced_as_one_tile_caught(monkeypatch):
     # every key block priced at one tile, the kernel's 128-key blocks included
     monkeypatch.setattr(sa, "block_tiles", lambda nbk, n_tokens, key_block: np.ones(nbk, dtype=np.int64))
-    monkeypatch.setattr(sa, "budget_blocks", lambda slack, per_block: slack)
     with pytest.raises(AssertionError):
-        ts.test_assignment_unchanged_and_makespan_kept(8, 128, 1000, False)
+        ts.test_purchase_is_the_longest_affordable_prefix(2, 1064, 4, 7, False, 128, 3)
 
 
 def test_mixed_block_eligibility_off_by_one_caught(monkeypatch):

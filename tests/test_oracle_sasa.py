@@ -1,10 +1,10 @@
 """Pins for the slack-aware augmentation oracle: a hand-worked example
-(tests/golden/sasa_union_priced.json) with a batch that a sequential LPT
-would assign differently, a tie and values that differ from one row's;
-the batched LPT against the sequential one where they must agree; brute
-force over candidate subsets (the bought blocks carry the most retained
-mass the slack can buy); the assignment unchanged after augmentation with
-the makespan kept; every row holding its item's union."""
+(tests/golden/sasa_slack_purchase.json) with a batch that a sequential LPT
+would assign differently and a first candidate that does not fit; the
+batched LPT against the sequential one where they must agree; the purchase
+checked against item costs counted from the masks (the longest affordable
+prefix of the value order); the assignment unchanged after augmentation with
+the makespan kept; row lists and causal eligibility."""
 import itertools
 import json
 import math
@@ -30,7 +30,7 @@ def _hand_case():
 
 
 def _golden(golden_dir):
-    with open(os.path.join(golden_dir, "sasa_union_priced.json")) as f:
+    with open(os.path.join(golden_dir, "sasa_slack_purchase.json")) as f:
         gd = json.load(f)
     sh = gd["shape"]
     prob = np.array(gd["prob_32nds"], dtype=np.float64)[None] / 32.0
@@ -48,16 +48,16 @@ def _golden(golden_dir):
 def _run_golden(golden_dir):
     gd, sh, prob, mask, order = _golden(golden_dir)
     return gd, oracle.augment(prob, mask, order, gd["work_list"], None, sh["group"], sh["workers"],
-                              sh["n_tokens"], sh["key_block"])
+                              sh["n_tokens"], sh["key_block"], sh["tile_fixed"])
 
 
-def test_golden_union_priced_example(golden_dir):
+def test_golden_slack_purchase_example(golden_dir):
     gd, a = _run_golden(golden_dir)
     ex = gd["expected"]
     assert a.worker_of.tolist() == ex["worker_of"]
     assert a.load.tolist() == ex["load"] and a.makespan == ex["makespan"]
     assert a.slack.tolist() == ex["slack"] and a.last_item.tolist() == ex["last_item"]
-    assert a.paid.tolist() == ex["paid"] and a.paid_tiles.tolist() == ex["paid"]
+    assert a.paid.tolist() == ex["paid"] and a.paid_cost.tolist() == ex["paid_cost"]
     assert a.mask[0].tolist() == ex["mask"]
     assert a.row_cnt[0].tolist() == ex["row_cnt"]
     assert a.head_cnt[0].tolist() == ex["head_cnt"]
@@ -102,7 +102,7 @@ def test_lpt_batched_batches(seed):
     assert l2.max() - l2.min() <= 7
 
 
-# ------------------------------------------------- union-priced augmentation ---
+# ---------------------------------------------------- slack purchase (SASA) ---
 
 def _routed(seed, B=1, H=2, N=300, d=8, block=64, p=0.6, causal=False, key_block=None):
     rng = np.random.default_rng(seed)
@@ -111,33 +111,40 @@ def _routed(seed, B=1, H=2, N=300, d=8, block=64, p=0.6, causal=False, key_block
     return oracle.route(q, k, block, p, causal=causal, key_block=key_block)
 
 
-def _augment(r, G, W, N, kb, window=0):
+def _augment(r, G, W, N, kb, F, window=0):
     order = oracle.work_list(oracle.group_costs(r.row_cnt, G), window)
-    return oracle.augment(r.prob, r.mask, r.order, order, r.valid, G, W, N, kb)
+    return oracle.augment(r.prob, r.mask, r.order, order, r.valid, G, W, N, kb, F)
 
 
-def _mass_gain(prob, valid, rows, S):
-    """Retained-mass gain of giving the blocks S to the rows (b, h, i), each
-    where eligible, computed from masks."""
-    gain = 0.0
-    for (b, h, i) in rows:
-        m = np.zeros(prob.shape[-1], dtype=bool)
-        for j in S:
-            if j < valid[b, h, i]:
-                m[j] = True
-        gain += float(oracle.retained_mass(prob[b, h, i], m))
-    return gain
+def _item_cost_from_masks(mask, g, G, N, kb, F):
+    """The cost of item g counted from a mask: F * its union tiles plus the
+    tiles of every row's selected blocks."""
+    B, H, nb, nbk = mask.shape
+    ng = -(-nb // G)
+    bh, gi = divmod(g, ng)
+    b, h = divmod(bh, H)
+    rows = mask[b, h, gi * G:min(nb, (gi + 1) * G)].astype(bool)
+    spb = kb // 64
+    t = [spb] * (nbk - 1) + [-(-(N - (nbk - 1) * kb) // 64)]
+    union = rows.any(0)
+    return F * sum(t[j] for j in range(nbk) if union[j]) + sum(t[j] for r in rows for j in range(nbk) if r[j])
 
 
-@pytest.mark.parametrize("seed", range(6))
-@pytest.mark.parametrize("N,G,W,causal", [(400, 2, 5, False), (512, 4, 3, False), (640, 4, 4, True), (300, 1, 6, False)])
-def test_brute_force_bought_blocks_carry_max_mass(seed, N, G, W, causal):
-    r = _routed(seed, N=N, p=0.3 + 0.1 * seed, causal=causal)
+CASES = [(400, 2, 5, False, 64, 3), (512, 4, 3, False, 64, 3), (640, 4, 4, True, 64, 2),
+         (300, 1, 6, False, 64, 3), (1064, 4, 7, False, 128, 3), (1064, 2, 5, True, 128, 1)]
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("N,G,W,causal,kb,F", CASES)
+def test_purchase_is_the_longest_affordable_prefix(seed, N, G, W, causal, kb, F):
+    # Counted from the masks, independently of the pair prices: the bought
+    # pairs raise the item's cost by paid_cost <= slack, they are the first
+    # pairs of the value order, and the next pair would not have fitted.
+    r = _routed(seed, N=N, p=0.3 + 0.1 * seed, causal=causal, key_block=kb)
     B, H, nb, nbk = r.mask.shape
     valid = r.valid if r.valid is not None else np.full((B, H, nb), nbk)
-    a = _augment(r, G, W, N, 64)
+    a = _augment(r, G, W, N, kb, F)
     ng = -(-nb // G)
-    old = oracle.item_unions(r.mask, G)
     for w in range(W):
         g = int(a.last_item[w])
         if g < 0:
@@ -145,78 +152,65 @@ def test_brute_force_bought_blocks_carry_max_mass(seed, N, G, W, causal):
             continue
         bh, gi = divmod(g, ng)
         b, h = divmod(bh, H)
-        rows = [(b, h, i) for i in range(gi * G, min(nb, (gi + 1) * G))]
-        nv = max(int(valid[x]) for x in rows)
-        cands = [j for j in range(nv) if not old[g, j]]
-        bought = [j for j in range(nbk) if a.union[g, j] and not old[g, j]]
-        kk = min(int(a.slack[w]), len(cands))
-        assert len(bought) == kk == a.paid[w]
-        if kk == 0 or math.comb(len(cands), kk) > 5000:
-            continue
-        best = max(_mass_gain(r.prob, valid, rows, S) for S in itertools.combinations(cands, kk))
-        assert _mass_gain(r.prob, valid, rows, bought) >= best * (1 - 1e-15)
+        rows = range(gi * G, min(nb, (gi + 1) * G))
+        cands = sorted(((float(r.prob[b, h, i, j]), i, j) for i in rows for j in range(int(valid[b, h, i]))
+                        if not r.mask[b, h, i, j]), key=lambda c: (-c[0], c[1], c[2]))
+        bought = {(i, j) for i in rows for j in range(nbk) if a.mask[b, h, i, j] and not r.mask[b, h, i, j]}
+        k = len(bought)
+        assert k == a.paid[w] and bought == {(i, j) for _, i, j in cands[:k]}
+        before = _item_cost_from_masks(r.mask, g, G, N, kb, F)
+        assert _item_cost_from_masks(a.mask, g, G, N, kb, F) - before == a.paid_cost[w] <= a.slack[w]
+        if k < len(cands):
+            nxt = r.mask.copy()
+            nxt[b, h, cands[k][1], cands[k][2]] = 1
+            for _, i, j in cands[:k]:
+                nxt[b, h, i, j] = 1
+            assert _item_cost_from_masks(nxt, g, G, N, kb, F) - before > a.slack[w]
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("W,kb,N", [(1, 64, 1000), (4, 64, 1000), (16, 64, 1000), (64, 64, 1000),
-                                    (8, 128, 1000), (24, 128, 1064)])
-def test_assignment_unchanged_and_makespan_kept(W, kb, N, causal):
-    # N = 1064 with 128-key blocks: a ragged last key block of one tile, so
-    # some slacks are odd
+@pytest.mark.parametrize("W,kb,N,F", [(1, 64, 1000, 3), (4, 64, 1000, 3), (16, 64, 1000, 3), (64, 64, 1000, 2),
+                                      (8, 128, 1000, 3), (24, 128, 1064, 3)])
+def test_assignment_unchanged_and_makespan_kept(W, kb, N, F, causal):
     r = _routed(10 + W, B=1, H=3, N=N, block=64, p=0.3, causal=causal, key_block=kb)
     G = 4
-    a = _augment(r, G, W, N, kb)
-    tiles = oracle.block_tiles(r.mask.shape[-1], N, kb)
-    new_costs = (a.union * tiles).sum(-1)
-    old_costs = (oracle.item_unions(r.mask, G) * tiles).sum(-1)
+    a = _augment(r, G, W, N, kb, F)
+    old = oracle.item_costs(r.mask, G, N, kb, F)
+    new = oracle.item_costs(a.mask, G, N, kb, F)
     order = oracle.work_list(oracle.group_costs(r.row_cnt, G), 0)
-    # priced in the tiles the kernel runs: the same assignment, every worker
-    # grown by the tiles it bought, none past the makespan
-    wo2, load2, last2 = oracle.lpt_batched(new_costs, order, W)
+    # priced from the new masks: the same assignment, every worker grown by
+    # what it bought, none past the makespan
+    wo2, load2, last2 = oracle.lpt_batched(new, order, W)
     assert wo2.tolist() == a.worker_of.tolist() and last2.tolist() == a.last_item.tolist()
-    assert (load2 == a.load + a.paid_tiles).all() and load2.max() == a.makespan
-    assert (a.paid * (kb // 64) >= a.paid_tiles).all()
-    assert ((a.slack - a.paid * (kb // 64)) >= 0).all()
-    # only last items grew
-    grown = np.nonzero(new_costs != old_costs)[0]
+    assert (load2 == a.load + a.paid_cost).all() and load2.max() == a.makespan
+    grown = np.nonzero(new != old)[0]
     assert set(grown.tolist()) <= set(int(g) for g in a.last_item if g >= 0)
+    assert (a.mask >= r.mask).all() and (a.row_cnt == r.mask.sum(-1) + a.added).all()
+    assert (a.head_cnt == a.row_cnt.sum(-1)).all()
+    assert (oracle.retained_mass(r.prob, a.mask) >= oracle.retained_mass(r.prob, r.mask)).all()
     if W == 1:
         assert a.paid.sum() == 0
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_rows_take_their_item_union(causal):
-    r = _routed(21, B=1, H=3, N=900, block=64, p=0.5, causal=causal)
-    G = 4
-    a = _augment(r, G, 7, 900, 64)
+def test_row_lists_and_eligibility():
+    r = _routed(21, B=1, H=3, N=900, block=64, p=0.3, causal=True)
+    a = _augment(r, 4, 7, 900, 64, 3)
+    assert a.paid.sum() > 0
     B, H, nb, nbk = r.mask.shape
-    ng = -(-nb // G)
-    valid = r.valid if r.valid is not None else np.full((B, H, nb), nbk)
     for h in range(H):
         for i in range(nb):
-            g = h * ng + i // G
-            want = {j for j in np.nonzero(a.union[g])[0].tolist() if j < valid[0, h, i]}
-            assert set(np.nonzero(a.mask[0, h, i])[0].tolist()) == want
-            k = len(want)
-            assert a.row_idx[0, h, i, :k].tolist() == sorted(want)
-            ranked = [int(j) for j in r.order[0, h, i] if j < valid[0, h, i] and j not in want]
+            sel = np.nonzero(a.mask[0, h, i])[0].tolist()
+            assert all(j < r.valid[0, h, i] for j in sel)
+            k = len(sel)
+            assert a.row_idx[0, h, i, :k].tolist() == sel
+            ranked = [int(j) for j in r.order[0, h, i] if j < r.valid[0, h, i] and j not in sel]
             assert a.row_idx[0, h, i, k:k + len(ranked)].tolist() == ranked
             assert (a.row_idx[0, h, i, k + len(ranked):] == -1).all()
-    assert (a.mask >= r.mask).all()
-    assert (a.row_cnt == r.mask.sum(-1) + a.added).all() and (a.head_cnt == a.row_cnt.sum(-1)).all()
-    assert (oracle.retained_mass(r.prob, a.mask) >= oracle.retained_mass(r.prob, r.mask)).all()
-    # a worker whose budget outlasted its candidates left its last item full
-    for w in range(7):
-        g = int(a.last_item[w])
-        if g >= 0 and a.slack[w] > a.paid[w]:
-            bh, gi = divmod(g, ng)
-            nv = max(int(valid[0, bh, i]) for i in range(gi * G, min(nb, (gi + 1) * G)))
-            assert a.union[g, :nv].all()
 
 
 def test_nothing_to_buy_at_p_one():
     r = _routed(3, p=1.0)
-    a = _augment(r, 2, 5, 300, 64)
+    a = _augment(r, 2, 5, 300, 64, 3)
     assert a.paid.sum() == 0 and a.added.sum() == 0 and (a.mask == 1).all()
 
 
