@@ -180,7 +180,8 @@ def parse():
     ap.add_argument("--block", type=int, default=None, help="query block size (default: the workload's)")
     ap.add_argument("--key-block", type=int, default=None, help="key block size (default: the query block size)")
     ap.add_argument("--sasa", action="store_true",
-                    help="slack-aware augmentation in the step: LPT model, attn_augment, a second schedule")
+                    help="slack-aware augmentation in the step: attn_augment over the step's work list "
+                         "(priced in row-tiles), the forward on the same list")
     ap.add_argument("--sasa-union", action="store_true",
                     help="slack filling inside work items in the step (attn_augment_union after the route)")
     ap.add_argument("--fp8", action="store_true",
@@ -381,15 +382,10 @@ def main():
                           torch.empty((B, H, nb, nbk), dtype=torch.float64, device=dev)
                           if (args.sasa or args.sasa_union) else None)
     work_list = torch.empty(pr.items, dtype=torch.int32, device=dev)
-    n_workers = torch.cuda.get_device_properties(dev).multi_processor_count
-    worker_of = torch.empty(pr.items, dtype=torch.int32, device=dev)
-    worker_load = torch.empty(n_workers, dtype=torch.int64, device=dev)
-    added = torch.empty(n_workers, dtype=torch.int32, device=dev)
-
-    def sasa_steps():
-        tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True, work_list=work_list,
-                     worker_of=worker_of, worker_load=worker_load)
-        tbs.augment(pr, route_out, worker_of, worker_load, ws, added=added)
+    n_workers = tbs.num_workers(pr, tbs.OP_SPARSE_FWD)
+    aug_out = tbs.Augmentation(torch.empty(pr.items, dtype=torch.int32, device=dev),
+                               torch.empty(n_workers, dtype=torch.int64, device=dev),
+                               torch.empty(n_workers, dtype=torch.int32, device=dev))
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     fp8 = bool(args.fp8)
@@ -421,11 +417,12 @@ def main():
             tbs.route(q, k, w.top_p, blk, ws=ws, out=route_out, causal=causal, key_block=kb)
         if ev is not None:
             ev[1].record()
-        if args.sasa:
-            sasa_steps()
         if args.sasa_union:
             tbs.augment_union(pr, route_out)
         tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
+        if args.sasa:
+            # the forward takes the items in the order the augmentation assumed
+            tbs.augment(pr, route_out, ws, work_list=work_list, out=aug_out)
         if ev is not None:
             ev[2].record()
         if ev is not None:
@@ -554,39 +551,68 @@ def main():
 
     sasa = None
     if args.sasa:
-        # The same routing without augmentation, for the retained mass and the forward time before SASA.
+        # The same routing without augmentation: retained mass, union tiles,
+        # and plain steps timed interleaved with augmented ones.
         plain = tbs.Route(pr, w.top_p, torch.empty_like(route_out.mask), torch.empty_like(route_out.row_cnt),
                           torch.empty_like(route_out.row_idx), torch.empty_like(route_out.head_cnt))
-        tbs.route(q, k, w.top_p, blk, ws=ws, out=plain, causal=causal, key_block=kb)
-        wl0 = tbs.schedule(pr, plain.row_cnt, ws, head_window=hw)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        tbs.route(q, k, w.top_p, blk, ws=ws, out=route_out, causal=causal, key_block=kb)
-        ev[0].record()
-        tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, lpt=True, work_list=work_list,
-                     worker_of=worker_of, worker_load=worker_load)
-        ev[1].record()
-        tbs.augment(pr, route_out, worker_of, worker_load, ws, added=added)
-        ev[2].record()
-        tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
-        ev[3].record()
-        for _ in range(3):
+        wl0 = torch.empty_like(work_list)
+
+        def plain_step():
+            tbs.route(q, k, w.top_p, blk, ws=ws, out=plain, causal=causal, key_block=kb)
+            tbs.schedule(pr, plain.row_cnt, ws, head_window=hw, work_list=wl0)
             fwd(plain.row_cnt, plain.row_idx, wl0)
-        ev[4].record()
+
+        reps = 10
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(reps)]
+        for r_ in range(reps):
+            e = ev[r_]
+            e[0].record()
+            plain_step()
+            e[1].record()
+            tbs.route(q, k, w.top_p, blk, ws=ws, out=route_out, causal=causal, key_block=kb)
+            tbs.schedule(pr, route_out.row_cnt, ws, head_window=hw, work_list=work_list)
+            e[2].record()
+            tbs.augment(pr, route_out, ws, work_list=work_list, out=aug_out)
+            e[3].record()
+            fwd(route_out.row_cnt, route_out.row_idx, work_list)
+            e[4].record()
+            fwd(plain.row_cnt, plain.row_idx, wl0)
+            e[5].record()
+            fwd(route_out.row_cnt, route_out.row_idx, work_list)
+            e[6].record()
         torch.cuda.synchronize()
+        step_plain = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        step_sasa = np.array([e[1].elapsed_time(e[4]) for e in ev])
+        aug_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+        fwd_plain = np.array([e[4].elapsed_time(e[5]) for e in ev])
+        fwd_sasa = np.array([0.5 * (e[3].elapsed_time(e[4]) + e[5].elapsed_time(e[6])) for e in ev])
         prob = route_out.block_prob.cpu().numpy()
         m0 = plain.mask.cpu().numpy()
         m1 = route_out.mask.cpu().numpy()
         mass0 = (prob * m0).sum(-1)
         mass1 = (prob * m1).sum(-1)
-        load = worker_load.cpu().numpy()
-        sasa = {"workers": int(n_workers), "lpt_makespan": int(load.max()), "lpt_lif": float(load.max() / load.mean()),
-                "slack_total": int((load.max() - load).sum()), "blocks_added": int(m1.sum() - m0.sum()),
-                "blocks_before": int(m0.sum()), "mean_retained_mass_before": float(mass0.mean()),
-                "mean_retained_mass_after": float(mass1.mean()), "min_retained_mass_before": float(mass0.min()),
-                "min_retained_mass_after": float(mass1.min()),
-                "lpt_ms": ev[0].elapsed_time(ev[1]), "augment_ms": ev[1].elapsed_time(ev[2]),
-                "reschedule_ms": ev[2].elapsed_time(ev[3]), "sparse_fwd_ms_before": ev[3].elapsed_time(ev[4]) / 3,
-                "sparse_fwd_ms_after": float(t_fwd.mean())}
+        load = aug_out.worker_load.cpu().numpy()
+        tiles0 = union_tiles(m0, N, blk, kb, pr.group)
+        tiles1 = union_tiles(m1, N, blk, kb, pr.group)
+        per_block = np.full(nbk, kb // 64, dtype=np.int64)
+        per_block[-1] = -(-(N - (nbk - 1) * kb) // 64)
+        rows0 = int((m0.astype(np.int64) * per_block).sum())
+        rows1 = int((m1.astype(np.int64) * per_block).sum())
+        F = tbs.SASA_TILE_FIXED
+        sasa = {"workers": int(n_workers), "tile_fixed_row_tiles": F,
+                "makespan_row_tiles": int(load.max()), "lif_batched": float(load.max() / load.mean()),
+                "slack_row_tiles": int((load.max() - load).sum()), "pairs_bought": int(aug_out.paid.sum().item()),
+                "cost_before": int(F * tiles0 + rows0), "cost_after": int(F * tiles1 + rows1),
+                "union_tiles_before": int(tiles0), "union_tiles_after": int(tiles1),
+                "row_tiles_before": rows0, "row_tiles_after": rows1,
+                "mean_retained_mass_before": float(mass0.mean()), "mean_retained_mass_after": float(mass1.mean()),
+                "min_retained_mass_before": float(mass0.min()), "min_retained_mass_after": float(mass1.min()),
+                "augment_ms": float(aug_ms.mean()), "augment_ms_median": float(np.median(aug_ms)),
+                "sparse_fwd_ms_before": float(fwd_plain.mean()), "sparse_fwd_ms_after": float(fwd_sasa.mean()),
+                "sparse_fwd_after_over_before": float(fwd_sasa.mean() / fwd_plain.mean()),
+                "step_ms_before": float(step_plain.mean()), "step_ms_after": float(step_sasa.mean()),
+                "step_after_over_before": float(step_sasa.mean() / step_plain.mean()),
+                "interleaved_reps": reps}
         del plain
 
     sasa_union = None

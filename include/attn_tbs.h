@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define ATTN_TBS_ABI_VERSION 7
+#define ATTN_TBS_ABI_VERSION 8
 
 /* Status codes. */
 #define ATTN_OK            0
@@ -213,7 +213,7 @@ int32_t attn_route(const attn_problem* problem, const void* q, const void* k, do
  *                computed when worker_of or worker_load is given: the greedy
  *                is sequential (one wavefront, loads in registers), so it
  *                costs time proportional to the number of work items; it
- *                serves load-balance reports and attn_augment.
+ *                serves load-balance reports.
  *   worker_load  [num_workers] int64 out, nullable: summed cost per worker
  *                under that assignment.
  * Requires nbk <= 1024 and num_workers <= 4096. */
@@ -221,36 +221,60 @@ int32_t attn_schedule(const attn_problem* problem, const int32_t* row_cnt, int32
                       int32_t num_workers, int32_t* work_list, int32_t* worker_of, int64_t* worker_load,
                       void* ws, size_t ws_bytes, void* stream);
 
-/* Slack-aware sparse augmentation (SASA) on one GPU.
+/* Fixed cost of one 64-key tile of the attention kernel, in row-tiles (one
+ * query block computing one tile): staging the tile and running the softmax
+ * pipeline cost about as much as three rows' products.  Measured: giving
+ * every row of the video-32k and skewed-32k problems the blocks of its work
+ * item's union added 18% / 12% row-tiles and 1.1% / 0.9% tiles and took 10.3%
+ * / 7.2% more time, which fits F = 2.4 to 3.0. */
+#define ATTN_SASA_TILE_FIXED 3
+
+/* Slack-aware sparse augmentation (SASA) on one GPU, priced in row-tiles.
  *
  * Source: FVAttn review page, section 1 (Key Terms, "Slack-Aware Sparse
  * Augmentation") and section 3 (Method): after load balancing, ranks with
- * slack compute extra high-value blocks.  Here the ranks are the workers of
- * the LPT model of attn_schedule: with M the largest worker load, worker w
- * has slack s_w = M - worker_load[w] and adds the first min(s_w, #candidates)
- * of its candidates -- the eligible unselected key blocks of the query blocks
- * of the work items assigned to it -- ordered by block probability
- * descending, then unit id, then key-block index (inside a row that is the
- * routing rank order, so every row's selection stays a prefix of its
- * ranking).  An added block costs one unit, like a selected one, so no
- * worker's modelled load exceeds M.  Updates the routing outputs in place;
- * call attn_schedule again for a work list over the new counts.
+ * slack compute extra high-value blocks.  A work item (attn_group_size query
+ * blocks of one head) runs the union of its rows' key blocks as 64-key tiles
+ * (key_block/64 per block, the last block only the tiles its keys reach); a
+ * tile costs F = ATTN_SASA_TILE_FIXED row-tiles plus one per row that
+ * selected it, so an item costs F * (union tiles) + (row tiles).  The ranks
+ * are num_workers workers that take the items in work_list order W positions
+ * at a time: before each batch the workers are ranked by (load, id) and the
+ * r-th ranked worker takes the batch's r-th item.  With M the largest load,
+ * worker w has slack M - load[w] and spends it on its last item (the one of
+ * the latest batch that reached it), where extra cost changes no other choice
+ * of the assignment.  Its candidates are the (row, key block) pairs of that
+ * item whose block is eligible for the row and not selected by it, ordered
+ * by the row's block probability descending, then row, then block; a pair
+ * costs the block's tiles, plus F times them when its block is in neither
+ * the item's union nor an earlier pair; the worker buys the longest prefix of
+ * that order whose cost fits its slack.  No worker's load exceeds M.  mask,
+ * row_cnt, row_idx and head_cnt are updated in place (only rows that bought
+ * pairs change); row_idx keeps the new selection ascending, then the row's
+ * remaining eligible blocks in their routing rank order.  Run the forward on
+ * the same work_list: its items then run in the order the assignment assumed.
+ * A problem whose attn_sparse_fwd splits its items along their keys (bf16,
+ * fewer than 4 items per compute unit, no ATTN_FLAG_NO_SPLIT) runs in equal
+ * shares of its tiles instead, with no modelled idle time: attn_augment then
+ * changes nothing (paid = 0; worker_of and worker_load are still written).
  *
  *   block_prob   [B,H,nb,nbk] double, from attn_route (block_prob output).
- *   worker_of    [B*H*ceil(nb/G)] int32, worker_load [num_workers] int64:
- *                from attn_schedule's LPT model with the same num_workers.
- *   num_workers  1 .. 4096.
+ *   work_list    [B*H*ceil(nb/G)] int32, a permutation of the items (from
+ *                attn_schedule over the same routing), nullable: item order.
+ *   num_workers  1 .. 4096 (the fwd kernel's workgroups: attn_num_workers).
  *   mask, row_cnt, row_idx, head_cnt   attn_route's outputs, updated in
  *                place; row_idx must hold the ranked tail attn_route writes
- *                after the selected blocks (its entries past the new count
- *                keep the remaining unselected blocks in rank order).
- *   added        [num_workers] int32 out, nullable: blocks added per worker.
+ *                after the selected blocks.
+ *   worker_of    [B*H*ceil(nb/G)] int32 out, nullable: the worker of every item.
+ *   worker_load  [num_workers] int64 out, nullable: cost per worker (row-tiles)
+ *                before augmentation.
+ *   paid         [num_workers] int32 out, nullable: pairs bought per worker.
  *   ws           attn_workspace_bytes(problem, ATTN_OP_AUGMENT) bytes; the
  *                control block is not touched.
  * Honours causal (the eligible blocks of routing).  Requires nbk <= 1024. */
-int32_t attn_augment(const attn_problem* problem, const double* block_prob, const int32_t* worker_of,
-                     const int64_t* worker_load, int32_t num_workers, uint8_t* mask, int32_t* row_cnt,
-                     int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, size_t ws_bytes,
+int32_t attn_augment(const attn_problem* problem, const double* block_prob, const int32_t* work_list,
+                     int32_t num_workers, uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
+                     int32_t* worker_of, int64_t* worker_load, int32_t* paid, void* ws, size_t ws_bytes,
                      void* stream);
 
 /* Slack-aware augmentation inside work items.

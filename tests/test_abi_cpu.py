@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
                           "attn_route_fp8", "attn_sparse_fwd_fp8", "attn_dense_fwd_fp8"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.attn_abi_version() == 7
+    assert L.attn_abi_version() == 8
 
 
 def _problem(B=1, H=40, N=32760, d=128, block=64, dtype=0, causal=0, flags=0, scale=0.0, key_block=0, reserved=0):
@@ -69,7 +69,13 @@ def test_workspace_sizes():
     assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_DENSE_FWD) == 256 + 16 * 4096
     U = 40 * nb
     up = lambda x: (x + 255) // 256 * 256
-    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_AUGMENT) == 256 + up(4 * 4097) + 2 * up(4 * U) + up(208 * U)
+    items, W = U // 4, 4096
+    # item bitmaps (16 words), item tiles, item costs, last items, bought
+    # pairs (4 rows x 32 words per worker), worker of every item, loads,
+    # pairs bought, makespan
+    assert L.attn_workspace_bytes(ctypes.byref(p), tbs.OP_AUGMENT) == (
+        256 + up(items * 16 * 4) + 2 * up(items * 4) + up(W * 4) + up(W * 4 * 32 * 4) + up(items * 4) + up(W * 8)
+        + up(W * 4) + 256)
     assert L.attn_workspace_bytes(ctypes.byref(p), 9) == 0
     assert L.attn_workspace_bytes(None, 0) == 0
 
@@ -140,15 +146,15 @@ def test_augment_validation():
     p = _problem()
     D = ctypes.c_void_p(0x10000)
 
-    def aug(pr=p, bp=D, wo=D, wl=D, W=256, mask=D, rc=D, ri=D, hc=D, added=None, ws=WS, wsb=1 << 30):
-        return L.attn_augment(ctypes.byref(pr) if pr is not None else None, bp, wo, wl, W, mask, rc, ri, hc, added,
-                              ws, wsb, None)
+    def aug(pr=p, bp=D, wlist=D, W=256, mask=D, rc=D, ri=D, hc=D, wo=None, wl=None, paid=None, ws=WS, wsb=1 << 30):
+        return L.attn_augment(ctypes.byref(pr) if pr is not None else None, bp, wlist, W, mask, rc, ri, hc, wo, wl,
+                              paid, ws, wsb, None)
     assert aug(pr=None) == 1
     assert aug(W=0) == 1 and aug(W=4097) == 1
     assert aug(bp=None) == 1 and aug(bp=ctypes.c_void_p(0x10004)) == 1
-    assert aug(wl=ctypes.c_void_p(0x10004)) == 1
-    assert aug(wo=None) == 1 and aug(mask=None) == 1 and aug(ri=ctypes.c_void_p(0x10002)) == 1
-    assert aug(added=ctypes.c_void_p(0x10001)) == 1
+    assert aug(wl=ctypes.c_void_p(0x10004)) == 1 and aug(wlist=ctypes.c_void_p(0x10002)) == 1
+    assert aug(mask=None) == 1 and aug(rc=None) == 1 and aug(ri=ctypes.c_void_p(0x10002)) == 1
+    assert aug(paid=ctypes.c_void_p(0x10001)) == 1 and aug(wo=ctypes.c_void_p(0x10001)) == 1
     assert aug(pr=_problem(N=64 * 1025)) == 2
     assert aug(wsb=1000) == 3 and aug(ws=None) == 3
     assert "workspace" in L.attn_last_error().decode()

@@ -78,30 +78,6 @@ def test_mixed_blocks_p1_equals_dense_bitwise(w, kb, causal):
     assert torch.equal(o, od) and torch.equal(lse, lsed)
 
 
-def test_mixed_blocks_augment_matches_oracle():
-    w = custom_workload(1, 4, 2000, 128, 128, "bf16", 0.8, wid=610)
-    kb, W, hw = 64, 16, 2
-    q, k, v = _inputs(w)
-    pr = tbs.make_problem(q, w.block, key_block=kb)
-    ws = tbs.workspace(pr, DEV)
-    r = tbs.route(q, k, w.top_p, w.block, ws=ws, key_block=kb, return_prob=True)
-    mask0 = r.mask.cpu().numpy()
-    wl, worker_of, worker_load = tbs.schedule(pr, r.row_cnt, ws, head_window=hw, num_workers=W, lpt=True)
-    added = tbs.augment(pr, r, worker_of, worker_load, ws)
-    torch.cuda.synchronize()
-    rr = oracle.route(to64(q), to64(k), w.block, w.top_p, key_block=kb)
-    assert (mask0 == rr.mask).all(), "routing differs on an ambiguous block; exact comparison not possible"
-    G = pr.group
-    ref = oracle.augment(rr.prob, rr.mask, rr.row_cnt, rr.valid, G, hw * -(-pr.num_blocks // G), W)
-    assert (r.mask.cpu().numpy() == ref.mask).all()
-    assert (r.row_cnt.cpu().numpy() == ref.row_cnt).all()
-    assert (added.cpu().numpy() == ref.added_per_worker).all()
-    rc = r.row_cnt.cpu().numpy()
-    valid = np.arange(pr.num_key_blocks) < rc[..., None]
-    assert (np.where(valid, r.row_idx.cpu().numpy(), -1) == ref.row_idx).all()
-    print(f"  {int(ref.added.sum())} blocks added", flush=True)
-
-
 def test_mixed_blocks_full_size_video_sample():
     # The video shape routed with 128-row query blocks over 64-key blocks.
     w = WORKLOADS["video-32k"]

@@ -142,7 +142,7 @@ def lib() -> ctypes.CDLL:
     L.attn_dense_fwd.restype = i32
     L.attn_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_augment.restype = i32
-    L.attn_augment.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_augment.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_augment_union.restype = i32
     L.attn_augment_union.argtypes = [P, vp, vp, vp, vp, vp]
     L.attn_quantize_qk_fp8.restype = i32
@@ -214,6 +214,9 @@ def num_workers(problem: Problem, op: int = OP_SPARSE_FWD) -> int:
     return int(lib().attn_num_workers(ctypes.byref(problem), op))
 
 
+_num_workers = num_workers     # for functions whose num_workers argument hides it
+
+
 @dataclasses.dataclass
 class Route:
     problem: Problem
@@ -282,23 +285,38 @@ def schedule(problem: Problem, row_cnt: torch.Tensor, ws: torch.Tensor, head_win
     return work_list
 
 
-def augment(problem: Problem, r: Route, worker_of: torch.Tensor, worker_load: torch.Tensor, ws: torch.Tensor,
-            added: Optional[torch.Tensor] = None, want_added: bool = True) -> Optional[torch.Tensor]:
-    """attn_augment: slack-aware augmentation of the routing `r` in place.
+SASA_TILE_FIXED = 3        # ATTN_SASA_TILE_FIXED: fixed cost of a tile, in row-tiles
 
-    worker_of / worker_load come from schedule(..., lpt=True) over the same
-    number of workers; r needs its block probabilities (route(...,
-    return_prob=True)).  Returns the blocks added per worker (int32)."""
+
+@dataclasses.dataclass
+class Augmentation:
+    worker_of: torch.Tensor     # [items] int32, the worker of every work item
+    worker_load: torch.Tensor   # [W] int64, cost per worker (row-tiles) before augmentation
+    paid: torch.Tensor          # [W] int32, (row, block) pairs bought per worker
+
+
+def augment(problem: Problem, r: Route, ws: torch.Tensor, work_list: Optional[torch.Tensor] = None,
+            num_workers: int = 0, out: Optional[Augmentation] = None) -> Augmentation:
+    """attn_augment: slack-aware augmentation of the routing `r` in place,
+    priced in row-tiles (items assigned in batches of W work-list positions,
+    each worker buying (row, block) pairs for its last item with its slack).
+    r needs its block probabilities (route(..., return_prob=True)); work_list
+    from schedule() over the same routing (None: item order); num_workers 0 =
+    the fwd kernel's workgroups."""
     if r.block_prob is None:
         raise ValueError("augment needs the block probabilities: route(..., return_prob=True)")
-    _require_device(worker_of, worker_load, ws, r.mask, r.row_cnt, r.row_idx, r.head_cnt, r.block_prob)
-    W = worker_load.numel()
-    if added is None and want_added:
-        added = torch.empty(W, dtype=torch.int32, device=worker_load.device)
-    _check(lib().attn_augment(ctypes.byref(problem), _ptr(r.block_prob), _ptr(worker_of), _ptr(worker_load), int(W),
-                              _ptr(r.mask), _ptr(r.row_cnt), _ptr(r.row_idx), _ptr(r.head_cnt), _ptr(added),
-                              _ptr(ws), ws.numel(), _stream()))
-    return added
+    _require_device(ws, r.mask, r.row_cnt, r.row_idx, r.head_cnt, r.block_prob, work_list)
+    dev = r.row_cnt.device
+    if out is None:
+        W = num_workers or _num_workers(problem, OP_SPARSE_FWD)
+        out = Augmentation(torch.empty(problem.items, dtype=torch.int32, device=dev),
+                           torch.empty(W, dtype=torch.int64, device=dev),
+                           torch.empty(W, dtype=torch.int32, device=dev))
+    W = out.worker_load.numel()
+    _check(lib().attn_augment(ctypes.byref(problem), _ptr(r.block_prob), _ptr(work_list), int(W), _ptr(r.mask),
+                              _ptr(r.row_cnt), _ptr(r.row_idx), _ptr(r.head_cnt), _ptr(out.worker_of),
+                              _ptr(out.worker_load), _ptr(out.paid), _ptr(ws), ws.numel(), _stream()))
+    return out
 
 
 def augment_union(problem: Problem, r: Route) -> Route:
@@ -469,8 +487,10 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
                      num_workers: int = 0, key_block: Optional[int] = None, fp8: bool = False):
     """route -> schedule -> sparse_fwd on the current stream; returns (o, lse, route, work_list).
 
-    With sasa=True: route -> schedule with the LPT model -> augment -> schedule
-    again over the augmented counts -> sparse_fwd.  With fp8=True the routing
+    With sasa=True: route -> schedule -> augment (priced in union tiles over
+    that work list) -> sparse_fwd on the same work list, so the kernel takes
+    the items in the order the augmentation's assignment assumed.  With
+    fp8=True the routing
     pass also quantises Q and K to E4M3 (route_fp8: one read of Q and K) and the
     forward is sparse_fwd_fp8; routing reads the bf16 Q and K either way."""
     pr = make_problem(q, block, causal=causal, scale=scale, key_block=key_block)
@@ -481,11 +501,9 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
                           key_block=key_block)
     else:
         r = route(q, k, top_p, block, scale=scale, ws=ws, causal=causal, return_prob=sasa, key_block=key_block)
-    if sasa:
-        _, worker_of, worker_load = schedule(pr, r.row_cnt, ws, head_window=head_window,
-                                             num_workers=num_workers, lpt=True)
-        augment(pr, r, worker_of, worker_load, ws, want_added=False)
     wl = schedule(pr, r.row_cnt, ws, head_window=head_window)
+    if sasa:
+        augment(pr, r, ws, work_list=wl, num_workers=num_workers)
     if fp8:
         o, lse = sparse_fwd_fp8(qk, v, r.row_cnt, r.row_idx, block, work_list=wl, scale=scale, ws=ws,
                                 want_lse=want_lse, causal=causal, key_block=key_block)
@@ -497,7 +515,7 @@ def sparse_attention(q, k, v, top_p: float, block: int, scale: Optional[float] =
 
 __all__ = [
     "lib", "AttnError", "Problem", "Route", "make_problem", "default_head_window", "workspace", "workspace_bytes", "num_workers",
-    "route", "schedule", "augment", "augment_union", "sparse_fwd", "sparse_fwd_noalloc", "dense_fwd",
+    "route", "schedule", "augment", "Augmentation", "SASA_TILE_FIXED", "augment_union", "sparse_fwd", "sparse_fwd_noalloc", "dense_fwd",
     "sparse_attention", "LIB_PATH",
     "QuantizedQK", "quantize_qk_fp8", "route_fp8", "sparse_fwd_fp8", "dense_fwd_fp8", "FP8_TILE",
 ]

@@ -233,10 +233,10 @@ TBS_EXPORT int32_t attn_schedule(const attn_problem* problem, const int32_t* row
   return ok();
 }
 
-TBS_EXPORT int32_t attn_augment(const attn_problem* problem, const double* block_prob, const int32_t* worker_of,
-                                const int64_t* worker_load, int32_t num_workers, uint8_t* mask, int32_t* row_cnt,
-                                int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, size_t ws_bytes,
-                                void* stream) {
+TBS_EXPORT int32_t attn_augment(const attn_problem* problem, const double* block_prob, const int32_t* work_list,
+                                int32_t num_workers, uint8_t* mask, int32_t* row_cnt, int32_t* row_idx,
+                                int32_t* head_cnt, int32_t* worker_of, int64_t* worker_load, int32_t* paid, void* ws,
+                                size_t ws_bytes, void* stream) {
   tbs::Shape s;
   int32_t st = check_problem(problem, &s);
   if (st != ATTN_OK) return st;
@@ -245,16 +245,16 @@ TBS_EXPORT int32_t attn_augment(const attn_problem* problem, const double* block
   if (num_workers < 1 || num_workers > kMaxWorkers)
     return fail(ATTN_E_INVALID, "num_workers must be in [1, %d] (got %d)", kMaxWorkers, num_workers);
   if (!block_prob || !aligned(block_prob, 8)) return fail(ATTN_E_INVALID, "block_prob is NULL or not 8-byte aligned");
-  if (!worker_load || !aligned(worker_load, 8))
-    return fail(ATTN_E_INVALID, "worker_load is NULL or not 8-byte aligned");
+  if (worker_load && !aligned(worker_load, 8)) return fail(ATTN_E_INVALID, "worker_load is not 8-byte aligned");
   if (!mask) return fail(ATTN_E_INVALID, "mask is NULL");
-  if ((st = check_i32(worker_of, "worker_of", false)) || (st = check_i32(row_cnt, "row_cnt", false)) ||
+  if ((st = check_i32(work_list, "work_list", true)) || (st = check_i32(row_cnt, "row_cnt", false)) ||
       (st = check_i32(row_idx, "row_idx", false)) || (st = check_i32(head_cnt, "head_cnt", false)) ||
-      (st = check_i32(added, "added", true)))
+      (st = check_i32(worker_of, "worker_of", true)) || (st = check_i32(paid, "paid", true)))
     return st;
   if ((st = check_ws(ws, ws_bytes, tbs::augment_ws_bytes(s, num_workers)))) return st;
-  hipError_t e = tbs::launch_augment(s, block_prob, worker_of, worker_load, num_workers, mask, row_cnt, row_idx,
-                                     head_cnt, added, ws, static_cast<hipStream_t>(stream));
+  hipError_t e = tbs::launch_augment(s, block_prob, work_list, num_workers, mask, row_cnt, row_idx, head_cnt,
+                                     worker_of, worker_load, paid, ws, static_cast<hipStream_t>(stream),
+                                     ATTN_SASA_TILE_FIXED);
   return device_status(e, "attn_augment launch");
 }
 

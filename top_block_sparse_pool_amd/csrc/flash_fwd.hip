@@ -1217,46 +1217,6 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ x,
   if (i < n) x[i] = 0u;
 }
 
-// Union tile count of every work item of a listed problem: the key blocks its
-// rows select, OR'ed into an LDS bitmap, each holding kb/64 key tiles (the
-// last block only the tiles its keys reach) -- the tiles the attention kernel
-// runs for the item.
-__global__ __launch_bounds__(256) void item_tiles_kernel(const int32_t* __restrict__ row_cnt,
-                                                         const int32_t* __restrict__ row_idx, int nb, int nbk,
-                                                         int kb, int N, int ng, int G, int* __restrict__ item_tiles) {
-  __shared__ unsigned bm[kMaxListWords];
-  const int g = blockIdx.x;
-  const int bh = g / ng;
-  const int i0 = (g - bh * ng) * G;
-  const int gsz = min(G, nb - i0);
-  const int nwords = (nbk + 31) / 32;
-  const int tid = threadIdx.x;
-  for (int x = tid; x < nwords; x += 256) bm[x] = 0u;
-  __syncthreads();
-  for (int m = 0; m < gsz; ++m) {
-    const long long u = static_cast<long long>(bh) * nb + i0 + m;
-    const int cnt = min(max(row_cnt[u], 0), nbk);
-    const int32_t* lst = row_idx + u * nbk;
-    for (int x = tid; x < cnt; x += 256) {
-      const int j = min(max(lst[x], 0), nbk - 1);
-      atomicOr(&bm[j >> 5], 1u << (j & 31));
-    }
-  }
-  __syncthreads();
-  if (tid < kWave) {
-    int c = 0;
-    for (int x = tid; x < nwords; x += kWave) c += __popc(bm[x]);
-    c = wave_sum_i32(c);
-    if (tid == 0) {
-      const int spb = kb / kKeyTile;
-      int tiles = c * spb;
-      if (spb > 1 && c > 0 && ((bm[(nbk - 1) >> 5] >> ((nbk - 1) & 31)) & 1u))
-        tiles = (c - 1) * spb + (N - (nbk - 1) * kb + kKeyTile - 1) / kKeyTile;
-      item_tiles[g] = tiles;
-    }
-  }
-}
-
 // Inclusive prefix sum over the kPlanThreads threads of one workgroup (every
 // thread calls it; s_w holds one int per wave).  Returns the thread's
 // inclusive sum and sets *total to the workgroup's sum.
@@ -1477,9 +1437,7 @@ hipError_t launch_fwd(const Shape& s, int mode, const FwdArgs& a, hipStream_t st
     p.starts = starts;
     if (grid < 1 || grid > sparse_split_max_workers()) return hipErrorInvalidValue;
     const int items = static_cast<int>(work_items(s));
-    hipLaunchKernelGGL(item_tiles_kernel, dim3(items), dim3(256), 0, stream, a.row_cnt, a.row_idx, s.nb, s.nbk, s.kb,
-                       s.N, p.ng, p.G, item_tiles);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_item_union(s, a.row_cnt, a.row_idx, item_tiles, nullptr, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, item_tiles, items, grid, entries,
                        n_entries, starts, p.part_cnt);

@@ -57,16 +57,35 @@ hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int head_wind
 hipError_t launch_lpt(const Shape& s, const int32_t* row_cnt, const int32_t* work_list,
                       int num_workers, int32_t* worker_of, int64_t* worker_load, hipStream_t stream);
 
-// Slack-aware augmentation: worker rows (CSR), a merge per worker, then the
-// rebuilt lists of the rows that gained blocks.  Workspace bytes after the
-// control block, for up to 4096 workers.
+// Union of every work item's rows' key blocks: its 64-key tiles (item_tiles,
+// [items]) and, when ubits is given, the bitmap ([items, ceil(nbk/32)]
+// words); when item_cost is given, the item's cost in row-tiles,
+// tile_fixed * (union tiles) + (the tiles of every row's listed blocks).
+// nbk <= kItemWords * 32.
+constexpr int kItemWords = 64;
+hipError_t launch_item_union(const Shape& s, const int32_t* row_cnt, const int32_t* row_idx, int* item_tiles,
+                             unsigned* ubits, hipStream_t stream, int tile_fixed = 0, int* item_cost = nullptr);
+// Longest-first assignment of the items (cost [items]) in work-list order
+// (natural order if work_list is null), W positions per batch, workers
+// ranked by (load, id) before each batch.  Writes worker_of [items],
+// worker_load [W], last_item [W] (-1: none) and makespan [1].
+constexpr int kMaxLptWorkers = 4096;
+hipError_t launch_lpt_batched(const Shape& s, const int* cost, const int32_t* work_list, int num_workers,
+                              int32_t* worker_of, int64_t* worker_load, int32_t* last_item, int64_t* makespan,
+                              hipStream_t stream);
+
+// Slack-aware augmentation priced in row-tiles: item unions and costs, the
+// batched assignment, each worker's purchase of (row, block) pairs for its
+// last item, then the rows that bought pairs are rewritten.  Workspace bytes
+// (control block included) for num_workers workers.
 size_t augment_ws_bytes(const Shape& s, int num_workers);
 // Work-item slack: every row takes the eligible blocks of its item's union.
 hipError_t launch_augment_union(const Shape& s, uint8_t* mask, int32_t* row_cnt, int32_t* row_idx,
                                 int32_t* head_cnt, hipStream_t stream);
-hipError_t launch_augment(const Shape& s, const double* block_prob, const int32_t* worker_of,
-                          const int64_t* worker_load, int num_workers, uint8_t* mask, int32_t* row_cnt,
-                          int32_t* row_idx, int32_t* head_cnt, int32_t* added, void* ws, hipStream_t stream);
+hipError_t launch_augment(const Shape& s, const double* block_prob, const int32_t* work_list, int num_workers,
+                          uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
+                          int32_t* worker_of, int64_t* worker_load, int32_t* paid, void* ws, hipStream_t stream,
+                          int tile_fixed);
 
 // FP8 (E4M3) quantisation of Q (per token) and K (per 64-token tile) for
 // the fp8 attention path; bf16 inputs, head_dim 128.

@@ -30,7 +30,16 @@
 //   ascending unit ids.
 // lpt_kernel: greedy longest-processing-time model of the same order over W
 //   workers (the worker of every item and every worker's load), for
-//   reporting load balance and for slack-aware augmentation.
+//   reporting load balance.
+// item_union_kernel: the union of every work item's rows' key blocks (a
+//   bitmap per item, optional) and the 64-key tiles it holds -- what the
+//   attention kernel runs for the item -- and, optionally, the item's cost
+//   in row-tiles: F * (union tiles) + the tiles of every row's blocks.
+// lpt_batched_kernel: longest-first assignment of the items in list order,
+//   W list positions at a time: before each batch the workers are ranked by
+//   (load, id) and take the batch's items in that order, one each, so each
+//   batch is one parallel step (used by slack-aware augmentation, with items
+//   priced in row-tiles).
 #include "device_common.h"
 #include "launch.h"
 
@@ -243,7 +252,223 @@ __global__ __launch_bounds__(kLptThreads) void lpt_kernel(const int32_t* __restr
   }
 }
 
+// One workgroup per work item: the rows' lists OR'ed into an LDS bitmap;
+// the union's key blocks hold kb/64 tiles each, the last block only the
+// tiles its keys reach.  Row tiles: every listed entry holds kb/64 tiles,
+// less for the entries naming the last block.
+constexpr int kUnionThreads = 256;
+constexpr int kTileKeys = 64;   // keys per tile of the attention kernel
+__global__ __launch_bounds__(kUnionThreads) void item_union_kernel(const int32_t* __restrict__ row_cnt,
+                                                                   const int32_t* __restrict__ row_idx, int nb,
+                                                                   int nbk, int kb, int N, int ng, int G,
+                                                                   int* __restrict__ item_tiles,
+                                                                   unsigned* __restrict__ ubits, int tile_fixed,
+                                                                   int* __restrict__ item_cost) {
+  __shared__ unsigned bm[kItemWords];
+  __shared__ int s_entries, s_last;
+  const int g = blockIdx.x;
+  const int bh = g / ng;
+  const int i0 = (g - bh * ng) * G;
+  const int gsz = min(G, nb - i0);
+  const int nwords = (nbk + 31) / 32;
+  const int tid = threadIdx.x;
+  for (int x = tid; x < nwords; x += kUnionThreads) bm[x] = 0u;
+  if (tid == 0) {
+    s_entries = 0;
+    s_last = 0;
+  }
+  __syncthreads();
+  int last_hits = 0;
+  for (int m = 0; m < gsz; ++m) {
+    const long long u = static_cast<long long>(bh) * nb + i0 + m;
+    const int cnt = min(max(row_cnt[u], 0), nbk);
+    if (tid == 0) s_entries += cnt;
+    const int32_t* lst = row_idx + u * nbk;
+    for (int x = tid; x < cnt; x += kUnionThreads) {
+      const int j = min(max(lst[x], 0), nbk - 1);
+      atomicOr(&bm[j >> 5], 1u << (j & 31));
+      last_hits += j == nbk - 1;
+    }
+  }
+  if (item_cost && last_hits) atomicAdd(&s_last, last_hits);
+  __syncthreads();
+  if (ubits)
+    for (int x = tid; x < nwords; x += kUnionThreads) ubits[static_cast<long long>(g) * nwords + x] = bm[x];
+  if (tid < kWave) {
+    int c = 0;
+    for (int x = tid; x < nwords; x += kWave) c += __popc(bm[x]);
+    c = wave_sum_i32(c);
+    if (tid == 0) {
+      const int spb = kb / kTileKeys;
+      const int t_last = (N - (nbk - 1) * kb + kTileKeys - 1) / kTileKeys;
+      int tiles = c * spb;
+      if (c > 0 && ((bm[(nbk - 1) >> 5] >> ((nbk - 1) & 31)) & 1u)) tiles = (c - 1) * spb + t_last;
+      item_tiles[g] = tiles;
+      if (item_cost) item_cost[g] = tile_fixed * tiles + s_entries * spb - s_last * (spb - t_last);
+    }
+  }
+}
+
+// Batched longest-first assignment (one workgroup, dynamic LDS of
+// lpt_batched_lds(W) bytes).  Worker w's key is load << 12 | w (W <= 4096,
+// so keys are distinct and equal loads order by id); its rank in a batch is
+// the number of smaller keys.  With W <= 1024 the 1024 threads count in
+// floor(1024 / W) slices of the other workers and add their counts in LDS;
+// with more workers each thread counts for up to four workers.  The worker
+// of rank r < m takes the batch's r-th item.  Loads run ahead of use: while a
+// batch is counted, the next batch's costs (its items are known) and the
+// items of the batch after it are in flight.
+constexpr int kLptBThreads = 1024;
+constexpr int kLptBPer = kMaxLptWorkers / kLptBThreads;
+size_t lpt_batched_lds(int W) { return static_cast<size_t>(W) * (sizeof(unsigned long long) + 3 * sizeof(int)); }
+
+__global__ __launch_bounds__(kLptBThreads) void lpt_batched_kernel(const int* __restrict__ cost,
+                                                                   const int32_t* __restrict__ work_list,
+                                                                   int items, int W,
+                                                                   int32_t* __restrict__ worker_of,
+                                                                   int64_t* __restrict__ worker_load,
+                                                                   int32_t* __restrict__ last_item,
+                                                                   int64_t* __restrict__ makespan) {
+  extern __shared__ unsigned long long s_dyn[];
+  unsigned long long* s_key = s_dyn;                              // [W], by worker
+  int* s_rank = reinterpret_cast<int*>(s_key + W);                // [W], by worker
+  int* s_g = s_rank + W;                                          // [W], by batch position
+  int* s_c = s_g + W;                                             // [W], by batch position
+  __shared__ unsigned long long s_max[kLptBThreads / kWave];
+  const int tid = threadIdx.x;
+  const int slices = W <= kLptBThreads ? kLptBThreads / W : 1;
+  const int mine = W <= kLptBThreads ? (tid < slices * W ? 1 : 0) : kLptBPer;
+  const int w0 = W <= kLptBThreads ? tid % W : tid;
+  const int slice = W <= kLptBThreads ? tid / W : 0;
+  const int v_lo = W <= kLptBThreads ? slice * W / slices : 0;
+  const int v_hi = W <= kLptBThreads ? (slice + 1) * W / slices : W;
+  const bool owner = W <= kLptBThreads ? tid < W : true;
+  unsigned long long load[kLptBPer];
+#pragma unroll
+  for (int q = 0; q < kLptBPer; ++q) {
+    load[q] = 0;
+    const int w = tid + q * kLptBThreads;
+    if (w < W) {
+      s_key[w] = static_cast<unsigned long long>(w);
+      last_item[w] = -1;
+    }
+  }
+  // item at list position p (-1 past the end) and its cost
+  auto item_at = [&](int p) { return p < items ? (work_list ? min(max(work_list[p], 0), items - 1) : p) : -1; };
+  int g_cur[kLptBPer], c_cur[kLptBPer], g_nxt[kLptBPer];
+#pragma unroll
+  for (int q = 0; q < kLptBPer; ++q) {
+    const int r = tid + q * kLptBThreads;
+    g_cur[q] = r < W ? item_at(r) : -1;
+    g_nxt[q] = r < W ? item_at(W + r) : -1;
+    c_cur[q] = g_cur[q] >= 0 ? cost[g_cur[q]] : 0;
+  }
+  for (int b = 0; b < items; b += W) {
+    const int m = min(W, items - b);
+    int c_nxt[kLptBPer], g_aft[kLptBPer];
+#pragma unroll
+    for (int q = 0; q < kLptBPer; ++q) {
+      const int r = tid + q * kLptBThreads;
+      if (r < W) {
+        s_g[r] = g_cur[q];
+        s_c[r] = c_cur[q];
+        s_rank[r] = 0;
+      }
+      c_nxt[q] = g_nxt[q] >= 0 ? cost[g_nxt[q]] : 0;
+      g_aft[q] = r < W ? item_at(b + 2 * W + r) : -1;
+    }
+    __syncthreads();
+    // ranks: smaller keys among the workers of this thread's slice
+    for (int q = 0; q < mine; ++q) {
+      const int w = w0 + q * kLptBThreads;
+      if (w >= W) break;
+      const unsigned long long kw = s_key[w];
+      int c = 0;
+      int v = v_lo;
+      // eight independent LDS reads in flight per step
+      for (; v + 8 <= v_hi; v += 8) {
+        unsigned long long kv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[e] = s_key[v + e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c += kv[e] < kw;
+      }
+      for (; v < v_hi; ++v) c += s_key[v] < kw;
+      if (c) atomicAdd(&s_rank[w], c);
+    }
+    __syncthreads();
+    if (owner) {
+#pragma unroll
+      for (int q = 0; q < kLptBPer; ++q) {
+        const int w = tid + q * kLptBThreads;
+        if (w < W) {
+          const int rank = s_rank[w];
+          if (rank < m) {
+            const int g = s_g[rank];
+            load[q] += static_cast<unsigned long long>(s_c[rank]);
+            s_key[w] = (load[q] << 12) | static_cast<unsigned>(w);
+            worker_of[g] = w;
+            last_item[w] = g;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kLptBPer; ++q) {
+      g_cur[q] = g_nxt[q];
+      c_cur[q] = c_nxt[q];
+      g_nxt[q] = g_aft[q];
+    }
+    __syncthreads();
+  }
+  unsigned long long mx = 0;
+#pragma unroll
+  for (int q = 0; q < kLptBPer; ++q) {
+    const int w = tid + q * kLptBThreads;
+    if (owner && w < W) {
+      worker_load[w] = static_cast<int64_t>(load[q]);
+      mx = max(mx, load[q]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = max(mx, static_cast<unsigned long long>(__shfl_xor(mx, o, kWave)));
+  if ((tid & (kWave - 1)) == 0) s_max[tid / kWave] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long all = 0;
+    for (int x = 0; x < kLptBThreads / kWave; ++x) all = max(all, s_max[x]);
+    makespan[0] = static_cast<int64_t>(all);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_item_union(const Shape& s, const int32_t* row_cnt, const int32_t* row_idx, int* item_tiles,
+                             unsigned* ubits, hipStream_t stream, int tile_fixed, int* item_cost) {
+  const int G = group_size(s);
+  const int ng = (s.nb + G - 1) / G;
+  const long long items = static_cast<long long>(s.B) * s.H * ng;
+  if (s.nbk > kItemWords * 32 || items < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(item_union_kernel, dim3(static_cast<unsigned>(items)), dim3(kUnionThreads), 0, stream, row_cnt,
+                     row_idx, s.nb, s.nbk, s.kb, s.N, ng, G, item_tiles, ubits, tile_fixed, item_cost);
+  return hipGetLastError();
+}
+
+hipError_t launch_lpt_batched(const Shape& s, const int* cost, const int32_t* work_list, int num_workers,
+                              int32_t* worker_of, int64_t* worker_load, int32_t* last_item, int64_t* makespan,
+                              hipStream_t stream) {
+  const int G = group_size(s);
+  const int ng = (s.nb + G - 1) / G;
+  const long long items = static_cast<long long>(s.B) * s.H * ng;
+  if (num_workers < 1 || num_workers > kMaxLptWorkers) return hipErrorInvalidValue;
+  const size_t lds = lpt_batched_lds(num_workers);
+  const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(lpt_batched_kernel),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(lpt_batched_kernel, dim3(1), dim3(kLptBThreads), lds, stream, cost, work_list,
+                     static_cast<int>(items), num_workers, worker_of, worker_load, last_item, makespan);
+  return hipGetLastError();
+}
 
 hipError_t launch_schedule(const Shape& s, const int32_t* row_cnt, int head_window, int32_t* work_list,
                            uint32_t* ctrl, hipStream_t stream) {
