@@ -1,4 +1,5 @@
-"""GPU edge cases against the fp64 oracle: exact ties in the block scores,
+"""GPU edge cases against the fp64 oracle: exact ties and near ties (equal
+to 2^-24 relative) in the block probabilities,
 the largest sizes the C ABI accepts (1024 key blocks for routing, 2048 for
 the sparse forward), and p so small that every row keeps one block.  Every
 call goes through the C ABI."""
@@ -42,6 +43,55 @@ def test_exact_ties_take_lowest_indices(causal):
         for i in (0, 1, 3, 7, 15, 63, 255, 511):              # i+1 a power of two: exact sums
             kk = int(np.ceil(0.9 * (i + 1)))
             assert (mask[:, :, i, :kk] == 1).all() and (mask[:, :, i, kk:] == 0).all()
+
+
+def _ranked_correctly(r, nv_of=None):
+    """Every row's selection ascending, then its ranked tail by (P desc, index asc)
+    on the GPU's own probabilities; the selection is a prefix of that order."""
+    prob = r.block_prob.cpu().numpy()
+    rc, ri = r.row_cnt.cpu().numpy(), r.row_idx.cpu().numpy()
+    B, H, nb, nbk = prob.shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                nv = nbk if nv_of is None else nv_of(i)
+                kk = int(rc[b, h, i])
+                sel, tail = ri[b, h, i, :kk], ri[b, h, i, kk:nv]
+                assert (np.diff(sel) > 0).all()
+                order = sorted(range(nv), key=lambda j: (-prob[b, h, i, j], j))
+                assert sorted(sel.tolist()) == sorted(order[:kk])
+                assert tail.tolist() == order[kk:]
+
+
+@pytest.mark.parametrize("nb", [64, 512])
+def test_near_ties_ranked_exactly(nb):
+    # Every query token is the same vector a, and key block 2t+1 is block 2t
+    # with one element one fp32 ulp larger where a is positive: the pair's
+    # probabilities differ by about 1e-10 relative (the same high bits of
+    # the double), the larger index larger, so the ranking must put the odd
+    # block first.  fp32 inputs, so the ulp survives.
+    d, block = 64, 64
+    N = nb * block
+    g = torch.Generator().manual_seed(5)
+    a = torch.rand(d, generator=g) + 0.5
+    q = a.expand(1, 1, N, d).contiguous()
+    kb = torch.randn(1, 1, nb // 2, block, d, generator=g) * 2
+    k = torch.empty(1, 1, nb, block, d)
+    k[:, :, 0::2] = kb
+    k[:, :, 1::2] = kb
+    k[:, :, 1::2, 0, 0] = torch.nextafter(kb[:, :, :, 0, 0], torch.tensor(float("inf")))
+    k = k.reshape(1, 1, N, d)
+    q, k = q.to(DEV), k.to(DEV)
+    r = tbs.route(q, k, 0.5, block, return_prob=True)
+    torch.cuda.synchronize()
+    prob = r.block_prob.cpu().numpy()[0, 0, 0]
+    assert (prob[1::2] > prob[0::2]).all()
+    rel = (prob[1::2] - prob[0::2]) / prob[0::2]
+    print(f"  relative gap of the planted pairs: {rel.min():.2e} .. {rel.max():.2e}", flush=True)
+    assert rel.max() < 2.0 ** -24
+    _ranked_correctly(r)
+    ref = oracle_route_per_head(q, k, block, 0.5)
+    compare_route(r, ref)
 
 
 def test_largest_routing_size():

@@ -19,9 +19,11 @@
 //                  staged in LDS and read as broadcasts, pooled K read
 //                  transposed so that lanes read consecutive key blocks, each
 //                  thread holding all of its key blocks' sums); then one wave per
-//                  row: a max/sum softmax, a register bitonic sort by
-//                  (P desc, index asc), a fixed-order prefix sum to find the
-//                  cut, and the outputs -- no workgroup barriers per row.
+//                  row: a max/sum softmax, a register bitonic sort of one
+//                  64-bit key per block (P's high bits, then the index), an
+//                  exact fix-up of runs with equal high bits, a fixed-order
+//                  prefix sum to find the cut, and the outputs -- no
+//                  workgroup barriers per row.
 //
 // Causal routing (decoder models): row i only considers key blocks j <= i.
 // They are cut before the softmax, so the probabilities of row i are a
@@ -280,8 +282,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_qk_kernel(
 }
 
 // Value of lane (lane ^ LX) for a 32-bit register, with VALU lane moves instead
-// of an LDS permute: DPP quad permutations (1, 2), two row shifts and a select
-// (4), a row rotation by half a row (8), and the gfx950 row swaps (16, 32).
+// of an LDS permute: DPP quad permutations (1, 2), a quad reversal followed by
+// a half-row mirror (4), a row rotation by half a row (8), and the gfx950 row
+// swaps (16, 32).
 template <int LX>
 __device__ __forceinline__ unsigned xor_lane(unsigned v) {
   const unsigned lane = __lane_id();
@@ -290,9 +293,10 @@ __device__ __forceinline__ unsigned xor_lane(unsigned v) {
   } else if constexpr (LX == 2) {
     return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
   } else if constexpr (LX == 4) {
-    const unsigned up = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false);   // row_shr:4 (lane - 4)
-    const unsigned dn = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0xF, false);   // row_shl:4 (lane + 4)
-    return (lane & 4) ? up : dn;
+    // quad reversal (l ^ 3) then the half-row mirror (7 - l within 8 lanes):
+    // lane l reads lane (7 - l) ^ 3 = l ^ 4
+    const unsigned r = __builtin_amdgcn_update_dpp(v, v, 0x1B, 0xF, 0xF, false);    // quad_perm [3,2,1,0]
+    return __builtin_amdgcn_update_dpp(r, r, 0x141, 0xF, 0xF, false);               // row_half_mirror
   } else if constexpr (LX == 8) {
     return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);  // row_ror:8
   } else if constexpr (LX == 16) {
@@ -312,19 +316,34 @@ __device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v) {
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
-// "a before b" in the ranking: larger probability first, then smaller index.
-// Probabilities are non-negative doubles, which order like their bit
-// patterns; padding elements (P = 0, index >= nb) rank after every real block.
-__device__ __forceinline__ bool ranks_before(unsigned long long ka, int ia, unsigned long long kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
+// Sort keys: the top 32 bits of P's bit pattern (non-negative doubles order
+// like their bits, so this is monotone in P), then the key-block index
+// inverted, so that a larger key ranks first and equal high bits rank the
+// smaller index first.  Equal high bits do not mean equal P: such runs are
+// put in exact order afterwards.
+__device__ __forceinline__ unsigned long long rank_key(double p, int idx) {
+  const unsigned hi = static_cast<unsigned>(static_cast<unsigned long long>(__double_as_longlong(p)) >> 31);
+  return (static_cast<unsigned long long>(hi) << 32) | (0xffffffffu - static_cast<unsigned>(idx));
 }
+__device__ __forceinline__ int key_index(unsigned long long key) {
+  return static_cast<int>(0xffffffffu - static_cast<unsigned>(key));
+}
+// Exact ranking of two keys with equal high bits: larger P (read by index from
+// the row's probabilities p) first, then the smaller index.
+__device__ __forceinline__ bool exact_before(const double* p, unsigned long long a, unsigned long long b) {
+  const int ia = key_index(a), ib = key_index(b);
+  const double pa = p[ia], pb = p[ib];
+  return pa > pb || (pa == pb && ia < ib);
+}
+__device__ __forceinline__ bool same_run(unsigned long long a, unsigned long long b) { return (a >> 32) == (b >> 32); }
 
 // Row phase of the selection, run by one wave per query-block row: E
 // elements per lane in blocked order (position = lane*E + i).  Key blocks
 // nv..nb-1 are not eligible (nv = nb except under causal routing): they get
-// P = 0, rank after every eligible block and are never selected.
+// P = 0, rank after every eligible block and are never selected.  zr holds
+// the row's scores on entry and its probabilities (by key-block index) after.
 template <int E>
-__device__ void select_row(const double* __restrict__ zr, int nb, int nv, double top_p, long long row, int bh,
+__device__ void select_row(double* __restrict__ zr, int nb, int nv, double top_p, long long row, int bh,
                            unsigned char* __restrict__ flag, uint8_t* __restrict__ mask,
                            int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx,
                            int32_t* __restrict__ head_cnt, double* __restrict__ block_prob) {
@@ -348,17 +367,19 @@ __device__ void select_row(const double* __restrict__ zr, int nb, int nv, double
     s += v[i];
   }
   s = wave_sum_f64(s);
+  const double inv = 1.0 / s;
   unsigned long long key[E];
-  int idx[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const double pj = v[i] / s;
+    const double pj = v[i] * inv;
     if (block_prob && base + i < nb) block_prob[row * nb + base + i] = pj;
-    key[i] = __double_as_longlong(pj);
-    idx[i] = base + i;
+    zr[base + i] = pj;
+    key[i] = rank_key(pj, base + i);
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 
-  // Bitonic sort into ranking order.
+  // Bitonic sort by key, larger first.
 #pragma unroll
   for (int k = 2; k <= NP; k <<= 1) {
 #pragma unroll
@@ -369,43 +390,93 @@ __device__ void select_row(const double* __restrict__ zr, int nb, int nv, double
           if (i & j) continue;
           const int b = i | j;
           const bool up = ((base + i) & k) == 0;
-          const bool b_first = ranks_before(key[b], idx[b], key[i], idx[i]);
-          if (b_first == up) {
-            const unsigned long long tk = key[i]; key[i] = key[b]; key[b] = tk;
-            const int ti = idx[i]; idx[i] = idx[b]; idx[b] = ti;
-          }
+          const bool sw = (key[b] > key[i]) == up;
+          const unsigned long long ki = key[i], kb = key[b];
+          key[i] = sw ? kb : ki;
+          key[b] = sw ? ki : kb;
         }
       } else {
         const int lx = j / E;   // partner lane distance
 #pragma unroll
         for (int i = 0; i < E; ++i) {
           unsigned long long ok;
-          int oi;
           switch (lx) {
-            case 1: ok = xor_lane64<1>(key[i]); oi = static_cast<int>(xor_lane<1>(idx[i])); break;
-            case 2: ok = xor_lane64<2>(key[i]); oi = static_cast<int>(xor_lane<2>(idx[i])); break;
-            case 4: ok = xor_lane64<4>(key[i]); oi = static_cast<int>(xor_lane<4>(idx[i])); break;
-            case 8: ok = xor_lane64<8>(key[i]); oi = static_cast<int>(xor_lane<8>(idx[i])); break;
-            case 16: ok = xor_lane64<16>(key[i]); oi = static_cast<int>(xor_lane<16>(idx[i])); break;
-            default: ok = xor_lane64<32>(key[i]); oi = static_cast<int>(xor_lane<32>(idx[i])); break;
+            case 1: ok = xor_lane64<1>(key[i]); break;
+            case 2: ok = xor_lane64<2>(key[i]); break;
+            case 4: ok = xor_lane64<4>(key[i]); break;
+            case 8: ok = xor_lane64<8>(key[i]); break;
+            case 16: ok = xor_lane64<16>(key[i]); break;
+            default: ok = xor_lane64<32>(key[i]); break;
           }
           const int pos = base + i;
           const bool lower = (pos & j) == 0;
           const bool up = (pos & k) == 0;
-          const bool mine_first = ranks_before(key[i], idx[i], ok, oi);
-          const bool keep = (lower == up) ? mine_first : !mine_first;
-          if (!keep) { key[i] = ok; idx[i] = oi; }
+          const bool mine_first = key[i] > ok;
+          key[i] = (lower == up) != mine_first ? ok : key[i];
         }
       }
     }
   }
+
+  // Exact order inside runs of equal high bits: odd-even transposition over
+  // neighbouring positions, comparing P itself, until a pass swaps nothing
+  // (usually at once: such runs need P equal to about 2^-21 relative).
+  for (;;) {
+    bool swapped = false;
+#pragma unroll
+    for (int phase = 0; phase < 2; ++phase) {
+      if constexpr (E == 1) {
+        // positions are lanes: partner lane^1 (phase 0) or the odd pair (phase 1)
+        const bool left = phase == 0 ? (lane & 1) == 0 : (lane & 1) == 1;
+        const int partner = left ? lane + 1 : lane - 1;
+        const unsigned long long ok = __shfl(key[0], partner & (kWave - 1), kWave);
+        const bool valid = partner >= 0 && partner < kWave;
+        if (valid && same_run(key[0], ok)) {
+          const bool in_order = left ? exact_before(zr, key[0], ok) : exact_before(zr, ok, key[0]);
+          if (!in_order) {
+            key[0] = ok;
+            swapped = true;
+          }
+        }
+      } else {
+        // in-lane pairs (i, i + 1) with i = phase, phase + 2, ...
+#pragma unroll
+        for (int i = phase; i + 1 < E; i += 2) {
+          if (same_run(key[i], key[i + 1]) && !exact_before(zr, key[i], key[i + 1])) {
+            const unsigned long long t = key[i];
+            key[i] = key[i + 1];
+            key[i + 1] = t;
+            swapped = true;
+          }
+        }
+        if (phase == 1) {
+          // across lanes: this lane's last element and the next lane's first
+          const unsigned long long right = __shfl_down(key[0], 1, kWave);
+          const unsigned long long left = __shfl_up(key[E - 1], 1, kWave);
+          const unsigned long long my_last = key[E - 1], my_first = key[0];
+          if (lane < kWave - 1 && same_run(my_last, right) && !exact_before(zr, my_last, right)) {
+            key[E - 1] = right;
+            swapped = true;
+          }
+          if (lane > 0 && same_run(left, my_first) && !exact_before(zr, left, my_first)) {
+            key[0] = left;
+            swapped = true;
+          }
+        }
+      }
+    }
+    if (!__any(swapped)) break;
+  }
+  int idx[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) idx[i] = key_index(key[i]);
 
   // Inclusive prefix of the ranked probabilities; first rank reaching top_p.
   double c[E];
   double run = 0.0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    run += __longlong_as_double(key[i]);
+    run += zr[idx[i]];
     c[i] = run;
   }
   double incl = run;
