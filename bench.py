@@ -119,6 +119,38 @@ def union_tiles(mask: np.ndarray, n_tokens: int, block: int, key_block: int, gro
     return int((union.astype(np.int64) * per_block).sum())
 
 
+def unit_lif(costs, num_workers: int, window_units: int = 0) -> dict:
+    """Load imbalance (max / mean) of single query-block units (cost = the
+    unit's selected key blocks) over num_workers workers: a contiguous static
+    partition of the natural order, and the greedy longest-first assignment
+    (each unit to the least-loaded worker, ties to the lowest id) over the
+    units sorted by (cost desc, id asc), in one window or in windows of
+    window_units consecutive unit ids."""
+    import heapq
+    costs = np.asarray(costs, dtype=np.int64).reshape(-1)
+    U = costs.size
+    static = np.array([costs[(w * U) // num_workers:((w + 1) * U) // num_workers].sum()
+                       for w in range(num_workers)], dtype=np.int64)
+
+    def lpt(order):
+        heap = [(0, w) for w in range(num_workers)]
+        load = np.zeros(num_workers, dtype=np.int64)
+        for u in order:
+            l, w = heapq.heappop(heap)
+            load[w] = l + costs[u]
+            heapq.heappush(heap, (int(load[w]), w))
+        return load
+
+    pure = np.argsort(-costs, kind="stable")
+    out = {"units": int(U), "static_partition": float(static.max() / static.mean()),
+           "longest_first_lpt": float(lpt(pure).max() / max(1e-300, costs.sum() / num_workers))}
+    if window_units and window_units < U:
+        order = np.concatenate([lo + np.argsort(-costs[lo:lo + window_units], kind="stable")
+                                for lo in range(0, U, window_units)])
+        out["longest_first_lpt_windowed"] = float(lpt(order).max() / (costs.sum() / num_workers))
+    return out
+
+
 def summarize_counters(fetch_db: str, write_db: str, kernel: str, calib_mib: int, first: int) -> dict:
     """HBM bytes per launch of `kernel` from two rocprofv3 counter databases
     (one FETCH_SIZE pass, one WRITE_SIZE pass of the same bench command with
@@ -493,6 +525,9 @@ def main():
     torch.cuda.synchronize()
     lp = lpt_pure.cpu().numpy()
     lif["longest_first_lpt_one_window"] = float(lp.max() / lp.mean())
+    # The same models over single query-block units (b, h, i), each costing
+    # its selected key blocks, as the work list itself is defined.
+    lif["per_query_block"] = unit_lif(route_out.row_cnt.cpu().numpy(), W, (hw or 0) * nb)
 
     def time_fwd(wl, reps=3):
         fwd(route_out.row_cnt, route_out.row_idx, wl)

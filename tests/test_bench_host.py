@@ -124,3 +124,21 @@ def test_summarize_trace_timed_dispatches(tmp_path):
     assert res["timed_min_us"] == 100.0 and res["timed_max_us"] == 400.0
     names = [r[0] for r in res["table"]]
     assert len(names) == 2 and res["table"][0][1] == 7
+
+
+def test_unit_lif_hand_example():
+    # costs 5, 1, 4, 2 over two workers: static halves [5+1, 4+2] = [6, 6];
+    # longest first 5 -> w0, 4 -> w1, 2 -> w1 (4 < 5), 1 -> w0 (5 < 6): [6, 6]
+    r = bench.unit_lif([5, 1, 4, 2], 2)
+    assert r["units"] == 4 and r["static_partition"] == 1.0 and r["longest_first_lpt"] == 1.0
+    # costs 4, 4, 1, 1 over two workers: static [8, 2] -> 8 / 5; LPT [5, 5] -> 1
+    r = bench.unit_lif([4, 4, 1, 1], 2)
+    assert abs(r["static_partition"] - 1.6) < 1e-12 and r["longest_first_lpt"] == 1.0
+    # windows of two units: [4, 4] then [1, 1] -> 4 -> w0, 4 -> w1, 1 -> w0, 1 -> w1: [5, 5]
+    r = bench.unit_lif([4, 4, 1, 1], 2, window_units=2)
+    assert r["longest_first_lpt_windowed"] == 1.0
+    # windows change the order: [1, 9 | 8, 2] over two workers, windows of two:
+    # 9 -> w0, 1 -> w1, 8 -> w1, 2 -> w0 (9 = 9, lowest id) = [11, 9] -> 11 / 10;
+    # pure: 9, 8, 2, 1 -> [10, 10]
+    r = bench.unit_lif([1, 9, 8, 2], 2, window_units=2)
+    assert abs(r["longest_first_lpt_windowed"] - 1.1) < 1e-12 and r["longest_first_lpt"] == 1.0
