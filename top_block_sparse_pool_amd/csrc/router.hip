@@ -687,10 +687,9 @@ hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qba
     auto kk = static_cast<const unsigned short*>(k);
     const bool wide = s.block == 128 || s.kb == 128;
     if (s.d == 128) {
-      if (wide)
-        launch_pool_qk_t<128, 128, false>(s, qq, kk, qbar, kbar_t, head_cnt, nullptr, nullptr, nullptr, nullptr, stream);
-      else
-        launch_pool_qk_t<128, 64, false>(s, qq, kk, qbar, kbar_t, head_cnt, nullptr, nullptr, nullptr, nullptr, stream);
+      // 64-token blocks too go two to a workgroup (half as many workgroups,
+      // 64 KB read by each; the same per-block sums)
+      launch_pool_qk_t<128, 128, false>(s, qq, kk, qbar, kbar_t, head_cnt, nullptr, nullptr, nullptr, nullptr, stream);
     } else {
       if (wide)
         launch_pool_qk_t<64, 128, false>(s, qq, kk, qbar, kbar_t, head_cnt, nullptr, nullptr, nullptr, nullptr, stream);
