@@ -1,5 +1,7 @@
 """Host-side logic of the benchmark: its executed-FLOP count must equal the
 oracle's definition (allowed token pairs of the selected block pairs)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -142,3 +144,16 @@ def test_unit_lif_hand_example():
     # pure: 9, 8, 2, 1 -> [10, 10]
     r = bench.unit_lif([1, 9, 8, 2], 2, window_units=2)
     assert abs(r["longest_first_lpt_windowed"] - 1.1) < 1e-12 and r["longest_first_lpt"] == 1.0
+
+
+def test_committed_traffic_summaries_match_their_keys():
+    # Each committed HBM counter summary names the workload it is read for; a
+    # summary filed under the wrong key would silently drop the traffic field
+    # (a summary taken on older kernel sources drops it on purpose).
+    import re
+    for key, rel in bench.TRAFFIC_SUMMARIES.items():
+        with open(os.path.join(bench.ROOT, rel)) as f:
+            fields = dict(re.findall(r"^- (\w+): (\S+)\s*$", f.read(), flags=re.M))
+        assert fields["workload"] == key, rel
+        assert len(fields["kernel_source_sha256"]) == 64, rel
+        assert float(fields["fetch_bytes_per_launch"]) > 0 and float(fields["write_bytes_per_launch"]) > 0, rel
