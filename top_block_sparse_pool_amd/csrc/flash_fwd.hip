@@ -372,7 +372,7 @@ struct GroupInfo {
 // 0-3 and 4-7) with one wave of each group on every SIMD.  A wave's work on
 // tile t is an MFMA part M(t) = S(t) = K(t) Q^T, then O^T += V^T P^T for
 // tile t - 1, and a VALU part V(t) = the online-softmax update of tile t.
-// The workgroup advances in steps separated by barriers; group 1 runs one
+// The workgroup advances in steps of one part each; group 1 runs one
 // step behind group 0, so on every SIMD one wave issues MFMAs while the other
 // computes exponentials and the matrix core and the VALU work side by side:
 //
@@ -381,12 +381,9 @@ struct GroupInfo {
 //   group 1    V(t-1)        M(t)          V(t)
 //
 // K(t) is read in steps 2t and 2t+1 and V(t) in steps 2t+2 and 2t+3; both
-// have two LDS stages, and the copies of K(t+1) and V(t) start at step 2t and
-// must land by the end of step 2t+1, two steps ahead of their first use.
-// The bf16 kernel keeps only the barrier at the end of every odd step (group
-// 0 after V(t), group 1 after M(t)), so the two groups need not change parts
-// at the same moment; the fp8 kernel, whose S product is much shorter than
-// its softmax part, ran faster with a barrier after every step.
+// have two LDS stages.  The copies of K(t+1) and V(t) are issued in steps 2t
+// and 2t+1 and land by the end of step 2t+1.  Only the end of every odd step
+// is a barrier, so the two groups need not change parts at the same moment.
 constexpr int kWaves = 8;
 
 template <int D, int BQ, int BK, int MODE, bool F8>
@@ -403,7 +400,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int NS = F8 ? D / 64 : D / 16;   // k-steps of S^T
   constexpr int NO = D / 32;            // 32-dim tiles of O^T
   static_assert(!F8 || D == 128, "the fp8 path takes head_dim 128");
-  constexpr bool kTwoBarriers = F8;     // a barrier after every step, not only every second one
   // LDS: K stage 0, K stage 1, V stage 0, V stage 1.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILEK + 2 * TILEB];
   __shared__ unsigned s_bm[fwd_listed(MODE) ? G * kMaxListWords : 1];
@@ -802,8 +798,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       asm volatile("" ::: "memory");
     };
 
-    // Copies started at global step 2t: K(t+1) into K stage (t+1)&1 and
-    // V(t) into V stage t&1 (P = t&1); every wave issues its share.
+    // The copies of tile t's interval: K(t+1) into K stage (t+1)&1 and V(t)
+    // into V stage t&1 (P = t&1); every wave issues its share.
     auto issue_k = [&](auto stage, int key0) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
       if constexpr (F8) {
@@ -819,26 +815,29 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       if (t < nt) loader.issue_one(vg, wkey0(w_t, t), p.N, lds + 2 * TILEK + P * TILEB);
     };
 
-    // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(nt).
-    // Global step 2t starts the copies of K(t+1) and V(t) (group 0 at the
-    // start of M(t), group 1 at the start of V(t-1)); each wave waits for its
-    // copies at the end of global step 2t+1 (group 0 after V(t), group 1
-    // after M(t)).  With one barrier per tile (bf16) only those two points
-    // are barriers: between two of them group 0 runs M(t) V(t) and group 1
-    // V(t-1) M(t), so each tile's copies have landed before any wave reads
-    // them, and a stage is refilled only after the barrier that follows its
-    // last reads (K(t-1), V(t-2), both read in M(t-1)).  With two barriers
-    // per tile (fp8) every part ends at a barrier and group 1 first passes
-    // one empty step, which puts it one step behind group 0.  Either way
-    // both groups pass the same number of barriers.  The loop is unrolled
+    // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(nt), group
+    // 1 one part behind group 0.  There is one barrier per tile, where each
+    // group has waited for its copies: group 0 after V(t), group 1 after
+    // M(t).  Between two barriers group 0 runs M(t) V(t) and group 1 V(t-1)
+    // M(t), and every wave issues its share of the copies of K(t+1) and V(t)
+    // just before its softmax part (group 1 right after the barrier, group 0
+    // after M(t)), so a wave about to issue MFMAs never waits behind a burst
+    // of copies.  Those copies land before the barrier that ends the
+    // interval, ahead of their first reads (K(t+1) in M(t+1), V(t) in
+    // M(t+1)), and the stages they fill were last read in M(t-1) (K(t-1),
+    // V(t-2)), before the barrier that opened it.  The loop is unrolled
     // twice so the LDS stages of K(t) and V(t-1) are compile-time constants.
     auto end_m = [&]() __attribute__((always_inline)) {
-      if (grp == 1) wait_vmem();
-      if (kTwoBarriers || grp == 1) step_barrier();
+      if (grp == 1) {
+        wait_vmem();
+        step_barrier();
+      }
     };
     auto end_v = [&]() __attribute__((always_inline)) {
-      if (grp == 0) wait_vmem();
-      if (kTwoBarriers || grp == 0) step_barrier();
+      if (grp == 0) {
+        wait_vmem();
+        step_barrier();
+      }
     };
     if (nt > 0) {
       // Union-list words of tiles t-1 .. t+3 (uniform).
@@ -846,24 +845,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       issue_k(Stage<0>{}, wkey0(w_0, 0));
       wait_vmem();
       step_barrier();
-      if (grp == 1) {
-        issue(Stage<0>{}, 0, w_1, w_0);
-        if (kTwoBarriers) step_barrier();
-      }
+      if (grp == 1) issue(Stage<0>{}, 0, w_1, w_0);
       for (int t = 0;; t += 2) {
         const unsigned pf_a = wread(t + 4), pf_b = wread(t + 5);   // tiles t+4, t+5, for the next iteration
-        if (grp == 0) issue(Stage<0>{}, t, w_1, w_0);
         mpart(Stage<0>{}, Stage<1>{}, t, w_0, w_m1);
         end_m();
         if (t == nt) break;
+        if (grp == 0) issue(Stage<0>{}, t, w_1, w_0);
         if (grp == 1) issue(Stage<1>{}, t + 1, w_2, w_1);
         vpart(t, w_0);
         end_v();
 
-        if (grp == 0) issue(Stage<1>{}, t + 1, w_2, w_1);
         mpart(Stage<1>{}, Stage<0>{}, t + 1, w_1, w_0);
         end_m();
         if (t + 1 == nt) break;
+        if (grp == 0) issue(Stage<1>{}, t + 1, w_2, w_1);
         if (grp == 1) issue(Stage<0>{}, t + 2, w_3, w_2);
         vpart(t + 1, w_1);
         end_v();
