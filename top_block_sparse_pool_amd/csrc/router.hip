@@ -20,10 +20,12 @@
 //                  transposed so that lanes read consecutive key blocks, each
 //                  thread holding all of its key blocks' sums); then one wave per
 //                  row: a max/sum softmax, a register bitonic sort of one
-//                  64-bit key per block (P's high bits, then the index), an
-//                  exact fix-up of runs with equal high bits, a fixed-order
-//                  prefix sum to find the cut, and the outputs -- no
-//                  workgroup barriers per row.
+//                  64-bit key per block (P's high bits, then the index;
+//                  rows of more than 512 blocks keep the stage loop rolled),
+//                  an exact fix-up of runs with equal high bits, a
+//                  fixed-order prefix sum to find the cut, and the outputs --
+//                  no workgroup barriers per row.  The pooled query rows
+//                  share LDS with the score tile, which they precede.
 //
 // Causal routing (decoder models): row i only considers key blocks j <= i.
 // They are cut before the softmax, so the probabilities of row i are a
@@ -380,11 +382,26 @@ __device__ void select_row(double* __restrict__ zr, int nb, int nv, double top_p
   __builtin_amdgcn_wave_barrier();
 
   // Bitonic sort by key, larger first.
+  if constexpr (E >= 16) {
+    // Rows of more than 512 blocks: the same stages with the stage loop kept
+    // rolled and cross-lane partners read with a lane permute at a run-time
+    // distance, so the code (and with it the register need) stays small.
+    for (int k = 2; k <= NP; k <<= 1) {
+      for (int j = k >> 1; j >= E; j >>= 1) {
+        const int lx = j / E;   // partner lane distance
 #pragma unroll
-  for (int k = 2; k <= NP; k <<= 1) {
+        for (int i = 0; i < E; ++i) {
+          const unsigned long long ok = __shfl_xor(key[i], lx, kWave);
+          const int pos = base + i;
+          const bool lower = (pos & j) == 0;
+          const bool up = (pos & k) == 0;
+          const bool mine_first = key[i] > ok;
+          key[i] = (lower == up) != mine_first ? ok : key[i];
+        }
+      }
 #pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < E) {
+      for (int j = E >> 1; j > 0; j >>= 1) {
+        if (j >= k) continue;
 #pragma unroll
         for (int i = 0; i < E; ++i) {
           if (i & j) continue;
@@ -395,24 +412,43 @@ __device__ void select_row(double* __restrict__ zr, int nb, int nv, double top_p
           key[i] = sw ? kb : ki;
           key[b] = sw ? ki : kb;
         }
-      } else {
-        const int lx = j / E;   // partner lane distance
+      }
+    }
+  } else {
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-          unsigned long long ok;
-          switch (lx) {
-            case 1: ok = xor_lane64<1>(key[i]); break;
-            case 2: ok = xor_lane64<2>(key[i]); break;
-            case 4: ok = xor_lane64<4>(key[i]); break;
-            case 8: ok = xor_lane64<8>(key[i]); break;
-            case 16: ok = xor_lane64<16>(key[i]); break;
-            default: ok = xor_lane64<32>(key[i]); break;
+    for (int k = 2; k <= NP; k <<= 1) {
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        if (j < E) {
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            if (i & j) continue;
+            const int b = i | j;
+            const bool up = ((base + i) & k) == 0;
+            const bool sw = (key[b] > key[i]) == up;
+            const unsigned long long ki = key[i], kb = key[b];
+            key[i] = sw ? kb : ki;
+            key[b] = sw ? ki : kb;
           }
-          const int pos = base + i;
-          const bool lower = (pos & j) == 0;
-          const bool up = (pos & k) == 0;
-          const bool mine_first = key[i] > ok;
-          key[i] = (lower == up) != mine_first ? ok : key[i];
+        } else {
+          const int lx = j / E;   // partner lane distance
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            unsigned long long ok;
+            switch (lx) {
+              case 1: ok = xor_lane64<1>(key[i]); break;
+              case 2: ok = xor_lane64<2>(key[i]); break;
+              case 4: ok = xor_lane64<4>(key[i]); break;
+              case 8: ok = xor_lane64<8>(key[i]); break;
+              case 16: ok = xor_lane64<16>(key[i]); break;
+              default: ok = xor_lane64<32>(key[i]); break;
+            }
+            const int pos = base + i;
+            const bool lower = (pos & j) == 0;
+            const bool up = (pos & k) == 0;
+            const bool mine_first = key[i] > ok;
+            key[i] = (lower == up) != mine_first ? ok : key[i];
+          }
         }
       }
     }
@@ -548,9 +584,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t* __restrict__ row_idx, int32_t* __restrict__ head_cnt, double* __restrict__ block_prob) {
   constexpr int NP = 64 * E;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  // The pooled query rows are read only before the scores are stored, so
+  // they share the score tile's memory.
+  constexpr int ZQ = NP > D ? NP : D;                                        // doubles per row of that memory
   double* z = reinterpret_cast<double*>(smem_raw);                           // [R][NP]
-  double* qs = z + R * NP;                                                   // [R][D]
-  unsigned char* flags = reinterpret_cast<unsigned char*>(qs + R * D);       // [waves][NP]
+  double* qs = z;                                                            // [R][D]
+  unsigned char* flags = reinterpret_cast<unsigned char*>(z + R * ZQ);       // [waves][NP]
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int bh = blockIdx.x / tiles_per_head;
@@ -568,15 +607,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // the sum over the head dimension runs in increasing order.
   constexpr int CU = NP > 2 * kSelThreads ? 4 : 8;   // head-dimension steps per batch of pooled-K loads
   constexpr int J = NP > kSelThreads ? NP / kSelThreads : 1;
+  double acc[J][R];
+  bool live[J];
+#pragma unroll
+  for (int u = 0; u < J; ++u) {
+    live[u] = tid + u * kSelThreads < nbk;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[u][r] = 0.0;
+  }
   if (tid < NP) {
-    double acc[J][R];
-    bool live[J];
-#pragma unroll
-    for (int u = 0; u < J; ++u) {
-      live[u] = tid + u * kSelThreads < nbk;
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[u][r] = 0.0;
-    }
     for (int c0 = 0; c0 < D; c0 += CU) {
       double kv[J][CU];
 #pragma unroll
@@ -593,6 +632,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           for (int u = 0; u < J; ++u) acc[u][r] = fma(qv, kv[u][c], acc[u][r]);
         }
     }
+  }
+  __syncthreads();   // every read of the pooled query rows is done
+  if (tid < NP) {
 #pragma unroll
     for (int u = 0; u < J; ++u)
 #pragma unroll
@@ -621,7 +663,7 @@ hipError_t launch_select_t(const Shape& s, const double* qbar, const double* kba
                            uint8_t* mask, int32_t* row_cnt, int32_t* row_idx, int32_t* head_cnt,
                            double* block_prob, hipStream_t stream) {
   constexpr int NP = 64 * E;
-  const size_t smem = sizeof(double) * static_cast<size_t>(R) * (NP + D) + static_cast<size_t>(kSelWaves) * NP;
+  const size_t smem = sizeof(double) * static_cast<size_t>(R) * (NP > D ? NP : D) + static_cast<size_t>(kSelWaves) * NP;
   auto kern = select_kernel<D, R, E>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
