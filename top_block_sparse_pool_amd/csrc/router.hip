@@ -332,7 +332,7 @@ __device__ __forceinline__ int key_index(unsigned long long key) {
 }
 // Exact ranking of two keys with equal high bits: larger P (read by index from
 // the row's probabilities p) first, then the smaller index.
-__device__ __forceinline__ bool exact_before(const double* p, unsigned long long a, unsigned long long b) {
+__device__ __forceinline__ bool exact_before(const TBS_LDS double* p, unsigned long long a, unsigned long long b) {
   const int ia = key_index(a), ib = key_index(b);
   const double pa = p[ia], pb = p[ib];
   return pa > pb || (pa == pb && ia < ib);
@@ -345,8 +345,8 @@ __device__ __forceinline__ bool same_run(unsigned long long a, unsigned long lon
 // P = 0, rank after every eligible block and are never selected.  zr holds
 // the row's scores on entry and its probabilities (by key-block index) after.
 template <int E>
-__device__ void select_row(double* __restrict__ zr, int nb, int nv, double top_p, long long row, int bh,
-                           unsigned char* __restrict__ flag, uint8_t* __restrict__ mask,
+__device__ void select_row(TBS_LDS double* __restrict__ zr, int nb, int nv, double top_p, long long row, int bh,
+                           TBS_LDS unsigned char* __restrict__ flag, uint8_t* __restrict__ mask,
                            int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx,
                            int32_t* __restrict__ head_cnt, double* __restrict__ block_prob) {
   constexpr int NP = 64 * E;
@@ -587,9 +587,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // The pooled query rows are read only before the scores are stored, so
   // they share the score tile's memory.
   constexpr int ZQ = NP > D ? NP : D;                                        // doubles per row of that memory
-  double* z = reinterpret_cast<double*>(smem_raw);                           // [R][NP]
-  double* qs = z;                                                            // [R][D]
-  unsigned char* flags = reinterpret_cast<unsigned char*>(z + R * ZQ);       // [waves][NP]
+  TBS_LDS double* z = (TBS_LDS double*)smem_raw;                             // [R][NP]
+  TBS_LDS double* qs = z;                                                    // [R][D]
+  TBS_LDS unsigned char* flags = (TBS_LDS unsigned char*)(z + R * ZQ);       // [waves][NP]
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int bh = blockIdx.x / tiles_per_head;
