@@ -63,7 +63,7 @@ def _ranked_correctly(r, nv_of=None):
                 assert tail.tolist() == order[kk:]
 
 
-@pytest.mark.parametrize("nb", [64, 512])
+@pytest.mark.parametrize("nb", [64, 512, 1000])   # 1000: rows of more than 512 blocks (rolled sort stages)
 def test_near_ties_ranked_exactly(nb):
     # Every query token is the same vector a, and key block 2t+1 is block 2t
     # with one element one fp32 ulp larger where a is positive: the pair's

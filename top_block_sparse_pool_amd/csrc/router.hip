@@ -144,7 +144,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_qk_kernel(
   __shared__ double red[NW][2][T][D];
   __shared__ float kmax_s[NW][T];
 
-  const int bh = blockIdx.x / nspan;
+  // Heads in reverse order: the first heads that the selection (and then
+  // the attention) reads are the ones pooled last, still in the caches.
+  const int bh = BH - 1 - static_cast<int>(blockIdx.x) / nspan;
   const int t0 = (blockIdx.x % nspan) * SPAN;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
