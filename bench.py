@@ -201,6 +201,34 @@ def summarize_trace(db: str, kernel: str, warmup: int, steps: int) -> dict:
             "timed_max_us": float(np.max(timed)), "timed_dispatches": len(timed)}
 
 
+def summarize_pmc(db: str, xcds: int = 8) -> list:
+    """Per-kernel means of every counter in a rocprofv3 --pmc database: one row
+    (kernel, dispatches, mean duration in ms, {counter: mean per dispatch})
+    per kernel, the counter values of a dispatch summed over the rows the
+    profiler stored for it.  Where GRBM_GUI_ACTIVE was collected (summed over
+    the XCDs), the row also carries the clock it implies, the mean over the
+    dispatches of GRBM_GUI_ACTIVE / xcds / duration, as 'clock_ghz'."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select dispatch_id, kernel_name, counter_name, sum(value), max(duration) from counters_collection "
+                       "group by dispatch_id, counter_name order by dispatch_id").fetchall()
+    con.close()
+    vals, durs = {}, {}
+    for disp, name, counter, value, dur in rows:
+        vals.setdefault(name, {}).setdefault(counter, {})[disp] = value
+        durs.setdefault(name, {})[disp] = dur
+    out = []
+    for name, counters in vals.items():
+        dur = durs[name]
+        means = {c: float(np.mean(list(v.values()))) for c, v in counters.items()}
+        if "GRBM_GUI_ACTIVE" in counters:
+            g = counters["GRBM_GUI_ACTIVE"]
+            means["clock_ghz"] = float(np.mean([g[d] / xcds / dur[d] for d in g if dur[d] > 0]))
+        out.append((name, len(dur), float(np.mean(list(dur.values()))) / 1e6, means))
+    out.sort(key=lambda r: -r[1] * r[2])
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +261,9 @@ def parse():
                     help="print the HBM bytes per launch of the sparse attention kernel from two rocprofv3 "
                          "counter databases (FETCH_SIZE and WRITE_SIZE passes of a run with "
                          "--copy-calibration-mib) and exit; needs no GPU")
+    ap.add_argument("--summarize-pmc", metavar="PMC_DB",
+                    help="print per-kernel means of every counter in a rocprofv3 --pmc database (and the clock "
+                         "implied by GRBM_GUI_ACTIVE) and exit; needs no GPU")
     ap.add_argument("--summarize-trace", metavar="TRACE_DB",
                     help="print per-kernel durations from a rocprofv3 --kernel-trace database and the mean of the "
                          "timed sparse-kernel dispatches (after --warmup, --steps of them) and exit; needs no GPU")
@@ -347,6 +378,17 @@ def cpu_baseline(q, k, v, w, mask_gpu, target_s, seed, causal=False, block=None,
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        rows = summarize_pmc(args.summarize_pmc)
+        counters = sorted({c for _, _, _, m in rows for c in m})
+        print("| kernel | dispatches | avg duration (ms) | " + " | ".join(counters) + " |")
+        print("|---|---|---|" + "---|" * len(counters))
+        for name, n, ms, m in rows:
+            short = name.replace("(anonymous namespace)::", "").split("(")[0] if "<" not in name else \
+                name.replace("(anonymous namespace)::", "").split(">(")[0] + ">"
+            cells = " | ".join(f"{m[c]:.4g}" if c in m else "" for c in counters)
+            print(f"| {short} | {n} | {ms:.4f} | {cells} |")
+        return
     if args.summarize_trace:
         res = summarize_trace(args.summarize_trace, args.counter_kernel, args.warmup, args.steps)
         print("| kernel | calls | avg (us) | min (us) | max (us) |")

@@ -157,3 +157,30 @@ def test_committed_traffic_summaries_match_their_keys():
         assert fields["workload"] == key, rel
         assert len(fields["kernel_source_sha256"]) == 64, rel
         assert float(fields["fetch_bytes_per_launch"]) > 0 and float(fields["write_bytes_per_launch"]) > 0, rel
+
+
+def test_summarize_pmc_means_and_clock(tmp_path):
+    import sqlite3
+    path = str(tmp_path / "p.db")
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (dispatch_id int, kernel_name text, counter_name text, "
+                "value real, duration int)")
+    k = "void ns::flash_fwd_bf16_pp<128, 64, 64, 0, false>(P)"
+    rows = []
+    # two dispatches of 1 ms and 2 ms; GRBM_GUI_ACTIVE summed over 8 XCDs at 2 GHz and 1.5 GHz,
+    # stored as two rows per dispatch (the halves add up)
+    for disp, dur, ghz in ((1, 1_000_000, 2.0), (2, 2_000_000, 1.5)):
+        total = ghz * dur * 8
+        rows += [(disp, k, "GRBM_GUI_ACTIVE", total / 2, dur), (disp, k, "GRBM_GUI_ACTIVE", total / 2, dur)]
+        rows += [(disp, k, "MfmaUtil", 50.0 + disp, dur)]
+    rows += [(3, "ns::other(int)", "MfmaUtil", 0.0, 1000)]
+    con.executemany("insert into counters_collection values (?, ?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    out = {name: (n, ms, m) for name, n, ms, m in bench.summarize_pmc(path)}
+    n, ms, m = out[k]
+    assert n == 2 and ms == 1.5
+    assert m["MfmaUtil"] == 51.5
+    assert abs(m["clock_ghz"] - 1.75) < 1e-12
+    assert abs(m["GRBM_GUI_ACTIVE"] - (2.0 * 1e6 * 8 + 1.5 * 2e6 * 8) / 2) < 1e-6
+    assert out["ns::other(int)"][0] == 1
