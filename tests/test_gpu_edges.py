@@ -146,3 +146,37 @@ def test_tiny_p_keeps_one_block_per_row():
     prob = r.block_prob.cpu().numpy()
     assert (r.row_idx[..., 0].cpu().numpy() == np.argmax(prob, axis=-1)).all()
     compare_route(r, oracle_route_per_head(q, k, w.block, w.top_p))
+
+
+@pytest.mark.parametrize("block,kb,causal", [(64, 64, True), (128, 64, False), (128, 64, True)],
+                         ids=["64-64-causal", "128-64", "128-64-causal"])
+def test_long_rows_route_and_sampled_attention(block, kb, causal):
+    # 700 key blocks (more than 512: the selection runs its rolled sort
+    # stages), with causal eligibility (row i ranks only its eligible
+    # blocks) and with 128-row query blocks over 64-key blocks; ragged tail.
+    N = 700 * 64 - 30
+    w = custom_workload(1, 2, N, 128, block, "bf16", 0.9, wid=720 + block + (1 if causal else 0))
+    q, k, v = _inputs(w)
+    pr = tbs.make_problem(q, block, causal=causal, key_block=kb)
+    assert pr.num_key_blocks == 700
+    ws = tbs.workspace(pr, DEV)
+    r = tbs.route(q, k, w.top_p, block, ws=ws, causal=causal, key_block=kb, return_prob=True)
+    wl = tbs.schedule(pr, r.row_cnt, ws)
+    o, lse = tbs.sparse_fwd(q, k, v, r.row_cnt, r.row_idx, block, work_list=wl, ws=ws, causal=causal,
+                            key_block=kb)
+    torch.cuda.synchronize()
+    nb, nbk = pr.num_blocks, pr.num_key_blocks
+    ref = oracle_route_per_head(q, k, block, w.top_p, causal=causal, key_block=kb)
+    cmp = compare_route(r, ref)
+    print(f"  ambiguous mismatches {cmp['ambiguous_mismatches']}", flush=True)
+    elig = oracle.causal_eligible(nb, nbk, block, kb) if causal else None
+    _ranked_correctly(r, None if elig is None else (lambda i: int(elig[i])))
+    rc = r.row_cnt.cpu().numpy()
+    rng = np.random.default_rng(11)
+    units = []
+    for h in range(pr.heads):
+        cand = {0, nb - 1, int(np.argmax(rc[0, h])), int(rng.integers(nb)), int(rng.integers(nb))}
+        units += [(0, h, i) for i in sorted(cand)]
+    units = routed_units(units, cmp)
+    e, le = compare_units(o, lse, q, k, v, block, units, cmp["gpu_mask"], q.dtype, causal=causal, key_block=kb)
+    print(f"  {len(units)} sampled blocks: max |O err| {e:.3e}, |LSE err| {le:.3e}", flush=True)
