@@ -19,10 +19,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
-__device__ __forceinline__ float bf16_bits_to_float(unsigned short b) {
-  return __uint_as_float(static_cast<unsigned>(b) << 16);
-}
-
 // Value held by the lane 32 positions away (lanes l and l^32 exchange).
 __device__ __forceinline__ float xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
