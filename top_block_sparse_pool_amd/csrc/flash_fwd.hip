@@ -1036,11 +1036,24 @@ __global__ __launch_bounds__(BQ * 2) void flash_fwd_f32(FwdParams p) {
     for (int t = 0; t < ui.ntiles; ++t) {
       const int key0 = ui.key0(p, t);
       __syncthreads();
-      for (int x = tid; x < kKeyTile * D; x += NT) {
-        const int r = x / D, c = x % D;
+      // 16-byte global loads (rows are 16-byte aligned: d is a multiple of
+      // 4 and the inputs 16-byte aligned), stored to the padded LDS rows
+      // element by element.
+      for (int x = tid; x < kKeyTile * D / 4; x += NT) {
+        const int r = (4 * x) / D, c = (4 * x) % D;
         const long long key = min(key0 + r, p.N - 1);
-        ks[r * LD + c] = ka[head_off + key * D + c];
-        vs[r * LD + c] = va[head_off + key * D + c];
+        const float4 k4 = *reinterpret_cast<const float4*>(ka + head_off + key * D + c);
+        const float4 v4 = *reinterpret_cast<const float4*>(va + head_off + key * D + c);
+        float* kd = ks + r * LD + c;
+        float* vd = vs + r * LD + c;
+        kd[0] = k4.x;
+        kd[1] = k4.y;
+        kd[2] = k4.z;
+        kd[3] = k4.w;
+        vd[0] = v4.x;
+        vd[1] = v4.y;
+        vd[2] = v4.z;
+        vd[3] = v4.w;
       }
       __syncthreads();
 
