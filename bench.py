@@ -103,6 +103,13 @@ def executed_flops(mask: np.ndarray, n_tokens: int, block: int, head_dim: int, c
     return int(4 * head_dim * int((mask.astype(np.int64) * pairs).sum()))
 
 
+def issued_flops(mask: np.ndarray, block: int, head_dim: int, key_block: int | None = None) -> int:
+    """4 * d * block * key_block per selected block pair: the FLOPs of full
+    (padded) blocks, ragged tails and causal cuts included."""
+    kb = key_block or block
+    return int(4 * head_dim * block * kb * int(mask.astype(np.int64).sum()))
+
+
 def union_tiles(mask: np.ndarray, n_tokens: int, block: int, key_block: int, group: int) -> int:
     """64-key tiles the attention kernel stages per launch: for every work item
     (`group` consecutive query blocks of one head) the union of its rows'
@@ -523,6 +530,7 @@ def main():
 
     mask = route_out.mask.cpu().numpy()
     flops = executed_flops(mask, N, blk, d, causal, kb)
+    flops_issued = issued_flops(mask, blk, d, kb)
     dense_flops = 4 * B * H * d * (N * (N + 1) // 2 if causal else N * N)
     # fraction of the eligible block pairs selected (the lower triangle under causal routing)
     if causal:
@@ -769,6 +777,7 @@ def main():
                    "top_p": w.top_p, "causal": causal, "sasa": bool(args.sasa), "sasa_union": bool(args.sasa_union),
                    "fp8_qk": fp8,
                    "head_window": hw, "density": density, "executed_tflop_per_step": flops / 1e12,
+                   "issued_tflop_per_step": flops_issued / 1e12,
                    "dense_tflop": dense_flops / 1e12,
                    "parallelism": f"one GPU's share of a {share['gpus']}-GPU split by heads" if share else "single GPU",
                    "share": share},

@@ -184,3 +184,12 @@ def test_summarize_pmc_means_and_clock(tmp_path):
     assert abs(m["clock_ghz"] - 1.75) < 1e-12
     assert abs(m["GRBM_GUI_ACTIVE"] - (2.0 * 1e6 * 8 + 1.5 * 2e6 * 8) / 2) < 1e-6
     assert out["ns::other(int)"][0] == 1
+
+
+def test_issued_flops_counts_full_blocks():
+    # two selected pairs in a ragged 2x2 block grid: issued counts both as full
+    # 64x64 blocks, executed only the valid tokens (N = 100: blocks of 64 and 36)
+    mask = np.array([[1, 0], [1, 1]], dtype=np.uint8)[None, None]
+    assert bench.issued_flops(mask, 64, 128) == 4 * 128 * 64 * 64 * 3
+    assert bench.issued_flops(mask, 128, 64, key_block=64) == 4 * 64 * 128 * 64 * 3
+    assert bench.executed_flops(mask, 100, 64, 128) == 4 * 128 * (64 * 64 + 36 * 64 + 36 * 36)
